@@ -1,0 +1,44 @@
+"""CPU oracle for paged KV storage and paged attention.
+
+TEST INFRASTRUCTURE ONLY.  This package is the plain, slow, obviously correct
+statement of what the paged hot path computes.  Only ``tests/``,
+``__graft_entry__.smoke()`` and the ``cpu_baseline`` leg of ``bench.py`` may
+import it.  The product library (``pagedattention_pkv_store_amd``) never
+imports, calls or links anything here, and this package imports nothing from
+the product: the two share no kernels, headers, helpers, tables or constants.
+The only code both sides use is the seeded input generator in ``synth/``,
+which holds none of the method's arithmetic.
+
+Everything is Python + NumPy.  Attention is computed in float64.
+
+Modules
+-------
+paging      block-table / slot model and the reference page allocator
+            (KV cache docs of TileInfer.jl, "Pages and block tables" and
+            "Growing, rolling back, releasing"; "KV Cache Management and
+            PagedAttention", Figures 1-3 and 6, "Return blocks after a request
+            ends"; Quail docs "KV", "Paged KV").
+planner     the sorted-adjacent-document prefix-sharing plan (Quail docs "KV",
+            "The sharing plan").
+attention   softmax attention over a sequence's logical K/V, gathered through
+            the block table ("KV Cache Management and PagedAttention",
+            "Compute attention over scattered KV", Figure 4).
+accounting  closed forms for KV bytes per position and per layer (TileInfer.jl
+            "Sizing" table and "INT8 cache"; ReKV section 2.1 eqs. (1)-(2) and
+            section 2.2 eq. (7)).
+
+Pinning status (what each function is checked against, in ``tests/``):
+  paging      P3 worked example (block counts, B=[P3,P0], C=[P1,P4], P5 growth),
+              invariants (truncate-then-reserve returns the same pages,
+              all-or-nothing OOM).
+  planner     P1 worked example (order/parent/shared, 1,916 vs 4,300 tokens);
+              brute force on tiny alphabets (maximal sharing, page identity).
+              The parent-link chase is pinned only by the page-identity
+              invariant: the pages' example never walks a link.
+  attention   closed forms, fp64 SDPA library special case, scalar brute force,
+              permutation invariance.
+  accounting  every cell of the TileInfer.jl sizing table and the ReKV byte
+              figures.
+"""
+
+from . import accounting, attention, paging, planner  # noqa: F401
