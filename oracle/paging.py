@@ -187,3 +187,18 @@ class Allocator:
     def _check(self, seq: int) -> None:
         if seq not in self._tables:
             raise InvalidArgument(f"unknown sequence {seq}")
+
+
+def store_rows(pool, slots: Sequence[int], rows) -> None:
+    """Write rows[t] ([Hkv][D]) into ``pool`` ([num_pages][Hkv][ps][D]) at slots[t].
+
+    The plain statement of TileInfer.jl's store_kv! ("Pages and block
+    tables"): each new token's vectors go to its slot's page and offset, for
+    every KV head.  Slots outside the pool are skipped.
+    """
+    page_size = pool.shape[2]
+    limit = pool.shape[0] * page_size
+    for t, slot in enumerate(slots):
+        slot = int(slot)
+        if 0 <= slot < limit:
+            pool[slot // page_size, :, slot % page_size, :] = rows[t]

@@ -1,0 +1,341 @@
+"""Paged KV storage and paged attention for MI355X (gfx950).
+
+A thin Python binding over libpkv.so (C ABI in include/pkv.h).  Every step of
+the path runs in the library: the host page allocator and prefix planner in
+C++, the KV scatter and the paged attention kernels in HIP.  This module only
+marshals arguments -- NumPy arrays for host calls, PyTorch tensors (device
+memory) and the current HIP stream for device calls -- and turns error codes
+into exceptions.  Nothing here computes a slot, a plan or an attention value.
+"""
+
+from __future__ import annotations
+
+import ctypes
+from dataclasses import dataclass
+from typing import Optional, Sequence, Tuple
+
+import numpy as np
+
+from . import _lib
+from ._lib import PKV_BF16, PKV_F32  # noqa: F401
+
+__all__ = [
+    "PkvError", "OutOfPagesError", "SharedPageError", "UnsupportedError",
+    "PoolDesc", "Allocator", "plan_prefix", "store_kv", "decode", "prefill_append",
+    "workspace_bytes", "validate_tables", "PKV_F32", "PKV_BF16",
+]
+
+
+class PkvError(RuntimeError):
+    """A libpkv call returned an error code."""
+
+    def __init__(self, code: int, message: str):
+        super().__init__(f"[{code}] {message}")
+        self.code = code
+
+
+class OutOfPagesError(PkvError):
+    pass
+
+
+class SharedPageError(PkvError):
+    pass
+
+
+class UnsupportedError(PkvError):
+    pass
+
+
+class BufferTooSmallError(PkvError):
+    pass
+
+
+_ERRORS = {
+    _lib.PKV_ERR_OUT_OF_PAGES: OutOfPagesError,
+    _lib.PKV_ERR_SHARED_PAGE: SharedPageError,
+    _lib.PKV_ERR_UNSUPPORTED: UnsupportedError,
+    _lib.PKV_ERR_BUFFER_TOO_SMALL: BufferTooSmallError,
+}
+
+
+def _check(rc: int) -> None:
+    if rc != _lib.PKV_OK:
+        raise _ERRORS.get(rc, PkvError)(rc, _lib.last_error())
+
+
+def _i32(a) -> np.ndarray:
+    return np.ascontiguousarray(a, dtype=np.int32)
+
+
+def _ptr(a: np.ndarray, ctype):
+    return a.ctypes.data_as(ctypes.POINTER(ctype))
+
+
+# ---------------------------------------------------------------------------
+# host: allocator and planner
+# ---------------------------------------------------------------------------
+class Allocator:
+    """Host page allocator (pkv_alloc_*): free stack, block tables, refcounts."""
+
+    def __init__(self, num_pages: int, page_size: int, free_order: Optional[Sequence[int]] = None):
+        L = _lib.lib()
+        handle = ctypes.c_void_p()
+        if free_order is None:
+            _check(L.pkv_alloc_create(num_pages, page_size, None, ctypes.byref(handle)))
+        else:
+            order = _i32(free_order)
+            if order.size != num_pages:
+                raise PkvError(_lib.PKV_ERR_INVALID_ARG, "free_order must have num_pages entries")
+            _check(L.pkv_alloc_create(num_pages, page_size, _ptr(order, ctypes.c_int32),
+                                      ctypes.byref(handle)))
+        self._h = handle
+        self._L = L
+        self.num_pages = num_pages
+        self.page_size = page_size
+
+    def close(self) -> None:
+        if self._h:
+            self._L.pkv_alloc_destroy(self._h)
+            self._h = ctypes.c_void_p()
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+    def seq_new(self) -> int:
+        out = ctypes.c_int32()
+        _check(self._L.pkv_seq_new(self._h, ctypes.byref(out)))
+        return out.value
+
+    def reserve(self, seq: int, n: int) -> None:
+        _check(self._L.pkv_reserve(self._h, seq, n))
+
+    def truncate(self, seq: int, n_keep: int) -> None:
+        _check(self._L.pkv_truncate(self._h, seq, n_keep))
+
+    def release(self, seq: int) -> None:
+        _check(self._L.pkv_release(self._h, seq))
+
+    def share_prefix(self, child: int, parent: int, n_tokens: int) -> None:
+        _check(self._L.pkv_share_prefix(self._h, child, parent, n_tokens))
+
+    def seq_len(self, seq: int) -> int:
+        out = ctypes.c_int32()
+        _check(self._L.pkv_seq_len(self._h, seq, ctypes.byref(out)))
+        return out.value
+
+    def num_free(self) -> int:
+        out = ctypes.c_int32()
+        _check(self._L.pkv_num_free(self._h, ctypes.byref(out)))
+        return out.value
+
+    def refcount(self, page: int) -> int:
+        out = ctypes.c_int32()
+        _check(self._L.pkv_page_refcount(self._h, page, ctypes.byref(out)))
+        return out.value
+
+    def num_blocks(self, seq: int) -> int:
+        out = ctypes.c_int32()
+        _check(self._L.pkv_seq_num_blocks(self._h, seq, ctypes.byref(out)))
+        return out.value
+
+    def block_table(self, seq: int) -> np.ndarray:
+        n = self.num_blocks(seq)
+        return self.block_tables([seq], n)[0]
+
+    def block_tables(self, seqs: Sequence[int], stride: int,
+                     out: Optional[np.ndarray] = None) -> np.ndarray:
+        seqs_a = _i32(seqs)
+        if out is None:
+            out = np.zeros((len(seqs_a), stride), dtype=np.int32)
+        if out.dtype != np.int32 or not out.flags.c_contiguous or out.shape != (len(seqs_a), stride):
+            raise PkvError(_lib.PKV_ERR_INVALID_ARG, "out must be a C-contiguous int32 [n][stride]")
+        _check(self._L.pkv_block_tables(self._h, _ptr(seqs_a, ctypes.c_int32), len(seqs_a),
+                                        stride, _ptr(out, ctypes.c_int32)))
+        return out
+
+    def prepare_step(self, seqs: Sequence[int], n_new: Sequence[int], bt_stride: int,
+                     slots_out: Optional[np.ndarray] = None, bt_out: Optional[np.ndarray] = None,
+                     lens_out: Optional[np.ndarray] = None):
+        """Reserve n_new[b] positions for each seqs[b] and return (slots of the
+        new positions packed in b order, block tables [n][bt_stride], new
+        lengths).  Preallocated (e.g. pinned) output arrays may be passed.
+        bt_stride 0 skips the block-table export."""
+        seqs_a = _i32(seqs)
+        n_a = _i32(n_new)
+        n = seqs_a.size
+        total = int(n_a.sum())
+        if slots_out is None:
+            slots_out = np.empty(total, np.int64)
+        if bt_out is None:
+            bt_out = np.empty((n, bt_stride), np.int32)
+        if lens_out is None:
+            lens_out = np.empty(n, np.int32)
+        if (slots_out.dtype != np.int64 or slots_out.size < total or bt_out.dtype != np.int32
+                or bt_out.size < n * bt_stride or lens_out.dtype != np.int32 or lens_out.size < n
+                or not (slots_out.flags.c_contiguous and bt_out.flags.c_contiguous
+                        and lens_out.flags.c_contiguous)):
+            raise PkvError(_lib.PKV_ERR_INVALID_ARG, "prepare_step: output arrays too small or wrong dtype")
+        bt_ptr = _ptr(bt_out, ctypes.c_int32) if bt_stride > 0 else None  # 0: no tables
+        _check(self._L.pkv_prepare_step(self._h, _ptr(seqs_a, ctypes.c_int32), n,
+                                        _ptr(n_a, ctypes.c_int32), bt_stride,
+                                        _ptr(slots_out, ctypes.c_int64), bt_ptr,
+                                        _ptr(lens_out, ctypes.c_int32)))
+        return slots_out[:total], bt_out.reshape(-1)[: n * bt_stride].reshape(n, bt_stride), lens_out[:n]
+
+    def slots(self, seq: int, start: int, n: int, out: Optional[np.ndarray] = None) -> np.ndarray:
+        if out is None:
+            out = np.empty(n, dtype=np.int64)
+        if out.dtype != np.int64 or not out.flags.c_contiguous or out.size < n:
+            raise PkvError(_lib.PKV_ERR_INVALID_ARG, "out must be a C-contiguous int64 array")
+        _check(self._L.pkv_slots(self._h, seq, start, n, _ptr(out, ctypes.c_int64)))
+        return out[:n]
+
+
+def plan_prefix(docs_tokens: Sequence[np.ndarray], page_size: int
+                ) -> Tuple[np.ndarray, np.ndarray, np.ndarray]:
+    """Sharing plan (order, parent, shared) of documents given as token arrays.
+
+    parent[d] = -1 for a document that shares nothing.
+    """
+    n = len(docs_tokens)
+    lens = np.array([len(d) for d in docs_tokens], dtype=np.int64)
+    offsets = np.zeros(n + 1, dtype=np.int64)
+    offsets[1:] = np.cumsum(lens)
+    tokens = (np.concatenate([np.asarray(d, dtype=np.int32) for d in docs_tokens])
+              if n else np.zeros(0, np.int32))
+    tokens = _i32(tokens)
+    return plan_prefix_packed(tokens, offsets, page_size)
+
+
+def plan_prefix_packed(tokens: np.ndarray, offsets: np.ndarray, page_size: int
+                       ) -> Tuple[np.ndarray, np.ndarray, np.ndarray]:
+    tokens = _i32(tokens)
+    offsets = np.ascontiguousarray(offsets, dtype=np.int64)
+    n = offsets.size - 1
+    order = np.empty(n, np.int32)
+    parent = np.empty(n, np.int32)
+    shared = np.empty(n, np.int32)
+    tok_ptr = _ptr(tokens, ctypes.c_int32) if tokens.size else None
+    _check(_lib.lib().pkv_plan_prefix(tok_ptr, _ptr(offsets, ctypes.c_int64), n, page_size,
+                                      _ptr(order, ctypes.c_int32), _ptr(parent, ctypes.c_int32),
+                                      _ptr(shared, ctypes.c_int32)))
+    return order, parent, shared
+
+
+# ---------------------------------------------------------------------------
+# device: store_kv / decode / prefill_append on PyTorch tensors
+# ---------------------------------------------------------------------------
+@dataclass(frozen=True)
+class PoolDesc:
+    dtype: int          # PKV_F32 or PKV_BF16
+    num_pages: int
+    page_size: int
+    num_kv_heads: int
+    head_dim: int
+
+    def c(self) -> _lib.PoolDescC:
+        return _lib.PoolDescC(self.dtype, self.num_pages, self.page_size, self.num_kv_heads,
+                              self.head_dim)
+
+    @property
+    def pool_shape(self) -> Tuple[int, int, int, int]:
+        return (self.num_pages, self.num_kv_heads, self.page_size, self.head_dim)
+
+    def torch_dtype(self):
+        import torch
+        return torch.bfloat16 if self.dtype == PKV_BF16 else torch.float32
+
+
+def _dev(t, name, dtype=None):
+    import torch
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a device (HIP) tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if dtype is not None and t.dtype != dtype:
+        raise TypeError(f"{name} must have dtype {dtype}, got {t.dtype}")
+    return ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream):
+    import torch
+    s = torch.cuda.current_stream() if stream is None else stream
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def store_kv(desc: PoolDesc, k_pool, v_pool, k_new, v_new, slots, stream=None) -> None:
+    """Scatter new K/V rows [T][Hkv][D] into the pools at int64 ``slots``."""
+    import torch
+    dt = desc.torch_dtype()
+    n = int(slots.numel())
+    _check(_lib.lib().pkv_store_kv(
+        ctypes.byref(desc.c()), _dev(k_pool, "k_pool", dt), _dev(v_pool, "v_pool", dt),
+        _dev(k_new, "k_new", dt), _dev(v_new, "v_new", dt), _dev(slots, "slots", torch.int64),
+        n, _stream(stream)))
+
+
+def workspace_bytes(desc: PoolDesc, n_seqs: int, num_q_heads: int, max_q_per_seq: int,
+                    max_seq_len: int) -> int:
+    return int(_lib.lib().pkv_workspace_bytes(ctypes.byref(desc.c()), n_seqs, num_q_heads,
+                                              max_q_per_seq, max_seq_len))
+
+
+def _workspace(ws, need):
+    import torch
+    if need == 0:
+        return ctypes.c_void_p(ws.data_ptr() if ws is not None else 0), 0
+    if ws is None:
+        raise PkvError(_lib.PKV_ERR_BUFFER_TOO_SMALL, f"workspace of {need} bytes required")
+    _dev(ws, "workspace")
+    return ctypes.c_void_p(ws.data_ptr()), ws.numel() * ws.element_size()
+
+
+def decode(desc: PoolDesc, k_pool, v_pool, q, block_tables, seq_lens, max_seq_len: int,
+           scale: float, out, workspace=None, stream=None) -> None:
+    """Paged decode: q [B][Hq][D] -> out [B][Hq][D] (one new query per sequence)."""
+    import torch
+    dt = desc.torch_dtype()
+    n_seqs, hq, _ = q.shape
+    need = workspace_bytes(desc, n_seqs, hq, 1, max_seq_len)
+    ws_ptr, ws_bytes = _workspace(workspace, need)
+    _check(_lib.lib().pkv_decode(
+        ctypes.byref(desc.c()), _dev(k_pool, "k_pool", dt), _dev(v_pool, "v_pool", dt),
+        _dev(q, "q", dt), n_seqs, hq, _dev(block_tables, "block_tables", torch.int32),
+        int(block_tables.shape[1]), _dev(seq_lens, "seq_lens", torch.int32), max_seq_len,
+        float(scale), _dev(out, "out", dt), ws_ptr, ws_bytes, _stream(stream)))
+
+
+def prefill_append(desc: PoolDesc, k_pool, v_pool, q, cu_q, block_tables, seq_lens,
+                   max_q_per_seq: int, max_seq_len: int, scale: float, out, workspace=None,
+                   stream=None) -> None:
+    """Paged prefill/append over packed queries q [Tq][Hq][D] -> out [Tq][Hq][D]."""
+    import torch
+    dt = desc.torch_dtype()
+    total_q, hq, _ = q.shape
+    n_seqs = int(cu_q.numel()) - 1
+    need = workspace_bytes(desc, n_seqs, hq, max_q_per_seq, max_seq_len)
+    ws_ptr, ws_bytes = _workspace(workspace, need)
+    _check(_lib.lib().pkv_prefill_append(
+        ctypes.byref(desc.c()), _dev(k_pool, "k_pool", dt), _dev(v_pool, "v_pool", dt),
+        _dev(q, "q", dt), total_q, _dev(cu_q, "cu_q", torch.int32), n_seqs, hq,
+        _dev(block_tables, "block_tables", torch.int32), int(block_tables.shape[1]),
+        _dev(seq_lens, "seq_lens", torch.int32), max_q_per_seq, max_seq_len, float(scale),
+        _dev(out, "out", dt), ws_ptr, ws_bytes, _stream(stream)))
+
+
+def validate_tables(desc: PoolDesc, block_tables: np.ndarray, seq_lens: np.ndarray,
+                    cu_q: Optional[np.ndarray] = None, max_q_per_seq: int = 0) -> None:
+    """Host check of block tables / lengths / cu_q before a device call."""
+    bt = _i32(block_tables)
+    sl = _i32(seq_lens)
+    cq = _i32(cu_q) if cu_q is not None else None
+    n_seqs = sl.size
+    stride = bt.shape[1] if bt.ndim == 2 else 0
+    _check(_lib.lib().pkv_validate_tables(
+        ctypes.byref(desc.c()), _ptr(bt, ctypes.c_int32), n_seqs, stride, _ptr(sl, ctypes.c_int32),
+        _ptr(cq, ctypes.c_int32) if cq is not None else None, max_q_per_seq))

@@ -1,0 +1,714 @@
+// Device half of libpkv: the KV scatter into the page pools and paged
+// attention (decode and prefill/append) for gfx950 (CDNA4, wave64).
+//
+// What is computed (see include/pkv.h for the exact contracts):
+//  * store_kv: each new token's K and V vectors go to the pools at their slot
+//    (TileInfer.jl docs "KV cache", "Pages and block tables": store_kv!).
+//  * attention: a query at position p attends to positions 0..p of its own
+//    sequence, read in place through the block table ("KV Cache Management
+//    and PagedAttention", "Compute attention over scattered KV", Figure 4).
+//
+// Kernel design (MI355X-first, not a translation of any page's design):
+//  * One workgroup (4 waves) owns one (sequence, KV head, query tile, KV
+//    split).  Its query rows are (query, head-in-group) pairs of one GQA
+//    group, so every K/V byte a workgroup reads serves the whole group.
+//  * K/V are staged 64 positions at a time in LDS, gathered page by page
+//    through the block table with 16-byte coalesced loads; the next tile's
+//    loads are in flight while the current tile is computed.
+//  * Scores are computed transposed, S^T = K Q^T, on MFMA (bf16:
+//    v_mfma_f32_16x16x32_bf16; fp32: v_mfma_f32_16x16x4_f32).  In that layout
+//    each lane holds one query row and four key positions, so the running
+//    max / sum of the online softmax need only in-lane work plus two
+//    wavefront shuffles, and the probabilities are already in the MFMA
+//    operand layout of O^T = V^T P^T (bf16: v_mfma_f32_16x16x16_bf16).  V is
+//    read transposed out of LDS.
+//  * Waves either split the query tile (long prefill tiles) or split the
+//    staged keys (decode, few rows); partial softmax states of waves are
+//    combined in LDS.  Long contexts are split across workgroups at fixed
+//    logical positions and merged with log-sum-exp by a second kernel, so
+//    the result depends only on the logical sequence, never on which
+//    physical pages hold it.
+
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cmath>
+#include <cstdint>
+#include <string>
+
+#include "../../include/pkv.h"
+#include "status.h"
+
+using pkv::fail;
+
+namespace {
+
+constexpr int kWave = 64;
+constexpr int kThreads = 256;   // 4 waves
+constexpr int kTileKeys = 64;   // positions staged in LDS per iteration
+constexpr int kTargetWorkgroups = 2048;
+constexpr int kMinSplitKeys = 256;
+
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+
+__device__ __forceinline__ uint16_t float_to_bf16_bits(float f) {
+  uint32_t u = __float_as_uint(f);
+  if ((u & 0x7fffffffu) > 0x7f800000u) return 0x7fc0;  // NaN stays NaN
+  u += 0x7fffu + ((u >> 16) & 1u);                      // round to nearest even
+  return static_cast<uint16_t>(u >> 16);
+}
+
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// Element storage: float for fp32, uint16_t bit patterns for bf16.
+template <typename T> struct Elem;
+template <> struct Elem<float> {
+  static constexpr int kQkPerMfma = 1;  // k-elements per lane per QK MFMA
+};
+template <> struct Elem<uint16_t> {
+  static constexpr int kQkPerMfma = 8;
+};
+
+struct AttnArgs {
+  const void* q;
+  void* out;
+  const void* k_pool;
+  const void* v_pool;
+  const int32_t* block_tables;
+  const int32_t* seq_lens;
+  const int32_t* cu_q;  // nullptr: decode, sequence b owns query row b
+  float* ws_o;          // split partials [tok][Hq][n_splits][D], or nullptr
+  float* ws_ml;         // [tok][Hq][n_splits][2] = (running max, sum)
+  int32_t bt_stride;
+  int32_t n_seqs;
+  int32_t num_q_heads;
+  int32_t num_kv_heads;
+  int32_t group;
+  int32_t num_pages;
+  int32_t page_size;
+  int32_t ps_shift;     // log2(page_size), or -1
+  int32_t total_q;
+  int32_t ws_tokens;    // rows of the split workspace: n_seqs * max_q_per_seq
+  int32_t split_len;    // positions per KV split (multiple of kTileKeys)
+  int32_t n_splits;
+  float scale_log2;     // softmax scale * log2(e)
+};
+
+// Elements per LDS row of a staged K/V tile: a 16-byte pad staggers rows
+// across banks; 512-byte rows go unpadded so two tiles fit in 64 KiB.
+template <typename T, int D>
+constexpr int row_stride() {
+  return D + (D * static_cast<int>(sizeof(T)) >= 512 ? 0 : 16 / static_cast<int>(sizeof(T)));
+}
+
+// LDS bytes: two staged tiles (K, V), reused by the epilogue.
+template <typename T, int D>
+constexpr int lds_bytes() {
+  constexpr int rs = row_stride<T, D>() * static_cast<int>(sizeof(T));
+  constexpr int tiles = 2 * kTileKeys * rs;
+  constexpr int epi = 64 * (D + 4) * 4 + 2 * 64 * 4;
+  return tiles > epi ? tiles : epi;
+}
+
+// RB: 16-row query blocks per workgroup; KG: waves sharing one row block,
+// each taking kTileKeys / KG of the staged positions.  RB * KG == 4.
+template <typename T, int D, int RB, int KG>
+__global__ __launch_bounds__(kThreads) void paged_attention_kernel(AttnArgs args) {
+  static_assert(RB * KG == kThreads / kWave, "4 waves");
+  constexpr int kEs = sizeof(T);
+  constexpr int kRowStride = row_stride<T, D>();
+  constexpr int kChunksPerRow = D * kEs / 16;        // 16-byte chunks per K/V row
+  constexpr int kChunks = kTileKeys * kChunksPerRow / kThreads;  // per thread per pool
+  constexpr int kDl = D / 4;                         // dims per lane in the QK operands
+  constexpr int kQkMfmas = kDl / Elem<T>::kQkPerMfma;
+  constexpr int kKeysPerWave = kTileKeys / KG;
+  constexpr int kBlocks = kKeysPerWave / 16;         // 16-position MFMA blocks per wave
+  constexpr int kDimBlocks = D / 16;
+  constexpr int kTileRows = 16 * RB;
+  static_assert(kChunks * kThreads == kTileKeys * kChunksPerRow, "even split of the tile");
+
+  extern __shared__ __align__(16) char smem[];
+  T* ks = reinterpret_cast<T*>(smem);
+  T* vs = ks + kTileKeys * kRowStride;
+
+  const int tid = threadIdx.x;
+  const int lane = tid & (kWave - 1);
+  const int wave = tid / kWave;
+  const int rb = wave / KG;
+  const int kg = wave % KG;
+  const int lrow = lane & 15;   // MFMA column: query row within the 16-row block
+  const int lgrp = lane >> 4;   // MFMA k/row group 0..3
+
+  const int hkv = args.num_kv_heads;
+  const int b = blockIdx.z / hkv;
+  const int g = blockIdx.z % hkv;
+  const int group = args.group;
+
+  int q0, n_b;
+  if (args.cu_q) {
+    q0 = args.cu_q[b];
+    n_b = args.cu_q[b + 1] - q0;
+  } else {
+    q0 = b;
+    n_b = 1;
+  }
+  const int rows_total = n_b * group;
+  const int row0 = blockIdx.y * kTileRows;
+  if (row0 >= rows_total) return;
+  const int seq_len = args.seq_lens[b];
+  const int start = seq_len - n_b;                    // position of new query 0
+  const int row_last = min(row0 + kTileRows, rows_total) - 1;
+  const int kv_end = start + row_last / group + 1;    // positions this tile can see
+  const int k_lo = blockIdx.x * args.split_len;
+  if (k_lo >= kv_end) return;
+  const int k_hi = min(k_lo + args.split_len, kv_end);
+
+  const int ps = args.page_size;
+  const int ps_shift = args.ps_shift;
+  const int32_t* bt_row = args.block_tables + static_cast<int64_t>(b) * args.bt_stride;
+  const T* kpool = static_cast<const T*>(args.k_pool);
+  const T* vpool = static_cast<const T*>(args.v_pool);
+
+  // ---- this lane's query row (B operand of S^T = K Q^T) ----
+  const int my_row = row0 + rb * 16 + lrow;           // row within (sequence, KV head)
+  const bool row_ok = my_row < rows_total;
+  const int my_qpos = start + (row_ok ? my_row / group : rows_total / group);
+  T qv[kDl];
+  {
+    const int qi = my_row / group;
+    const int hh = my_row - qi * group;
+    const int tok = q0 + qi;
+    if (row_ok && tok < args.total_q) {
+      const T* src = static_cast<const T*>(args.q) +
+                     (static_cast<int64_t>(tok) * args.num_q_heads + g * group + hh) * D +
+                     lgrp * kDl;
+#pragma unroll
+      for (int c = 0; c < kDl * kEs / 16; ++c)
+        *reinterpret_cast<uint4*>(&qv[c * 16 / kEs]) = reinterpret_cast<const uint4*>(src)[c];
+    } else {
+#pragma unroll
+      for (int c = 0; c < kDl; ++c) qv[c] = T(0);
+    }
+  }
+
+  // ---- global -> register staging of one tile of K and V ----
+  uint4 kreg[kChunks], vreg[kChunks];
+  auto load_tile = [&](int base) {
+#pragma unroll
+    for (int c = 0; c < kChunks; ++c) {
+      const int chunk = c * kThreads + tid;
+      const int row = chunk / kChunksPerRow;
+      const int part = chunk - row * kChunksPerRow;
+      const int pos = base + row;
+      uint4 kx = make_uint4(0, 0, 0, 0), vx = make_uint4(0, 0, 0, 0);
+      if (pos < k_hi) {
+        const int blk = ps_shift >= 0 ? (pos >> ps_shift) : pos / ps;
+        const int off = pos - blk * ps;
+        if (blk < args.bt_stride) {
+          const int page = bt_row[blk];
+          if (static_cast<unsigned>(page) < static_cast<unsigned>(args.num_pages)) {
+            const int64_t e = ((static_cast<int64_t>(page) * hkv + g) * ps + off) * D +
+                              part * (16 / kEs);
+            kx = *reinterpret_cast<const uint4*>(kpool + e);
+            vx = *reinterpret_cast<const uint4*>(vpool + e);
+          }
+        }
+      }
+      kreg[c] = kx;
+      vreg[c] = vx;
+    }
+  };
+  auto store_tile = [&]() {
+#pragma unroll
+    for (int c = 0; c < kChunks; ++c) {
+      const int chunk = c * kThreads + tid;
+      const int row = chunk / kChunksPerRow;
+      const int part = chunk - row * kChunksPerRow;
+      *reinterpret_cast<uint4*>(ks + row * kRowStride + part * (16 / kEs)) = kreg[c];
+      *reinterpret_cast<uint4*>(vs + row * kRowStride + part * (16 / kEs)) = vreg[c];
+    }
+  };
+
+  // ---- online softmax state (log2 domain) ----
+  float m_run = -INFINITY;
+  float l_part = 0.f;                 // this lane's share of the row sum
+  f32x4 o_acc[kDimBlocks];            // O^T: lane holds row lrow, dims 4*lgrp+i of each block
+#pragma unroll
+  for (int d = 0; d < kDimBlocks; ++d) o_acc[d] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  load_tile(k_lo);
+  for (int base = k_lo; base < k_hi; base += kTileKeys) {
+    __syncthreads();                  // previous tile fully consumed
+    store_tile();
+    __syncthreads();
+    if (base + kTileKeys < k_hi) load_tile(base + kTileKeys);
+
+    const int wbase = base + kg * kKeysPerWave;
+    if (wbase >= k_hi) continue;      // nothing valid for this wave in this tile
+
+    // S^T blocks: rows = 16 key positions, columns = 16 query rows.
+    f32x4 s[kBlocks];
+#pragma unroll
+    for (int nb = 0; nb < kBlocks; ++nb) {
+      s[nb] = f32x4{0.f, 0.f, 0.f, 0.f};
+      const T* krow = ks + (kg * kKeysPerWave + nb * 16 + lrow) * kRowStride + lgrp * kDl;
+#pragma unroll
+      for (int kk = 0; kk < kQkMfmas; ++kk) {
+        if constexpr (sizeof(T) == 2) {
+          const bf16x8 a = *reinterpret_cast<const bf16x8*>(krow + kk * 8);
+          const bf16x8 bq = *reinterpret_cast<const bf16x8*>(&qv[kk * 8]);
+          s[nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, bq, s[nb], 0, 0, 0);
+        } else {
+          s[nb] = __builtin_amdgcn_mfma_f32_16x16x4f32(krow[kk], qv[kk], s[nb], 0, 0, 0);
+        }
+      }
+    }
+
+    // Mask, then the running max over this wave's positions.
+    float mx = -INFINITY;
+#pragma unroll
+    for (int nb = 0; nb < kBlocks; ++nb) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int pos = wbase + nb * 16 + lgrp * 4 + i;
+        const float x = s[nb][i] * args.scale_log2;
+        s[nb][i] = (pos < k_hi && pos <= my_qpos) ? x : -INFINITY;
+        mx = fmaxf(mx, s[nb][i]);
+      }
+    }
+    mx = fmaxf(mx, __shfl_xor(mx, 16));
+    mx = fmaxf(mx, __shfl_xor(mx, 32));
+    const float m_new = fmaxf(m_run, mx);
+    const float m_use = m_new == -INFINITY ? 0.f : m_new;
+    const float alpha = fast_exp2(m_run - m_use);
+    m_run = m_new;
+    float psum = 0.f;
+#pragma unroll
+    for (int nb = 0; nb < kBlocks; ++nb) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        s[nb][i] = fast_exp2(s[nb][i] - m_use);
+        psum += s[nb][i];
+      }
+    }
+    l_part = l_part * alpha + psum;
+#pragma unroll
+    for (int d = 0; d < kDimBlocks; ++d) o_acc[d] *= alpha;
+
+    // O^T += V^T P^T, 16 positions per step.
+#pragma unroll
+    for (int nb = 0; nb < kBlocks; ++nb) {
+      const T* vblk = vs + (kg * kKeysPerWave + nb * 16 + lgrp * 4) * kRowStride + lrow;
+      if constexpr (sizeof(T) == 2) {
+        i16x4 pb;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) pb[i] = static_cast<short>(float_to_bf16_bits(s[nb][i]));
+#pragma unroll
+        for (int d = 0; d < kDimBlocks; ++d) {
+          i16x4 a;
+#pragma unroll
+          for (int i = 0; i < 4; ++i) a[i] = static_cast<short>(vblk[i * kRowStride + d * 16]);
+          o_acc[d] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a, pb, o_acc[d], 0, 0, 0);
+        }
+      } else {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+#pragma unroll
+          for (int d = 0; d < kDimBlocks; ++d)
+            o_acc[d] = __builtin_amdgcn_mfma_f32_16x16x4f32(vblk[i * kRowStride + d * 16],
+                                                            s[nb][i], o_acc[d], 0, 0, 0);
+        }
+      }
+    }
+  }
+
+  // ---- epilogue: combine the KG waves of each row block in LDS ----
+  float l_row = l_part;
+  l_row += __shfl_xor(l_row, 16);
+  l_row += __shfl_xor(l_row, 32);
+  __syncthreads();                    // tiles no longer needed
+  constexpr int kEpiStride = D + 4;
+  float* eo = reinterpret_cast<float*>(smem);               // [KG][kTileRows][kEpiStride]
+  float* em = eo + 64 * kEpiStride;                         // [KG][kTileRows]
+  float* el = em + 64;
+  {
+    const int erow = kg * kTileRows + rb * 16 + lrow;
+#pragma unroll
+    for (int d = 0; d < kDimBlocks; ++d)
+      *reinterpret_cast<f32x4*>(eo + erow * kEpiStride + d * 16 + lgrp * 4) = o_acc[d];
+    if (lgrp == 0) {
+      em[erow] = m_run;
+      el[erow] = l_row;
+    }
+  }
+  __syncthreads();
+
+  const bool split_mode = args.n_splits > 1;
+  constexpr int kQuads = D / 4;
+  for (int idx = tid; idx < kTileRows * kQuads; idx += kThreads) {
+    const int tr = idx / kQuads;
+    const int d4 = (idx - tr * kQuads) * 4;
+    const int r = row0 + tr;
+    if (r >= rows_total) continue;
+    const int qi = r / group;
+    const int tok = q0 + qi;
+    if (tok >= args.total_q) continue;
+    const int h = g * group + (r - qi * group);
+    float mmax = -INFINITY;
+#pragma unroll
+    for (int w = 0; w < KG; ++w) mmax = fmaxf(mmax, em[w * kTileRows + tr]);
+    const float mref = mmax == -INFINITY ? 0.f : mmax;
+    f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
+    float lsum = 0.f;
+#pragma unroll
+    for (int w = 0; w < KG; ++w) {
+      const float wt = fast_exp2(em[w * kTileRows + tr] - mref);
+      lsum += wt * el[w * kTileRows + tr];
+      acc += wt * *reinterpret_cast<const f32x4*>(eo + (w * kTileRows + tr) * kEpiStride + d4);
+    }
+    const int64_t orow = static_cast<int64_t>(tok) * args.num_q_heads + h;
+    if (split_mode) {
+      if (tok >= args.ws_tokens) continue;
+      const int64_t slot = orow * args.n_splits + blockIdx.x;
+      *reinterpret_cast<f32x4*>(args.ws_o + slot * D + d4) = acc;
+      if (d4 == 0) {
+        args.ws_ml[slot * 2] = mmax;
+        args.ws_ml[slot * 2 + 1] = lsum;
+      }
+    } else {
+      const float inv = lsum > 0.f ? 1.f / lsum : 0.f;
+      acc *= inv;
+      if constexpr (sizeof(T) == 2) {
+        uint16_t* o = static_cast<uint16_t*>(args.out) + orow * D + d4;
+        uint2 packed;
+        packed.x = float_to_bf16_bits(acc[0]) | (static_cast<uint32_t>(float_to_bf16_bits(acc[1])) << 16);
+        packed.y = float_to_bf16_bits(acc[2]) | (static_cast<uint32_t>(float_to_bf16_bits(acc[3])) << 16);
+        *reinterpret_cast<uint2*>(o) = packed;
+      } else {
+        *reinterpret_cast<f32x4*>(static_cast<float*>(args.out) + orow * D + d4) = acc;
+      }
+    }
+  }
+}
+
+// Log-sum-exp merge of the KV splits of one (query, head) row.  Grid:
+// (num_q_heads, max_q_per_seq, n_seqs), one wave per row.
+template <typename T, int D>
+__global__ __launch_bounds__(kWave) void merge_splits_kernel(AttnArgs args) {
+  const int h = blockIdx.x;
+  const int qi = blockIdx.y;
+  const int b = blockIdx.z;
+  int q0, n_b;
+  if (args.cu_q) {
+    q0 = args.cu_q[b];
+    n_b = args.cu_q[b + 1] - q0;
+  } else {
+    q0 = b;
+    n_b = 1;
+  }
+  if (qi >= n_b) return;
+  const int tok = q0 + qi;
+  if (tok >= args.total_q || tok >= args.ws_tokens) return;
+  const int qpos = args.seq_lens[b] - n_b + qi;
+  // Splits that hold at least one position this query sees.
+  const int ns = qpos < 0 ? 0 : min(args.n_splits, qpos / args.split_len + 1);
+  const int64_t orow = static_cast<int64_t>(tok) * args.num_q_heads + h;
+  const int64_t base = orow * args.n_splits;
+  float mmax = -INFINITY;
+  for (int s = 0; s < ns; ++s) mmax = fmaxf(mmax, args.ws_ml[(base + s) * 2]);
+  const float mref = mmax == -INFINITY ? 0.f : mmax;
+  constexpr int kPer = D / kWave;
+  float acc[kPer];
+#pragma unroll
+  for (int j = 0; j < kPer; ++j) acc[j] = 0.f;
+  float lsum = 0.f;
+  for (int s = 0; s < ns; ++s) {
+    const float wt = fast_exp2(args.ws_ml[(base + s) * 2] - mref);
+    lsum += wt * args.ws_ml[(base + s) * 2 + 1];
+    const float* o = args.ws_o + (base + s) * D;
+#pragma unroll
+    for (int j = 0; j < kPer; ++j) acc[j] += wt * o[threadIdx.x * kPer + j];
+  }
+  const float inv = lsum > 0.f ? 1.f / lsum : 0.f;
+#pragma unroll
+  for (int j = 0; j < kPer; ++j) {
+    const float v = acc[j] * inv;
+    const int64_t e = orow * D + threadIdx.x * kPer + j;
+    if constexpr (sizeof(T) == 2)
+      static_cast<uint16_t*>(args.out)[e] = float_to_bf16_bits(v);
+    else
+      static_cast<float*>(args.out)[e] = v;
+  }
+}
+
+// KV scatter: one thread per 16-byte chunk of a (token, KV head) row, K and
+// V handled by the two halves of the grid.
+template <int kEs>
+__global__ __launch_bounds__(kThreads) void store_kv_kernel(
+    char* __restrict__ k_pool, char* __restrict__ v_pool, const char* __restrict__ k_new,
+    const char* __restrict__ v_new, const int64_t* __restrict__ slots, int32_t n_tokens,
+    int32_t hkv, int32_t head_dim, int32_t page_size, int32_t ps_shift, int64_t pool_slots) {
+  const int chunks_per_row = head_dim * kEs / 16;
+  const int64_t per_pool = static_cast<int64_t>(n_tokens) * hkv * chunks_per_row;
+  int64_t idx = static_cast<int64_t>(blockIdx.x) * kThreads + threadIdx.x;
+  if (idx >= 2 * per_pool) return;
+  const bool is_v = idx >= per_pool;
+  if (is_v) idx -= per_pool;
+  const int part = static_cast<int>(idx % chunks_per_row);
+  const int64_t row = idx / chunks_per_row;         // token * hkv + g
+  const int64_t t = row / hkv;
+  const int g = static_cast<int>(row - t * hkv);
+  const int64_t slot = slots[t];
+  if (slot < 0 || slot >= pool_slots) return;
+  const int64_t page = ps_shift >= 0 ? (slot >> ps_shift) : slot / page_size;
+  const int64_t off = slot - page * page_size;
+  const int64_t row_bytes = static_cast<int64_t>(head_dim) * kEs;
+  const int64_t dst = ((page * hkv + g) * page_size + off) * row_bytes + part * 16;
+  const int64_t src = row * row_bytes + part * 16;
+  const uint4 val = *reinterpret_cast<const uint4*>((is_v ? v_new : k_new) + src);
+  *reinterpret_cast<uint4*>((is_v ? v_pool : k_pool) + dst) = val;
+}
+
+// ---------------------------------------------------------------------------
+// host-side launch planning
+// ---------------------------------------------------------------------------
+int log2_exact(int x) {
+  if (x <= 0 || (x & (x - 1))) return -1;
+  int s = 0;
+  while ((1 << s) < x) ++s;
+  return s;
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+int check_desc(const pkv_pool_desc* d, const char* fn) {
+  if (!d) return fail(PKV_ERR_INVALID_ARG, std::string(fn) + ": NULL desc");
+  if (d->dtype != PKV_F32 && d->dtype != PKV_BF16)
+    return fail(PKV_ERR_UNSUPPORTED, std::string(fn) + ": dtype must be PKV_F32 or PKV_BF16");
+  if (d->head_dim != 64 && d->head_dim != 128)
+    return fail(PKV_ERR_UNSUPPORTED, std::string(fn) + ": head_dim must be 64 or 128");
+  if (d->page_size < 1 || d->page_size > 256)
+    return fail(PKV_ERR_UNSUPPORTED, std::string(fn) + ": page_size must be in 1..256");
+  if (d->num_kv_heads < 1 || d->num_pages < 1)
+    return fail(PKV_ERR_INVALID_ARG, std::string(fn) + ": num_kv_heads and num_pages must be >= 1");
+  if (static_cast<int64_t>(d->num_pages) * d->num_kv_heads * d->page_size * d->head_dim >
+      (int64_t{1} << 40))
+    return fail(PKV_ERR_UNSUPPORTED, std::string(fn) + ": pool larger than 2^40 elements");
+  return PKV_OK;
+}
+
+struct Plan {
+  int max_q = 0;
+  int rb = 4, kg = 1;
+  int tile_rows = 64;
+  int q_tiles = 0;
+  int split_len = 0;
+  int n_splits = 1;
+  size_t ws_bytes = 0;
+};
+
+// The launch shape is a pure function of host scalars, so the workspace size
+// and the split positions are reproducible from the same arguments.
+int make_plan(const pkv_pool_desc* d, int n_seqs, int hq, int max_q, int max_seq_len, Plan* p,
+              const char* fn) {
+  int rc = check_desc(d, fn);
+  if (rc != PKV_OK) return rc;
+  if (n_seqs < 0 || max_q < 0 || max_seq_len < 0)
+    return fail(PKV_ERR_INVALID_ARG, std::string(fn) + ": negative size");
+  if (hq < 1 || hq % d->num_kv_heads != 0)
+    return fail(PKV_ERR_UNSUPPORTED, std::string(fn) + ": num_q_heads must be a multiple of num_kv_heads");
+  const int group = hq / d->num_kv_heads;
+  p->max_q = max_q;
+  if (group > 16) return fail(PKV_ERR_UNSUPPORTED, std::string(fn) + ": GQA group above 16");
+  const int64_t rows = static_cast<int64_t>(max_q) * group;
+  if (rows <= 16) {
+    p->rb = 1; p->kg = 4;
+  } else if (rows <= 32) {
+    p->rb = 2; p->kg = 2;
+  } else {
+    p->rb = 4; p->kg = 1;
+  }
+  p->tile_rows = 16 * p->rb;
+  const int64_t q_tiles = (rows + p->tile_rows - 1) / p->tile_rows;
+  if (q_tiles > 65535) return fail(PKV_ERR_UNSUPPORTED, std::string(fn) + ": too many queries per sequence");
+  p->q_tiles = static_cast<int>(q_tiles);
+  const int64_t units = static_cast<int64_t>(n_seqs) * d->num_kv_heads * q_tiles;
+  const int64_t max_tiles = (static_cast<int64_t>(max_seq_len) + kTileKeys - 1) / kTileKeys;
+  int64_t want = units > 0 ? (kTargetWorkgroups + units - 1) / units : 1;
+  const int64_t max_by_len = (max_seq_len + kMinSplitKeys - 1) / kMinSplitKeys;
+  want = std::max<int64_t>(1, std::min<int64_t>(want, std::max<int64_t>(1, max_by_len)));
+  int64_t tiles_per_split = (max_tiles + want - 1) / want;
+  if (tiles_per_split < 1) tiles_per_split = 1;
+  p->split_len = static_cast<int>(tiles_per_split * kTileKeys);
+  p->n_splits = static_cast<int>(std::max<int64_t>(1, (max_tiles + tiles_per_split - 1) / tiles_per_split));
+  if (p->n_splits > 65535) return fail(PKV_ERR_UNSUPPORTED, std::string(fn) + ": too many splits");
+  p->ws_bytes = 0;
+  if (p->n_splits > 1) {
+    const int64_t rows_out = static_cast<int64_t>(n_seqs) * max_q * hq * p->n_splits;
+    p->ws_bytes = static_cast<size_t>(rows_out) * (d->head_dim + 2) * sizeof(float);
+  }
+  return PKV_OK;
+}
+
+template <typename T, int D, int RB, int KG>
+void launch_attention_t(const AttnArgs& a, const Plan& p, int n_seqs, int hkv, hipStream_t st) {
+  dim3 grid(p.n_splits, p.q_tiles, n_seqs * hkv);
+  constexpr int kLds = lds_bytes<T, D>();
+  paged_attention_kernel<T, D, RB, KG><<<grid, dim3(kThreads), kLds, st>>>(a);
+}
+
+template <typename T, int D>
+void launch_attention_d(const AttnArgs& a, const Plan& p, int n_seqs, int hkv, hipStream_t st) {
+  if (p.rb == 1)
+    launch_attention_t<T, D, 1, 4>(a, p, n_seqs, hkv, st);
+  else if (p.rb == 2)
+    launch_attention_t<T, D, 2, 2>(a, p, n_seqs, hkv, st);
+  else
+    launch_attention_t<T, D, 4, 1>(a, p, n_seqs, hkv, st);
+  if (p.n_splits > 1) {
+    dim3 grid(a.num_q_heads, p.max_q, n_seqs);
+    merge_splits_kernel<T, D><<<grid, dim3(kWave), 0, st>>>(a);
+  }
+}
+
+int run_attention(const char* fn, const pkv_pool_desc* desc, const void* k_pool,
+                  const void* v_pool, const void* q, int32_t total_q, const int32_t* cu_q,
+                  int32_t n_seqs, int32_t hq, const int32_t* block_tables, int32_t bt_stride,
+                  const int32_t* seq_lens, int32_t max_q, int32_t max_seq_len, float scale,
+                  void* out, void* workspace, size_t ws_bytes, void* stream) {
+  Plan p;
+  int rc = make_plan(desc, n_seqs, hq, max_q, max_seq_len, &p, fn);
+  if (rc != PKV_OK) return rc;
+  if (n_seqs == 0 || total_q == 0 || max_q == 0) return PKV_OK;
+  if (total_q < 0 || bt_stride < 0) return fail(PKV_ERR_INVALID_ARG, std::string(fn) + ": negative size");
+  if (!k_pool || !v_pool || !q || !out || !block_tables || !seq_lens)
+    return fail(PKV_ERR_INVALID_ARG, std::string(fn) + ": NULL device pointer");
+  if (!aligned16(k_pool) || !aligned16(v_pool) || !aligned16(q) || !aligned16(out))
+    return fail(PKV_ERR_INVALID_ARG, std::string(fn) + ": pools, q and out must be 16-byte aligned");
+  if (!(scale > 0.f) || !std::isfinite(scale))
+    return fail(PKV_ERR_INVALID_ARG, std::string(fn) + ": scale must be positive and finite");
+  if (p.ws_bytes > 0) {
+    if (!workspace || ws_bytes < p.ws_bytes)
+      return fail(PKV_ERR_BUFFER_TOO_SMALL, std::string(fn) + ": workspace needs " +
+                                                std::to_string(p.ws_bytes) + " bytes");
+    if (!aligned16(workspace))
+      return fail(PKV_ERR_INVALID_ARG, std::string(fn) + ": workspace must be 16-byte aligned");
+  }
+  AttnArgs a{};
+  a.q = q;
+  a.out = out;
+  a.k_pool = k_pool;
+  a.v_pool = v_pool;
+  a.block_tables = block_tables;
+  a.seq_lens = seq_lens;
+  a.cu_q = cu_q;
+  a.bt_stride = bt_stride;
+  a.n_seqs = n_seqs;
+  a.num_q_heads = hq;
+  a.num_kv_heads = desc->num_kv_heads;
+  a.group = hq / desc->num_kv_heads;
+  a.num_pages = desc->num_pages;
+  a.page_size = desc->page_size;
+  a.ps_shift = log2_exact(desc->page_size);
+  a.total_q = total_q;
+  a.ws_tokens = static_cast<int32_t>(std::min<int64_t>(INT32_MAX, static_cast<int64_t>(n_seqs) * max_q));
+  a.split_len = p.split_len;
+  a.n_splits = p.n_splits;
+  a.scale_log2 = scale * 1.4426950408889634f;
+  if (p.n_splits > 1) {
+    const size_t rows_out = static_cast<size_t>(n_seqs) * max_q * hq * p.n_splits;
+    a.ws_o = static_cast<float*>(workspace);
+    a.ws_ml = a.ws_o + rows_out * desc->head_dim;
+  }
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  const int hkv = desc->num_kv_heads;
+  (void)hipGetLastError();
+  if (desc->dtype == PKV_BF16) {
+    if (desc->head_dim == 128)
+      launch_attention_d<uint16_t, 128>(a, p, n_seqs, hkv, st);
+    else
+      launch_attention_d<uint16_t, 64>(a, p, n_seqs, hkv, st);
+  } else {
+    if (desc->head_dim == 128)
+      launch_attention_d<float, 128>(a, p, n_seqs, hkv, st);
+    else
+      launch_attention_d<float, 64>(a, p, n_seqs, hkv, st);
+  }
+  hipError_t err = hipGetLastError();
+  if (err != hipSuccess)
+    return fail(PKV_ERR_DEVICE, std::string(fn) + ": launch failed: " + hipGetErrorString(err));
+  return PKV_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int pkv_store_kv(const pkv_pool_desc* desc, void* k_pool, void* v_pool, const void* k_new,
+                 const void* v_new, const int64_t* slots, int32_t n_tokens, void* stream) {
+  int rc = check_desc(desc, "pkv_store_kv");
+  if (rc != PKV_OK) return rc;
+  if (n_tokens < 0) return fail(PKV_ERR_INVALID_ARG, "pkv_store_kv: n_tokens < 0");
+  if (n_tokens == 0) return PKV_OK;
+  if (!k_pool || !v_pool || !k_new || !v_new || !slots)
+    return fail(PKV_ERR_INVALID_ARG, "pkv_store_kv: NULL device pointer");
+  if (!aligned16(k_pool) || !aligned16(v_pool) || !aligned16(k_new) || !aligned16(v_new) ||
+      (reinterpret_cast<uintptr_t>(slots) & 7u))
+    return fail(PKV_ERR_INVALID_ARG, "pkv_store_kv: misaligned device pointer");
+  const int es = desc->dtype == PKV_BF16 ? 2 : 4;
+  const int64_t chunks = 2 * static_cast<int64_t>(n_tokens) * desc->num_kv_heads *
+                         (desc->head_dim * es / 16);
+  const int64_t blocks = (chunks + kThreads - 1) / kThreads;
+  if (blocks > INT32_MAX) return fail(PKV_ERR_UNSUPPORTED, "pkv_store_kv: too many tokens");
+  const int64_t pool_slots = static_cast<int64_t>(desc->num_pages) * desc->page_size;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  (void)hipGetLastError();
+  if (es == 2)
+    store_kv_kernel<2><<<dim3(static_cast<unsigned>(blocks)), dim3(kThreads), 0, st>>>(
+                       static_cast<char*>(k_pool), static_cast<char*>(v_pool),
+                       static_cast<const char*>(k_new), static_cast<const char*>(v_new), slots,
+                       n_tokens, desc->num_kv_heads, desc->head_dim, desc->page_size,
+                       log2_exact(desc->page_size), pool_slots);
+  else
+    store_kv_kernel<4><<<dim3(static_cast<unsigned>(blocks)), dim3(kThreads), 0, st>>>(
+                       static_cast<char*>(k_pool), static_cast<char*>(v_pool),
+                       static_cast<const char*>(k_new), static_cast<const char*>(v_new), slots,
+                       n_tokens, desc->num_kv_heads, desc->head_dim, desc->page_size,
+                       log2_exact(desc->page_size), pool_slots);
+  hipError_t err = hipGetLastError();
+  if (err != hipSuccess)
+    return fail(PKV_ERR_DEVICE, std::string("pkv_store_kv: launch failed: ") + hipGetErrorString(err));
+  return PKV_OK;
+}
+
+size_t pkv_workspace_bytes(const pkv_pool_desc* desc, int32_t n_seqs, int32_t num_q_heads,
+                           int32_t max_q_per_seq, int32_t max_seq_len) {
+  Plan p;
+  if (make_plan(desc, n_seqs, num_q_heads, max_q_per_seq, max_seq_len, &p, "pkv_workspace_bytes") != PKV_OK)
+    return 0;
+  return p.ws_bytes;
+}
+
+int pkv_decode(const pkv_pool_desc* desc, const void* k_pool, const void* v_pool, const void* q,
+               int32_t n_seqs, int32_t num_q_heads, const int32_t* block_tables,
+               int32_t bt_stride, const int32_t* seq_lens, int32_t max_seq_len, float scale,
+               void* out, void* workspace, size_t ws_bytes, void* stream) {
+  return run_attention("pkv_decode", desc, k_pool, v_pool, q, n_seqs, nullptr, n_seqs,
+                       num_q_heads, block_tables, bt_stride, seq_lens, 1, max_seq_len, scale,
+                       out, workspace, ws_bytes, stream);
+}
+
+int pkv_prefill_append(const pkv_pool_desc* desc, const void* k_pool, const void* v_pool,
+                       const void* q, int32_t total_q, const int32_t* cu_q, int32_t n_seqs,
+                       int32_t num_q_heads, const int32_t* block_tables, int32_t bt_stride,
+                       const int32_t* seq_lens, int32_t max_q_per_seq, int32_t max_seq_len,
+                       float scale, void* out, void* workspace, size_t ws_bytes, void* stream) {
+  if (!cu_q && n_seqs > 0) return fail(PKV_ERR_INVALID_ARG, "pkv_prefill_append: NULL cu_q");
+  return run_attention("pkv_prefill_append", desc, k_pool, v_pool, q, total_q, cu_q, n_seqs,
+                       num_q_heads, block_tables, bt_stride, seq_lens, max_q_per_seq,
+                       max_seq_len, scale, out, workspace, ws_bytes, stream);
+}
+
+}  // extern "C"

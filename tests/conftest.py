@@ -23,3 +23,17 @@ def golden():
         with open(os.path.join(GOLDEN, name)) as f:
             return json.load(f)
     return load
+
+
+def ensure_library():
+    """Load the built HIP library; build it only when nothing is built."""
+    from pagedattention_pkv_store_amd import _lib
+    if not os.path.exists(_lib.LIB_PATH):
+        from pagedattention_pkv_store_amd.build import build
+        build()
+    return _lib.lib()
+
+
+@pytest.fixture(scope="session")
+def pkv_lib():
+    return ensure_library()

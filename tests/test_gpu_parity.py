@@ -1,0 +1,391 @@
+"""GPU parity: libpkv's HIP path against the fp64 oracle on the same inputs.
+
+Bars: block tables, slots, plans and the stored pool contents are bit-exact;
+attention is within 1e-5 max-abs of the oracle for fp32 and within 2e-2
+max-abs and 1e-2 mean-abs for bf16 K/V with fp32 accumulation.  Pools start
+NaN-filled, so any read of a slot that was never written (or of another
+sequence's page) would turn an output into NaN.
+
+Small cases run the oracle on every output; the full-size workloads (the five
+configurations at their stated sizes, in the same launch configuration the
+benchmark times) compare seeded samples of outputs row by row.
+"""
+
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import oracle_path as ref
+import pagedattention_pkv_store_amd as pkv
+import synth
+from conftest import ensure_library
+from gpu_path import (DEV, Session, dev_tensor, host_f64, i64, run_decode, run_prefix,
+                      run_rewind, run_spec, run_tiny)
+from oracle.attention import attend, attend_row, paged_attention
+from oracle.paging import Allocator as OracleAllocator
+from oracle.paging import store_rows
+
+pytestmark = pytest.mark.gpu
+
+F32_TOL = 1e-5
+BF16_MAX, BF16_MEAN = 2e-2, 1e-2
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _lib():
+    ensure_library()
+    assert torch.cuda.is_available(), "GPU tests need a HIP device"
+
+
+def check_close(out: np.ndarray, expect: np.ndarray, dtype: str, what: str):
+    assert out.shape == expect.shape, what
+    assert np.isfinite(out).all(), f"{what}: non-finite output"
+    err = np.abs(out - expect)
+    if dtype == synth.F32:
+        assert err.max() <= F32_TOL, f"{what}: max abs err {err.max():.3g}"
+    else:
+        assert err.max() <= BF16_MAX, f"{what}: max abs err {err.max():.3g}"
+        assert err.mean() <= BF16_MEAN, f"{what}: mean abs err {err.mean():.3g}"
+
+
+def check_slots_and_tables(session: Session, oalloc: OracleAllocator, seqs):
+    for seq, start, slots in session.log.get("slots", []):
+        assert slots.tolist() == oalloc.slots(seq, start, len(slots)), "slots differ"
+    for s in seqs:
+        assert session.alloc.block_table(s).tolist() == oalloc.block_table(s)
+
+
+# ---------------------------------------------------------------------------
+# store_kv
+# ---------------------------------------------------------------------------
+@pytest.mark.parametrize("dtype,D,ps,hkv", [(synth.BF16, 128, 16, 8), (synth.F32, 64, 3, 2),
+                                            (synth.BF16, 64, 1, 1), (synth.F32, 128, 64, 4)])
+def test_store_kv_bit_exact(dtype, D, ps, hkv):
+    print(f"store_kv dtype={dtype} D={D} ps={ps} hkv={hkv}", flush=True)
+    rng = np.random.default_rng(7)
+    num_pages = 37
+    T = 50
+    slots = rng.permutation(num_pages * ps)[:T].astype(np.int64)
+    slots[3] = -1                              # padding token: skipped
+    slots[7] = num_pages * ps                  # out of range: skipped
+    kv = synth.normal_values(rng, (2, T, hkv, D), dtype)
+    desc = pkv.PoolDesc(pkv.PKV_BF16 if dtype == synth.BF16 else pkv.PKV_F32, num_pages, ps, hkv, D)
+    kp = torch.zeros(desc.pool_shape, dtype=desc.torch_dtype(), device=DEV)
+    vp = torch.zeros_like(kp)
+    pkv.store_kv(desc, kp, vp, dev_tensor(kv[0], dtype), dev_tensor(kv[1], dtype), i64(slots))
+    torch.cuda.synchronize()
+    for pool, vals in ((kp, kv[0]), (vp, kv[1])):
+        expect = np.zeros(desc.pool_shape)
+        store_rows(expect, slots, synth.to_f64(vals, dtype))
+        assert np.array_equal(host_f64(pool), expect)
+
+
+# ---------------------------------------------------------------------------
+# workload 1: tiny fp32 (page_size 4, 6 pages, lengths 7 and 6)
+# ---------------------------------------------------------------------------
+@pytest.mark.parametrize("free_order", [None, [3, 0, 1, 4, 5, 2]])
+def test_tiny_fp32(free_order):
+    print(f"tiny fp32 free_order={free_order}", flush=True)
+    w = synth.tiny_batch(free_order=free_order)
+    s, seqs, prefill, dec = run_tiny(w)
+    tables, slots, ref_prefill, ref_dec = ref.tiny_reference(w, s.scale)
+    assert [s.alloc.block_table(q).tolist() for q in seqs] == tables
+    assert [x[2].tolist() for x in s.log["slots"]] == slots
+    if free_order is not None:
+        assert tables == [[3, 0], [1, 4]]      # the blog's Figure 2 mapping
+    check_close(host_f64(prefill), ref_prefill, w.dtype, "tiny prefill")
+    check_close(host_f64(dec), ref_dec, w.dtype, "tiny decode")
+    # first query of each sequence sees only position 0: output = v_0 exactly
+    p = host_f64(prefill)
+    for b in range(2):
+        lo = int(w.offsets[b])
+        for h in range(w.num_q_heads):
+            assert np.array_equal(p[lo, h], synth.to_f64(w.v[lo, 0], w.dtype))
+    # 13 of 16 slots filled; the 3 empty slots are untouched NaN
+    kp = host_f64(s.k_pool)
+    assert np.isnan(kp).sum() == (6 * 4 - 13) * 64
+
+
+# ---------------------------------------------------------------------------
+# workload 2 shape: paged decode
+# ---------------------------------------------------------------------------
+def _decode_full_check(w, s, seqs, out):
+    oalloc, oseqs = ref.decode_allocator(w)
+    assert oseqs == seqs
+    check_slots_and_tables(s, oalloc, seqs)
+    expect = ref.decode_reference(w, s.scale)
+    o = host_f64(out)
+    e = np.stack([np.stack([expect[(b, h)] for h in range(w.num_q_heads)])
+                  for b in range(len(seqs))])
+    check_close(o, e, w.dtype, "decode")
+
+
+@pytest.mark.parametrize("n_seqs,len_lo,len_hi", [(24, 1, 1500), (64, 1, 200), (3, 4000, 9000)])
+def test_decode_bf16(n_seqs, len_lo, len_hi):
+    print(f"decode bf16 B={n_seqs} L=[{len_lo},{len_hi}]", flush=True)
+    total_pages = n_seqs * (-(-len_hi // 16)) + 64
+    w = synth.decode_batch(n_seqs=n_seqs, len_lo=len_lo, len_hi=len_hi, num_pages=total_pages,
+                           seed=n_seqs)
+    s, seqs, out = run_decode(w)
+    _decode_full_check(w, s, seqs, out)
+
+
+def test_decode_gather_form_equals_logical():
+    """A host copy of the device pools, read through the oracle's block tables,
+    reproduces the logical K/V bit for bit (store_kv + slots placed every row)."""
+    w = synth.decode_batch(n_seqs=6, len_lo=1, len_hi=90, num_pages=160, page_size=4,
+                           num_q_heads=4, num_kv_heads=2, head_dim=64, dtype=synth.F32)
+    s, seqs, out = run_decode(w)
+    oalloc, _ = ref.decode_allocator(w)
+    kp, vp = host_f64(s.k_pool), host_f64(s.v_pool)
+    tables = [oalloc.block_table(q) for q in seqs]
+    cu = np.arange(len(seqs) + 1)
+    gathered = paged_attention(synth.to_f64(w.q, w.dtype), cu, w.lengths, tables, kp, vp, s.scale)
+    logical = np.stack([attend(synth.to_f64(w.q[b:b + 1], w.dtype),
+                               synth.to_f64(w.k[w.offsets[b]:w.offsets[b + 1]], w.dtype),
+                               synth.to_f64(w.v[w.offsets[b]:w.offsets[b + 1]], w.dtype), s.scale)[0]
+                        for b in range(len(seqs))])
+    assert np.array_equal(gathered, logical)
+    check_close(host_f64(out), logical, w.dtype, "decode fp32")
+
+
+@pytest.mark.parametrize("dtype,D,ps,hq,hkv,len_hi", [
+    (synth.F32, 128, 16, 8, 2, 700),
+    (synth.F32, 64, 1, 4, 4, 300),
+    (synth.BF16, 64, 4, 16, 1, 900),
+    (synth.BF16, 128, 3, 8, 8, 500),
+    (synth.BF16, 128, 256, 16, 1, 2000),
+    (synth.BF16, 128, 64, 64, 8, 5000),
+])
+def test_decode_variants(dtype, D, ps, hq, hkv, len_hi):
+    print(f"decode variant {dtype} D={D} ps={ps} hq={hq} hkv={hkv}", flush=True)
+    n = 9
+    w = synth.decode_batch(n_seqs=n, len_lo=1, len_hi=len_hi, page_size=ps,
+                           num_pages=n * (-(-len_hi // ps)) + 5, num_q_heads=hq,
+                           num_kv_heads=hkv, head_dim=D, dtype=dtype, seed=D + ps)
+    s, seqs, out = run_decode(w)
+    _decode_full_check(w, s, seqs, out)
+
+
+def test_decode_page_permutation_bit_exact():
+    w = synth.decode_batch(n_seqs=16, len_lo=1, len_hi=1200, num_pages=2000, seed=3)
+    outs = []
+    for k in range(3):
+        order = np.random.default_rng(100 + k).permutation(w.num_pages).astype(np.int32)
+        _, _, out = run_decode(w, free_order=order)
+        outs.append(out)
+    assert torch.equal(outs[0], outs[1]) and torch.equal(outs[0], outs[2])
+
+
+def test_decode_edge_cases():
+    # empty batch is a no-op; a one-position sequence returns its value exactly
+    w = synth.decode_batch(n_seqs=2, len_lo=1, len_hi=1, num_pages=4, seed=1)
+    s, seqs, out = run_decode(w)
+    o = host_f64(out)
+    for b in range(2):
+        for h in range(w.num_q_heads):
+            assert np.array_equal(o[b, h], synth.to_f64(w.v[b, h // 4], w.dtype))
+    q = torch.zeros((0, 32, 128), dtype=torch.bfloat16, device=DEV)
+    empty = torch.zeros((0, 1), dtype=torch.int32, device=DEV)
+    pkv.decode(s.desc, s.k_pool, s.v_pool, q, empty, torch.zeros(0, dtype=torch.int32, device=DEV),
+               0, 0.1, torch.empty_like(q))
+    torch.cuda.synchronize()
+
+
+# ---------------------------------------------------------------------------
+# workload 3 shape: prefix-shared prefill
+# ---------------------------------------------------------------------------
+def test_prefix_shared_prefill_reduced():
+    print("prefix reduced", flush=True)
+    w = synth.prefix_traces(n_rows=20, n_traces=5, first_rows=(100, 140, 190), len_lo=100,
+                            len_hi=600, trace_len=600, num_pages=1200)
+    s, (order, parent, shared), seqs, n_new, out = run_prefix(w)
+    o_order, o_parent, o_shared = ref.prefix_plan(w)
+    assert order.tolist() == o_order
+    assert [None if p < 0 else int(p) for p in parent] == o_parent
+    assert shared.tolist() == o_shared
+    assert shared[:3].tolist() == [0, 96, 128]
+    check_close(host_f64(out), ref.prefix_reference_full(w, o_shared, s.scale), w.dtype, "prefix")
+    # pages were adopted, not copied: child's first pages are its parent's
+    for d in range(len(seqs)):
+        if parent[d] >= 0:
+            npg = shared[d] // w.page_size
+            assert (s.alloc.block_table(seqs[d])[:npg] ==
+                    s.alloc.block_table(seqs[parent[d]])[:npg]).all()
+
+
+def test_prefix_paper_rows():
+    """The three rows of the sharing-plan example (1,000 / 1,400 / 1,900 tokens)."""
+    w = synth.prefix_traces(n_rows=3, n_traces=2, trace_len=1900, len_hi=1900, num_pages=400,
+                            num_q_heads=8, num_kv_heads=2)
+    s, (order, parent, shared), seqs, n_new, out = run_prefix(w)
+    assert shared.tolist() == [0, 992, 1392] and parent.tolist() == [-1, 0, 1]
+    assert sum(n_new) == 1916
+    check_close(host_f64(out), ref.prefix_reference_full(w, shared.tolist(), s.scale), w.dtype,
+                "prefix paper rows")
+
+
+# ---------------------------------------------------------------------------
+# workload 4 shape: KV rewind
+# ---------------------------------------------------------------------------
+def test_rewind_reduced():
+    print("rewind reduced", flush=True)
+    w = synth.rewind_docs(n_docs=24, num_pages=24 * 22 + 10)
+    s, seqs, outs = run_rewind(w)
+    expect = ref.rewind_reference(w, s.scale)
+    for p in range(2):
+        o = host_f64(outs[p]).reshape(24, w.q_len, w.num_q_heads, w.head_dim)
+        e = np.stack([expect[p][d] for d in range(24)])
+        check_close(o, e, w.dtype, f"rewind pass {p + 1}")
+
+
+def test_truncated_slots_are_never_read():
+    """After truncate, the dropped positions' slots hold stale data; poison them
+    with NaN and decode the kept sequence: the output stays finite and exact."""
+    w = synth.decode_batch(n_seqs=4, len_lo=40, len_hi=60, num_pages=40, page_size=16, seed=5)
+    s, seqs, _ = run_decode(w)
+    stale = []
+    for b, seq in enumerate(seqs):
+        L = s.alloc.seq_len(seq)
+        stale.append(s.alloc.slots(seq, L - 7, 7))
+        s.alloc.truncate(seq, L - 7)
+    st = np.concatenate(stale)
+    nan_rows = torch.full((len(st), w.num_kv_heads, w.head_dim), float("nan"),
+                          dtype=torch.bfloat16, device=DEV)
+    pkv.store_kv(s.desc, s.k_pool, s.v_pool, nan_rows, nan_rows, i64(st))
+    q = dev_tensor(w.q, w.dtype)
+    out = host_f64(s.decode(seqs, q))
+    for b in range(4):
+        L = int(w.lengths[b]) - 7
+        lo = int(w.offsets[b])
+        for h in range(w.num_q_heads):
+            e = attend_row(synth.to_f64(w.q[b, h], w.dtype), synth.to_f64(w.k[lo:lo + L, h // 4], w.dtype),
+                           synth.to_f64(w.v[lo:lo + L, h // 4], w.dtype), L - 1, s.scale)
+            assert np.isfinite(out[b, h]).all()
+            assert np.abs(out[b, h] - e).max() <= BF16_MAX
+
+
+# ---------------------------------------------------------------------------
+# workload 5 shape: long decode + speculative rollback
+# ---------------------------------------------------------------------------
+def test_spec_rollback_reduced():
+    print("spec reduced", flush=True)
+    w = synth.spec_decode(n_seqs=3, len_lo=2000, len_hi=6000, steps=4)
+    s, seqs, outs = run_spec(w)
+    expect = ref.spec_reference(w, s.scale, 4)
+    for st in range(4):
+        o = host_f64(outs[st]).reshape(3, w.drafts, w.num_q_heads, w.head_dim)
+        check_close(o, np.stack([expect[st][b] for b in range(3)]), w.dtype, f"spec step {st}")
+
+
+def test_prefill_mixed_query_counts():
+    """Sequences with 0, 1, 17 and 300 new queries in one launch."""
+    rng = np.random.default_rng(3)
+    lens = [50, 1, 40, 700]
+    n_new = [0, 1, 17, 300]
+    hq, hkv, D = 32, 8, 128
+    w = synth.decode_batch(n_seqs=4, num_pages=200, num_q_heads=hq, seed=11)
+    s = Session.open(w)
+    seqs = [s.alloc.seq_new() for _ in lens]
+    kv = [synth.normal_values(rng, (2, L, hkv, D), synth.BF16) for L in lens]
+    for b, seq in enumerate(seqs):
+        s.alloc.reserve(seq, lens[b])
+        s.store(seq, 0, kv[b][0], kv[b][1], synth.BF16)
+    qs = [synth.normal_values(rng, (n, hq, D), synth.BF16) for n in n_new]
+    out = host_f64(s.append(seqs, n_new, dev_tensor(np.concatenate(qs), synth.BF16)))
+    row = 0
+    for b in range(4):
+        if n_new[b]:
+            e = attend(synth.to_f64(qs[b], synth.BF16), synth.to_f64(kv[b][0], synth.BF16),
+                       synth.to_f64(kv[b][1], synth.BF16), s.scale)
+            check_close(out[row:row + n_new[b]], e, synth.BF16, f"mixed seq {b}")
+        row += n_new[b]
+
+
+# ---------------------------------------------------------------------------
+# full-size workloads, sampled outputs
+# ---------------------------------------------------------------------------
+def _sample(rng, n, k):
+    return sorted(set(rng.choice(n, size=min(n, k), replace=False).tolist()))
+
+
+def test_full_decode_workload2():
+    print("full workload 2", flush=True)
+    w = synth.decode_batch()
+    s, seqs, out = run_decode(w)
+    oalloc, _ = ref.decode_allocator(w)
+    check_slots_and_tables(s, oalloc, seqs)
+    rng = np.random.default_rng(0)
+    rows = [(b, h) for b in _sample(rng, 64, 24) for h in _sample(rng, 32, 4)]
+    expect = ref.decode_reference(w, s.scale, rows)
+    o = host_f64(out)
+    got = np.stack([o[b, h] for b, h in rows])
+    check_close(got, np.stack([expect[r] for r in rows]), w.dtype, "full decode")
+
+
+def test_full_prefix_workload3():
+    print("full workload 3", flush=True)
+    w = synth.prefix_traces()
+    s, (order, parent, shared), seqs, n_new, out = run_prefix(w)
+    o_order, o_parent, o_shared = ref.prefix_plan(w)
+    assert order.tolist() == o_order and shared.tolist() == o_shared
+    assert [None if p < 0 else int(p) for p in parent] == o_parent
+    assert shared[:3].tolist() == [0, 992, 1392]
+    rng = np.random.default_rng(1)
+    cu = np.concatenate([[0], np.cumsum(n_new)])
+    rows = []
+    for d in _sample(rng, len(seqs), 40):
+        for i in {0, n_new[d] - 1, int(rng.integers(0, n_new[d]))}:
+            rows.append((d, i, int(rng.integers(0, w.num_q_heads))))
+    expect = ref.prefix_reference_rows(w, o_shared, s.scale, rows)
+    o = host_f64(out[torch.tensor([cu[d] + i for d, i, _ in rows], device=DEV)])
+    got = np.stack([o[j, h] for j, (_, _, h) in enumerate(rows)])
+    check_close(got, np.stack([expect[r] for r in rows]), w.dtype, "full prefix")
+
+
+def test_full_rewind_workload4():
+    print("full workload 4", flush=True)
+    w = synth.rewind_docs()
+    s, seqs, outs = run_rewind(w)
+    rng = np.random.default_rng(2)
+    docs = _sample(rng, 1000, 12)
+    expect = ref.rewind_reference(w, s.scale, docs)
+    for p in range(2):
+        o = outs[p].reshape(1000, w.q_len, w.num_q_heads, w.head_dim)
+        got = host_f64(o[torch.tensor(docs, device=DEV)])
+        check_close(got, np.stack([expect[p][d] for d in docs]), w.dtype, f"full rewind {p + 1}")
+
+
+def test_full_spec_workload5():
+    print("full workload 5", flush=True)
+    w = synth.spec_decode()
+    s, seqs, outs = run_spec(w)
+    grp = w.num_q_heads // w.num_kv_heads
+    rng = np.random.default_rng(3)
+    kept = {b: int(w.ctx_len[b]) for b in range(8)}
+    for st in range(w.keep.shape[0]):
+        o = host_f64(outs[st]).reshape(8, w.drafts, w.num_q_heads, w.head_dim)
+        if st in (0, 7, 15):
+            for b in _sample(rng, 8, 3):
+                lo = int(w.ctx_offsets[b])
+                L0 = int(w.ctx_len[b])
+                # logical K/V of the sequence: its context, the drafts kept in
+                # earlier steps, then this step's drafts
+                ks_, vs_ = [w.ctx_k[lo:lo + L0]], [w.ctx_v[lo:lo + L0]]
+                for p in range(st):
+                    ks_.append(w.draft_k[p, b, : int(w.keep[p, b])])
+                    vs_.append(w.draft_v[p, b, : int(w.keep[p, b])])
+                ks_.append(w.draft_k[st, b])
+                vs_.append(w.draft_v[st, b])
+                for i in (0, w.drafts - 1):
+                    h = int(rng.integers(0, w.num_q_heads))
+                    g = h // grp
+                    K = synth.to_f64(np.concatenate([x[:, g] for x in ks_]), w.dtype)
+                    V = synth.to_f64(np.concatenate([x[:, g] for x in vs_]), w.dtype)
+                    pos = kept[b] + i
+                    e = attend_row(synth.to_f64(w.draft_q[st, b, i, h], w.dtype), K, V, pos, s.scale)
+                    check_close(o[b, i, h][None], e[None], w.dtype, f"full spec step {st} seq {b}")
+        for b in range(8):
+            kept[b] += int(w.keep[st, b])

@@ -20,7 +20,7 @@ import pytest
 import torch
 
 from oracle.attention import attend, attend_row, gather_kv, paged_attention
-from oracle.paging import Allocator
+from oracle.paging import Allocator, store_rows
 
 
 def _rand(rng, *shape):
@@ -134,9 +134,16 @@ def test_attend_row_matches_attend():
 
 
 def _store(pool, alloc, seq, values, start):
-    ps = pool.shape[2]
-    for i, s in enumerate(alloc.slots(seq, start, values.shape[0])):
-        pool[s // ps, :, s % ps, :] = values[i]
+    store_rows(pool, alloc.slots(seq, start, values.shape[0]), values)
+
+
+def test_store_rows_places_each_row_at_its_slot():
+    pool = np.zeros((3, 2, 4, 5))
+    rows = np.arange(3 * 2 * 5, dtype=float).reshape(3, 2, 5) + 1
+    store_rows(pool, [9, 2, -1], rows)
+    assert np.array_equal(pool[2, :, 1, :], rows[0])   # slot 9 = page 2, offset 1
+    assert np.array_equal(pool[0, :, 2, :], rows[1])   # slot 2 = page 0, offset 2
+    assert np.count_nonzero(pool) == 2 * 2 * 5          # slot -1 skipped
 
 
 @pytest.mark.parametrize("ps", [1, 3, 4, 16])
