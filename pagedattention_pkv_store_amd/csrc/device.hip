@@ -47,11 +47,16 @@ constexpr int kWave = 64;
 constexpr int kThreads = 256;   // 4 waves
 constexpr int kTileKeys = 64;   // positions staged in LDS per iteration
 constexpr int kTargetWorkgroups = 2048;
+constexpr int kDecodeTargetWorkgroups = 8192;
 constexpr int kMinSplitKeys = 256;
+#ifndef PKV_DECODE_DEPTH
+#define PKV_DECODE_DEPTH 2           // K/V blocks in flight per wave in the decode loop
+#endif
 
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef short i16x4 __attribute__((ext_vector_type(4)));
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef unsigned u32x4 __attribute__((ext_vector_type(4)));   // 16-byte load unit
 
 __device__ __forceinline__ uint16_t float_to_bf16_bits(float f) {
   uint32_t u = __float_as_uint(f);
@@ -62,6 +67,14 @@ __device__ __forceinline__ uint16_t float_to_bf16_bits(float f) {
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
+// Four fp32 -> bf16 (round to nearest even, gfx950 v_cvt_pk_bf16_f32).
+__device__ __forceinline__ i16x4 pack_bf16x4(f32x4 x) {
+  typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+  const bf16x4 v = {static_cast<__bf16>(x[0]), static_cast<__bf16>(x[1]), static_cast<__bf16>(x[2]),
+                    static_cast<__bf16>(x[3])};
+  return __builtin_bit_cast(i16x4, v);
+}
+
 // Element storage: float for fp32, uint16_t bit patterns for bf16.
 template <typename T> struct Elem;
 template <> struct Elem<float> {
@@ -70,6 +83,42 @@ template <> struct Elem<float> {
 template <> struct Elem<uint16_t> {
   static constexpr int kQkPerMfma = 8;
 };
+
+// MFMA operand fragments of the QK product, held in their operand type (no
+// type-punned local arrays, which the compiler would keep in scratch).
+// A lane's share of a row is kDl contiguous elements: bf16 -> kDl/8 packs of
+// 8 (16x16x32 bf16 MFMA), fp32 -> kDl floats (16x16x4 f32 MFMA).
+template <typename T, int kDl> struct QkFrag;
+template <int kDl> struct QkFrag<uint16_t, kDl> {
+  static constexpr int kN = kDl / 8;
+  bf16x8 v[kN];
+  __device__ __forceinline__ void load16(int c, u32x4 x) { v[c] = __builtin_bit_cast(bf16x8, x); }
+  __device__ __forceinline__ void zero() {
+#pragma unroll
+    for (int i = 0; i < kN; ++i) v[i] = __builtin_bit_cast(bf16x8, u32x4{0u, 0u, 0u, 0u});
+  }
+};
+template <int kDl> struct QkFrag<float, kDl> {
+  static constexpr int kN = kDl;
+  float v[kN];
+  __device__ __forceinline__ void load16(int c, u32x4 x) {
+    v[4 * c + 0] = __uint_as_float(x[0]);
+    v[4 * c + 1] = __uint_as_float(x[1]);
+    v[4 * c + 2] = __uint_as_float(x[2]);
+    v[4 * c + 3] = __uint_as_float(x[3]);
+  }
+  __device__ __forceinline__ void zero() {
+#pragma unroll
+    for (int i = 0; i < kN; ++i) v[i] = 0.f;
+  }
+};
+
+__device__ __forceinline__ f32x4 mfma_qk(bf16x8 a, bf16x8 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+__device__ __forceinline__ f32x4 mfma_qk(float a, float b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
+}
 
 struct AttnArgs {
   const void* q;
@@ -92,6 +141,7 @@ struct AttnArgs {
   int32_t total_q;
   int32_t ws_tokens;    // rows of the split workspace: n_seqs * max_q_per_seq
   int32_t split_len;    // positions per KV split (multiple of kTileKeys)
+  int32_t epi_rows;     // decode kernel: query rows per 16-row block (<= 16)
   int32_t n_splits;
   float scale_log2;     // softmax scale * log2(e)
 };
@@ -110,6 +160,66 @@ constexpr int lds_bytes() {
   constexpr int tiles = 2 * kTileKeys * rs;
   constexpr int epi = 64 * (D + 4) * 4 + 2 * 64 * 4;
   return tiles > epi ? tiles : epi;
+}
+
+// Combine the partial softmax states of NW producers per row, staged in LDS
+// (eo [NW][n_rows][D + 4] un-normalised outputs, em / el [NW][n_rows] running
+// max and sum, log2 domain), and write rows row0 .. row0 + n_rows - 1 of the
+// (sequence, KV head) tile: normalised to `out` when the launch has one KV
+// split, else as this split's partial to the workspace.
+template <typename T, int D, int NW>
+__device__ __forceinline__ void combine_rows(const AttnArgs& args, const float* eo, const float* em,
+                                             const float* el, int n_rows, int row0, int rows_total,
+                                             int q0, int g, bool final_write, int split) {
+  const int kRows = n_rows;
+  constexpr int kEpiStride = D + 4;
+  constexpr int kQuads = D / 4;
+  const int group = args.group;
+  const bool split_mode = !final_write;
+  for (int idx = threadIdx.x; idx < kRows * kQuads; idx += kThreads) {
+    const int tr = idx / kQuads;
+    const int d4 = (idx - tr * kQuads) * 4;
+    const int r = row0 + tr;
+    if (r >= rows_total) continue;
+    const int qi = r / group;
+    const int tok = q0 + qi;
+    if (tok >= args.total_q) continue;
+    const int h = g * group + (r - qi * group);
+    float mmax = -INFINITY;
+#pragma unroll
+    for (int w = 0; w < NW; ++w) mmax = fmaxf(mmax, em[w * kRows + tr]);
+    const float mref = mmax == -INFINITY ? 0.f : mmax;
+    f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
+    float lsum = 0.f;
+#pragma unroll
+    for (int w = 0; w < NW; ++w) {
+      const float wt = fast_exp2(em[w * kRows + tr] - mref);
+      lsum += wt * el[w * kRows + tr];
+      acc += wt * *reinterpret_cast<const f32x4*>(eo + (w * kRows + tr) * kEpiStride + d4);
+    }
+    const int64_t orow = static_cast<int64_t>(tok) * args.num_q_heads + h;
+    if (split_mode) {
+      if (tok >= args.ws_tokens) continue;
+      const int64_t slot = orow * args.n_splits + split;
+      *reinterpret_cast<f32x4*>(args.ws_o + slot * D + d4) = acc;
+      if (d4 == 0) {
+        args.ws_ml[slot * 2] = mmax;
+        args.ws_ml[slot * 2 + 1] = lsum;
+      }
+    } else {
+      const float inv = lsum > 0.f ? 1.f / lsum : 0.f;
+      acc *= inv;
+      if constexpr (sizeof(T) == 2) {
+        uint16_t* o = static_cast<uint16_t*>(args.out) + orow * D + d4;
+        uint2 packed;
+        packed.x = float_to_bf16_bits(acc[0]) | (static_cast<uint32_t>(float_to_bf16_bits(acc[1])) << 16);
+        packed.y = float_to_bf16_bits(acc[2]) | (static_cast<uint32_t>(float_to_bf16_bits(acc[3])) << 16);
+        *reinterpret_cast<uint2*>(o) = packed;
+      } else {
+        *reinterpret_cast<f32x4*>(static_cast<float*>(args.out) + orow * D + d4) = acc;
+      }
+    }
+  }
 }
 
 // RB: 16-row query blocks per workgroup; KG: waves sharing one row block,
@@ -195,7 +305,7 @@ __global__ __launch_bounds__(kThreads) void paged_attention_kernel(AttnArgs args
 
   // ---- global -> register staging of one tile of K and V ----
   uint4 kreg[kChunks], vreg[kChunks];
-  auto load_tile = [&](int base) {
+  auto load_tile = [&](int base) __attribute__((always_inline)) {
 #pragma unroll
     for (int c = 0; c < kChunks; ++c) {
       const int chunk = c * kThreads + tid;
@@ -220,7 +330,7 @@ __global__ __launch_bounds__(kThreads) void paged_attention_kernel(AttnArgs args
       vreg[c] = vx;
     }
   };
-  auto store_tile = [&]() {
+  auto store_tile = [&]() __attribute__((always_inline)) {
 #pragma unroll
     for (int c = 0; c < kChunks; ++c) {
       const int chunk = c * kThreads + tid;
@@ -345,97 +455,504 @@ __global__ __launch_bounds__(kThreads) void paged_attention_kernel(AttnArgs args
   }
   __syncthreads();
 
-  const bool split_mode = args.n_splits > 1;
-  constexpr int kQuads = D / 4;
-  for (int idx = tid; idx < kTileRows * kQuads; idx += kThreads) {
-    const int tr = idx / kQuads;
-    const int d4 = (idx - tr * kQuads) * 4;
-    const int r = row0 + tr;
-    if (r >= rows_total) continue;
-    const int qi = r / group;
-    const int tok = q0 + qi;
-    if (tok >= args.total_q) continue;
-    const int h = g * group + (r - qi * group);
-    float mmax = -INFINITY;
-#pragma unroll
-    for (int w = 0; w < KG; ++w) mmax = fmaxf(mmax, em[w * kTileRows + tr]);
-    const float mref = mmax == -INFINITY ? 0.f : mmax;
-    f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
-    float lsum = 0.f;
-#pragma unroll
-    for (int w = 0; w < KG; ++w) {
-      const float wt = fast_exp2(em[w * kTileRows + tr] - mref);
-      lsum += wt * el[w * kTileRows + tr];
-      acc += wt * *reinterpret_cast<const f32x4*>(eo + (w * kTileRows + tr) * kEpiStride + d4);
+  combine_rows<T, D, KG>(args, eo, em, el, kTileRows, row0, rows_total, q0, g, args.n_splits == 1,
+                         blockIdx.x);
+}
+
+// ---------------------------------------------------------------------------
+// Paged decode and short appends (at most 16 * RBW query rows per sequence and
+// KV head): a schedule kernel, a persistent attention kernel and a merge.
+//
+// Work is cut into equal items of `chunk` positions of one sequence and one KV
+// head.  decode_schedule_kernel lists every (sequence, chunk) in a dense
+// array and resets the work-queue counter; paged_decode_kernel runs as many
+// workgroups as the chip holds at once, and each workgroup repeatedly takes
+// the next item from the queue (one atomic per item), so long and short
+// sequences balance across all CUs.  Inside an item, 16-position block j goes
+// to wave j % 4:
+//  * its K and V rows are loaded with fully coalesced 16-byte loads (each
+//    instruction reads 1 KB of whole rows) and written into a 16-row slice of
+//    LDS private to the wave.  The 16-byte chunks of row r are stored XOR-
+//    swizzled by r, so the MFMA operand reads that follow hit distinct banks;
+//  * the next block's loads are issued before the current block is computed;
+//    every load is unconditional (a position past the item re-reads the
+//    item's first row and is masked), so no branch forces a full wait on
+//    outstanding loads;
+//  * S^T = K Q^T and O^T = V^T P^T run on MFMA, the softmax max/sum on
+//    wavefront shuffles.
+// At the end of an item the four waves' softmax states are combined in LDS and
+// written: normalised to `out` when the item spans its whole sequence, else
+// as a partial that merge_chunks_kernel folds in with log-sum-exp.
+// ---------------------------------------------------------------------------
+
+// Positions of sequence b's KV range for its (single) row tile and the number
+// of chunks covering it.  Shared by the schedule and merge kernels.
+template <int RBW>
+__device__ __forceinline__ int decode_kv_end(const AttnArgs& a, int b, int* q0_out, int* n_b_out) {
+  int q0, n_b;
+  if (a.cu_q) {
+    q0 = a.cu_q[b];
+    n_b = a.cu_q[b + 1] - q0;
+  } else {
+    q0 = b;
+    n_b = 1;
+  }
+  *q0_out = q0;
+  *n_b_out = n_b;
+  const int rows = min(n_b * a.group, 16 * RBW);
+  if (rows <= 0) return 0;
+  return a.seq_lens[b] - n_b + (rows - 1) / a.group + 1;
+}
+
+struct DecodeQueue {
+  int32_t n_chunks;    // items listed by the schedule kernel
+  int32_t next;        // work-queue counter (reset to 0 by the schedule kernel)
+  int32_t pad[62];
+};
+
+template <int RBW>
+__global__ __launch_bounds__(kThreads) void decode_schedule_kernel(AttnArgs a, DecodeQueue* q,
+                                                                   int4* items) {
+  __shared__ int s_scan[kThreads];
+  __shared__ int s_carry;
+  const int tid = threadIdx.x;
+  if (tid == 0) s_carry = 0;
+  __syncthreads();
+  for (int base = 0; base < a.n_seqs; base += kThreads) {
+    const int b = base + tid;
+    int nc = 0, kv_end = 0;
+    if (b < a.n_seqs) {
+      int q0, n_b;
+      kv_end = decode_kv_end<RBW>(a, b, &q0, &n_b);
+      if (kv_end > 0) nc = min((kv_end + a.split_len - 1) / a.split_len, a.n_splits);
     }
-    const int64_t orow = static_cast<int64_t>(tok) * args.num_q_heads + h;
-    if (split_mode) {
-      if (tok >= args.ws_tokens) continue;
-      const int64_t slot = orow * args.n_splits + blockIdx.x;
-      *reinterpret_cast<f32x4*>(args.ws_o + slot * D + d4) = acc;
-      if (d4 == 0) {
-        args.ws_ml[slot * 2] = mmax;
-        args.ws_ml[slot * 2 + 1] = lsum;
-      }
-    } else {
-      const float inv = lsum > 0.f ? 1.f / lsum : 0.f;
-      acc *= inv;
-      if constexpr (sizeof(T) == 2) {
-        uint16_t* o = static_cast<uint16_t*>(args.out) + orow * D + d4;
-        uint2 packed;
-        packed.x = float_to_bf16_bits(acc[0]) | (static_cast<uint32_t>(float_to_bf16_bits(acc[1])) << 16);
-        packed.y = float_to_bf16_bits(acc[2]) | (static_cast<uint32_t>(float_to_bf16_bits(acc[3])) << 16);
-        *reinterpret_cast<uint2*>(o) = packed;
+    s_scan[tid] = nc;
+    __syncthreads();
+    for (int off = 1; off < kThreads; off <<= 1) {
+      const int v = tid >= off ? s_scan[tid - off] : 0;
+      __syncthreads();
+      s_scan[tid] += v;
+      __syncthreads();
+    }
+    const int first = s_carry + s_scan[tid] - nc;
+    for (int c = 0; c < nc; ++c)
+      items[first + c] = make_int4(b, c * a.split_len, min((c + 1) * a.split_len, kv_end), nc);
+    __syncthreads();
+    if (tid == kThreads - 1) s_carry += s_scan[tid];
+    __syncthreads();
+  }
+  if (tid == 0) {
+    q->n_chunks = s_carry;
+    q->next = 0;
+  }
+}
+
+// kPageMode 0: page_size a power of two >= 16 (a 16-position block lies in
+// one page); 1: a power of two < 16; 2: any other page size.
+template <typename T, int D, int RBW, int kPageMode>
+#ifndef PKV_DECODE_WAVES_PER_SIMD
+#define PKV_DECODE_WAVES_PER_SIMD 2
+#endif
+__global__ __launch_bounds__(kThreads, RBW == 1 ? PKV_DECODE_WAVES_PER_SIMD : 1) void paged_decode_kernel(AttnArgs args, const DecodeQueue* queue,
+                                                                const int4* __restrict__ items) {
+  constexpr int kEs = sizeof(T);
+  constexpr int kRowBytes = D * kEs;
+  constexpr int kCpr = kRowBytes / 16;                  // 16-byte chunks per row
+  constexpr int kLoads = 16 * kRowBytes / (16 * kWave); // 16-byte loads per lane per pool per block
+  constexpr int kDl = D / 4;                            // dims per lane in the QK operands
+  constexpr int kFragChunks = kDl * kEs / 16;           // 16-byte chunks of one lane's K fragment
+  constexpr int kQkMfmas = kDl / Elem<T>::kQkPerMfma;
+  constexpr int kDimBlocks = D / 16;
+  constexpr int kWaves = kThreads / kWave;
+  constexpr int kEpiStride = D + 4;
+  // LDS rows are padded by 16 bytes: the 16-lane phases of the K operand
+  // reads, the transposed V reads and the staging writes then all hit
+  // distinct banks, and every address is a per-lane base plus an immediate.
+  // (512-byte rows stay unpadded so four waves' slices fit in 64 KiB.)
+  constexpr int kLdsRow = kRowBytes + (kRowBytes >= 512 ? 0 : 16);
+  constexpr int kStageBytes = 2 * 16 * kLdsRow;         // K + V slice of one wave
+
+  extern __shared__ __align__(16) char smem[];
+  const int tid = threadIdx.x;
+  const int lane = tid & (kWave - 1);
+  const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
+  const int lrow = lane & 15;
+  const int lgrp = lane >> 4;
+  char* kst = smem + wave * kStageBytes;
+  char* vst = kst + 16 * kLdsRow;
+
+  const int hkv = args.num_kv_heads;
+  const int group = args.group;
+  const int ps = args.page_size;
+  const int ps_shift = args.ps_shift;
+  const T* kpool = static_cast<const T*>(args.k_pool);
+  const T* vpool = static_cast<const T*>(args.v_pool);
+  const int n_work = queue->n_chunks * hkv;
+
+  // byte offset in a wave slice of 16-byte chunk `c` of row `r`
+  auto slot = [](int r, int c) __attribute__((always_inline)) { return r * kLdsRow + c * 16; };
+
+  // Items are dealt round-robin; their sizes are equal but for each
+  // sequence's last one, so every workgroup gets the same share +- one.
+  for (int w = blockIdx.x; w < n_work; w += gridDim.x) {
+    const int4 it = items[w / hkv];
+    const int g = w % hkv;
+    const int b = __builtin_amdgcn_readfirstlane(it.x);
+    const int k_lo = __builtin_amdgcn_readfirstlane(it.y);
+    const int k_hi = __builtin_amdgcn_readfirstlane(it.z);
+    const bool whole = __builtin_amdgcn_readfirstlane(it.w) == 1;
+    int q0, n_b;
+    const int kv_end = decode_kv_end<RBW>(args, b, &q0, &n_b);
+    (void)kv_end;
+    const int rows_total = min(n_b * group, 16 * RBW);
+    const int start = args.seq_lens[b] - n_b;
+    const int32_t* bt_row = args.block_tables + static_cast<int64_t>(b) * args.bt_stride;
+
+    // ---- query rows (B operand of S^T = K Q^T) ----
+    QkFrag<T, kDl> qv[RBW];
+    int qpos[RBW];
+#pragma unroll
+    for (int rb = 0; rb < RBW; ++rb) {
+      const int r = rb * 16 + lrow;
+      const bool ok = r < rows_total;
+      const int qi = r / group;
+      qpos[rb] = start + (ok ? qi : rows_total / group);
+      const int tok = q0 + qi;
+      if (ok && tok < args.total_q) {
+        const T* src = static_cast<const T*>(args.q) +
+                       (static_cast<int64_t>(tok) * args.num_q_heads + g * group + (r - qi * group)) * D +
+                       lgrp * kDl;
+#pragma unroll
+        for (int c = 0; c < kFragChunks; ++c) qv[rb].load16(c, reinterpret_cast<const u32x4*>(src)[c]);
       } else {
-        *reinterpret_cast<f32x4*>(static_cast<float*>(args.out) + orow * D + d4) = acc;
+        qv[rb].zero();
       }
+    }
+
+    float m_run[RBW], l_part[RBW];
+    f32x4 o_acc[RBW][kDimBlocks];
+#pragma unroll
+    for (int rb = 0; rb < RBW; ++rb) {
+      m_run[rb] = -INFINITY;
+      l_part[rb] = 0.f;
+#pragma unroll
+      for (int d = 0; d < kDimBlocks; ++d) o_acc[rb][d] = f32x4{0.f, 0.f, 0.f, 0.f};
+    }
+
+    const int n_blocks = (k_hi - k_lo + 15) >> 4;
+
+    // The item's block-table slice lives in lane registers (lane i holds the
+    // page of logical block blk_lo + i, -1 if out of range) and is read with
+    // a lane permute, so no block-table load waits behind K/V loads.
+    const int blk_lo = kPageMode != 2 ? (k_lo >> ps_shift) : k_lo / ps;
+    int bt_lane = -1;
+    {
+      const int blk = blk_lo + lane;
+      const int last = kPageMode != 2 ? ((k_hi - 1) >> ps_shift) : (k_hi - 1) / ps;
+      if (blk <= last && blk < args.bt_stride) {
+        const int page = bt_row[blk];
+        bt_lane = static_cast<unsigned>(page) < static_cast<unsigned>(args.num_pages) ? page : -1;
+      }
+    }
+
+    // Issue the loads of block j (clamped into the item).  Load c of a lane
+    // covers 16-byte chunk q % kCpr of row q / kCpr (q = c * 64 + lane):
+    // consecutive lanes read consecutive bytes of whole rows.  Rows past the
+    // item, or on an invalid page, read a valid row and are flagged in okm
+    // for zeroing.
+    auto load_block = [&](int j, u32x4 (&kr)[kLoads], u32x4 (&vr)[kLoads], uint32_t& okm) __attribute__((always_inline)) {
+      j = min(j, n_blocks - 1);
+      const int pos0 = k_lo + 16 * j;
+      okm = 0;
+      if constexpr (kPageMode == 0) {
+        // one page for the whole block: a scalar read of the lane-held slice
+        const int blk = pos0 >> ps_shift;
+        int page = __builtin_amdgcn_readlane(bt_lane, blk - blk_lo);
+        const bool page_ok = page >= 0;
+        page = page_ok ? page : 0;
+        const int64_t base = ((static_cast<int64_t>(page) * hkv + g) * ps + (pos0 & (ps - 1))) * D;
+        const T* kb = kpool + base;     // wave-uniform row-0 pointers: scalar base +
+        const T* vb = vpool + base;     // a 32-bit per-lane offset per load
+#pragma unroll
+        for (int c = 0; c < kLoads; ++c) {
+          const int q = c * kWave + lane;
+          const int r = q / kCpr;
+          const int chunk = q % kCpr;
+          okm |= (page_ok && pos0 + r < k_hi) ? (1u << c) : 0u;
+          const int off = r * D + chunk * (16 / kEs);
+          kr[c] = *reinterpret_cast<const u32x4*>(kb + off);
+          vr[c] = *reinterpret_cast<const u32x4*>(vb + off);
+        }
+      } else {
+#pragma unroll
+        for (int c = 0; c < kLoads; ++c) {
+          const int q = c * kWave + lane;
+          const int r = q / kCpr;
+          const int chunk = q % kCpr;
+          const int pos_raw = pos0 + r;
+          const int pos = min(pos_raw, k_hi - 1);
+          const int blk = kPageMode == 1 ? (pos >> ps_shift) : pos / ps;
+          const int page = __shfl(bt_lane, blk - blk_lo);
+          okm |= (pos_raw < k_hi && page >= 0) ? (1u << c) : 0u;
+          const int64_t e = ((static_cast<int64_t>(page >= 0 ? page : 0) * hkv + g) * ps + (pos - blk * ps)) * D +
+                            chunk * (16 / kEs);
+          kr[c] = *reinterpret_cast<const u32x4*>(kpool + e);
+          vr[c] = *reinterpret_cast<const u32x4*>(vpool + e);
+        }
+      }
+    };
+
+    // Write a block's loaded rows into the wave's LDS slice.  V rows past
+    // the item or on an invalid page are zeroed (their probability is 0, but
+    // stale slots may hold anything, NaN included); K rows need no zeroing,
+    // their scores are masked.  Only a block that is partial or whose page
+    // is invalid needs the mask.
+    auto stage_block = [&](const u32x4 (&kr)[kLoads], const u32x4 (&vr)[kLoads], uint32_t okm) __attribute__((always_inline)) {
+      constexpr uint32_t kFull = (1u << kLoads) - 1u;
+      if (__all(okm == kFull)) {
+#pragma unroll
+        for (int c = 0; c < kLoads; ++c) {
+          const int q = c * kWave + lane;
+          const int off = slot(q / kCpr, q % kCpr);
+          *reinterpret_cast<u32x4*>(kst + off) = kr[c];
+          *reinterpret_cast<u32x4*>(vst + off) = vr[c];
+        }
+      } else {
+#pragma unroll
+        for (int c = 0; c < kLoads; ++c) {
+          const int q = c * kWave + lane;
+          const int off = slot(q / kCpr, q % kCpr);
+          const unsigned keep = 0u - ((okm >> c) & 1u);   // all ones or zero
+          *reinterpret_cast<u32x4*>(kst + off) = kr[c];
+          *reinterpret_cast<u32x4*>(vst + off) = vr[c] & keep;
+        }
+      }
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+      __builtin_amdgcn_wave_barrier();
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    };
+
+    auto compute_block = [&](int j) __attribute__((always_inline)) {
+      const int pos0 = k_lo + 16 * j;
+      // K fragment: position lrow, dims lgrp * kDl .. + kDl
+      QkFrag<T, kDl> kf;
+#pragma unroll
+      for (int c = 0; c < kFragChunks; ++c)
+        kf.load16(c, *reinterpret_cast<const u32x4*>(kst + slot(lrow, lgrp * kFragChunks + c)));
+      f32x4 s[RBW];
+#pragma unroll
+      for (int rb = 0; rb < RBW; ++rb) {
+        s[rb] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int kk = 0; kk < kQkMfmas; ++kk) s[rb] = mfma_qk(kf.v[kk], qv[rb].v[kk], s[rb]);
+      }
+#pragma unroll
+      for (int rb = 0; rb < RBW; ++rb) {
+        float mx = -INFINITY;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int pos = pos0 + lgrp * 4 + i;
+          const float x = s[rb][i] * args.scale_log2;
+          s[rb][i] = (pos < k_hi && pos <= qpos[rb]) ? x : -INFINITY;
+          mx = fmaxf(mx, s[rb][i]);
+        }
+        mx = fmaxf(mx, __shfl_xor(mx, 16));
+        mx = fmaxf(mx, __shfl_xor(mx, 32));
+        const float m_new = fmaxf(m_run[rb], mx);
+        const float m_use = m_new == -INFINITY ? 0.f : m_new;
+        const float alpha = fast_exp2(m_run[rb] - m_use);
+        m_run[rb] = m_new;
+        float psum = 0.f;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          s[rb][i] = fast_exp2(s[rb][i] - m_use);
+          psum += s[rb][i];
+        }
+        l_part[rb] = l_part[rb] * alpha + psum;
+        if (__any(alpha != 1.f)) {       // the running max moved for some row
+#pragma unroll
+          for (int d = 0; d < kDimBlocks; ++d) o_acc[rb][d] *= alpha;
+        }
+      }
+      // O^T += V^T P^T: the A operand is V transposed, read element-wise
+      if constexpr (sizeof(T) == 2) {
+        i16x4 pb[RBW];
+#pragma unroll
+        for (int rb = 0; rb < RBW; ++rb) pb[rb] = pack_bf16x4(s[rb]);
+#pragma unroll
+        for (int d = 0; d < kDimBlocks; ++d) {
+          const int dim = d * 16 + lrow;
+          i16x4 a;
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const int r = lgrp * 4 + i;
+            a[i] = *reinterpret_cast<const short*>(vst + slot(r, (dim * 2) >> 4) + ((dim * 2) & 15));
+          }
+#pragma unroll
+          for (int rb = 0; rb < RBW; ++rb)
+            o_acc[rb][d] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a, pb[rb], o_acc[rb][d], 0, 0, 0);
+        }
+      } else {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int r = lgrp * 4 + i;
+#pragma unroll
+          for (int d = 0; d < kDimBlocks; ++d) {
+            const int dim = d * 16 + lrow;
+            const float a = *reinterpret_cast<const float*>(vst + slot(r, (dim * 4) >> 4) + ((dim * 4) & 15));
+#pragma unroll
+            for (int rb = 0; rb < RBW; ++rb)
+              o_acc[rb][d] = __builtin_amdgcn_mfma_f32_16x16x4f32(a, s[rb][i], o_acc[rb][d], 0, 0, 0);
+          }
+        }
+      }
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+      __builtin_amdgcn_wave_barrier();
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    };
+
+#if PKV_DECODE_DEPTH == 1
+    if (wave < n_blocks) {
+      // One register buffer: block j is staged to LDS, then block j + 4's
+      // loads go out into the same registers while block j is computed.
+      u32x4 kr[kLoads], vr[kLoads];
+      uint32_t okm;
+      load_block(wave, kr, vr, okm);
+      for (int j = wave; j < n_blocks; j += kWaves) {
+        stage_block(kr, vr, okm);
+        load_block(j + kWaves, kr, vr, okm);
+        compute_block(j);
+      }
+    }
+#else
+    if (wave < n_blocks) {
+      // Two register buffers, two blocks in flight per wave: a block is
+      // staged to LDS, the loads of the block two steps ahead go out into the
+      // registers it freed, then the staged block is computed.  Loads are
+      // unconditional (clamped into the item) and the loop has one exit, so
+      // every path carries the same outstanding loads and the wait before a
+      // staging covers only the older buffer; only the compute of a block
+      // past the item is skipped.
+      u32x4 ka[kLoads], va[kLoads], kb[kLoads], vb[kLoads];
+      uint32_t oka, okb;
+      load_block(wave, ka, va, oka);
+      load_block(wave + kWaves, kb, vb, okb);
+      for (int j = wave; j < n_blocks; j += 2 * kWaves) {
+        stage_block(ka, va, oka);
+        load_block(j + 2 * kWaves, ka, va, oka);
+        compute_block(j);
+        stage_block(kb, vb, okb);
+        load_block(j + 3 * kWaves, kb, vb, okb);
+        if (j + kWaves < n_blocks) compute_block(j + kWaves);
+      }
+    }
+#endif
+
+    // ---- combine the four waves, one 16-row block at a time ----
+    const int er = args.epi_rows;
+    float* eo = reinterpret_cast<float*>(smem);
+    float* em = eo + kWaves * er * kEpiStride;
+    float* el = em + kWaves * er;
+    const int chunk_idx = k_lo / args.split_len;
+#pragma unroll
+    for (int rb = 0; rb < RBW; ++rb) {
+      float l_row = l_part[rb];
+      l_row += __shfl_xor(l_row, 16);
+      l_row += __shfl_xor(l_row, 32);
+      __syncthreads();
+      if (lrow < er) {
+        const int erow = wave * er + lrow;
+#pragma unroll
+        for (int d = 0; d < kDimBlocks; ++d)
+          *reinterpret_cast<f32x4*>(eo + erow * kEpiStride + d * 16 + lgrp * 4) = o_acc[rb][d];
+        if (lgrp == 0) {
+          em[erow] = m_run[rb];
+          el[erow] = l_row;
+        }
+      }
+      __syncthreads();
+      combine_rows<T, D, kWaves>(args, eo, em, el, er, rb * 16, rows_total, q0, g, whole, chunk_idx);
     }
   }
 }
 
-// Log-sum-exp merge of the KV splits of one (query, head) row.  Grid:
-// (num_q_heads, max_q_per_seq, n_seqs), one wave per row.
-template <typename T, int D>
-__global__ __launch_bounds__(kWave) void merge_splits_kernel(AttnArgs args) {
+// Log-sum-exp merge of the KV-split partials of one (query, head) row.  Grid:
+// (num_q_heads, max_q_per_seq, n_seqs), one wave per row.  RBW > 0: the
+// decode path, where rows whose sequence fits one chunk were written final
+// by the attention kernel; RBW = 0: the tile kernel, every split partial.
+template <typename T, int D, int RBW>
+__global__ __launch_bounds__(kWave) void merge_chunks_kernel(AttnArgs args) {
   const int h = blockIdx.x;
   const int qi = blockIdx.y;
   const int b = blockIdx.z;
   int q0, n_b;
-  if (args.cu_q) {
-    q0 = args.cu_q[b];
-    n_b = args.cu_q[b + 1] - q0;
+  int n_chunks = args.n_splits;
+  if constexpr (RBW > 0) {
+    const int kv_end = decode_kv_end<RBW>(args, b, &q0, &n_b);
+    n_chunks = kv_end > 0 ? min((kv_end + args.split_len - 1) / args.split_len, args.n_splits) : 0;
+    if (n_chunks <= 1) return;
   } else {
-    q0 = b;
-    n_b = 1;
+    if (args.cu_q) {
+      q0 = args.cu_q[b];
+      n_b = args.cu_q[b + 1] - q0;
+    } else {
+      q0 = b;
+      n_b = 1;
+    }
   }
   if (qi >= n_b) return;
   const int tok = q0 + qi;
   if (tok >= args.total_q || tok >= args.ws_tokens) return;
   const int qpos = args.seq_lens[b] - n_b + qi;
-  // Splits that hold at least one position this query sees.
-  const int ns = qpos < 0 ? 0 : min(args.n_splits, qpos / args.split_len + 1);
+  const int ns = qpos < 0 ? 0 : min(n_chunks, qpos / args.split_len + 1);
+  const int lane = threadIdx.x;
   const int64_t orow = static_cast<int64_t>(tok) * args.num_q_heads + h;
   const int64_t base = orow * args.n_splits;
-  float mmax = -INFINITY;
-  for (int s = 0; s < ns; ++s) mmax = fmaxf(mmax, args.ws_ml[(base + s) * 2]);
-  const float mref = mmax == -INFINITY ? 0.f : mmax;
   constexpr int kPer = D / kWave;
+  // pass 1: global max; each lane holds the states of chunks lane, lane + 64, ...
+  float mmax = -INFINITY;
+  for (int s = lane; s < ns; s += kWave) mmax = fmaxf(mmax, args.ws_ml[(base + s) * 2]);
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) mmax = fmaxf(mmax, __shfl_xor(mmax, off));
+  const float mref = mmax == -INFINITY ? 0.f : mmax;
   float acc[kPer];
 #pragma unroll
   for (int j = 0; j < kPer; ++j) acc[j] = 0.f;
   float lsum = 0.f;
-  for (int s = 0; s < ns; ++s) {
-    const float wt = fast_exp2(args.ws_ml[(base + s) * 2] - mref);
-    lsum += wt * args.ws_ml[(base + s) * 2 + 1];
-    const float* o = args.ws_o + (base + s) * D;
+  for (int s0 = 0; s0 < ns; s0 += kWave) {
+    const int sl = s0 + lane;
+    float wt = 0.f;
+    if (sl < ns) {
+      wt = fast_exp2(args.ws_ml[(base + sl) * 2] - mref);
+      lsum += wt * args.ws_ml[(base + sl) * 2 + 1];
+    }
+    const int cnt = min(kWave, ns - s0);
+    // eight partial rows in flight at a time (indices clamped, weights zero)
+    for (int k0 = 0; k0 < cnt; k0 += 8) {
+      float part[8][kPer];
 #pragma unroll
-    for (int j = 0; j < kPer; ++j) acc[j] += wt * o[threadIdx.x * kPer + j];
+      for (int u = 0; u < 8; ++u) {
+        const int k = min(k0 + u, cnt - 1);
+        const float* o = args.ws_o + (base + s0 + k) * D + lane * kPer;
+#pragma unroll
+        for (int j = 0; j < kPer; ++j) part[u][j] = o[j];
+      }
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        const float wk = __shfl(wt, min(k0 + u, kWave - 1));
+        const float w_use = (k0 + u < cnt) ? wk : 0.f;
+#pragma unroll
+        for (int j = 0; j < kPer; ++j) acc[j] += w_use * part[u][j];
+      }
+    }
   }
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) lsum += __shfl_xor(lsum, off);
   const float inv = lsum > 0.f ? 1.f / lsum : 0.f;
 #pragma unroll
   for (int j = 0; j < kPer; ++j) {
     const float v = acc[j] * inv;
-    const int64_t e = orow * D + threadIdx.x * kPer + j;
+    const int64_t e = orow * D + lane * kPer + j;
     if constexpr (sizeof(T) == 2)
       static_cast<uint16_t*>(args.out)[e] = float_to_bf16_bits(v);
     else
@@ -501,13 +1018,26 @@ int check_desc(const pkv_pool_desc* d, const char* fn) {
 
 struct Plan {
   int max_q = 0;
-  int rb = 4, kg = 1;
+  bool decode = false;  // decode path (few rows) vs paged_attention_kernel (tiles)
+  int rbw = 1;          // decode: 16-row blocks each wave holds
+  int epi_rows = 16;    // decode: rows of a block that carry queries
+  int rb = 4, kg = 1;   // tile kernel: row blocks x key groups of the 4 waves
   int tile_rows = 64;
   int q_tiles = 0;
-  int split_len = 0;
-  int n_splits = 1;
-  size_t ws_bytes = 0;
+  int split_len = 0;    // tile kernel: positions per split; decode: positions per item
+  int n_splits = 1;     // most splits / items of one sequence
+  int grid = 0;         // decode: persistent workgroups
+  size_t items_off = 0, partial_off = 0, ws_bytes = 0;
 };
+
+// Decode-path tunables (overridable at build time for sweeps).
+#ifndef PKV_DECODE_WORKGROUPS
+#define PKV_DECODE_WORKGROUPS 512    // persistent decode workgroups (2 per CU)
+#endif
+#ifndef PKV_DECODE_MIN_CHUNK
+#define PKV_DECODE_MIN_CHUNK 256     // smallest work item, in positions
+#endif
+constexpr int kDecodeWorkgroups = PKV_DECODE_WORKGROUPS;
 
 // The launch shape is a pure function of host scalars, so the workspace size
 // and the split positions are reproducible from the same arguments.
@@ -523,13 +1053,41 @@ int make_plan(const pkv_pool_desc* d, int n_seqs, int hq, int max_q, int max_seq
   p->max_q = max_q;
   if (group > 16) return fail(PKV_ERR_UNSUPPORTED, std::string(fn) + ": GQA group above 16");
   const int64_t rows = static_cast<int64_t>(max_q) * group;
-  if (rows <= 16) {
-    p->rb = 1; p->kg = 4;
-  } else if (rows <= 32) {
-    p->rb = 2; p->kg = 2;
-  } else {
-    p->rb = 4; p->kg = 1;
+  const int ps = d->page_size;
+  if (n_seqs == 0 || max_q == 0) return PKV_OK;  // nothing to launch, no workspace
+  if (rows <= 48) {
+    // decode path: items of `chunk` positions.  Larger items for more rows
+    // keep the partials small next to the K/V they summarise; smaller ones
+    // keep enough items to balance the persistent workgroups.  An item spans
+    // at most 64 pages (its block-table slice sits in one register per lane).
+    p->decode = true;
+    p->rbw = static_cast<int>(std::max<int64_t>(1, (rows + 15) / 16));
+    p->epi_rows = static_cast<int>(std::max<int64_t>(1, std::min<int64_t>(16, rows)));
+    p->tile_rows = 16 * p->rbw;
+    p->q_tiles = 1;
+    int64_t chunk = std::max<int64_t>(PKV_DECODE_MIN_CHUNK, 64 * rows);
+    chunk = std::min<int64_t>(chunk, 4096);
+    const int64_t est_len = std::max<int64_t>(1, max_seq_len);
+    while (chunk > PKV_DECODE_MIN_CHUNK &&
+           static_cast<int64_t>(n_seqs) * d->num_kv_heads * ((est_len + chunk - 1) / chunk) < 4 * kDecodeWorkgroups)
+      chunk /= 2;
+    chunk = std::min<int64_t>(chunk, static_cast<int64_t>(63) * ps);
+    chunk = std::max<int64_t>(16, chunk & ~int64_t{15});
+    p->split_len = static_cast<int>(chunk);
+    p->n_splits = static_cast<int>(std::max<int64_t>(1, (est_len + chunk - 1) / chunk));
+    if (static_cast<int64_t>(n_seqs) * p->n_splits > (int64_t{1} << 30))
+      return fail(PKV_ERR_UNSUPPORTED, std::string(fn) + ": too many work items");
+    const int64_t items = static_cast<int64_t>(n_seqs) * p->n_splits * d->num_kv_heads;
+    p->grid = static_cast<int>(std::max<int64_t>(1, std::min<int64_t>(items, kDecodeWorkgroups)));
+    p->items_off = 256;
+    p->partial_off = p->items_off + static_cast<size_t>(n_seqs) * p->n_splits * 16;
+    p->ws_bytes = p->partial_off;
+    if (p->n_splits > 1)
+      p->ws_bytes += static_cast<size_t>(n_seqs) * max_q * hq * p->n_splits * (d->head_dim + 2) * sizeof(float);
+    return PKV_OK;
   }
+  p->rb = 4;
+  p->kg = 1;
   p->tile_rows = 16 * p->rb;
   const int64_t q_tiles = (rows + p->tile_rows - 1) / p->tile_rows;
   if (q_tiles > 65535) return fail(PKV_ERR_UNSUPPORTED, std::string(fn) + ": too many queries per sequence");
@@ -544,6 +1102,7 @@ int make_plan(const pkv_pool_desc* d, int n_seqs, int hq, int max_q, int max_seq
   p->split_len = static_cast<int>(tiles_per_split * kTileKeys);
   p->n_splits = static_cast<int>(std::max<int64_t>(1, (max_tiles + tiles_per_split - 1) / tiles_per_split));
   if (p->n_splits > 65535) return fail(PKV_ERR_UNSUPPORTED, std::string(fn) + ": too many splits");
+  p->partial_off = 0;
   p->ws_bytes = 0;
   if (p->n_splits > 1) {
     const int64_t rows_out = static_cast<int64_t>(n_seqs) * max_q * hq * p->n_splits;
@@ -559,17 +1118,41 @@ void launch_attention_t(const AttnArgs& a, const Plan& p, int n_seqs, int hkv, h
   paged_attention_kernel<T, D, RB, KG><<<grid, dim3(kThreads), kLds, st>>>(a);
 }
 
-template <typename T, int D>
-void launch_attention_d(const AttnArgs& a, const Plan& p, int n_seqs, int hkv, hipStream_t st) {
-  if (p.rb == 1)
-    launch_attention_t<T, D, 1, 4>(a, p, n_seqs, hkv, st);
-  else if (p.rb == 2)
-    launch_attention_t<T, D, 2, 2>(a, p, n_seqs, hkv, st);
+template <typename T, int D, int RBW>
+void launch_decode_t(const AttnArgs& a, const Plan& p, int n_seqs, char* ws, hipStream_t st) {
+  DecodeQueue* queue = reinterpret_cast<DecodeQueue*>(ws);
+  int4* items = reinterpret_cast<int4*>(ws + p.items_off);
+  decode_schedule_kernel<RBW><<<1, kThreads, 0, st>>>(a, queue, items);
+  constexpr int kRowB = D * static_cast<int>(sizeof(T));
+  constexpr int kStage = 4 * 2 * 16 * (kRowB + (kRowB >= 512 ? 0 : 16));
+  const int epi = (4 * p.epi_rows * (D + 4) + 2 * 4 * p.epi_rows) * static_cast<int>(sizeof(float));
+  const int lds = std::max(kStage, epi);
+  if (a.ps_shift >= 4)
+    paged_decode_kernel<T, D, RBW, 0><<<p.grid, dim3(kThreads), lds, st>>>(a, queue, items);
+  else if (a.ps_shift >= 0)
+    paged_decode_kernel<T, D, RBW, 1><<<p.grid, dim3(kThreads), lds, st>>>(a, queue, items);
   else
-    launch_attention_t<T, D, 4, 1>(a, p, n_seqs, hkv, st);
+    paged_decode_kernel<T, D, RBW, 2><<<p.grid, dim3(kThreads), lds, st>>>(a, queue, items);
   if (p.n_splits > 1) {
     dim3 grid(a.num_q_heads, p.max_q, n_seqs);
-    merge_splits_kernel<T, D><<<grid, dim3(kWave), 0, st>>>(a);
+    merge_chunks_kernel<T, D, RBW><<<grid, dim3(kWave), 0, st>>>(a);
+  }
+}
+
+template <typename T, int D>
+void launch_attention_d(const AttnArgs& a, const Plan& p, int n_seqs, int hkv, char* ws, hipStream_t st) {
+  if (p.decode) {
+    switch (p.rbw) {
+      case 1: launch_decode_t<T, D, 1>(a, p, n_seqs, ws, st); break;
+      case 2: launch_decode_t<T, D, 2>(a, p, n_seqs, ws, st); break;
+      default: launch_decode_t<T, D, 3>(a, p, n_seqs, ws, st); break;
+    }
+    return;
+  }
+  launch_attention_t<T, D, 4, 1>(a, p, n_seqs, hkv, st);
+  if (p.n_splits > 1) {
+    dim3 grid(a.num_q_heads, p.max_q, n_seqs);
+    merge_chunks_kernel<T, D, 0><<<grid, dim3(kWave), 0, st>>>(a);
   }
 }
 
@@ -615,26 +1198,28 @@ int run_attention(const char* fn, const pkv_pool_desc* desc, const void* k_pool,
   a.total_q = total_q;
   a.ws_tokens = static_cast<int32_t>(std::min<int64_t>(INT32_MAX, static_cast<int64_t>(n_seqs) * max_q));
   a.split_len = p.split_len;
+  a.epi_rows = p.epi_rows;
   a.n_splits = p.n_splits;
   a.scale_log2 = scale * 1.4426950408889634f;
   if (p.n_splits > 1) {
     const size_t rows_out = static_cast<size_t>(n_seqs) * max_q * hq * p.n_splits;
-    a.ws_o = static_cast<float*>(workspace);
+    a.ws_o = reinterpret_cast<float*>(static_cast<char*>(workspace) + p.partial_off);
     a.ws_ml = a.ws_o + rows_out * desc->head_dim;
   }
   hipStream_t st = static_cast<hipStream_t>(stream);
   const int hkv = desc->num_kv_heads;
+  char* ws = static_cast<char*>(workspace);
   (void)hipGetLastError();
   if (desc->dtype == PKV_BF16) {
     if (desc->head_dim == 128)
-      launch_attention_d<uint16_t, 128>(a, p, n_seqs, hkv, st);
+      launch_attention_d<uint16_t, 128>(a, p, n_seqs, hkv, ws, st);
     else
-      launch_attention_d<uint16_t, 64>(a, p, n_seqs, hkv, st);
+      launch_attention_d<uint16_t, 64>(a, p, n_seqs, hkv, ws, st);
   } else {
     if (desc->head_dim == 128)
-      launch_attention_d<float, 128>(a, p, n_seqs, hkv, st);
+      launch_attention_d<float, 128>(a, p, n_seqs, hkv, ws, st);
     else
-      launch_attention_d<float, 64>(a, p, n_seqs, hkv, st);
+      launch_attention_d<float, 64>(a, p, n_seqs, hkv, ws, st);
   }
   hipError_t err = hipGetLastError();
   if (err != hipSuccess)
