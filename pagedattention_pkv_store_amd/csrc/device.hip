@@ -49,9 +49,6 @@ constexpr int kTileKeys = 64;   // positions staged in LDS per iteration
 constexpr int kTargetWorkgroups = 2048;
 constexpr int kDecodeTargetWorkgroups = 8192;
 constexpr int kMinSplitKeys = 256;
-#ifndef PKV_DECODE_DEPTH
-#define PKV_DECODE_DEPTH 2           // K/V blocks in flight per wave in the decode loop
-#endif
 
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef short i16x4 __attribute__((ext_vector_type(4)));
@@ -506,13 +503,19 @@ __device__ __forceinline__ int decode_kv_end(const AttnArgs& a, int b, int* q0_o
 
 struct DecodeQueue {
   int32_t n_chunks;    // items listed by the schedule kernel
-  int32_t next;        // work-queue counter (reset to 0 by the schedule kernel)
-  int32_t pad[62];
+  int32_t pad[63];
+};
+
+// One work item: positions [k_lo, k_hi) of sequence b (for every KV head),
+// with the scalars the attention kernel needs precomputed.
+struct DecodeItem {
+  int32_t b, k_lo, k_hi, n_chunks;      // n_chunks of the sequence (1: final write)
+  int32_t q0, start, rows_total, pad;   // first query row, position of query 0, rows
 };
 
 template <int RBW>
 __global__ __launch_bounds__(kThreads) void decode_schedule_kernel(AttnArgs a, DecodeQueue* q,
-                                                                   int4* items) {
+                                                                   DecodeItem* items) {
   __shared__ int s_scan[kThreads];
   __shared__ int s_carry;
   const int tid = threadIdx.x;
@@ -520,9 +523,8 @@ __global__ __launch_bounds__(kThreads) void decode_schedule_kernel(AttnArgs a, D
   __syncthreads();
   for (int base = 0; base < a.n_seqs; base += kThreads) {
     const int b = base + tid;
-    int nc = 0, kv_end = 0;
+    int nc = 0, kv_end = 0, q0 = 0, n_b = 0;
     if (b < a.n_seqs) {
-      int q0, n_b;
       kv_end = decode_kv_end<RBW>(a, b, &q0, &n_b);
       if (kv_end > 0) nc = min((kv_end + a.split_len - 1) / a.split_len, a.n_splits);
     }
@@ -535,26 +537,35 @@ __global__ __launch_bounds__(kThreads) void decode_schedule_kernel(AttnArgs a, D
       __syncthreads();
     }
     const int first = s_carry + s_scan[tid] - nc;
-    for (int c = 0; c < nc; ++c)
-      items[first + c] = make_int4(b, c * a.split_len, min((c + 1) * a.split_len, kv_end), nc);
+    const int rows = min(n_b * a.group, 16 * RBW);
+    const int start = b < a.n_seqs ? a.seq_lens[b] - n_b : 0;
+    for (int c = 0; c < nc; ++c) {
+      DecodeItem it;
+      it.b = b;
+      it.k_lo = c * a.split_len;
+      it.k_hi = min((c + 1) * a.split_len, kv_end);
+      it.n_chunks = nc;
+      it.q0 = q0;
+      it.start = start;
+      it.rows_total = rows;
+      it.pad = 0;
+      items[first + c] = it;
+    }
     __syncthreads();
     if (tid == kThreads - 1) s_carry += s_scan[tid];
     __syncthreads();
   }
-  if (tid == 0) {
-    q->n_chunks = s_carry;
-    q->next = 0;
-  }
+  if (tid == 0) q->n_chunks = s_carry;
 }
 
 // kPageMode 0: page_size a power of two >= 16 (a 16-position block lies in
 // one page); 1: a power of two < 16; 2: any other page size.
-template <typename T, int D, int RBW, int kPageMode>
 #ifndef PKV_DECODE_WAVES_PER_SIMD
 #define PKV_DECODE_WAVES_PER_SIMD 2
 #endif
-__global__ __launch_bounds__(kThreads, RBW == 1 ? PKV_DECODE_WAVES_PER_SIMD : 1) void paged_decode_kernel(AttnArgs args, const DecodeQueue* queue,
-                                                                const int4* __restrict__ items) {
+template <typename T, int D, int RBW, int kPageMode>
+__global__ __launch_bounds__(kThreads, RBW == 1 ? PKV_DECODE_WAVES_PER_SIMD : 1) void paged_decode_kernel(
+    AttnArgs args, const DecodeQueue* queue, const DecodeItem* __restrict__ items) {
   constexpr int kEs = sizeof(T);
   constexpr int kRowBytes = D * kEs;
   constexpr int kCpr = kRowBytes / 16;                  // 16-byte chunks per row
@@ -588,49 +599,252 @@ __global__ __launch_bounds__(kThreads, RBW == 1 ? PKV_DECODE_WAVES_PER_SIMD : 1)
   const T* kpool = static_cast<const T*>(args.k_pool);
   const T* vpool = static_cast<const T*>(args.v_pool);
   const int n_work = queue->n_chunks * hkv;
+  const int grid = gridDim.x;
 
-  // byte offset in a wave slice of 16-byte chunk `c` of row `r`
   auto slot = [](int r, int c) __attribute__((always_inline)) { return r * kLdsRow + c * 16; };
 
-  // Items are dealt round-robin; their sizes are equal but for each
-  // sequence's last one, so every workgroup gets the same share +- one.
-  for (int w = blockIdx.x; w < n_work; w += gridDim.x) {
-    const int4 it = items[w / hkv];
-    const int g = w % hkv;
-    const int b = __builtin_amdgcn_readfirstlane(it.x);
-    const int k_lo = __builtin_amdgcn_readfirstlane(it.y);
-    const int k_hi = __builtin_amdgcn_readfirstlane(it.z);
-    const bool whole = __builtin_amdgcn_readfirstlane(it.w) == 1;
-    int q0, n_b;
-    const int kv_end = decode_kv_end<RBW>(args, b, &q0, &n_b);
-    (void)kv_end;
-    const int rows_total = min(n_b * group, 16 * RBW);
-    const int start = args.seq_lens[b] - n_b;
-    const int32_t* bt_row = args.block_tables + static_cast<int64_t>(b) * args.bt_stride;
-
-    // ---- query rows (B operand of S^T = K Q^T) ----
-    QkFrag<T, kDl> qv[RBW];
-    int qpos[RBW];
+  // ---- per-item scalars (wave-uniform) ----
+  struct ItemS {
+    int valid, b, g, k_lo, k_hi, nb, whole, q0, start, rows_total, blk_lo;
+  };
+  auto fetch = [&](int wi) __attribute__((always_inline)) {
+    ItemS s;
+    s.valid = wi < n_work;
+    const int idx = s.valid ? wi / hkv : 0;
+    const DecodeItem rec = items[idx];
+    s.b = __builtin_amdgcn_readfirstlane(rec.b);
+    s.g = s.valid ? wi % hkv : 0;
+    s.k_lo = __builtin_amdgcn_readfirstlane(rec.k_lo);
+    s.k_hi = __builtin_amdgcn_readfirstlane(rec.k_hi);
+    s.whole = __builtin_amdgcn_readfirstlane(rec.n_chunks) == 1;
+    s.q0 = __builtin_amdgcn_readfirstlane(rec.q0);
+    s.start = __builtin_amdgcn_readfirstlane(rec.start);
+    s.rows_total = __builtin_amdgcn_readfirstlane(rec.rows_total);
+    s.nb = s.valid ? (s.k_hi - s.k_lo + 15) >> 4 : 0;
+    s.blk_lo = kPageMode != 2 ? (s.k_lo >> ps_shift) : s.k_lo / ps;
+    return s;
+  };
+  // The item's block-table slice lives in lane registers (lane i holds the
+  // page of logical block blk_lo + i, -1 if out of range); items span at most
+  // 64 pages.  Reading it needs no memory access once loaded.
+  // Branch-free: the load always goes to an in-range entry of the table
+  // (a record of an invalid item is item 0's, a real sequence).
+  auto load_bt = [&](const ItemS& it) __attribute__((always_inline)) {
+    const int blk = it.blk_lo + lane;
+    const int last = kPageMode != 2 ? ((it.k_hi - 1) >> ps_shift) : (it.k_hi - 1) / ps;
+    const int blk_c = max(0, min(blk, min(last, args.bt_stride - 1)));
+    const int p = args.block_tables[static_cast<int64_t>(it.b) * args.bt_stride + blk_c];
+    const bool ok = it.valid && blk <= last && blk < args.bt_stride &&
+                    static_cast<unsigned>(p) < static_cast<unsigned>(args.num_pages);
+    return ok ? p : -1;
+  };
+  // Query rows (B operand of S^T = K Q^T): row r = (query r / group, head
+  // g * group + r % group); this lane holds row rb * 16 + lrow, dims
+  // lgrp * kDl .. + kDl.
+  auto load_q = [&](const ItemS& it, QkFrag<T, kDl> (&qv)[RBW], int (&qpos)[RBW]) __attribute__((always_inline)) {
 #pragma unroll
     for (int rb = 0; rb < RBW; ++rb) {
       const int r = rb * 16 + lrow;
-      const bool ok = r < rows_total;
       const int qi = r / group;
-      qpos[rb] = start + (ok ? qi : rows_total / group);
-      const int tok = q0 + qi;
-      if (ok && tok < args.total_q) {
-        const T* src = static_cast<const T*>(args.q) +
-                       (static_cast<int64_t>(tok) * args.num_q_heads + g * group + (r - qi * group)) * D +
-                       lgrp * kDl;
+      const int tok = it.q0 + qi;
+      const bool ok = it.valid && r < it.rows_total && tok < args.total_q;
+      qpos[rb] = it.start + (r < it.rows_total ? qi : it.rows_total / group);
+      // branch-free: rows without a query read row 0 and are zeroed
+      const int tok_c = ok ? tok : 0;
+      const T* src = static_cast<const T*>(args.q) +
+                     (static_cast<int64_t>(tok_c) * args.num_q_heads + it.g * group + (r - qi * group)) * D +
+                     lgrp * kDl;
+      const unsigned keep = ok ? ~0u : 0u;
 #pragma unroll
-        for (int c = 0; c < kFragChunks; ++c) qv[rb].load16(c, reinterpret_cast<const u32x4*>(src)[c]);
-      } else {
-        qv[rb].zero();
+      for (int c = 0; c < kFragChunks; ++c) qv[rb].load16(c, reinterpret_cast<const u32x4*>(src)[c] & keep);
+    }
+  };
+
+  // Issue the loads of block j of item `it` (clamped into the item; an
+  // invalid item reads page 0 and flags everything for zeroing).  Load c of
+  // a lane covers 16-byte chunk q % kCpr of row q / kCpr (q = c * 64 +
+  // lane): consecutive lanes read consecutive bytes of whole rows.
+  auto load_block = [&](const ItemS& it, int bt, int j, u32x4 (&kr)[kLoads], u32x4 (&vr)[kLoads],
+                        uint32_t& okm) __attribute__((always_inline)) {
+    j = max(0, min(j, it.nb - 1));
+    const int pos0 = it.k_lo + 16 * j;
+    okm = 0;
+    if constexpr (kPageMode == 0) {
+      const int blk = pos0 >> ps_shift;
+      int page = __builtin_amdgcn_readlane(bt, blk - it.blk_lo);
+      const bool page_ok = it.valid && page >= 0;
+      page = page_ok ? page : 0;
+      const int64_t base = ((static_cast<int64_t>(page) * hkv + it.g) * ps + (pos0 & (ps - 1))) * D;
+      const T* kb = kpool + base;     // wave-uniform row-0 pointers: scalar base +
+      const T* vb = vpool + base;     // a 32-bit per-lane offset per load
+#pragma unroll
+      for (int c = 0; c < kLoads; ++c) {
+        const int q = c * kWave + lane;
+        const int r = q / kCpr;
+        const int chunk = q % kCpr;
+        okm |= (page_ok && pos0 + r < it.k_hi) ? (1u << c) : 0u;
+        const int off = r * D + chunk * (16 / kEs);
+        kr[c] = *reinterpret_cast<const u32x4*>(kb + off);
+        vr[c] = *reinterpret_cast<const u32x4*>(vb + off);
+      }
+    } else {
+#pragma unroll
+      for (int c = 0; c < kLoads; ++c) {
+        const int q = c * kWave + lane;
+        const int r = q / kCpr;
+        const int chunk = q % kCpr;
+        const int pos_raw = pos0 + r;
+        const int pos = max(0, min(pos_raw, it.k_hi - 1));
+        const int blk = kPageMode == 1 ? (pos >> ps_shift) : pos / ps;
+        const int page = __shfl(bt, max(0, min(blk - it.blk_lo, kWave - 1)));
+        const bool ok = it.valid && pos_raw < it.k_hi && page >= 0;
+        okm |= ok ? (1u << c) : 0u;
+        const int64_t e = ((static_cast<int64_t>(ok ? page : 0) * hkv + it.g) * ps + (ok ? pos - blk * ps : 0)) * D +
+                          chunk * (16 / kEs);
+        kr[c] = *reinterpret_cast<const u32x4*>(kpool + e);
+        vr[c] = *reinterpret_cast<const u32x4*>(vpool + e);
       }
     }
+  };
 
-    float m_run[RBW], l_part[RBW];
-    f32x4 o_acc[RBW][kDimBlocks];
+  // Write a block's loaded rows into the wave's LDS slice.  V rows past the
+  // item or on an invalid page are zeroed (their probability is 0, but stale
+  // slots may hold anything, NaN included); K rows need no zeroing, their
+  // scores are masked.  Only a partial block needs the mask.
+  auto stage_block = [&](const u32x4 (&kr)[kLoads], const u32x4 (&vr)[kLoads], uint32_t okm) __attribute__((always_inline)) {
+    constexpr uint32_t kFull = (1u << kLoads) - 1u;
+    if (__all(okm == kFull)) {
+#pragma unroll
+      for (int c = 0; c < kLoads; ++c) {
+        const int q = c * kWave + lane;
+        const int off = slot(q / kCpr, q % kCpr);
+        *reinterpret_cast<u32x4*>(kst + off) = kr[c];
+        *reinterpret_cast<u32x4*>(vst + off) = vr[c];
+      }
+    } else {
+#pragma unroll
+      for (int c = 0; c < kLoads; ++c) {
+        const int q = c * kWave + lane;
+        const int off = slot(q / kCpr, q % kCpr);
+        const unsigned keep = 0u - ((okm >> c) & 1u);   // all ones or zero
+        *reinterpret_cast<u32x4*>(kst + off) = kr[c];
+        *reinterpret_cast<u32x4*>(vst + off) = vr[c] & keep;
+      }
+    }
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+  };
+
+  // ---- online softmax state of the current item (log2 domain) ----
+  float m_run[RBW], l_part[RBW];
+  f32x4 o_acc[RBW][kDimBlocks];
+
+  auto compute_block = [&](const ItemS& it, const QkFrag<T, kDl> (&qv)[RBW], const int (&qpos)[RBW],
+                           int j) __attribute__((always_inline)) {
+    const int pos0 = it.k_lo + 16 * j;
+    // K fragment: position lrow, dims lgrp * kDl .. + kDl
+    QkFrag<T, kDl> kf;
+#pragma unroll
+    for (int c = 0; c < kFragChunks; ++c)
+      kf.load16(c, *reinterpret_cast<const u32x4*>(kst + slot(lrow, lgrp * kFragChunks + c)));
+    f32x4 s[RBW];
+#pragma unroll
+    for (int rb = 0; rb < RBW; ++rb) {
+      s[rb] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int kk = 0; kk < kQkMfmas; ++kk) s[rb] = mfma_qk(kf.v[kk], qv[rb].v[kk], s[rb]);
+    }
+#pragma unroll
+    for (int rb = 0; rb < RBW; ++rb) {
+      float mx = -INFINITY;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int pos = pos0 + lgrp * 4 + i;
+        const float x = s[rb][i] * args.scale_log2;
+        s[rb][i] = (pos < it.k_hi && pos <= qpos[rb]) ? x : -INFINITY;
+        mx = fmaxf(mx, s[rb][i]);
+      }
+      mx = fmaxf(mx, __shfl_xor(mx, 16));
+      mx = fmaxf(mx, __shfl_xor(mx, 32));
+      const float m_new = fmaxf(m_run[rb], mx);
+      const float m_use = m_new == -INFINITY ? 0.f : m_new;
+      const float alpha = fast_exp2(m_run[rb] - m_use);
+      m_run[rb] = m_new;
+      float psum = 0.f;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        s[rb][i] = fast_exp2(s[rb][i] - m_use);
+        psum += s[rb][i];
+      }
+      l_part[rb] = l_part[rb] * alpha + psum;
+      if (__any(alpha != 1.f)) {       // the running max moved for some row
+#pragma unroll
+        for (int d = 0; d < kDimBlocks; ++d) o_acc[rb][d] *= alpha;
+      }
+    }
+    // O^T += V^T P^T: the A operand is V transposed, read element-wise
+    if constexpr (sizeof(T) == 2) {
+      i16x4 pb[RBW];
+#pragma unroll
+      for (int rb = 0; rb < RBW; ++rb) pb[rb] = pack_bf16x4(s[rb]);
+#pragma unroll
+      for (int d = 0; d < kDimBlocks; ++d) {
+        const int dim = d * 16 + lrow;
+        i16x4 a;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) a[i] = *reinterpret_cast<const short*>(vst + slot(lgrp * 4 + i, 0) + dim * 2);
+#pragma unroll
+        for (int rb = 0; rb < RBW; ++rb)
+          o_acc[rb][d] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a, pb[rb], o_acc[rb][d], 0, 0, 0);
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+#pragma unroll
+        for (int d = 0; d < kDimBlocks; ++d) {
+          const int dim = d * 16 + lrow;
+          const float a = *reinterpret_cast<const float*>(vst + slot(lgrp * 4 + i, 0) + dim * 4);
+#pragma unroll
+          for (int rb = 0; rb < RBW; ++rb)
+            o_acc[rb][d] = __builtin_amdgcn_mfma_f32_16x16x4f32(a, s[rb][i], o_acc[rb][d], 0, 0, 0);
+        }
+      }
+    }
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+  };
+
+  // ---- the item stream of this workgroup: items w, w + grid, w + 2 grid ... ----
+  int w = blockIdx.x;
+  ItemS cur = fetch(w);
+  if (!cur.valid) return;
+  int bt_cur = load_bt(cur);
+  QkFrag<T, kDl> q_cur[RBW];
+  int qpos_cur[RBW];
+  load_q(cur, q_cur, qpos_cur);
+  ItemS nxt = fetch(w + grid);
+
+  // Two register buffers, two blocks in flight per wave.  A block is staged
+  // to LDS, the loads two steps ahead go out into the registers it freed,
+  // then the staged block is computed.  An item's last step issues the next
+  // item's first two blocks instead, so loads stay in flight through the
+  // epilogue and the next item's start.  Loads are never skipped (an index
+  // past the item is clamped and the rows masked), so every path carries the
+  // same outstanding loads and each staging waits for the older buffer only.
+  u32x4 ka[kLoads], va[kLoads], kb[kLoads], vb[kLoads];
+  uint32_t oka, okb;
+  load_block(cur, bt_cur, wave, ka, va, oka);
+  load_block(cur, bt_cur, wave + kWaves, kb, vb, okb);
+
+  for (;;) {
+    const int bt_nxt = load_bt(nxt);
+    QkFrag<T, kDl> q_nxt[RBW];
+    int qpos_nxt[RBW];
+    load_q(nxt, q_nxt, qpos_nxt);
+    const ItemS nxt2 = fetch(w + 2 * grid);
+
 #pragma unroll
     for (int rb = 0; rb < RBW; ++rb) {
       m_run[rb] = -INFINITY;
@@ -639,221 +853,30 @@ __global__ __launch_bounds__(kThreads, RBW == 1 ? PKV_DECODE_WAVES_PER_SIMD : 1)
       for (int d = 0; d < kDimBlocks; ++d) o_acc[rb][d] = f32x4{0.f, 0.f, 0.f, 0.f};
     }
 
-    const int n_blocks = (k_hi - k_lo + 15) >> 4;
-
-    // The item's block-table slice lives in lane registers (lane i holds the
-    // page of logical block blk_lo + i, -1 if out of range) and is read with
-    // a lane permute, so no block-table load waits behind K/V loads.
-    const int blk_lo = kPageMode != 2 ? (k_lo >> ps_shift) : k_lo / ps;
-    int bt_lane = -1;
-    {
-      const int blk = blk_lo + lane;
-      const int last = kPageMode != 2 ? ((k_hi - 1) >> ps_shift) : (k_hi - 1) / ps;
-      if (blk <= last && blk < args.bt_stride) {
-        const int page = bt_row[blk];
-        bt_lane = static_cast<unsigned>(page) < static_cast<unsigned>(args.num_pages) ? page : -1;
-      }
+    for (int j = wave;; j += 2 * kWaves) {
+      const bool last = j + 2 * kWaves >= cur.nb;   // the item's final step for this wave
+      // where the loads issued in this step go: two steps ahead in this item,
+      // or the next item's first two steps (a dummy re-read when none)
+      const bool to_next = last && nxt.valid;
+      const ItemS tgt = to_next ? nxt : cur;
+      const int tgt_bt = to_next ? bt_nxt : bt_cur;
+      const int ja = last ? (to_next ? wave : cur.nb - 1) : j + 2 * kWaves;
+      const int jb = last ? (to_next ? wave + kWaves : cur.nb - 1) : j + 3 * kWaves;
+      stage_block(ka, va, oka);
+      load_block(tgt, tgt_bt, ja, ka, va, oka);
+      if (j < cur.nb) compute_block(cur, q_cur, qpos_cur, j);
+      stage_block(kb, vb, okb);
+      load_block(tgt, tgt_bt, jb, kb, vb, okb);
+      if (j + kWaves < cur.nb) compute_block(cur, q_cur, qpos_cur, j + kWaves);
+      if (last) break;
     }
-
-    // Issue the loads of block j (clamped into the item).  Load c of a lane
-    // covers 16-byte chunk q % kCpr of row q / kCpr (q = c * 64 + lane):
-    // consecutive lanes read consecutive bytes of whole rows.  Rows past the
-    // item, or on an invalid page, read a valid row and are flagged in okm
-    // for zeroing.
-    auto load_block = [&](int j, u32x4 (&kr)[kLoads], u32x4 (&vr)[kLoads], uint32_t& okm) __attribute__((always_inline)) {
-      j = min(j, n_blocks - 1);
-      const int pos0 = k_lo + 16 * j;
-      okm = 0;
-      if constexpr (kPageMode == 0) {
-        // one page for the whole block: a scalar read of the lane-held slice
-        const int blk = pos0 >> ps_shift;
-        int page = __builtin_amdgcn_readlane(bt_lane, blk - blk_lo);
-        const bool page_ok = page >= 0;
-        page = page_ok ? page : 0;
-        const int64_t base = ((static_cast<int64_t>(page) * hkv + g) * ps + (pos0 & (ps - 1))) * D;
-        const T* kb = kpool + base;     // wave-uniform row-0 pointers: scalar base +
-        const T* vb = vpool + base;     // a 32-bit per-lane offset per load
-#pragma unroll
-        for (int c = 0; c < kLoads; ++c) {
-          const int q = c * kWave + lane;
-          const int r = q / kCpr;
-          const int chunk = q % kCpr;
-          okm |= (page_ok && pos0 + r < k_hi) ? (1u << c) : 0u;
-          const int off = r * D + chunk * (16 / kEs);
-          kr[c] = *reinterpret_cast<const u32x4*>(kb + off);
-          vr[c] = *reinterpret_cast<const u32x4*>(vb + off);
-        }
-      } else {
-#pragma unroll
-        for (int c = 0; c < kLoads; ++c) {
-          const int q = c * kWave + lane;
-          const int r = q / kCpr;
-          const int chunk = q % kCpr;
-          const int pos_raw = pos0 + r;
-          const int pos = min(pos_raw, k_hi - 1);
-          const int blk = kPageMode == 1 ? (pos >> ps_shift) : pos / ps;
-          const int page = __shfl(bt_lane, blk - blk_lo);
-          okm |= (pos_raw < k_hi && page >= 0) ? (1u << c) : 0u;
-          const int64_t e = ((static_cast<int64_t>(page >= 0 ? page : 0) * hkv + g) * ps + (pos - blk * ps)) * D +
-                            chunk * (16 / kEs);
-          kr[c] = *reinterpret_cast<const u32x4*>(kpool + e);
-          vr[c] = *reinterpret_cast<const u32x4*>(vpool + e);
-        }
-      }
-    };
-
-    // Write a block's loaded rows into the wave's LDS slice.  V rows past
-    // the item or on an invalid page are zeroed (their probability is 0, but
-    // stale slots may hold anything, NaN included); K rows need no zeroing,
-    // their scores are masked.  Only a block that is partial or whose page
-    // is invalid needs the mask.
-    auto stage_block = [&](const u32x4 (&kr)[kLoads], const u32x4 (&vr)[kLoads], uint32_t okm) __attribute__((always_inline)) {
-      constexpr uint32_t kFull = (1u << kLoads) - 1u;
-      if (__all(okm == kFull)) {
-#pragma unroll
-        for (int c = 0; c < kLoads; ++c) {
-          const int q = c * kWave + lane;
-          const int off = slot(q / kCpr, q % kCpr);
-          *reinterpret_cast<u32x4*>(kst + off) = kr[c];
-          *reinterpret_cast<u32x4*>(vst + off) = vr[c];
-        }
-      } else {
-#pragma unroll
-        for (int c = 0; c < kLoads; ++c) {
-          const int q = c * kWave + lane;
-          const int off = slot(q / kCpr, q % kCpr);
-          const unsigned keep = 0u - ((okm >> c) & 1u);   // all ones or zero
-          *reinterpret_cast<u32x4*>(kst + off) = kr[c];
-          *reinterpret_cast<u32x4*>(vst + off) = vr[c] & keep;
-        }
-      }
-      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-      __builtin_amdgcn_wave_barrier();
-      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-    };
-
-    auto compute_block = [&](int j) __attribute__((always_inline)) {
-      const int pos0 = k_lo + 16 * j;
-      // K fragment: position lrow, dims lgrp * kDl .. + kDl
-      QkFrag<T, kDl> kf;
-#pragma unroll
-      for (int c = 0; c < kFragChunks; ++c)
-        kf.load16(c, *reinterpret_cast<const u32x4*>(kst + slot(lrow, lgrp * kFragChunks + c)));
-      f32x4 s[RBW];
-#pragma unroll
-      for (int rb = 0; rb < RBW; ++rb) {
-        s[rb] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int kk = 0; kk < kQkMfmas; ++kk) s[rb] = mfma_qk(kf.v[kk], qv[rb].v[kk], s[rb]);
-      }
-#pragma unroll
-      for (int rb = 0; rb < RBW; ++rb) {
-        float mx = -INFINITY;
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int pos = pos0 + lgrp * 4 + i;
-          const float x = s[rb][i] * args.scale_log2;
-          s[rb][i] = (pos < k_hi && pos <= qpos[rb]) ? x : -INFINITY;
-          mx = fmaxf(mx, s[rb][i]);
-        }
-        mx = fmaxf(mx, __shfl_xor(mx, 16));
-        mx = fmaxf(mx, __shfl_xor(mx, 32));
-        const float m_new = fmaxf(m_run[rb], mx);
-        const float m_use = m_new == -INFINITY ? 0.f : m_new;
-        const float alpha = fast_exp2(m_run[rb] - m_use);
-        m_run[rb] = m_new;
-        float psum = 0.f;
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          s[rb][i] = fast_exp2(s[rb][i] - m_use);
-          psum += s[rb][i];
-        }
-        l_part[rb] = l_part[rb] * alpha + psum;
-        if (__any(alpha != 1.f)) {       // the running max moved for some row
-#pragma unroll
-          for (int d = 0; d < kDimBlocks; ++d) o_acc[rb][d] *= alpha;
-        }
-      }
-      // O^T += V^T P^T: the A operand is V transposed, read element-wise
-      if constexpr (sizeof(T) == 2) {
-        i16x4 pb[RBW];
-#pragma unroll
-        for (int rb = 0; rb < RBW; ++rb) pb[rb] = pack_bf16x4(s[rb]);
-#pragma unroll
-        for (int d = 0; d < kDimBlocks; ++d) {
-          const int dim = d * 16 + lrow;
-          i16x4 a;
-#pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            const int r = lgrp * 4 + i;
-            a[i] = *reinterpret_cast<const short*>(vst + slot(r, (dim * 2) >> 4) + ((dim * 2) & 15));
-          }
-#pragma unroll
-          for (int rb = 0; rb < RBW; ++rb)
-            o_acc[rb][d] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a, pb[rb], o_acc[rb][d], 0, 0, 0);
-        }
-      } else {
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int r = lgrp * 4 + i;
-#pragma unroll
-          for (int d = 0; d < kDimBlocks; ++d) {
-            const int dim = d * 16 + lrow;
-            const float a = *reinterpret_cast<const float*>(vst + slot(r, (dim * 4) >> 4) + ((dim * 4) & 15));
-#pragma unroll
-            for (int rb = 0; rb < RBW; ++rb)
-              o_acc[rb][d] = __builtin_amdgcn_mfma_f32_16x16x4f32(a, s[rb][i], o_acc[rb][d], 0, 0, 0);
-          }
-        }
-      }
-      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-      __builtin_amdgcn_wave_barrier();
-      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-    };
-
-#if PKV_DECODE_DEPTH == 1
-    if (wave < n_blocks) {
-      // One register buffer: block j is staged to LDS, then block j + 4's
-      // loads go out into the same registers while block j is computed.
-      u32x4 kr[kLoads], vr[kLoads];
-      uint32_t okm;
-      load_block(wave, kr, vr, okm);
-      for (int j = wave; j < n_blocks; j += kWaves) {
-        stage_block(kr, vr, okm);
-        load_block(j + kWaves, kr, vr, okm);
-        compute_block(j);
-      }
-    }
-#else
-    if (wave < n_blocks) {
-      // Two register buffers, two blocks in flight per wave: a block is
-      // staged to LDS, the loads of the block two steps ahead go out into the
-      // registers it freed, then the staged block is computed.  Loads are
-      // unconditional (clamped into the item) and the loop has one exit, so
-      // every path carries the same outstanding loads and the wait before a
-      // staging covers only the older buffer; only the compute of a block
-      // past the item is skipped.
-      u32x4 ka[kLoads], va[kLoads], kb[kLoads], vb[kLoads];
-      uint32_t oka, okb;
-      load_block(wave, ka, va, oka);
-      load_block(wave + kWaves, kb, vb, okb);
-      for (int j = wave; j < n_blocks; j += 2 * kWaves) {
-        stage_block(ka, va, oka);
-        load_block(j + 2 * kWaves, ka, va, oka);
-        compute_block(j);
-        stage_block(kb, vb, okb);
-        load_block(j + 3 * kWaves, kb, vb, okb);
-        if (j + kWaves < n_blocks) compute_block(j + kWaves);
-      }
-    }
-#endif
 
     // ---- combine the four waves, one 16-row block at a time ----
     const int er = args.epi_rows;
     float* eo = reinterpret_cast<float*>(smem);
     float* em = eo + kWaves * er * kEpiStride;
     float* el = em + kWaves * er;
-    const int chunk_idx = k_lo / args.split_len;
+    const int chunk_idx = cur.k_lo / args.split_len;
 #pragma unroll
     for (int rb = 0; rb < RBW; ++rb) {
       float l_row = l_part[rb];
@@ -871,8 +894,21 @@ __global__ __launch_bounds__(kThreads, RBW == 1 ? PKV_DECODE_WAVES_PER_SIMD : 1)
         }
       }
       __syncthreads();
-      combine_rows<T, D, kWaves>(args, eo, em, el, er, rb * 16, rows_total, q0, g, whole, chunk_idx);
+      combine_rows<T, D, kWaves>(args, eo, em, el, er, rb * 16, cur.rows_total, cur.q0, cur.g, cur.whole,
+                                 chunk_idx);
     }
+    __syncthreads();   // the epilogue's LDS reads finish before the next staging
+
+    if (!nxt.valid) break;
+    w += grid;
+    cur = nxt;
+    bt_cur = bt_nxt;
+#pragma unroll
+    for (int rb = 0; rb < RBW; ++rb) {
+      q_cur[rb] = q_nxt[rb];
+      qpos_cur[rb] = qpos_nxt[rb];
+    }
+    nxt = nxt2;
   }
 }
 
@@ -1080,7 +1116,7 @@ int make_plan(const pkv_pool_desc* d, int n_seqs, int hq, int max_q, int max_seq
     const int64_t items = static_cast<int64_t>(n_seqs) * p->n_splits * d->num_kv_heads;
     p->grid = static_cast<int>(std::max<int64_t>(1, std::min<int64_t>(items, kDecodeWorkgroups)));
     p->items_off = 256;
-    p->partial_off = p->items_off + static_cast<size_t>(n_seqs) * p->n_splits * 16;
+    p->partial_off = p->items_off + static_cast<size_t>(n_seqs) * p->n_splits * 32;
     p->ws_bytes = p->partial_off;
     if (p->n_splits > 1)
       p->ws_bytes += static_cast<size_t>(n_seqs) * max_q * hq * p->n_splits * (d->head_dim + 2) * sizeof(float);
@@ -1121,7 +1157,7 @@ void launch_attention_t(const AttnArgs& a, const Plan& p, int n_seqs, int hkv, h
 template <typename T, int D, int RBW>
 void launch_decode_t(const AttnArgs& a, const Plan& p, int n_seqs, char* ws, hipStream_t st) {
   DecodeQueue* queue = reinterpret_cast<DecodeQueue*>(ws);
-  int4* items = reinterpret_cast<int4*>(ws + p.items_off);
+  DecodeItem* items = reinterpret_cast<DecodeItem*>(ws + p.items_off);
   decode_schedule_kernel<RBW><<<1, kThreads, 0, st>>>(a, queue, items);
   constexpr int kRowB = D * static_cast<int>(sizeof(T));
   constexpr int kStage = 4 * 2 * 16 * (kRowB + (kRowB >= 512 ? 0 : 16));
