@@ -35,6 +35,7 @@
 #include <cmath>
 #include <cstdint>
 #include <string>
+#include <type_traits>
 
 #include "../../include/pkv.h"
 #include "status.h"
@@ -912,6 +913,372 @@ __global__ __launch_bounds__(kThreads, RBW == 1 ? PKV_DECODE_WAVES_PER_SIMD : 1)
   }
 }
 
+// ---------------------------------------------------------------------------
+// Paged prefill/append in bf16 for more than 48 query rows per sequence and
+// KV head.
+//  * A workgroup owns 128 query rows of one (sequence, KV head) unit; rows are
+//    (query, head-in-group) pairs, so every K/V byte it stages serves the
+//    whole GQA group.  Wave w owns rows 32w..32w+31 as two 16-row MFMA
+//    blocks and keeps its own softmax state: no cross-wave combine.
+//  * K/V tiles of 64 positions are gathered through the block table with
+//    16-byte loads into registers one tile ahead and written to one of two
+//    LDS buffers; rows are padded by 16 bytes so every operand read below is
+//    free of bank conflicts.  One barrier per tile.  Block-table entries are
+//    fetched a further tile ahead.
+//  * S^T = K Q^T on v_mfma_f32_16x16x32_bf16 with Q held in registers.  A
+//    lane then holds one query row and 4 positions of each 16-key block: the
+//    row max is in-lane work plus two shuffles.  The reference max of a row
+//    is raised only when a tile's max exceeds it by more than 8 (log2
+//    units), so most tiles skip the rescale and probabilities stay <= 256.
+//  * O^T += V^T P^T on the same MFMA.  P^T is already in B-operand layout
+//    once the MFMA's k index is permuted the same way on both operands
+//    (k-slots 8g..8g+3 <-> keys 4g..4g+3 of the first 16-key block, 8g+4..
+//    8g+7 <-> the same of the second), and V^T comes straight out of LDS with
+//    ds_read_b64_tr_b16.  Row sums run on the MFMA as well (a ones operand
+//    times P^T), from the same bf16 P the numerator uses.
+//  * Workgroups are dealt to the 8 XCDs round robin, so workgroup i serves
+//    unit i % 8 of a block of 8 units: all q-tiles of a unit run on one XCD
+//    and re-read its K/V from that XCD's L2.  Within a block the tiles with
+//    the most keys go first.  A one-workgroup schedule kernel lists the
+//    blocks' tile counts; the grid is a host-side upper bound and surplus
+//    workgroups exit at once.
+// ---------------------------------------------------------------------------
+constexpr int kPfRows = 128;   // query rows per workgroup
+constexpr int kPfKeys = 64;    // positions per staged tile
+
+template <int D>
+constexpr int pf_row_bytes() { return D * 2 + 16; }
+template <int D>
+constexpr int pf_lds_bytes() { return 2 * 2 * kPfKeys * pf_row_bytes<D>(); }
+
+// row_off[k] = sum over blocks < k of (q-tiles of the block) * n_splits,
+// where a block's q-tiles are the most any of its 8 units needs.
+__global__ __launch_bounds__(kThreads) void prefill_schedule_kernel(AttnArgs a, int32_t* row_off,
+                                                                    int n_blocks) {
+  __shared__ int s_scan[kThreads];
+  __shared__ int s_carry;
+  const int tid = threadIdx.x;
+  if (tid == 0) {
+    s_carry = 0;
+    row_off[0] = 0;
+  }
+  __syncthreads();
+  const int units = a.n_seqs * a.num_kv_heads;
+  for (int base = 0; base < n_blocks; base += kThreads) {
+    const int blk = base + tid;
+    int tiles = 0;
+    if (blk < n_blocks) {
+      int prev = -1;
+      for (int u = blk * 8; u < min(units, blk * 8 + 8); ++u) {
+        const int b = u / a.num_kv_heads;
+        if (b == prev) continue;
+        prev = b;
+        const int n_b = a.cu_q[b + 1] - a.cu_q[b];
+        tiles = max(tiles, (n_b * a.group + kPfRows - 1) / kPfRows);
+      }
+    }
+    const int v = tiles * a.n_splits;
+    s_scan[tid] = v;
+    __syncthreads();
+    for (int off = 1; off < kThreads; off <<= 1) {
+      const int w = tid >= off ? s_scan[tid - off] : 0;
+      __syncthreads();
+      s_scan[tid] += w;
+      __syncthreads();
+    }
+    if (blk < n_blocks) row_off[blk + 1] = s_carry + s_scan[tid];
+    __syncthreads();
+    if (tid == kThreads - 1) s_carry += s_scan[tid];
+    __syncthreads();
+  }
+}
+
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) bf16x4 lds_bf16x4;
+
+// Four bf16 of one column of a 4 x 16 block, transposed across a 16-lane
+// group (gfx950 ds_read_b64_tr_b16): lane i of the group receives column i
+// of rows 0..3 when lane k of the group addresses row k / 4, columns
+// 4 (k % 4) .. 4 (k % 4) + 3.
+__device__ __forceinline__ bf16x4 lds_read_tr(const char* p) {
+  return __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(p));
+}
+
+// kPow2: page_size is a power of two (block index by shift).
+template <int D, bool kPow2>
+__global__ __launch_bounds__(kThreads, 2) void paged_prefill_kernel(AttnArgs a,
+                                                                   const int32_t* __restrict__ row_off,
+                                                                   int n_blocks) {
+  constexpr int kRowB = pf_row_bytes<D>();              // LDS row stride, bytes
+  constexpr int kCpr = D * 2 / 16;                      // 16-byte chunks per K/V row
+  constexpr int kChunks = kPfKeys * kCpr / kThreads;    // per thread per pool
+  constexpr int kRowsPerPass = kThreads / kCpr;         // rows staged per chunk index
+  constexpr int kQk = D / 32;                           // MFMAs per 16x16 score block
+  constexpr int kDb = D / 16;                           // 16-dim blocks of O^T
+  constexpr int kTileB = kPfKeys * kRowB;               // bytes of one staged K or V tile
+  static_assert(kChunks * kRowsPerPass == kPfKeys, "tile split");
+  extern __shared__ __align__(16) char smem[];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & (kWave - 1);
+  const int wave = tid / kWave;
+  const int lrow = lane & 15;
+  const int lgrp = lane >> 4;
+
+  // ---- work item ----
+  const int r = blockIdx.x >> 3;
+  if (r >= row_off[n_blocks]) return;
+  int lo = 0, hi = n_blocks;   // row_off[lo] <= r < row_off[hi]
+  while (hi - lo > 1) {
+    const int mid = (lo + hi) >> 1;
+    if (row_off[mid] <= r) lo = mid;
+    else hi = mid;
+  }
+  const int n_sp = a.n_splits;
+  const int local = r - row_off[lo];
+  const int tiles_blk = (row_off[lo + 1] - row_off[lo]) / n_sp;
+  const int qt = tiles_blk - 1 - local / n_sp;
+  const int split = local - (local / n_sp) * n_sp;
+  const int hkv = a.num_kv_heads;
+  const int u = lo * 8 + (blockIdx.x & 7);
+  if (u >= a.n_seqs * hkv) return;
+  const int b = u / hkv;
+  const int g = u - b * hkv;
+  const int group = a.group;
+  const int q0 = a.cu_q[b];
+  const int n_b = a.cu_q[b + 1] - q0;
+  const int rows_total = n_b * group;
+  const int row0 = qt * kPfRows;
+  if (row0 >= rows_total) return;
+  const int start = a.seq_lens[b] - n_b;                 // position of new query 0
+  const int kv_end = start + (min(row0 + kPfRows, rows_total) - 1) / group + 1;
+  const int k_lo = split * a.split_len;
+  if (k_lo >= kv_end) return;
+  const int k_hi = min(k_lo + a.split_len, kv_end);
+  const int n_tiles = (k_hi - k_lo + kPfKeys - 1) / kPfKeys;
+
+  // ---- staging: this thread's rows srow0 + c * kRowsPerPass, chunk spart ----
+  const int ps = a.page_size;
+  const int ps_shift = a.ps_shift;
+  const int32_t* bt_row = a.block_tables + static_cast<int64_t>(b) * a.bt_stride;
+  const int srow0 = tid / kCpr;
+  const int spart = tid - srow0 * kCpr;
+  const uint32_t head_bytes = static_cast<uint32_t>(ps) * D * 2;   // one (page, head) block
+  const char* kbytes = static_cast<const char*>(a.k_pool);
+  const char* vbytes = static_cast<const char*>(a.v_pool);
+
+  int pg_next[kChunks], pg_next2[kChunks];
+  u32x4 kr[kChunks], vr[kChunks];
+  // position of staged row c of tile t (past the split's end: its last position)
+  auto pos_of = [&](int t, int c) __attribute__((always_inline)) {
+    return min(k_lo + t * kPfKeys + srow0 + c * kRowsPerPass, k_hi - 1);
+  };
+  auto blk_of = [&](int pos) __attribute__((always_inline)) {
+    if constexpr (kPow2) return pos >> ps_shift;
+    else return pos / ps;
+  };
+  auto fetch_pages = [&](int t) __attribute__((always_inline)) {
+    const int tl = min(t, n_tiles - 1);
+#pragma unroll
+    for (int c = 0; c < kChunks; ++c) pg_next2[c] = bt_row[blk_of(pos_of(tl, c))];
+  };
+  auto load_kv = [&](int t) __attribute__((always_inline)) {
+    const int tl = min(t, n_tiles - 1);
+#pragma unroll
+    for (int c = 0; c < kChunks; ++c) {
+      const int pos = pos_of(tl, c);
+      const int off = pos - blk_of(pos) * ps;
+      const uint32_t page = static_cast<uint32_t>(min(max(pg_next[c], 0), a.num_pages - 1));
+      const uint64_t boff = static_cast<uint64_t>(page * hkv + g) * head_bytes +
+                            static_cast<uint32_t>(off * (D * 2) + spart * 16);
+      kr[c] = *reinterpret_cast<const u32x4*>(kbytes + boff);
+      vr[c] = *reinterpret_cast<const u32x4*>(vbytes + boff);
+    }
+  };
+  auto stage = [&](int buf) __attribute__((always_inline)) {
+    char* kb = smem + buf * 2 * kTileB;
+    char* vb = kb + kTileB;
+#pragma unroll
+    for (int c = 0; c < kChunks; ++c) {
+      const int row = srow0 + c * kRowsPerPass;
+      *reinterpret_cast<u32x4*>(kb + row * kRowB + spart * 16) = kr[c];
+      *reinterpret_cast<u32x4*>(vb + row * kRowB + spart * 16) = vr[c];
+    }
+  };
+
+  // ---- this lane's two query rows (B operand of S^T = K Q^T) ----
+  // Lane group lgrp holds dims [lgrp * D/4, (lgrp + 1) * D/4); MFMA kk takes
+  // the kk-th 8 of them (the same permutation is applied to K).
+  const int wr0 = row0 + 32 * wave;
+  bf16x8 qf[2][kQk];
+  int qpos[2];
+#pragma unroll
+  for (int rb = 0; rb < 2; ++rb) {
+    const int rr = wr0 + 16 * rb + lrow;
+    const int qi = rr / group;
+    const bool ok = rr < rows_total && q0 + qi < a.total_q;
+    qpos[rb] = ok ? start + qi : -1;
+    const uint16_t* src = static_cast<const uint16_t*>(a.q) +
+                          (static_cast<int64_t>(q0 + qi) * a.num_q_heads + g * group + (rr - qi * group)) * D +
+                          lgrp * (D / 4);
+#pragma unroll
+    for (int kk = 0; kk < kQk; ++kk) {
+      u32x4 v = u32x4{0u, 0u, 0u, 0u};
+      if (ok) v = *reinterpret_cast<const u32x4*>(src + kk * 8);
+      qf[rb][kk] = __builtin_bit_cast(bf16x8, v);
+    }
+  }
+
+  const bool w_active = wr0 < rows_total;
+  const int w_qmin = start + wr0 / group;
+  const int w_qmax = start + (min(wr0 + 31, rows_total - 1)) / group;
+  const float c2 = a.scale_log2;
+
+  f32x4 o[kDb][2];
+  f32x4 lsum[2];
+  float mc[2] = {-INFINITY, -INFINITY};   // reference max per row, log2 units
+#pragma unroll
+  for (int rb = 0; rb < 2; ++rb) {
+    lsum[rb] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int d = 0; d < kDb; ++d) o[d][rb] = f32x4{0.f, 0.f, 0.f, 0.f};
+  }
+  const bf16x8 ones = __builtin_bit_cast(bf16x8, u32x4{0x3f803f80u, 0x3f803f80u, 0x3f803f80u, 0x3f803f80u});
+
+  // lane parts of the LDS operand addresses
+  const int k_lane = lrow * kRowB + lgrp * (D / 4) * 2;
+  const int v_lane = (4 * lgrp + (lrow >> 2)) * kRowB + ((lrow & 3) >> 1) * 16 + (lrow & 1) * 8;
+
+  auto compute = [&](const char* kt, const char* vt, int tb, auto mask_tag) __attribute__((always_inline)) {
+    constexpr bool kMask = decltype(mask_tag)::value;
+    f32x4 s[4][2];
+#pragma unroll
+    for (int kb = 0; kb < 4; ++kb) {
+      bf16x8 kf[kQk];
+#pragma unroll
+      for (int kk = 0; kk < kQk; ++kk)
+        kf[kk] = *reinterpret_cast<const bf16x8*>(kt + k_lane + kb * 16 * kRowB + kk * 16);
+#pragma unroll
+      for (int rb = 0; rb < 2; ++rb) {
+        f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int kk = 0; kk < kQk; ++kk) acc = mfma_qk(kf[kk], qf[rb][kk], acc);
+        s[kb][rb] = acc;
+      }
+    }
+    bf16x8 pk[2][2];
+#pragma unroll
+    for (int rb = 0; rb < 2; ++rb) {
+      if constexpr (kMask) {
+#pragma unroll
+        for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+          for (int i = 0; i < 4; ++i)
+            s[kb][rb][i] = (tb + kb * 16 + 4 * lgrp + i <= qpos[rb]) ? s[kb][rb][i] : -INFINITY;
+      }
+      float mx = s[0][rb][0];
+#pragma unroll
+      for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) mx = fmaxf(mx, s[kb][rb][i]);
+      mx = fmaxf(mx, __shfl_xor(mx, 16));
+      mx = fmaxf(mx, __shfl_xor(mx, 32));
+      const float mxc = mx * c2;
+      const bool up = mxc > mc[rb] + 8.f;
+      const float mnew = up ? mxc : mc[rb];
+      const float alpha = up ? fast_exp2(mc[rb] - mnew) : 1.f;
+      mc[rb] = mnew;
+      if (__any(up)) {
+        lsum[rb] *= alpha;
+#pragma unroll
+        for (int d = 0; d < kDb; ++d) o[d][rb] *= alpha;
+      }
+      const float muse = mnew == -INFINITY ? 0.f : mnew;
+#pragma unroll
+      for (int ks = 0; ks < 2; ++ks) {
+        bf16x8 p;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          p[i] = static_cast<__bf16>(fast_exp2(fmaf(s[2 * ks][rb][i], c2, -muse)));
+          p[4 + i] = static_cast<__bf16>(fast_exp2(fmaf(s[2 * ks + 1][rb][i], c2, -muse)));
+        }
+        pk[rb][ks] = p;
+        lsum[rb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ones, p, lsum[rb], 0, 0, 0);
+      }
+    }
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks) {
+#pragma unroll
+      for (int d = 0; d < kDb; ++d) {
+        const char* vp = vt + v_lane + 32 * ks * kRowB + d * 32;
+        const bf16x4 v0 = lds_read_tr(vp);
+        const bf16x4 v1 = lds_read_tr(vp + 16 * kRowB);
+        const bf16x8 vf = __builtin_shufflevector(v0, v1, 0, 1, 2, 3, 4, 5, 6, 7);
+#pragma unroll
+        for (int rb = 0; rb < 2; ++rb)
+          o[d][rb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf, pk[rb][ks], o[d][rb], 0, 0, 0);
+      }
+    }
+  };
+
+  // ---- main loop over the split's tiles ----
+  fetch_pages(0);
+#pragma unroll
+  for (int c = 0; c < kChunks; ++c) pg_next[c] = pg_next2[c];
+  load_kv(0);
+  fetch_pages(1);
+  stage(0);
+#pragma unroll
+  for (int c = 0; c < kChunks; ++c) pg_next[c] = pg_next2[c];
+  __syncthreads();
+  for (int t = 0; t < n_tiles; ++t) {
+    load_kv(t + 1);            // clamped: the last tile reloads itself
+    fetch_pages(t + 2);
+    const int tb = k_lo + t * kPfKeys;
+    if (w_active && tb <= w_qmax) {
+      const char* kt = smem + (t & 1) * 2 * kTileB;
+      if (tb + kPfKeys - 1 <= w_qmin)
+        compute(kt, kt + kTileB, tb, std::integral_constant<bool, false>());
+      else
+        compute(kt, kt + kTileB, tb, std::integral_constant<bool, true>());
+    }
+    stage((t + 1) & 1);
+#pragma unroll
+    for (int c = 0; c < kChunks; ++c) pg_next[c] = pg_next2[c];
+    __syncthreads();
+  }
+
+  // ---- epilogue: rows of this wave ----
+  if (!w_active) return;
+  const bool final_write = n_sp == 1;
+#pragma unroll
+  for (int rb = 0; rb < 2; ++rb) {
+    const int rr = wr0 + 16 * rb + lrow;
+    if (qpos[rb] < 0) continue;
+    const int qi = rr / group;
+    const int tok = q0 + qi;
+    const int64_t orow = static_cast<int64_t>(tok) * a.num_q_heads + g * group + (rr - qi * group);
+    const float l = lsum[rb][0];
+    if (final_write) {
+      const float inv = l > 0.f ? 1.f / l : 0.f;
+      uint16_t* dst = static_cast<uint16_t*>(a.out) + orow * D + 4 * lgrp;
+#pragma unroll
+      for (int d = 0; d < kDb; ++d)
+        *reinterpret_cast<i16x4*>(dst + 16 * d) = pack_bf16x4(o[d][rb] * inv);
+    } else {
+      if (tok >= a.ws_tokens) continue;
+      const int64_t slot = orow * n_sp + split;
+      float* dst = a.ws_o + slot * D + 4 * lgrp;
+#pragma unroll
+      for (int d = 0; d < kDb; ++d) *reinterpret_cast<f32x4*>(dst + 16 * d) = o[d][rb];
+      if (lgrp == 0) {
+        a.ws_ml[slot * 2] = mc[rb];
+        a.ws_ml[slot * 2 + 1] = l;
+      }
+    }
+  }
+}
+
 // Log-sum-exp merge of the KV-split partials of one (query, head) row.  Grid:
 // (num_q_heads, max_q_per_seq, n_seqs), one wave per row.  RBW > 0: the
 // decode path, where rows whose sequence fits one chunk were written final
@@ -1049,12 +1416,16 @@ int check_desc(const pkv_pool_desc* d, const char* fn) {
   if (static_cast<int64_t>(d->num_pages) * d->num_kv_heads * d->page_size * d->head_dim >
       (int64_t{1} << 40))
     return fail(PKV_ERR_UNSUPPORTED, std::string(fn) + ": pool larger than 2^40 elements");
+  if (static_cast<int64_t>(d->num_pages) * d->num_kv_heads > INT32_MAX)
+    return fail(PKV_ERR_UNSUPPORTED, std::string(fn) + ": num_pages * num_kv_heads above 2^31 - 1");
   return PKV_OK;
 }
 
 struct Plan {
   int max_q = 0;
-  bool decode = false;  // decode path (few rows) vs paged_attention_kernel (tiles)
+  bool decode = false;  // decode path (few rows) vs a tile kernel
+  bool prefill = false; // bf16 tiles: paged_prefill_kernel, else paged_attention_kernel
+  int n_blocks = 0;     // prefill: blocks of 8 (sequence, KV head) units
   int rbw = 1;          // decode: 16-row blocks each wave holds
   int epi_rows = 16;    // decode: rows of a block that carry queries
   int rb = 4, kg = 1;   // tile kernel: row blocks x key groups of the 4 waves
@@ -1122,6 +1493,31 @@ int make_plan(const pkv_pool_desc* d, int n_seqs, int hq, int max_q, int max_seq
       p->ws_bytes += static_cast<size_t>(n_seqs) * max_q * hq * p->n_splits * (d->head_dim + 2) * sizeof(float);
     return PKV_OK;
   }
+  if (d->dtype == PKV_BF16) {
+    // paged_prefill_kernel: 128-row tiles; KV splits only when the units'
+    // tiles alone cannot fill the chip.
+    p->prefill = true;
+    p->tile_rows = kPfRows;
+    if (rows > (int64_t{1} << 28)) return fail(PKV_ERR_UNSUPPORTED, std::string(fn) + ": too many queries per sequence");
+    const int64_t q_tiles = (rows + kPfRows - 1) / kPfRows;
+    p->q_tiles = static_cast<int>(q_tiles);
+    const int64_t units = static_cast<int64_t>(n_seqs) * d->num_kv_heads;
+    p->n_blocks = static_cast<int>((units + 7) / 8);
+    const int64_t max_tiles = (static_cast<int64_t>(max_seq_len) + kPfKeys - 1) / kPfKeys;
+    int64_t want = (kTargetWorkgroups + units * q_tiles - 1) / (units * q_tiles);
+    want = std::max<int64_t>(1, std::min<int64_t>(want, (max_seq_len + kMinSplitKeys - 1) / kMinSplitKeys));
+    const int64_t tiles_per_split = std::max<int64_t>(1, (max_tiles + want - 1) / want);
+    p->split_len = static_cast<int>(tiles_per_split * kPfKeys);
+    p->n_splits = static_cast<int>(std::max<int64_t>(1, (max_tiles + tiles_per_split - 1) / tiles_per_split));
+    const int64_t sched_rows = static_cast<int64_t>(p->n_blocks) * q_tiles * p->n_splits;
+    if (sched_rows > (int64_t{1} << 27)) return fail(PKV_ERR_UNSUPPORTED, std::string(fn) + ": too many work items");
+    p->items_off = 0;
+    p->partial_off = (static_cast<size_t>(p->n_blocks + 1) * sizeof(int32_t) + 255) & ~size_t{255};
+    p->ws_bytes = p->partial_off;
+    if (p->n_splits > 1)
+      p->ws_bytes += static_cast<size_t>(n_seqs) * max_q * hq * p->n_splits * (d->head_dim + 2) * sizeof(float);
+    return PKV_OK;
+  }
   p->rb = 4;
   p->kg = 1;
   p->tile_rows = 16 * p->rb;
@@ -1173,6 +1569,34 @@ void launch_decode_t(const AttnArgs& a, const Plan& p, int n_seqs, char* ws, hip
     dim3 grid(a.num_q_heads, p.max_q, n_seqs);
     merge_chunks_kernel<T, D, RBW><<<grid, dim3(kWave), 0, st>>>(a);
   }
+}
+
+// Upper bound on the prefill tile-rows the schedule kernel can list, from
+// host scalars: a block's q-tiles are at most its units' sequences' q-tiles
+// summed, and a sequence's units fall in at most hkv / 8 + 2 blocks.
+int64_t prefill_grid(const Plan& p, int n_seqs, int hkv, int group, int total_q) {
+  const int64_t tiles_all = (static_cast<int64_t>(total_q) * group + kPfRows - 1) / kPfRows + n_seqs;
+  const int64_t per_seq_blocks = hkv % 8 == 0 ? hkv / 8 : hkv / 8 + 2;
+  const int64_t rows = std::min<int64_t>(static_cast<int64_t>(p.n_blocks) * p.q_tiles, per_seq_blocks * tiles_all);
+  return 8 * rows * p.n_splits;
+}
+
+template <int D, bool kPow2>
+int launch_prefill_t(const AttnArgs& a, const Plan& p, char* ws, hipStream_t st) {
+  constexpr int kLds = pf_lds_bytes<D>();
+  static const hipError_t attr = hipFuncSetAttribute(reinterpret_cast<const void*>(&paged_prefill_kernel<D, kPow2>),
+                                                     hipFuncAttributeMaxDynamicSharedMemorySize, kLds);
+  if (attr != hipSuccess) return fail(PKV_ERR_DEVICE, std::string("prefill: LDS attribute: ") + hipGetErrorString(attr));
+  int32_t* row_off = reinterpret_cast<int32_t*>(ws + p.items_off);
+  prefill_schedule_kernel<<<1, kThreads, 0, st>>>(a, row_off, p.n_blocks);
+  const int64_t grid = prefill_grid(p, a.n_seqs, a.num_kv_heads, a.group, a.total_q);
+  if (grid > INT32_MAX) return fail(PKV_ERR_UNSUPPORTED, "prefill: grid too large");
+  if (grid > 0) paged_prefill_kernel<D, kPow2><<<static_cast<int>(grid), dim3(kThreads), kLds, st>>>(a, row_off, p.n_blocks);
+  if (p.n_splits > 1) {
+    dim3 mg(a.num_q_heads, p.max_q, a.n_seqs);
+    merge_chunks_kernel<uint16_t, D, 0><<<mg, dim3(kWave), 0, st>>>(a);
+  }
+  return PKV_OK;
 }
 
 template <typename T, int D>
@@ -1246,7 +1670,14 @@ int run_attention(const char* fn, const pkv_pool_desc* desc, const void* k_pool,
   const int hkv = desc->num_kv_heads;
   char* ws = static_cast<char*>(workspace);
   (void)hipGetLastError();
-  if (desc->dtype == PKV_BF16) {
+  if (p.prefill) {
+    const bool pow2 = a.ps_shift >= 0;
+    if (desc->head_dim == 128)
+      rc = pow2 ? launch_prefill_t<128, true>(a, p, ws, st) : launch_prefill_t<128, false>(a, p, ws, st);
+    else
+      rc = pow2 ? launch_prefill_t<64, true>(a, p, ws, st) : launch_prefill_t<64, false>(a, p, ws, st);
+    if (rc != PKV_OK) return rc;
+  } else if (desc->dtype == PKV_BF16) {
     if (desc->head_dim == 128)
       launch_attention_d<uint16_t, 128>(a, p, n_seqs, hkv, ws, st);
     else

@@ -304,6 +304,48 @@ def test_prefill_mixed_query_counts():
         row += n_new[b]
 
 
+class _Pools:
+    """Minimal pool description for hand-built prefill cases."""
+
+    def __init__(self, dtype, D, ps, hkv, num_pages, seed):
+        self.dtype, self.head_dim, self.page_size = dtype, D, ps
+        self.num_kv_heads, self.num_pages = hkv, num_pages
+        self.free_order = np.random.default_rng(seed).permutation(num_pages).astype(np.int32)
+
+
+@pytest.mark.parametrize("dtype,D,ps,hq,hkv,ctx,news", [
+    (synth.BF16, 128, 16, 32, 8, [300, 0, 1000], [200, 64, 150]),
+    (synth.BF16, 64, 3, 8, 8, [100, 37], [49, 130]),
+    (synth.BF16, 128, 64, 16, 2, [500, 20, 90, 0], [80, 300, 13, 64]),
+    (synth.BF16, 128, 1, 1, 1, [3000], [60]),
+    (synth.BF16, 64, 16, 6, 3, [2500, 700], [100, 20]),
+    (synth.F32, 64, 4, 4, 2, [100, 30], [70, 40]),
+])
+def test_prefill_variants(dtype, D, ps, hq, hkv, ctx, news):
+    """Append of several queries per sequence over cached positions: GQA groups
+    1..16, page sizes 1..64 (power of two or not), one or several KV splits,
+    KV-head counts that do or do not fill blocks of 8 units."""
+    print(f"prefill variant {dtype} D={D} ps={ps} hq={hq} hkv={hkv} ctx={ctx} new={news}", flush=True)
+    rng = np.random.default_rng(D * 7 + ps)
+    lens = [c + n for c, n in zip(ctx, news)]
+    pages = sum(-(-L // ps) for L in lens) + 3
+    s = Session.open(_Pools(dtype, D, ps, hkv, pages, seed=ps + hq))
+    seqs = [s.alloc.seq_new() for _ in lens]
+    kv = [synth.normal_values(rng, (2, L, hkv, D), dtype) for L in lens]
+    for b, seq in enumerate(seqs):
+        s.alloc.reserve(seq, lens[b])
+        s.store(seq, 0, kv[b][0], kv[b][1], dtype)
+    qs = [synth.normal_values(rng, (n, hq, D), dtype) for n in news]
+    out = host_f64(s.append(seqs, news, dev_tensor(np.concatenate(qs), dtype)))
+    row = 0
+    for b in range(len(lens)):
+        if news[b]:
+            e = attend(synth.to_f64(qs[b], dtype), synth.to_f64(kv[b][0], dtype),
+                       synth.to_f64(kv[b][1], dtype), s.scale)
+            check_close(out[row:row + news[b]], e, dtype, f"prefill variant seq {b}")
+        row += news[b]
+
+
 # ---------------------------------------------------------------------------
 # full-size workloads, sampled outputs
 # ---------------------------------------------------------------------------

@@ -190,7 +190,9 @@ def test_validate_tables(pkv_lib):
 def test_workspace_and_descriptor_checks(pkv_lib):
     ok = pkv.PoolDesc(pkv.PKV_BF16, 300_000, 16, 8, 128)
     assert pkv.workspace_bytes(ok, 64, 32, 1, 4096) > 0        # long contexts are split
-    assert pkv.workspace_bytes(ok, 256, 32, 8000, 8000) == 0   # long prefill: one split
+    # long prefill: one split, so only the work table of (256 * 8 / 8 + 1) int32
+    assert pkv.workspace_bytes(ok, 256, 32, 8000, 8000) == 1280
+    assert pkv.workspace_bytes(pkv.PoolDesc(pkv.PKV_F32, 1000, 16, 8, 128), 256, 32, 8000, 8000) == 0
     for bad in [pkv.PoolDesc(7, 10, 16, 8, 128), pkv.PoolDesc(pkv.PKV_BF16, 10, 16, 8, 96),
                 pkv.PoolDesc(pkv.PKV_BF16, 10, 0, 8, 128), pkv.PoolDesc(pkv.PKV_BF16, 10, 300, 8, 128)]:
         assert pkv.workspace_bytes(bad, 4, 32, 1, 100) == 0
