@@ -38,6 +38,7 @@ if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0
+MFMA_BF16_PEAK_TFLOPS = 2500.0   # dense bf16 MFMA, MI355X
 METRIC = "paged-decode KV GB/s (% of HBM peak); prefill-append tokens/s (% MFMA peak)"
 
 
@@ -55,7 +56,120 @@ def parse():
     ap.add_argument("--cpu-seconds", type=float, default=15.0,
                     help="bound on the CPU oracle's sample (0 disables the cpu_baseline leg)")
     ap.add_argument("--seed", type=int, default=0)
+    ap.add_argument("--prefill-reps", type=int, default=10,
+                    help="timed repetitions of the prefix-shared prefill leg (0 disables it)")
+    ap.add_argument("--copy-calibration-mib", type=int, default=0,
+                    help="finally copy a buffer of this many MiB three times (a plain copy of known "
+                         "size, the reference for the FETCH_SIZE / WRITE_SIZE counters)")
     return ap.parse_args()
+
+
+def prefill_leg(args, torch, pkv, synth, dev: str) -> dict:
+    """The prefix-shared prefill workload: 256 agent-trace rows (the first
+    three 1,000 / 1,400 / 1,900 tokens of one trace, the rest U{1000..8000}
+    tokens of 31 others), 16-position pages over a shuffled 100,000-page pool,
+    32 / 8 heads of 128, bf16.  The C++ planner sorts the rows and the
+    allocator adopts each row's shared full pages from its parent; one step
+    stores every row's unshared suffix (store_kv) and runs one causal
+    prefill/append over all suffixes.  Q/K/V values are N(0,1) drawn on the
+    device from a seeded torch generator (the structure comes from the same
+    seeded host generator the parity tests use)."""
+    w = synth.prefix_traces(seed=args.seed, values=False)
+    ps, hq, hkv, D = w.page_size, w.num_q_heads, w.num_kv_heads, w.head_dim
+    n = len(w.row_len)
+    t0 = time.perf_counter()
+    order, parent, shared = pkv.plan_prefix([w.row_tokens(r) for r in range(n)], ps)
+    plan_ms = (time.perf_counter() - t0) * 1e3
+    desc = pkv.PoolDesc(pkv.PKV_BF16, w.num_pages, ps, hkv, D)
+    k_pool = torch.full(desc.pool_shape, float("nan"), dtype=torch.bfloat16, device=dev)
+    v_pool = torch.full_like(k_pool, float("nan"))
+    alloc = pkv.Allocator(w.num_pages, ps, w.free_order)
+    seqs = [-1] * n
+    lens = w.row_len.astype(np.int64)
+    sh = shared.astype(np.int64)
+    for d in order.tolist():
+        seqs[d] = alloc.seq_new()
+        if parent[d] >= 0:
+            alloc.share_prefix(seqs[d], seqs[parent[d]], int(sh[d]))
+        alloc.reserve(seqs[d], int(lens[d] - sh[d]))
+    n_new = (lens - sh).astype(np.int64)
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(1000 + args.seed)
+    n_tr, t_len = w.trace_tokens.shape
+    flat = torch.from_numpy(np.concatenate(
+        [w.row_trace[d] * t_len + np.arange(sh[d], lens[d]) for d in range(n)])).to(dev)
+
+    def draw(heads):
+        x = torch.empty((n_tr * t_len, heads, D), dtype=torch.bfloat16, device=dev)
+        for t in range(n_tr):
+            x[t * t_len:(t + 1) * t_len] = torch.randn((t_len, heads, D), generator=gen, device=dev).to(torch.bfloat16)
+        return x[flat].contiguous()
+
+    q, k_new, v_new = draw(hq), draw(hkv), draw(hkv)
+    slots = torch.from_numpy(np.concatenate(
+        [alloc.slots(seqs[d], int(sh[d]), int(n_new[d])) for d in range(n)])).to(dev)
+    stride = max(alloc.num_blocks(x) for x in seqs)
+    bt = torch.from_numpy(alloc.block_tables(seqs, stride)).to(dev)
+    d_lens = torch.from_numpy(lens.astype(np.int32)).to(dev)
+    cu = torch.from_numpy(np.concatenate([[0], np.cumsum(n_new)]).astype(np.int32)).to(dev)
+    max_q, max_len = int(n_new.max()), int(lens.max())
+    ws = torch.empty(max(16, pkv.workspace_bytes(desc, n, hq, max_q, max_len)), dtype=torch.uint8, device=dev)
+    out = torch.empty_like(q)
+    scale = 1.0 / float(np.sqrt(D))
+
+    def step(ev=None):
+        if ev:
+            ev[0].record()
+        pkv.store_kv(desc, k_pool, v_pool, k_new, v_new, slots)
+        if ev:
+            ev[1].record()
+        pkv.prefill_append(desc, k_pool, v_pool, q, cu, bt, d_lens, max_q, max_len, scale, out, ws)
+        if ev:
+            ev[2].record()
+
+    for _ in range(2):
+        step()
+    torch.cuda.synchronize()
+    evs = [tuple(torch.cuda.Event(enable_timing=True) for _ in range(3)) for _ in range(args.prefill_reps)]
+    t0 = time.perf_counter()
+    for ev in evs:
+        step(ev)
+    torch.cuda.synchronize()
+    wall = (time.perf_counter() - t0) / args.prefill_reps
+    store_ms = np.array([a.elapsed_time(b) for a, b, _ in evs])
+    attn_ms = np.array([b.elapsed_time(c) for _, b, c in evs])
+    assert torch.isfinite(out.float()).all(), "non-finite prefill output"
+    tokens = int(n_new.sum())
+    pairs = int(sum((lens[d] * (lens[d] + 1) - sh[d] * (sh[d] + 1)) // 2 for d in range(n)))
+    flops = 4.0 * D * hq * pairs
+    attn_s = float(attn_ms.mean()) / 1e3
+    achieved = flops / attn_s / 1e12
+    return {
+        "workload": "prefix-shared prefill: 256 agent-trace rows (1,000/1,400/1,900 tokens of one trace, "
+                    "then U{1000..8000} of 31 traces), page_size 16, 100k-page shuffled pool, 32 q / 8 KV "
+                    "heads, head_dim 128, bf16; step = store_kv of unshared suffixes + one prefill_append",
+        "value": round(tokens / wall, 1),
+        "unit": "tokens/s",
+        "tokens_per_step": tokens,
+        "tokens_unshared": int(lens.sum()),
+        "ms_per_step": round(wall * 1e3, 3),
+        "reps": args.prefill_reps,
+        "planner_ms": round(plan_ms, 2),
+        "store_kv_avg_us": round(float(store_ms.mean()) * 1e3, 1),
+        "roofline": {
+            "bound": "mfma",
+            "achieved": round(achieved, 1),
+            "peak": MFMA_BF16_PEAK_TFLOPS,
+            "unit": "TFLOP/s",
+            "frac": round(achieved / MFMA_BF16_PEAK_TFLOPS, 4),
+            "traffic": None,
+            "kernel": "pkv_prefill_append (prefill_schedule_kernel + paged_prefill_kernel)",
+            "kernel_avg_us": round(attn_s * 1e6, 1),
+            "kernel_median_us": round(float(np.median(attn_ms)) * 1e3, 1),
+            "algorithmic_flops_per_launch": flops,
+            "unmasked_pairs": pairs,
+        },
+    }
 
 
 def cpu_baseline(w, scale: float, budget_s: float):
@@ -146,20 +260,26 @@ def main():
     torch.cuda.synchronize()
 
     # pinned staging, double-buffered: the host fills set k%2 while the copy
-    # of the previous step's set may still be in flight
+    # of the previous step's set may still be in flight.  One buffer per set
+    # holds slots (int64 [B]), block tables (int32 [B][stride]) and lengths
+    # (int32 [B]), so a step uploads them with one copy.
+    nbytes = B * 8 + B * stride * 4 + B * 4
+
+    def views(buf):
+        return (buf[:B * 8].view(torch.int64), buf[B * 8:B * 8 + B * stride * 4].view(torch.int32).view(B, stride),
+                buf[B * 8 + B * stride * 4:nbytes].view(torch.int32))
+
     pinned = []
     for _ in range(2):
-        pinned.append({
-            "slots": torch.empty(B, dtype=torch.int64, pin_memory=True),
-            "bt": torch.empty((B, stride), dtype=torch.int32, pin_memory=True),
-            "lens": torch.empty(B, dtype=torch.int32, pin_memory=True),
-            "done": None,
-        })
-    d_slots = torch.empty(B, dtype=torch.int64, device=dev)
-    d_bt = torch.empty((B, stride), dtype=torch.int32, device=dev)
-    d_lens = torch.empty(B, dtype=torch.int32, device=dev)
+        hb = torch.empty(nbytes, dtype=torch.uint8, pin_memory=True)
+        hs, hbt, hl = views(hb)
+        pinned.append({"buf": hb, "np": (hs.numpy(), hbt.numpy(), hl.numpy()), "done": torch.cuda.Event()})
+    d_buf = torch.empty(nbytes, dtype=torch.uint8, device=dev)
+    d_slots, d_bt, d_lens = views(d_buf)
     ones = np.ones(B, np.int32)
     stream = torch.cuda.current_stream()
+    store_call = pkv.bind_store_kv(desc, k_pool, v_pool, k_new, v_new, d_slots, stream)
+    decode_call = pkv.bind_decode(desc, k_pool, v_pool, q, d_bt, d_lens, max_len, scale, out, ws, stream)
     ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
           for _ in range(args.steps)]
     kv_bytes = []
@@ -167,20 +287,16 @@ def main():
     def step(k: int, timed_idx: int):
         r = k % R
         buf = pinned[k % 2]
-        if buf["done"] is not None:
+        if k >= 2:
             buf["done"].synchronize()
-        s_np, bt_np, l_np = buf["slots"].numpy(), buf["bt"].numpy(), buf["lens"].numpy()
+        s_np, bt_np, l_np = buf["np"]
         alloc.prepare_step(inst[r], ones, stride, s_np, bt_np, l_np)
-        d_slots.copy_(buf["slots"], non_blocking=True)
-        d_bt.copy_(buf["bt"], non_blocking=True)
-        d_lens.copy_(buf["lens"], non_blocking=True)
-        e = torch.cuda.Event()
-        e.record(stream)
-        buf["done"] = e
-        pkv.store_kv(desc, k_pool, v_pool, k_new, v_new, d_slots)
+        d_buf.copy_(buf["buf"], non_blocking=True)
+        buf["done"].record(stream)
+        store_call()
         if timed_idx >= 0:
             ev[timed_idx][0].record(stream)
-        pkv.decode(desc, k_pool, v_pool, q, d_bt, d_lens, max_len, scale, out, ws)
+        decode_call()
         if timed_idx >= 0:
             ev[timed_idx][1].record(stream)
             kv_bytes.append(int(l_np.astype(np.int64).sum()) * per_pos)
@@ -231,12 +347,25 @@ def main():
             "unit": "GB/s",
             "frac": round(achieved / HBM_PEAK_GBS, 4),
             "traffic": None,
-            "kernel": "pkv_decode (paged_attention_kernel + merge_splits_kernel)",
+            "kernel": "pkv_decode (decode_schedule_kernel + paged_decode_kernel + merge_chunks_kernel)",
             "kernel_avg_us": round(dec_avg_s * 1e6, 2),
             "kernel_median_us": round(float(np.median(dec_ms)) * 1e3, 2),
             "algorithmic_bytes_per_launch": int(alg_per_launch),
         },
     }
+    del k_pool, v_pool
+    torch.cuda.empty_cache()
+    if args.prefill_reps > 0:
+        rec["prefill_append"] = prefill_leg(args, torch, pkv, synth, dev)
+    if args.copy_calibration_mib > 0:
+        n_f32 = args.copy_calibration_mib * (1 << 20) // 4
+        src = torch.ones(n_f32, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        rec["copy_calibration_bytes"] = n_f32 * 4
+        del src, dst
     if args.cpu_seconds > 0:
         rec["cpu_baseline"] = cpu_baseline(w, scale, args.cpu_seconds)
     print(json.dumps(rec), flush=True)

@@ -28,10 +28,13 @@ accounting  closed forms for KV bytes per position and per layer (TileInfer.jl
             section 2.2 eq. (7)).
 
 Pinning status (what each function is checked against, in ``tests/``):
-  paging      P3 worked example (block counts, B=[P3,P0], C=[P1,P4], P5 growth),
+  paging      the worked example of "KV Cache Management and PagedAttention"
+              (block counts; B in physical blocks 3, 0 and C in 1, 4; growth
+              into block 5),
               invariants (truncate-then-reserve returns the same pages,
               all-or-nothing OOM).
-  planner     P1 worked example (order/parent/shared, 1,916 vs 4,300 tokens);
+  planner     Quail "KV" worked example (order/parent/shared, 1,916 vs 4,300
+              tokens);
               brute force on tiny alphabets (maximal sharing, page identity).
               The parent-link chase is pinned only by the page-identity
               invariant: the pages' example never walks a link.

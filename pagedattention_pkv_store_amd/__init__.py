@@ -23,6 +23,7 @@ __all__ = [
     "PkvError", "OutOfPagesError", "SharedPageError", "UnsupportedError",
     "PoolDesc", "Allocator", "plan_prefix", "store_kv", "decode", "prefill_append",
     "workspace_bytes", "validate_tables", "PKV_F32", "PKV_BF16",
+    "BoundCall", "bind_store_kv", "bind_decode", "bind_prefill_append",
 ]
 
 
@@ -268,15 +269,40 @@ def _stream(stream):
     return ctypes.c_void_p(s.cuda_stream)
 
 
-def store_kv(desc: PoolDesc, k_pool, v_pool, k_new, v_new, slots, stream=None) -> None:
-    """Scatter new K/V rows [T][Hkv][D] into the pools at int64 ``slots``."""
+class BoundCall:
+    """A device call whose arguments were checked and marshalled once.
+
+    Calling it enqueues the same launch again, with the same pointers, sizes
+    and stream, for loops that repeat a call on fixed buffers (the values in
+    those buffers may change between calls).  It keeps the tensors it was
+    bound to alive."""
+
+    __slots__ = ("_fn", "_args", "_keep")
+
+    def __init__(self, fn, args, keep):
+        self._fn, self._args, self._keep = fn, args, keep
+
+    def __call__(self) -> None:
+        rc = self._fn(*self._args)
+        if rc != _lib.PKV_OK:
+            _check(rc)
+
+
+def bind_store_kv(desc: PoolDesc, k_pool, v_pool, k_new, v_new, slots, stream=None) -> BoundCall:
+    """pkv_store_kv with its arguments bound (see store_kv)."""
     import torch
     dt = desc.torch_dtype()
     n = int(slots.numel())
-    _check(_lib.lib().pkv_store_kv(
-        ctypes.byref(desc.c()), _dev(k_pool, "k_pool", dt), _dev(v_pool, "v_pool", dt),
-        _dev(k_new, "k_new", dt), _dev(v_new, "v_new", dt), _dev(slots, "slots", torch.int64),
-        n, _stream(stream)))
+    c_desc = desc.c()
+    args = (ctypes.byref(c_desc), _dev(k_pool, "k_pool", dt), _dev(v_pool, "v_pool", dt),
+            _dev(k_new, "k_new", dt), _dev(v_new, "v_new", dt), _dev(slots, "slots", torch.int64),
+            n, _stream(stream))
+    return BoundCall(_lib.lib().pkv_store_kv, args, (c_desc, k_pool, v_pool, k_new, v_new, slots))
+
+
+def store_kv(desc: PoolDesc, k_pool, v_pool, k_new, v_new, slots, stream=None) -> None:
+    """Scatter new K/V rows [T][Hkv][D] into the pools at int64 ``slots``."""
+    bind_store_kv(desc, k_pool, v_pool, k_new, v_new, slots, stream)()
 
 
 def workspace_bytes(desc: PoolDesc, n_seqs: int, num_q_heads: int, max_q_per_seq: int,
@@ -286,7 +312,6 @@ def workspace_bytes(desc: PoolDesc, n_seqs: int, num_q_heads: int, max_q_per_seq
 
 
 def _workspace(ws, need):
-    import torch
     if need == 0:
         return ctypes.c_void_p(ws.data_ptr() if ws is not None else 0), 0
     if ws is None:
@@ -295,37 +320,56 @@ def _workspace(ws, need):
     return ctypes.c_void_p(ws.data_ptr()), ws.numel() * ws.element_size()
 
 
-def decode(desc: PoolDesc, k_pool, v_pool, q, block_tables, seq_lens, max_seq_len: int,
-           scale: float, out, workspace=None, stream=None) -> None:
-    """Paged decode: q [B][Hq][D] -> out [B][Hq][D] (one new query per sequence)."""
+def bind_decode(desc: PoolDesc, k_pool, v_pool, q, block_tables, seq_lens, max_seq_len: int,
+                scale: float, out, workspace=None, stream=None) -> BoundCall:
+    """pkv_decode with its arguments bound (see decode)."""
     import torch
     dt = desc.torch_dtype()
     n_seqs, hq, _ = q.shape
     need = workspace_bytes(desc, n_seqs, hq, 1, max_seq_len)
     ws_ptr, ws_bytes = _workspace(workspace, need)
-    _check(_lib.lib().pkv_decode(
-        ctypes.byref(desc.c()), _dev(k_pool, "k_pool", dt), _dev(v_pool, "v_pool", dt),
-        _dev(q, "q", dt), n_seqs, hq, _dev(block_tables, "block_tables", torch.int32),
-        int(block_tables.shape[1]), _dev(seq_lens, "seq_lens", torch.int32), max_seq_len,
-        float(scale), _dev(out, "out", dt), ws_ptr, ws_bytes, _stream(stream)))
+    c_desc = desc.c()
+    args = (ctypes.byref(c_desc), _dev(k_pool, "k_pool", dt), _dev(v_pool, "v_pool", dt),
+            _dev(q, "q", dt), n_seqs, hq, _dev(block_tables, "block_tables", torch.int32),
+            int(block_tables.shape[1]), _dev(seq_lens, "seq_lens", torch.int32), max_seq_len,
+            float(scale), _dev(out, "out", dt), ws_ptr, ws_bytes, _stream(stream))
+    keep = (c_desc, k_pool, v_pool, q, block_tables, seq_lens, out, workspace)
+    return BoundCall(_lib.lib().pkv_decode, args, keep)
 
 
-def prefill_append(desc: PoolDesc, k_pool, v_pool, q, cu_q, block_tables, seq_lens,
-                   max_q_per_seq: int, max_seq_len: int, scale: float, out, workspace=None,
-                   stream=None) -> None:
-    """Paged prefill/append over packed queries q [Tq][Hq][D] -> out [Tq][Hq][D]."""
+def decode(desc: PoolDesc, k_pool, v_pool, q, block_tables, seq_lens, max_seq_len: int,
+           scale: float, out, workspace=None, stream=None) -> None:
+    """Paged decode: q [B][Hq][D] -> out [B][Hq][D] (one new query per sequence)."""
+    bind_decode(desc, k_pool, v_pool, q, block_tables, seq_lens, max_seq_len, scale, out,
+                workspace, stream)()
+
+
+def bind_prefill_append(desc: PoolDesc, k_pool, v_pool, q, cu_q, block_tables, seq_lens,
+                        max_q_per_seq: int, max_seq_len: int, scale: float, out, workspace=None,
+                        stream=None) -> BoundCall:
+    """pkv_prefill_append with its arguments bound (see prefill_append)."""
     import torch
     dt = desc.torch_dtype()
     total_q, hq, _ = q.shape
     n_seqs = int(cu_q.numel()) - 1
     need = workspace_bytes(desc, n_seqs, hq, max_q_per_seq, max_seq_len)
     ws_ptr, ws_bytes = _workspace(workspace, need)
-    _check(_lib.lib().pkv_prefill_append(
-        ctypes.byref(desc.c()), _dev(k_pool, "k_pool", dt), _dev(v_pool, "v_pool", dt),
-        _dev(q, "q", dt), total_q, _dev(cu_q, "cu_q", torch.int32), n_seqs, hq,
-        _dev(block_tables, "block_tables", torch.int32), int(block_tables.shape[1]),
-        _dev(seq_lens, "seq_lens", torch.int32), max_q_per_seq, max_seq_len, float(scale),
-        _dev(out, "out", dt), ws_ptr, ws_bytes, _stream(stream)))
+    c_desc = desc.c()
+    args = (ctypes.byref(c_desc), _dev(k_pool, "k_pool", dt), _dev(v_pool, "v_pool", dt),
+            _dev(q, "q", dt), total_q, _dev(cu_q, "cu_q", torch.int32), n_seqs, hq,
+            _dev(block_tables, "block_tables", torch.int32), int(block_tables.shape[1]),
+            _dev(seq_lens, "seq_lens", torch.int32), max_q_per_seq, max_seq_len, float(scale),
+            _dev(out, "out", dt), ws_ptr, ws_bytes, _stream(stream))
+    keep = (c_desc, k_pool, v_pool, q, cu_q, block_tables, seq_lens, out, workspace)
+    return BoundCall(_lib.lib().pkv_prefill_append, args, keep)
+
+
+def prefill_append(desc: PoolDesc, k_pool, v_pool, q, cu_q, block_tables, seq_lens,
+                   max_q_per_seq: int, max_seq_len: int, scale: float, out, workspace=None,
+                   stream=None) -> None:
+    """Paged prefill/append over packed queries q [Tq][Hq][D] -> out [Tq][Hq][D]."""
+    bind_prefill_append(desc, k_pool, v_pool, q, cu_q, block_tables, seq_lens, max_q_per_seq,
+                        max_seq_len, scale, out, workspace, stream)()
 
 
 def validate_tables(desc: PoolDesc, block_tables: np.ndarray, seq_lens: np.ndarray,

@@ -141,6 +141,7 @@ struct AttnArgs {
   int32_t split_len;    // positions per KV split (multiple of kTileKeys)
   int32_t epi_rows;     // decode kernel: query rows per 16-row block (<= 16)
   int32_t n_splits;
+  int32_t max_q;        // queries computed per sequence (later ones are not)
   float scale_log2;     // softmax scale * log2(e)
 };
 
@@ -973,7 +974,7 @@ __global__ __launch_bounds__(kThreads) void prefill_schedule_kernel(AttnArgs a, 
         const int b = u / a.num_kv_heads;
         if (b == prev) continue;
         prev = b;
-        const int n_b = a.cu_q[b + 1] - a.cu_q[b];
+        const int n_b = min(a.cu_q[b + 1] - a.cu_q[b], a.max_q);
         tiles = max(tiles, (n_b * a.group + kPfRows - 1) / kPfRows);
       }
     }
@@ -1047,7 +1048,7 @@ __global__ __launch_bounds__(kThreads, 2) void paged_prefill_kernel(AttnArgs a,
   const int group = a.group;
   const int q0 = a.cu_q[b];
   const int n_b = a.cu_q[b + 1] - q0;
-  const int rows_total = n_b * group;
+  const int rows_total = min(n_b, a.max_q) * group;   // queries past max_q are not computed
   const int row0 = qt * kPfRows;
   if (row0 >= rows_total) return;
   const int start = a.seq_lens[b] - n_b;                 // position of new query 0
@@ -1660,6 +1661,7 @@ int run_attention(const char* fn, const pkv_pool_desc* desc, const void* k_pool,
   a.split_len = p.split_len;
   a.epi_rows = p.epi_rows;
   a.n_splits = p.n_splits;
+  a.max_q = max_q;
   a.scale_log2 = scale * 1.4426950408889634f;
   if (p.n_splits > 1) {
     const size_t rows_out = static_cast<size_t>(n_seqs) * max_q * hq * p.n_splits;

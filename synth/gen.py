@@ -187,9 +187,9 @@ class PrefixTraces:
     trace_tokens: np.ndarray   # [n_traces][trace_len] int32
     row_trace: np.ndarray      # [n_rows] int64
     row_len: np.ndarray        # [n_rows] int64
-    q: np.ndarray
-    k: np.ndarray
-    v: np.ndarray
+    q: Optional[np.ndarray]    # None when drawn without values
+    k: Optional[np.ndarray]
+    v: Optional[np.ndarray]
 
     def row_tokens(self, r: int) -> np.ndarray:
         return self.trace_tokens[self.row_trace[r], : self.row_len[r]]
@@ -201,7 +201,8 @@ def prefix_traces(n_rows: int = 256, n_traces: int = 32,
                   num_pages: int = 100_000, page_size: int = 16,
                   num_q_heads: int = 32, num_kv_heads: int = 8, head_dim: int = 128,
                   dtype: str = BF16, seed: int = 0, instance: int = 0,
-                  workload: int = 3) -> PrefixTraces:
+                  workload: int = 3, values: bool = True) -> PrefixTraces:
+    """``values=False`` draws only the structure (tokens, lengths, pages)."""
     g = lambda s: generator(workload, s, seed, instance)  # noqa: E731
     n_rest = n_rows - len(first_rows)
     rest_trace = g("trace_of").integers(1, n_traces - 1, size=n_rest, endpoint=True)
@@ -214,9 +215,9 @@ def prefix_traces(n_rows: int = 256, n_traces: int = 32,
         free_order=g("pages").permutation(num_pages).astype(np.int32),
         num_q_heads=num_q_heads, num_kv_heads=num_kv_heads, head_dim=head_dim,
         trace_tokens=tokens, row_trace=row_trace, row_len=row_len,
-        q=normal_values(g("q"), (n_traces, trace_len, num_q_heads, head_dim), dtype),
-        k=normal_values(g("k"), (n_traces, trace_len, num_kv_heads, head_dim), dtype),
-        v=normal_values(g("v"), (n_traces, trace_len, num_kv_heads, head_dim), dtype),
+        q=normal_values(g("q"), (n_traces, trace_len, num_q_heads, head_dim), dtype) if values else None,
+        k=normal_values(g("k"), (n_traces, trace_len, num_kv_heads, head_dim), dtype) if values else None,
+        v=normal_values(g("v"), (n_traces, trace_len, num_kv_heads, head_dim), dtype) if values else None,
     )
 
 
