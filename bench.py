@@ -26,6 +26,7 @@ oracle on a bounded sample of the same sequences.
 from __future__ import annotations
 
 import argparse
+import gc
 import json
 import os
 import sys
@@ -130,12 +131,15 @@ def prefill_leg(args, torch, pkv, synth, dev: str) -> dict:
     for _ in range(2):
         step()
     torch.cuda.synchronize()
+    gc.collect()
+    gc.disable()
     evs = [tuple(torch.cuda.Event(enable_timing=True) for _ in range(3)) for _ in range(args.prefill_reps)]
     t0 = time.perf_counter()
     for ev in evs:
         step(ev)
     torch.cuda.synchronize()
     wall = (time.perf_counter() - t0) / args.prefill_reps
+    gc.enable()
     store_ms = np.array([a.elapsed_time(b) for a, b, _ in evs])
     attn_ms = np.array([b.elapsed_time(c) for _, b, c in evs])
     assert torch.isfinite(out.float()).all(), "non-finite prefill output"
@@ -280,8 +284,13 @@ def main():
     stream = torch.cuda.current_stream()
     store_call = pkv.bind_store_kv(desc, k_pool, v_pool, k_new, v_new, d_slots, stream)
     decode_call = pkv.bind_decode(desc, k_pool, v_pool, q, d_bt, d_lens, max_len, scale, out, ws, stream)
+    # A small ring of timing-event pairs, read back before reuse (a pair is
+    # reused EV_RING steps later, long after it completed): many live timing
+    # events slow down every record.
+    EV_RING = 32
     ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-          for _ in range(args.steps)]
+          for _ in range(EV_RING)]
+    dec_ms = []
     kv_bytes = []
 
     def step(k: int, timed_idx: int):
@@ -294,23 +303,36 @@ def main():
         d_buf.copy_(buf["buf"], non_blocking=True)
         buf["done"].record(stream)
         store_call()
-        if timed_idx >= 0:
-            ev[timed_idx][0].record(stream)
+        pair = ev[timed_idx % EV_RING] if timed_idx >= 0 else None
+        if pair is not None:
+            if timed_idx >= EV_RING:
+                pair[1].synchronize()
+                dec_ms.append(pair[0].elapsed_time(pair[1]))
+            pair[0].record(stream)
         decode_call()
-        if timed_idx >= 0:
-            ev[timed_idx][1].record(stream)
+        if pair is not None:
+            pair[1].record(stream)
             kv_bytes.append(int(l_np.astype(np.int64).sum()) * per_pos)
 
     for k in range(args.warmup):
         step(k, -1)
     torch.cuda.synchronize()
+    # Keep the garbage collector out of the timed loop: with the workload's
+    # arrays alive a full collection takes tens of milliseconds.
+    gc.collect()
+    gc.freeze()
+    gc.disable()
     t0 = time.perf_counter()
     for i in range(args.steps):
         step(args.warmup + i, i)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
+    gc.enable()
 
-    dec_ms = np.array([a.elapsed_time(b) for a, b in ev])
+    for k in range(max(0, args.steps - EV_RING), args.steps):
+        a, b = ev[k % EV_RING]
+        dec_ms.append(a.elapsed_time(b))
+    dec_ms = np.array(dec_ms)
     total_kv = float(sum(kv_bytes))
     qo_bytes = 2 * B * hq * D * 2                      # q read + out written per launch
     alg_per_launch = total_kv / args.steps + qo_bytes

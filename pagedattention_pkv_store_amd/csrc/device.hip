@@ -142,6 +142,7 @@ struct AttnArgs {
   int32_t epi_rows;     // decode kernel: query rows per 16-row block (<= 16)
   int32_t n_splits;
   int32_t max_q;        // queries computed per sequence (later ones are not)
+  int32_t waves;        // decode: one-wave workgroups of the launch
   float scale_log2;     // softmax scale * log2(e)
 };
 
@@ -460,34 +461,50 @@ __global__ __launch_bounds__(kThreads) void paged_attention_kernel(AttnArgs args
 
 // ---------------------------------------------------------------------------
 // Paged decode and short appends (at most 16 * RBW query rows per sequence and
-// KV head): a schedule kernel, a persistent attention kernel and a merge.
+// KV head), split evenly over waves ("stream-K").
 //
-// Work is cut into equal items of `chunk` positions of one sequence and one KV
-// head.  decode_schedule_kernel lists every (sequence, chunk) in a dense
-// array and resets the work-queue counter; paged_decode_kernel runs as many
-// workgroups as the chip holds at once, and each workgroup repeatedly takes
-// the next item from the queue (one atomic per item), so long and short
-// sequences balance across all CUs.  Inside an item, 16-position block j goes
-// to wave j % 4:
-//  * its K and V rows are loaded with fully coalesced 16-byte loads (each
-//    instruction reads 1 KB of whole rows) and written into a 16-row slice of
-//    LDS private to the wave.  The 16-byte chunks of row r are stored XOR-
-//    swizzled by r, so the MFMA operand reads that follow hit distinct banks;
-//  * the next block's loads are issued before the current block is computed;
-//    every load is unconditional (a position past the item re-reads the
-//    item's first row and is masked), so no branch forces a full wait on
-//    outstanding loads;
-//  * S^T = K Q^T and O^T = V^T P^T run on MFMA, the softmax max/sum on
-//    wavefront shuffles.
-// At the end of an item the four waves' softmax states are combined in LDS and
-// written: normalised to `out` when the item spans its whole sequence, else
-// as a partial that merge_chunks_kernel folds in with log-sum-exp.
+// The work is the list of 16-position blocks of every (sequence, KV head)
+// unit, sequence-major, then KV head, then position.  paged_decode_kernel runs
+// a fixed number of one-wave workgroups; each wave scans the sequences' block
+// counts (a wavefront prefix sum per 64 sequences) and takes the contiguous
+// range of `per` blocks starting at w * per.  Every wave moves the same bytes
+// and no wave ever waits on another: the kernel has no barrier.  A wave walks
+// its range with two blocks in flight, across unit boundaries:
+//  * a block's K and V rows are loaded with fully coalesced 16-byte loads
+//    (each instruction reads 1 KB of whole rows) into registers, two blocks
+//    ahead, then written to the wave's LDS slices (K rows padded by 16 bytes,
+//    V rows by 32, so the operand reads below are free of bank conflicts);
+//  * S^T = K Q^T runs on MFMA with the unit's queries held in registers (the
+//    next unit's are fetched one unit ahead); a lane then holds one query row
+//    and 4 positions, so the online softmax takes in-lane work and two
+//    wavefront shuffles; O^T += V^T P^T takes V^T straight out of LDS with
+//    ds_read_b64_tr_b16 (bf16);
+//  * loads are never skipped: past the range's end the last block is read
+//    again, past a unit's end rows are masked, so no branch forces a full
+//    wait on outstanding loads.
+// Where a wave's range covers a whole unit it writes the normalised output;
+// otherwise it writes the unit's partial state (un-normalised O, max, sum) to
+// slot unit + wave, and merge_segments_kernel folds a unit's slots with
+// log-sum-exp.  Segment boundaries are fixed positions of the logical
+// sequence, so results never depend on which physical pages hold it.
 // ---------------------------------------------------------------------------
 
-// Positions of sequence b's KV range for its (single) row tile and the number
-// of chunks covering it.  Shared by the schedule and merge kernels.
+#ifndef PKV_DECODE_WAVES
+#define PKV_DECODE_WAVES 2048          // one-wave workgroups (8 per CU)
+#endif
+#ifndef PKV_DECODE_MIN_BLOCKS
+#define PKV_DECODE_MIN_BLOCKS 4        // smallest range of a wave, in blocks
+#endif
+#ifndef PKV_DECODE_WAVES_PER_SIMD
+#define PKV_DECODE_WAVES_PER_SIMD 2
+#endif
+constexpr int kDecodeWaves = PKV_DECODE_WAVES;
+
+// Queries of sequence b seen by the decode path (at most 16 * RBW rows) and
+// the positions they see: [0, kv_end).
 template <int RBW>
-__device__ __forceinline__ int decode_kv_end(const AttnArgs& a, int b, int* q0_out, int* n_b_out) {
+__device__ __forceinline__ int decode_kv_end(const AttnArgs& a, int b, int* q0_out, int* n_b_out,
+                                             int* rows_out) {
   int q0, n_b;
   if (a.cu_q) {
     q0 = a.cu_q[b];
@@ -498,76 +515,25 @@ __device__ __forceinline__ int decode_kv_end(const AttnArgs& a, int b, int* q0_o
   }
   *q0_out = q0;
   *n_b_out = n_b;
-  const int rows = min(n_b * a.group, 16 * RBW);
+  const int rows = max(0, min(min(n_b, a.max_q) * a.group, 16 * RBW));
+  *rows_out = rows;
   if (rows <= 0) return 0;
   return a.seq_lens[b] - n_b + (rows - 1) / a.group + 1;
 }
 
-struct DecodeQueue {
-  int32_t n_chunks;    // items listed by the schedule kernel
-  int32_t pad[63];
-};
-
-// One work item: positions [k_lo, k_hi) of sequence b (for every KV head),
-// with the scalars the attention kernel needs precomputed.
-struct DecodeItem {
-  int32_t b, k_lo, k_hi, n_chunks;      // n_chunks of the sequence (1: final write)
-  int32_t q0, start, rows_total, pad;   // first query row, position of query 0, rows
-};
-
-template <int RBW>
-__global__ __launch_bounds__(kThreads) void decode_schedule_kernel(AttnArgs a, DecodeQueue* q,
-                                                                   DecodeItem* items) {
-  __shared__ int s_scan[kThreads];
-  __shared__ int s_carry;
-  const int tid = threadIdx.x;
-  if (tid == 0) s_carry = 0;
-  __syncthreads();
-  for (int base = 0; base < a.n_seqs; base += kThreads) {
-    const int b = base + tid;
-    int nc = 0, kv_end = 0, q0 = 0, n_b = 0;
-    if (b < a.n_seqs) {
-      kv_end = decode_kv_end<RBW>(a, b, &q0, &n_b);
-      if (kv_end > 0) nc = min((kv_end + a.split_len - 1) / a.split_len, a.n_splits);
-    }
-    s_scan[tid] = nc;
-    __syncthreads();
-    for (int off = 1; off < kThreads; off <<= 1) {
-      const int v = tid >= off ? s_scan[tid - off] : 0;
-      __syncthreads();
-      s_scan[tid] += v;
-      __syncthreads();
-    }
-    const int first = s_carry + s_scan[tid] - nc;
-    const int rows = min(n_b * a.group, 16 * RBW);
-    const int start = b < a.n_seqs ? a.seq_lens[b] - n_b : 0;
-    for (int c = 0; c < nc; ++c) {
-      DecodeItem it;
-      it.b = b;
-      it.k_lo = c * a.split_len;
-      it.k_hi = min((c + 1) * a.split_len, kv_end);
-      it.n_chunks = nc;
-      it.q0 = q0;
-      it.start = start;
-      it.rows_total = rows;
-      it.pad = 0;
-      items[first + c] = it;
-    }
-    __syncthreads();
-    if (tid == kThreads - 1) s_carry += s_scan[tid];
-    __syncthreads();
-  }
-  if (tid == 0) q->n_chunks = s_carry;
+// Blocks per wave: the same in the attention and merge kernels.
+__device__ __forceinline__ int decode_per(int total, int waves, int min_blocks) {
+  return max(min_blocks, (total + waves - 1) / waves);
 }
+
+typedef __bf16 dec_bf16x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) dec_bf16x4 lds_dec_bf16x4;
 
 // kPageMode 0: page_size a power of two >= 16 (a 16-position block lies in
 // one page); 1: a power of two < 16; 2: any other page size.
-#ifndef PKV_DECODE_WAVES_PER_SIMD
-#define PKV_DECODE_WAVES_PER_SIMD 2
-#endif
 template <typename T, int D, int RBW, int kPageMode>
-__global__ __launch_bounds__(kThreads, RBW == 1 ? PKV_DECODE_WAVES_PER_SIMD : 1) void paged_decode_kernel(
-    AttnArgs args, const DecodeQueue* queue, const DecodeItem* __restrict__ items) {
+__global__ __launch_bounds__(kWave, RBW == 1 ? PKV_DECODE_WAVES_PER_SIMD : 1) void paged_decode_kernel(
+    AttnArgs args, int32_t* __restrict__ seq_blk) {
   constexpr int kEs = sizeof(T);
   constexpr int kRowBytes = D * kEs;
   constexpr int kCpr = kRowBytes / 16;                  // 16-byte chunks per row
@@ -576,85 +542,133 @@ __global__ __launch_bounds__(kThreads, RBW == 1 ? PKV_DECODE_WAVES_PER_SIMD : 1)
   constexpr int kFragChunks = kDl * kEs / 16;           // 16-byte chunks of one lane's K fragment
   constexpr int kQkMfmas = kDl / Elem<T>::kQkPerMfma;
   constexpr int kDimBlocks = D / 16;
-  constexpr int kWaves = kThreads / kWave;
-  constexpr int kEpiStride = D + 4;
-  // LDS rows are padded by 16 bytes: the 16-lane phases of the K operand
-  // reads, the transposed V reads and the staging writes then all hit
-  // distinct banks, and every address is a per-lane base plus an immediate.
-  // (512-byte rows stay unpadded so four waves' slices fit in 64 KiB.)
-  constexpr int kLdsRow = kRowBytes + (kRowBytes >= 512 ? 0 : 16);
-  constexpr int kStageBytes = 2 * 16 * kLdsRow;         // K + V slice of one wave
+  constexpr int kRowsCap = 16 * RBW;
+  // K rows padded by 16 bytes, V rows by 32 (bf16): the K operand reads (16
+  // rows, one 16-byte column each) and the transposed V reads (8 rows of 32
+  // bytes per half-wave) then hit distinct banks.  512-byte fp32 rows stay
+  // unpadded.
+  constexpr int kKRow = kRowBytes + (kRowBytes >= 512 ? 0 : 16);
+  constexpr int kVRow = kRowBytes + (kRowBytes >= 512 ? 0 : 32);
+  static_assert(kLoads * kWave * 16 == 16 * kRowBytes, "block split");
 
   extern __shared__ __align__(16) char smem[];
-  const int tid = threadIdx.x;
-  const int lane = tid & (kWave - 1);
-  const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
+  char* kst = smem;
+  char* vst = smem + 16 * kKRow;
+  const int lane = threadIdx.x;
   const int lrow = lane & 15;
   const int lgrp = lane >> 4;
-  char* kst = smem + wave * kStageBytes;
-  char* vst = kst + 16 * kLdsRow;
 
   const int hkv = args.num_kv_heads;
   const int group = args.group;
   const int ps = args.page_size;
   const int ps_shift = args.ps_shift;
-  const T* kpool = static_cast<const T*>(args.k_pool);
-  const T* vpool = static_cast<const T*>(args.v_pool);
-  const int n_work = queue->n_chunks * hkv;
-  const int grid = gridDim.x;
+  const int n_seqs = args.n_seqs;
+  const char* kbytes = static_cast<const char*>(args.k_pool);
+  const char* vbytes = static_cast<const char*>(args.v_pool);
 
-  auto slot = [](int r, int c) __attribute__((always_inline)) { return r * kLdsRow + c * 16; };
+  // ---- the block list: each wave scans the sequences' block counts ----
+  // nb(b) = 16-position blocks of sequence b per KV head.  Lane l of chunk c
+  // handles sequence 64 c + l; wave 0 also writes the prefix seq_blk[] that
+  // the merge kernel reads.
+  auto nb_of = [&](int b) __attribute__((always_inline)) {
+    int q0, n_b, rows;
+    const int kv_end = decode_kv_end<RBW>(args, b, &q0, &n_b, &rows);
+    return kv_end > 0 ? (kv_end + 15) >> 4 : 0;
+  };
+  int total_seq = 0;                       // blocks per KV head of all sequences
+  for (int c0 = 0; c0 < n_seqs; c0 += kWave) {
+    const int b = c0 + lane;
+    const int nb = b < n_seqs ? nb_of(b) : 0;
+    int incl = nb;                         // inclusive prefix within the chunk
+#pragma unroll
+    for (int off = 1; off < kWave; off <<= 1) {
+      const int v = __shfl_up(incl, off);
+      if (lane >= off) incl += v;
+    }
+    if (blockIdx.x == 0 && b < n_seqs) seq_blk[b] = total_seq + incl - nb;
+    total_seq += __shfl(incl, kWave - 1);
+  }
+  if (blockIdx.x == 0 && lane == 0) seq_blk[n_seqs] = total_seq;
 
-  // ---- per-item scalars (wave-uniform) ----
-  struct ItemS {
-    int valid, b, g, k_lo, k_hi, nb, whole, q0, start, rows_total, blk_lo;
+  // ---- this wave's block range ----
+  const int total = total_seq * hkv;
+  const int per = decode_per(total, gridDim.x, args.split_len);
+  const int i0 = blockIdx.x * per;
+  if (i0 >= total) return;
+  const int i1 = min(total, i0 + per);
+
+  // A position in the block list: sequence b, KV head g, block j of nb.
+  struct Cur {
+    int b, g, j, nb;
   };
-  auto fetch = [&](int wi) __attribute__((always_inline)) {
-    ItemS s;
-    s.valid = wi < n_work;
-    const int idx = s.valid ? wi / hkv : 0;
-    const DecodeItem rec = items[idx];
-    s.b = __builtin_amdgcn_readfirstlane(rec.b);
-    s.g = s.valid ? wi % hkv : 0;
-    s.k_lo = __builtin_amdgcn_readfirstlane(rec.k_lo);
-    s.k_hi = __builtin_amdgcn_readfirstlane(rec.k_hi);
-    s.whole = __builtin_amdgcn_readfirstlane(rec.n_chunks) == 1;
-    s.q0 = __builtin_amdgcn_readfirstlane(rec.q0);
-    s.start = __builtin_amdgcn_readfirstlane(rec.start);
-    s.rows_total = __builtin_amdgcn_readfirstlane(rec.rows_total);
-    s.nb = s.valid ? (s.k_hi - s.k_lo + 15) >> 4 : 0;
-    s.blk_lo = kPageMode != 2 ? (s.k_lo >> ps_shift) : s.k_lo / ps;
-    return s;
+  auto locate = [&](int i) __attribute__((always_inline)) {
+    // the sequence whose blocks hold i: first b with (prefix through b) * hkv > i
+    int base = 0;
+    Cur c;
+    c.b = 0;
+    c.nb = 0;
+    for (int c0 = 0; c0 < n_seqs; c0 += kWave) {
+      const int b = c0 + lane;
+      const int nb = b < n_seqs ? nb_of(b) : 0;
+      int incl = nb;
+#pragma unroll
+      for (int off = 1; off < kWave; off <<= 1) {
+        const int v = __shfl_up(incl, off);
+        if (lane >= off) incl += v;
+      }
+      const unsigned long long hit = __ballot((base + incl) * hkv > i);
+      if (hit) {
+        const int l = __builtin_ctzll(hit);
+        c.b = c0 + l;
+        c.nb = __shfl(nb, l);
+        base += __shfl(incl, l) - c.nb;
+        break;
+      }
+      base += __shfl(incl, kWave - 1);
+    }
+    const int r = i - base * hkv;
+    c.g = r / c.nb;
+    c.j = r - c.g * c.nb;
+    return c;
   };
-  // The item's block-table slice lives in lane registers (lane i holds the
-  // page of logical block blk_lo + i, -1 if out of range); items span at most
-  // 64 pages.  Reading it needs no memory access once loaded.
-  // Branch-free: the load always goes to an in-range entry of the table
-  // (a record of an invalid item is item 0's, a real sequence).
-  auto load_bt = [&](const ItemS& it) __attribute__((always_inline)) {
-    const int blk = it.blk_lo + lane;
-    const int last = kPageMode != 2 ? ((it.k_hi - 1) >> ps_shift) : (it.k_hi - 1) / ps;
-    const int blk_c = max(0, min(blk, min(last, args.bt_stride - 1)));
-    const int p = args.block_tables[static_cast<int64_t>(it.b) * args.bt_stride + blk_c];
-    const bool ok = it.valid && blk <= last && blk < args.bt_stride &&
-                    static_cast<unsigned>(p) < static_cast<unsigned>(args.num_pages);
-    return ok ? p : -1;
+  auto advance = [&](Cur& c) __attribute__((always_inline)) {
+    if (++c.j < c.nb) return;
+    c.j = 0;
+    if (++c.g < hkv) return;
+    c.g = 0;
+    do {
+      ++c.b;
+      c.nb = nb_of(c.b);
+    } while (c.nb == 0 && c.b + 1 < n_seqs);
   };
+
+  // Per-unit scalars.
+  struct Unit {
+    int q0, start, rows, kv_end;
+  };
+  auto unit_of = [&](int b) __attribute__((always_inline)) {
+    Unit u;
+    int n_b;
+    u.kv_end = decode_kv_end<RBW>(args, b, &u.q0, &n_b, &u.rows);
+    u.start = args.seq_lens[b] - n_b;
+    return u;
+  };
+
   // Query rows (B operand of S^T = K Q^T): row r = (query r / group, head
   // g * group + r % group); this lane holds row rb * 16 + lrow, dims
-  // lgrp * kDl .. + kDl.
-  auto load_q = [&](const ItemS& it, QkFrag<T, kDl> (&qv)[RBW], int (&qpos)[RBW]) __attribute__((always_inline)) {
+  // lgrp * kDl .. + kDl.  Branch-free: rows without a query read row 0 of the
+  // batch and are zeroed.
+  auto load_q = [&](int b, int g, const Unit& u, QkFrag<T, kDl> (&qv)[RBW], int (&qpos)[RBW]) __attribute__((always_inline)) {
 #pragma unroll
     for (int rb = 0; rb < RBW; ++rb) {
       const int r = rb * 16 + lrow;
       const int qi = r / group;
-      const int tok = it.q0 + qi;
-      const bool ok = it.valid && r < it.rows_total && tok < args.total_q;
-      qpos[rb] = it.start + (r < it.rows_total ? qi : it.rows_total / group);
-      // branch-free: rows without a query read row 0 and are zeroed
+      const int tok = u.q0 + qi;
+      const bool ok = r < u.rows && tok < args.total_q;
+      qpos[rb] = u.start + (r < u.rows ? qi : -1);
       const int tok_c = ok ? tok : 0;
       const T* src = static_cast<const T*>(args.q) +
-                     (static_cast<int64_t>(tok_c) * args.num_q_heads + it.g * group + (r - qi * group)) * D +
+                     (static_cast<int64_t>(tok_c) * args.num_q_heads + g * group + (r - qi * group)) * D +
                      lgrp * kDl;
       const unsigned keep = ok ? ~0u : 0u;
 #pragma unroll
@@ -662,94 +676,87 @@ __global__ __launch_bounds__(kThreads, RBW == 1 ? PKV_DECODE_WAVES_PER_SIMD : 1)
     }
   };
 
-  // Issue the loads of block j of item `it` (clamped into the item; an
-  // invalid item reads page 0 and flags everything for zeroing).  Load c of
-  // a lane covers 16-byte chunk q % kCpr of row q / kCpr (q = c * 64 +
-  // lane): consecutive lanes read consecutive bytes of whole rows.
-  auto load_block = [&](const ItemS& it, int bt, int j, u32x4 (&kr)[kLoads], u32x4 (&vr)[kLoads],
+  // Issue the loads of the block at cursor c (kv_end: its unit's).  Load ci
+  // of a lane covers 16-byte chunk q % kCpr of row q / kCpr (q = ci * 64 +
+  // lane): consecutive lanes read consecutive bytes of whole rows.  okm marks
+  // the rows inside the unit.
+  auto load_block = [&](const Cur& c, int kv_end, int page_hint, u32x4 (&kr)[kLoads], u32x4 (&vr)[kLoads],
                         uint32_t& okm) __attribute__((always_inline)) {
-    j = max(0, min(j, it.nb - 1));
-    const int pos0 = it.k_lo + 16 * j;
+    const int pos0 = 16 * c.j;
+    const int32_t* bt_row = args.block_tables + static_cast<int64_t>(c.b) * args.bt_stride;
     okm = 0;
     if constexpr (kPageMode == 0) {
-      const int blk = pos0 >> ps_shift;
-      int page = __builtin_amdgcn_readlane(bt, blk - it.blk_lo);
-      const bool page_ok = it.valid && page >= 0;
-      page = page_ok ? page : 0;
-      const int64_t base = ((static_cast<int64_t>(page) * hkv + it.g) * ps + (pos0 & (ps - 1))) * D;
-      const T* kb = kpool + base;     // wave-uniform row-0 pointers: scalar base +
-      const T* vb = vpool + base;     // a 32-bit per-lane offset per load
+      const uint32_t page = static_cast<uint32_t>(min(max(page_hint, 0), args.num_pages - 1));
+      const uint64_t base = (static_cast<uint64_t>(page * hkv + c.g) * ps + (pos0 & (ps - 1))) * kRowBytes;
 #pragma unroll
-      for (int c = 0; c < kLoads; ++c) {
-        const int q = c * kWave + lane;
+      for (int ci = 0; ci < kLoads; ++ci) {
+        const int q = ci * kWave + lane;
         const int r = q / kCpr;
-        const int chunk = q % kCpr;
-        okm |= (page_ok && pos0 + r < it.k_hi) ? (1u << c) : 0u;
-        const int off = r * D + chunk * (16 / kEs);
-        kr[c] = *reinterpret_cast<const u32x4*>(kb + off);
-        vr[c] = *reinterpret_cast<const u32x4*>(vb + off);
+        okm |= (pos0 + r < kv_end) ? (1u << ci) : 0u;
+        const uint32_t off = r * kRowBytes + (q % kCpr) * 16;
+        kr[ci] = *reinterpret_cast<const u32x4*>(kbytes + base + off);
+        vr[ci] = *reinterpret_cast<const u32x4*>(vbytes + base + off);
       }
     } else {
 #pragma unroll
-      for (int c = 0; c < kLoads; ++c) {
-        const int q = c * kWave + lane;
+      for (int ci = 0; ci < kLoads; ++ci) {
+        const int q = ci * kWave + lane;
         const int r = q / kCpr;
-        const int chunk = q % kCpr;
         const int pos_raw = pos0 + r;
-        const int pos = max(0, min(pos_raw, it.k_hi - 1));
+        const int pos = min(pos_raw, kv_end - 1);
         const int blk = kPageMode == 1 ? (pos >> ps_shift) : pos / ps;
-        const int page = __shfl(bt, max(0, min(blk - it.blk_lo, kWave - 1)));
-        const bool ok = it.valid && pos_raw < it.k_hi && page >= 0;
-        okm |= ok ? (1u << c) : 0u;
-        const int64_t e = ((static_cast<int64_t>(ok ? page : 0) * hkv + it.g) * ps + (ok ? pos - blk * ps : 0)) * D +
-                          chunk * (16 / kEs);
-        kr[c] = *reinterpret_cast<const u32x4*>(kpool + e);
-        vr[c] = *reinterpret_cast<const u32x4*>(vpool + e);
+        const int page = min(max(bt_row[blk], 0), args.num_pages - 1);
+        okm |= (pos_raw < kv_end) ? (1u << ci) : 0u;
+        const uint64_t e = (static_cast<uint64_t>(page * hkv + c.g) * ps + (pos - blk * ps)) * kRowBytes +
+                           (q % kCpr) * 16;
+        kr[ci] = *reinterpret_cast<const u32x4*>(kbytes + e);
+        vr[ci] = *reinterpret_cast<const u32x4*>(vbytes + e);
       }
     }
   };
+  // page of the block at cursor c (page mode 0: one page per block)
+  auto page_of = [&](const Cur& c) __attribute__((always_inline)) {
+    return args.block_tables[static_cast<int64_t>(c.b) * args.bt_stride + ((16 * c.j) >> max(ps_shift, 0))];
+  };
 
-  // Write a block's loaded rows into the wave's LDS slice.  V rows past the
-  // item or on an invalid page are zeroed (their probability is 0, but stale
-  // slots may hold anything, NaN included); K rows need no zeroing, their
-  // scores are masked.  Only a partial block needs the mask.
+  // Write a block's rows into the wave's LDS slices.  V rows past the unit
+  // are zeroed (their probability is 0, but stale slots may hold anything,
+  // NaN included); K rows need no zeroing, their scores are masked.
   auto stage_block = [&](const u32x4 (&kr)[kLoads], const u32x4 (&vr)[kLoads], uint32_t okm) __attribute__((always_inline)) {
-    constexpr uint32_t kFull = (1u << kLoads) - 1u;
-    if (__all(okm == kFull)) {
 #pragma unroll
-      for (int c = 0; c < kLoads; ++c) {
-        const int q = c * kWave + lane;
-        const int off = slot(q / kCpr, q % kCpr);
-        *reinterpret_cast<u32x4*>(kst + off) = kr[c];
-        *reinterpret_cast<u32x4*>(vst + off) = vr[c];
-      }
-    } else {
-#pragma unroll
-      for (int c = 0; c < kLoads; ++c) {
-        const int q = c * kWave + lane;
-        const int off = slot(q / kCpr, q % kCpr);
-        const unsigned keep = 0u - ((okm >> c) & 1u);   // all ones or zero
-        *reinterpret_cast<u32x4*>(kst + off) = kr[c];
-        *reinterpret_cast<u32x4*>(vst + off) = vr[c] & keep;
-      }
+    for (int ci = 0; ci < kLoads; ++ci) {
+      const int q = ci * kWave + lane;
+      const int r = q / kCpr;
+      const int cc = q % kCpr;
+      const unsigned keep = 0u - ((okm >> ci) & 1u);   // all ones or zero
+      *reinterpret_cast<u32x4*>(kst + r * kKRow + cc * 16) = kr[ci];
+      *reinterpret_cast<u32x4*>(vst + r * kVRow + cc * 16) = vr[ci] & keep;
     }
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
     __builtin_amdgcn_wave_barrier();
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
   };
 
-  // ---- online softmax state of the current item (log2 domain) ----
+  // ---- online softmax state of the current segment (log2 domain) ----
   float m_run[RBW], l_part[RBW];
   f32x4 o_acc[RBW][kDimBlocks];
+  auto reset_state = [&]() __attribute__((always_inline)) {
+#pragma unroll
+    for (int rb = 0; rb < RBW; ++rb) {
+      m_run[rb] = -INFINITY;
+      l_part[rb] = 0.f;
+#pragma unroll
+      for (int d = 0; d < kDimBlocks; ++d) o_acc[rb][d] = f32x4{0.f, 0.f, 0.f, 0.f};
+    }
+  };
 
-  auto compute_block = [&](const ItemS& it, const QkFrag<T, kDl> (&qv)[RBW], const int (&qpos)[RBW],
-                           int j) __attribute__((always_inline)) {
-    const int pos0 = it.k_lo + 16 * j;
+  auto compute_block = [&](int pos0, int kv_end, const QkFrag<T, kDl> (&qv)[RBW], const int (&qpos)[RBW])
+      __attribute__((always_inline)) {
     // K fragment: position lrow, dims lgrp * kDl .. + kDl
     QkFrag<T, kDl> kf;
 #pragma unroll
     for (int c = 0; c < kFragChunks; ++c)
-      kf.load16(c, *reinterpret_cast<const u32x4*>(kst + slot(lrow, lgrp * kFragChunks + c)));
+      kf.load16(c, *reinterpret_cast<const u32x4*>(kst + lrow * kKRow + (lgrp * kFragChunks + c) * 16));
     f32x4 s[RBW];
 #pragma unroll
     for (int rb = 0; rb < RBW; ++rb) {
@@ -764,7 +771,7 @@ __global__ __launch_bounds__(kThreads, RBW == 1 ? PKV_DECODE_WAVES_PER_SIMD : 1)
       for (int i = 0; i < 4; ++i) {
         const int pos = pos0 + lgrp * 4 + i;
         const float x = s[rb][i] * args.scale_log2;
-        s[rb][i] = (pos < it.k_hi && pos <= qpos[rb]) ? x : -INFINITY;
+        s[rb][i] = (pos < kv_end && pos <= qpos[rb]) ? x : -INFINITY;
         mx = fmaxf(mx, s[rb][i]);
       }
       mx = fmaxf(mx, __shfl_xor(mx, 16));
@@ -785,17 +792,18 @@ __global__ __launch_bounds__(kThreads, RBW == 1 ? PKV_DECODE_WAVES_PER_SIMD : 1)
         for (int d = 0; d < kDimBlocks; ++d) o_acc[rb][d] *= alpha;
       }
     }
-    // O^T += V^T P^T: the A operand is V transposed, read element-wise
+    // O^T += V^T P^T
     if constexpr (sizeof(T) == 2) {
       i16x4 pb[RBW];
 #pragma unroll
       for (int rb = 0; rb < RBW; ++rb) pb[rb] = pack_bf16x4(s[rb]);
+      // lane k of a 16-lane group addresses row 4 lgrp + k / 4, dims 4 (k % 4)..;
+      // it receives dim lrow of rows 4 lgrp .. 4 lgrp + 3
+      const char* vl = vst + (4 * lgrp + (lrow >> 2)) * kVRow + (lrow & 3) * 8;
 #pragma unroll
       for (int d = 0; d < kDimBlocks; ++d) {
-        const int dim = d * 16 + lrow;
-        i16x4 a;
-#pragma unroll
-        for (int i = 0; i < 4; ++i) a[i] = *reinterpret_cast<const short*>(vst + slot(lgrp * 4 + i, 0) + dim * 2);
+        const dec_bf16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_dec_bf16x4*)(vl + d * 32));
+        const i16x4 a = __builtin_bit_cast(i16x4, v);
 #pragma unroll
         for (int rb = 0; rb < RBW; ++rb)
           o_acc[rb][d] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a, pb[rb], o_acc[rb][d], 0, 0, 0);
@@ -806,7 +814,7 @@ __global__ __launch_bounds__(kThreads, RBW == 1 ? PKV_DECODE_WAVES_PER_SIMD : 1)
 #pragma unroll
         for (int d = 0; d < kDimBlocks; ++d) {
           const int dim = d * 16 + lrow;
-          const float a = *reinterpret_cast<const float*>(vst + slot(lgrp * 4 + i, 0) + dim * 4);
+          const float a = *reinterpret_cast<const float*>(vst + (lgrp * 4 + i) * kVRow + dim * 4);
 #pragma unroll
           for (int rb = 0; rb < RBW; ++rb)
             o_acc[rb][d] = __builtin_amdgcn_mfma_f32_16x16x4f32(a, s[rb][i], o_acc[rb][d], 0, 0, 0);
@@ -818,99 +826,124 @@ __global__ __launch_bounds__(kThreads, RBW == 1 ? PKV_DECODE_WAVES_PER_SIMD : 1)
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
   };
 
-  // ---- the item stream of this workgroup: items w, w + grid, w + 2 grid ... ----
-  int w = blockIdx.x;
-  ItemS cur = fetch(w);
-  if (!cur.valid) return;
-  int bt_cur = load_bt(cur);
-  QkFrag<T, kDl> q_cur[RBW];
-  int qpos_cur[RBW];
-  load_q(cur, q_cur, qpos_cur);
-  ItemS nxt = fetch(w + grid);
-
-  // Two register buffers, two blocks in flight per wave.  A block is staged
-  // to LDS, the loads two steps ahead go out into the registers it freed,
-  // then the staged block is computed.  An item's last step issues the next
-  // item's first two blocks instead, so loads stay in flight through the
-  // epilogue and the next item's start.  Loads are never skipped (an index
-  // past the item is clamped and the rows masked), so every path carries the
-  // same outstanding loads and each staging waits for the older buffer only.
-  u32x4 ka[kLoads], va[kLoads], kb[kLoads], vb[kLoads];
-  uint32_t oka, okb;
-  load_block(cur, bt_cur, wave, ka, va, oka);
-  load_block(cur, bt_cur, wave + kWaves, kb, vb, okb);
-
-  for (;;) {
-    const int bt_nxt = load_bt(nxt);
-    QkFrag<T, kDl> q_nxt[RBW];
-    int qpos_nxt[RBW];
-    load_q(nxt, q_nxt, qpos_nxt);
-    const ItemS nxt2 = fetch(w + 2 * grid);
-
-#pragma unroll
-    for (int rb = 0; rb < RBW; ++rb) {
-      m_run[rb] = -INFINITY;
-      l_part[rb] = 0.f;
-#pragma unroll
-      for (int d = 0; d < kDimBlocks; ++d) o_acc[rb][d] = f32x4{0.f, 0.f, 0.f, 0.f};
-    }
-
-    for (int j = wave;; j += 2 * kWaves) {
-      const bool last = j + 2 * kWaves >= cur.nb;   // the item's final step for this wave
-      // where the loads issued in this step go: two steps ahead in this item,
-      // or the next item's first two steps (a dummy re-read when none)
-      const bool to_next = last && nxt.valid;
-      const ItemS tgt = to_next ? nxt : cur;
-      const int tgt_bt = to_next ? bt_nxt : bt_cur;
-      const int ja = last ? (to_next ? wave : cur.nb - 1) : j + 2 * kWaves;
-      const int jb = last ? (to_next ? wave + kWaves : cur.nb - 1) : j + 3 * kWaves;
-      stage_block(ka, va, oka);
-      load_block(tgt, tgt_bt, ja, ka, va, oka);
-      if (j < cur.nb) compute_block(cur, q_cur, qpos_cur, j);
-      stage_block(kb, vb, okb);
-      load_block(tgt, tgt_bt, jb, kb, vb, okb);
-      if (j + kWaves < cur.nb) compute_block(cur, q_cur, qpos_cur, j + kWaves);
-      if (last) break;
-    }
-
-    // ---- combine the four waves, one 16-row block at a time ----
-    const int er = args.epi_rows;
-    float* eo = reinterpret_cast<float*>(smem);
-    float* em = eo + kWaves * er * kEpiStride;
-    float* el = em + kWaves * er;
-    const int chunk_idx = cur.k_lo / args.split_len;
+  // End of a segment of unit (b, g): normalised output when it covers the
+  // unit, else the partial state in slot unit + wave.
+  auto write_segment = [&](int b, int g, const Unit& u, bool whole) __attribute__((always_inline)) {
+    const int slot = b * hkv + g + static_cast<int>(blockIdx.x);
 #pragma unroll
     for (int rb = 0; rb < RBW; ++rb) {
       float l_row = l_part[rb];
       l_row += __shfl_xor(l_row, 16);
       l_row += __shfl_xor(l_row, 32);
-      __syncthreads();
-      if (lrow < er) {
-        const int erow = wave * er + lrow;
+      const int r = rb * 16 + lrow;
+      if (r >= u.rows) continue;
+      const int qi = r / group;
+      const int tok = u.q0 + qi;
+      if (tok >= args.total_q) continue;
+      const int64_t orow = static_cast<int64_t>(tok) * args.num_q_heads + g * group + (r - qi * group);
+      if (whole) {
+        const float inv = l_row > 0.f ? 1.f / l_row : 0.f;
+#pragma unroll
+        for (int d = 0; d < kDimBlocks; ++d) {
+          const f32x4 v = o_acc[rb][d] * inv;
+          if constexpr (sizeof(T) == 2)
+            *reinterpret_cast<i16x4*>(static_cast<uint16_t*>(args.out) + orow * D + d * 16 + lgrp * 4) = pack_bf16x4(v);
+          else
+            *reinterpret_cast<f32x4*>(static_cast<float*>(args.out) + orow * D + d * 16 + lgrp * 4) = v;
+        }
+      } else {
+        const int64_t row = static_cast<int64_t>(slot) * kRowsCap + r;
 #pragma unroll
         for (int d = 0; d < kDimBlocks; ++d)
-          *reinterpret_cast<f32x4*>(eo + erow * kEpiStride + d * 16 + lgrp * 4) = o_acc[rb][d];
+          *reinterpret_cast<f32x4*>(args.ws_o + row * D + d * 16 + lgrp * 4) = o_acc[rb][d];
         if (lgrp == 0) {
-          em[erow] = m_run[rb];
-          el[erow] = l_row;
+          args.ws_ml[row * 2] = m_run[rb];
+          args.ws_ml[row * 2 + 1] = l_row;
         }
       }
-      __syncthreads();
-      combine_rows<T, D, kWaves>(args, eo, em, el, er, rb * 16, cur.rows_total, cur.q0, cur.g, cur.whole,
-                                 chunk_idx);
     }
-    __syncthreads();   // the epilogue's LDS reads finish before the next staging
+  };
 
-    if (!nxt.valid) break;
-    w += grid;
-    cur = nxt;
-    bt_cur = bt_nxt;
-#pragma unroll
-    for (int rb = 0; rb < RBW; ++rb) {
-      q_cur[rb] = q_nxt[rb];
-      qpos_cur[rb] = qpos_nxt[rb];
+  // ---- the walk ----
+  Cur cc = locate(i0);              // block being computed
+  Cur lc = cc;                      // block whose loads are issued next
+  u32x4 ka[kLoads], va[kLoads], kb[kLoads], vb[kLoads];
+  uint32_t oka, okb;
+  Unit ul = unit_of(lc.b);          // unit of the load cursor
+  int page_l = kPageMode == 0 ? page_of(lc) : 0;
+  auto issue = [&](int li, u32x4 (&kr)[kLoads], u32x4 (&vr)[kLoads], uint32_t& okm) __attribute__((always_inline)) {
+    load_block(lc, ul.kv_end, page_l, kr, vr, okm);
+    if (li + 1 < i1) {              // move the load cursor on (it stays on the last block)
+      const int b_old = lc.b;
+      advance(lc);
+      if (lc.b != b_old) ul = unit_of(lc.b);
+      if constexpr (kPageMode == 0) page_l = page_of(lc);
     }
-    nxt = nxt2;
+  };
+  issue(i0, ka, va, oka);
+  issue(i0 + 1, kb, vb, okb);
+
+  Unit uc = unit_of(cc.b);
+  QkFrag<T, kDl> q_cur[RBW], q_nxt[RBW];
+  int qpos_cur[RBW], qpos_nxt[RBW];
+  load_q(cc.b, cc.g, uc, q_cur, qpos_cur);
+  // the unit after the current one, if the range reaches it
+  Cur nc = cc;
+  int seg_first = cc.j;             // block at which the current segment started
+  auto next_unit = [&]() __attribute__((always_inline)) {
+    Cur n = cc;
+    n.j = n.nb - 1;
+    advance(n);
+    return n;
+  };
+  const int rest0 = cc.nb - cc.j;   // blocks of the current unit left in the range
+  Unit un = uc;
+  bool has_next = i0 + rest0 < i1;
+  if (has_next) {
+    nc = next_unit();
+    un = unit_of(nc.b);
+    load_q(nc.b, nc.g, un, q_nxt, qpos_nxt);
+  }
+  reset_state();
+
+  for (int i = i0; i < i1; i += 2) {
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      if (h == 1 && i + 1 >= i1) break;
+      const int ii = i + h;
+      if (h == 0) {
+        stage_block(ka, va, oka);
+        issue(ii + 2, ka, va, oka);
+      } else {
+        stage_block(kb, vb, okb);
+        issue(ii + 2, kb, vb, okb);
+      }
+      compute_block(16 * cc.j, uc.kv_end, q_cur, qpos_cur);
+      const bool unit_end = cc.j == cc.nb - 1;
+      if (unit_end || ii + 1 == i1) {
+        write_segment(cc.b, cc.g, uc, seg_first == 0 && unit_end);
+        if (ii + 1 < i1) {
+          // the next unit becomes current; fetch the one after it
+          cc = nc;
+          uc = un;
+#pragma unroll
+          for (int rb = 0; rb < RBW; ++rb) {
+            q_cur[rb] = q_nxt[rb];
+            qpos_cur[rb] = qpos_nxt[rb];
+          }
+          seg_first = 0;
+          reset_state();
+          has_next = ii + 1 + cc.nb < i1;
+          if (has_next) {
+            nc = next_unit();
+            un = unit_of(nc.b);
+            load_q(nc.b, nc.g, un, q_nxt, qpos_nxt);
+          }
+        }
+      } else {
+        advance(cc);
+      }
+    }
   }
 }
 
@@ -923,9 +956,11 @@ __global__ __launch_bounds__(kThreads, RBW == 1 ? PKV_DECODE_WAVES_PER_SIMD : 1)
 //    blocks and keeps its own softmax state: no cross-wave combine.
 //  * K/V tiles of 64 positions are gathered through the block table with
 //    16-byte loads into registers one tile ahead and written to one of two
-//    LDS buffers; rows are padded by 16 bytes so every operand read below is
-//    free of bank conflicts.  One barrier per tile.  Block-table entries are
-//    fetched a further tile ahead.
+//    LDS buffers.  K rows are padded to D*2 + 16 bytes and V rows to
+//    D*2 + 32, which keeps both operand reads below free of bank conflicts.
+//    One barrier per tile; block-table entries are fetched a tile earlier
+//    still.  When a power-of-two page holds all rows a wave stages in one
+//    pass, the page lookup is scalar and each lane adds a 32-bit offset.
 //  * S^T = K Q^T on v_mfma_f32_16x16x32_bf16 with Q held in registers.  A
 //    lane then holds one query row and 4 positions of each 16-key block: the
 //    row max is in-lane work plus two shuffles.  The reference max of a row
@@ -936,7 +971,9 @@ __global__ __launch_bounds__(kThreads, RBW == 1 ? PKV_DECODE_WAVES_PER_SIMD : 1)
 //    (k-slots 8g..8g+3 <-> keys 4g..4g+3 of the first 16-key block, 8g+4..
 //    8g+7 <-> the same of the second), and V^T comes straight out of LDS with
 //    ds_read_b64_tr_b16.  Row sums run on the MFMA as well (a ones operand
-//    times P^T), from the same bf16 P the numerator uses.
+//    times P^T), from the same bf16 P the numerator uses.  The exponentials,
+//    the row sums and the PV products of a tile form one basic block, so the
+//    scheduler can overlap VALU and MFMA work.
 //  * Workgroups are dealt to the 8 XCDs round robin, so workgroup i serves
 //    unit i % 8 of a block of 8 units: all q-tiles of a unit run on one XCD
 //    and re-read its K/V from that XCD's L2.  Within a block the tiles with
@@ -944,13 +981,22 @@ __global__ __launch_bounds__(kThreads, RBW == 1 ? PKV_DECODE_WAVES_PER_SIMD : 1)
 //    blocks' tile counts; the grid is a host-side upper bound and surplus
 //    workgroups exit at once.
 // ---------------------------------------------------------------------------
-constexpr int kPfRows = 128;   // query rows per workgroup
+#ifndef PKV_PREFILL_ROW_BLOCKS
+#define PKV_PREFILL_ROW_BLOCKS 2
+#endif
+constexpr int kPfRb = PKV_PREFILL_ROW_BLOCKS;   // 16-row MFMA blocks per wave
+constexpr int kPfRows = 64 * kPfRb;             // query rows per workgroup (4 waves)
 constexpr int kPfKeys = 64;    // positions per staged tile
 
 template <int D>
-constexpr int pf_row_bytes() { return D * 2 + 16; }
+constexpr int pf_k_row_bytes() { return D * 2 + 16; }
 template <int D>
-constexpr int pf_lds_bytes() { return 2 * 2 * kPfKeys * pf_row_bytes<D>(); }
+constexpr int pf_v_row_bytes() { return D * 2 + 32; }
+template <int D>
+constexpr int pf_lds_bytes() { return 2 * kPfKeys * (pf_k_row_bytes<D>() + pf_v_row_bytes<D>()); }
+// Rows one wave stages per pass (a pass = one 16-byte chunk per thread).
+template <int D>
+constexpr int pf_wave_rows() { return kWave / (D * 2 / 16); }
 
 // row_off[k] = sum over blocks < k of (q-tiles of the block) * n_splits,
 // where a block's q-tiles are the most any of its 8 units needs.
@@ -1005,18 +1051,22 @@ __device__ __forceinline__ bf16x4 lds_read_tr(const char* p) {
   return __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(p));
 }
 
-// kPow2: page_size is a power of two (block index by shift).
-template <int D, bool kPow2>
-__global__ __launch_bounds__(kThreads, 2) void paged_prefill_kernel(AttnArgs a,
+// kPageMode 0: page_size a power of two >= the rows a wave stages per pass
+// (those rows then share one page: scalar lookup); 1: other powers of two;
+// 2: any page size.
+template <int D, int kPageMode>
+__global__ __launch_bounds__(kThreads, kPfRb >= 3 ? 1 : 2) void paged_prefill_kernel(AttnArgs a,
                                                                    const int32_t* __restrict__ row_off,
                                                                    int n_blocks) {
-  constexpr int kRowB = pf_row_bytes<D>();              // LDS row stride, bytes
+  constexpr int kKRowB = pf_k_row_bytes<D>();            // LDS row strides, bytes
+  constexpr int kVRowB = pf_v_row_bytes<D>();
   constexpr int kCpr = D * 2 / 16;                      // 16-byte chunks per K/V row
   constexpr int kChunks = kPfKeys * kCpr / kThreads;    // per thread per pool
   constexpr int kRowsPerPass = kThreads / kCpr;         // rows staged per chunk index
   constexpr int kQk = D / 32;                           // MFMAs per 16x16 score block
   constexpr int kDb = D / 16;                           // 16-dim blocks of O^T
-  constexpr int kTileB = kPfKeys * kRowB;               // bytes of one staged K or V tile
+  constexpr int kKTileB = kPfKeys * kKRowB;             // bytes of one staged K tile
+  constexpr int kBufB = kPfKeys * (kKRowB + kVRowB);    // one K + V buffer
   static_assert(kChunks * kRowsPerPass == kPfKeys, "tile split");
   extern __shared__ __align__(16) char smem[];
 
@@ -1062,59 +1112,67 @@ __global__ __launch_bounds__(kThreads, 2) void paged_prefill_kernel(AttnArgs a,
   const int ps = a.page_size;
   const int ps_shift = a.ps_shift;
   const int32_t* bt_row = a.block_tables + static_cast<int64_t>(b) * a.bt_stride;
-  const int srow0 = tid / kCpr;
-  const int spart = tid - srow0 * kCpr;
   const uint32_t head_bytes = static_cast<uint32_t>(ps) * D * 2;   // one (page, head) block
   const char* kbytes = static_cast<const char*>(a.k_pool);
   const char* vbytes = static_cast<const char*>(a.v_pool);
+  const int srow0 = tid / kCpr;
+  const int spart = tid - srow0 * kCpr;
+  // first row this wave stages in a pass (wave-uniform)
+  const int wrow0 = __builtin_amdgcn_readfirstlane(srow0);
 
   int pg_next[kChunks], pg_next2[kChunks];
   u32x4 kr[kChunks], vr[kChunks];
-  // position of staged row c of tile t (past the split's end: its last position)
-  auto pos_of = [&](int t, int c) __attribute__((always_inline)) {
-    return min(k_lo + t * kPfKeys + srow0 + c * kRowsPerPass, k_hi - 1);
+  // position of staged row `row` of tile t (past the split's end: its last position)
+  auto pos_of = [&](int t, int row) __attribute__((always_inline)) {
+    return min(k_lo + t * kPfKeys + row, k_hi - 1);
   };
   auto blk_of = [&](int pos) __attribute__((always_inline)) {
-    if constexpr (kPow2) return pos >> ps_shift;
+    if constexpr (kPageMode <= 1) return pos >> ps_shift;
     else return pos / ps;
   };
   auto fetch_pages = [&](int t) __attribute__((always_inline)) {
     const int tl = min(t, n_tiles - 1);
 #pragma unroll
-    for (int c = 0; c < kChunks; ++c) pg_next2[c] = bt_row[blk_of(pos_of(tl, c))];
+    for (int c = 0; c < kChunks; ++c) {
+      if constexpr (kPageMode == 0)
+        pg_next2[c] = bt_row[blk_of(pos_of(tl, wrow0 + c * kRowsPerPass))];
+      else
+        pg_next2[c] = bt_row[blk_of(pos_of(tl, srow0 + c * kRowsPerPass))];
+    }
   };
   auto load_kv = [&](int t) __attribute__((always_inline)) {
     const int tl = min(t, n_tiles - 1);
 #pragma unroll
     for (int c = 0; c < kChunks; ++c) {
-      const int pos = pos_of(tl, c);
-      const int off = pos - blk_of(pos) * ps;
+      const int pos = pos_of(tl, srow0 + c * kRowsPerPass);
       const uint32_t page = static_cast<uint32_t>(min(max(pg_next[c], 0), a.num_pages - 1));
-      const uint64_t boff = static_cast<uint64_t>(page * hkv + g) * head_bytes +
-                            static_cast<uint32_t>(off * (D * 2) + spart * 16);
-      kr[c] = *reinterpret_cast<const u32x4*>(kbytes + boff);
-      vr[c] = *reinterpret_cast<const u32x4*>(vbytes + boff);
+      const uint32_t off = kPageMode <= 1 ? (pos & (ps - 1)) : (pos - blk_of(pos) * ps);
+      const uint32_t voff = off * (D * 2) + spart * 16;
+      const uint64_t base = static_cast<uint64_t>(page * hkv + g) * head_bytes;
+      kr[c] = *reinterpret_cast<const u32x4*>(kbytes + base + voff);
+      vr[c] = *reinterpret_cast<const u32x4*>(vbytes + base + voff);
     }
   };
   auto stage = [&](int buf) __attribute__((always_inline)) {
-    char* kb = smem + buf * 2 * kTileB;
-    char* vb = kb + kTileB;
+    char* kb = smem + buf * kBufB;
+    char* vb = kb + kKTileB;
 #pragma unroll
     for (int c = 0; c < kChunks; ++c) {
       const int row = srow0 + c * kRowsPerPass;
-      *reinterpret_cast<u32x4*>(kb + row * kRowB + spart * 16) = kr[c];
-      *reinterpret_cast<u32x4*>(vb + row * kRowB + spart * 16) = vr[c];
+      *reinterpret_cast<u32x4*>(kb + row * kKRowB + spart * 16) = kr[c];
+      *reinterpret_cast<u32x4*>(vb + row * kVRowB + spart * 16) = vr[c];
     }
   };
 
   // ---- this lane's two query rows (B operand of S^T = K Q^T) ----
   // Lane group lgrp holds dims [lgrp * D/4, (lgrp + 1) * D/4); MFMA kk takes
   // the kk-th 8 of them (the same permutation is applied to K).
-  const int wr0 = row0 + 32 * wave;
-  bf16x8 qf[2][kQk];
-  int qpos[2];
+  constexpr int kWr = 16 * kPfRb;                       // rows per wave
+  const int wr0 = row0 + kWr * wave;
+  bf16x8 qf[kPfRb][kQk];
+  int qpos[kPfRb];
 #pragma unroll
-  for (int rb = 0; rb < 2; ++rb) {
+  for (int rb = 0; rb < kPfRb; ++rb) {
     const int rr = wr0 + 16 * rb + lrow;
     const int qi = rr / group;
     const bool ok = rr < rows_total && q0 + qi < a.total_q;
@@ -1132,44 +1190,48 @@ __global__ __launch_bounds__(kThreads, 2) void paged_prefill_kernel(AttnArgs a,
 
   const bool w_active = wr0 < rows_total;
   const int w_qmin = start + wr0 / group;
-  const int w_qmax = start + (min(wr0 + 31, rows_total - 1)) / group;
+  const int w_qmax = start + (min(wr0 + kWr - 1, rows_total - 1)) / group;
   const float c2 = a.scale_log2;
 
-  f32x4 o[kDb][2];
-  f32x4 lsum[2];
-  float mc[2] = {-INFINITY, -INFINITY};   // reference max per row, log2 units
+  f32x4 o[kDb][kPfRb];
+  f32x4 lsum[kPfRb];
+  float mc[kPfRb];                        // reference max per row, log2 units
 #pragma unroll
-  for (int rb = 0; rb < 2; ++rb) {
+  for (int rb = 0; rb < kPfRb; ++rb) {
     lsum[rb] = f32x4{0.f, 0.f, 0.f, 0.f};
+    mc[rb] = -INFINITY;
 #pragma unroll
     for (int d = 0; d < kDb; ++d) o[d][rb] = f32x4{0.f, 0.f, 0.f, 0.f};
   }
   const bf16x8 ones = __builtin_bit_cast(bf16x8, u32x4{0x3f803f80u, 0x3f803f80u, 0x3f803f80u, 0x3f803f80u});
 
   // lane parts of the LDS operand addresses
-  const int k_lane = lrow * kRowB + lgrp * (D / 4) * 2;
-  const int v_lane = (4 * lgrp + (lrow >> 2)) * kRowB + ((lrow & 3) >> 1) * 16 + (lrow & 1) * 8;
+  const int k_lane = lrow * kKRowB + lgrp * (D / 4) * 2;
+  const int v_lane = (4 * lgrp + (lrow >> 2)) * kVRowB + ((lrow & 3) >> 1) * 16 + (lrow & 1) * 8;
 
   auto compute = [&](const char* kt, const char* vt, int tb, auto mask_tag) __attribute__((always_inline)) {
     constexpr bool kMask = decltype(mask_tag)::value;
-    f32x4 s[4][2];
+    f32x4 s[4][kPfRb];
 #pragma unroll
     for (int kb = 0; kb < 4; ++kb) {
       bf16x8 kf[kQk];
 #pragma unroll
       for (int kk = 0; kk < kQk; ++kk)
-        kf[kk] = *reinterpret_cast<const bf16x8*>(kt + k_lane + kb * 16 * kRowB + kk * 16);
+        kf[kk] = *reinterpret_cast<const bf16x8*>(kt + k_lane + kb * 16 * kKRowB + kk * 16);
 #pragma unroll
-      for (int rb = 0; rb < 2; ++rb) {
+      for (int rb = 0; rb < kPfRb; ++rb) {
         f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int kk = 0; kk < kQk; ++kk) acc = mfma_qk(kf[kk], qf[rb][kk], acc);
         s[kb][rb] = acc;
       }
     }
-    bf16x8 pk[2][2];
+    // row maxima, then one (rarely taken) rescale branch for both row blocks
+    float muse[kPfRb];
+    bool up_any = false;
+    float alpha[kPfRb];
 #pragma unroll
-    for (int rb = 0; rb < 2; ++rb) {
+    for (int rb = 0; rb < kPfRb; ++rb) {
       if constexpr (kMask) {
 #pragma unroll
         for (int kb = 0; kb < 4; ++kb)
@@ -1177,47 +1239,49 @@ __global__ __launch_bounds__(kThreads, 2) void paged_prefill_kernel(AttnArgs a,
           for (int i = 0; i < 4; ++i)
             s[kb][rb][i] = (tb + kb * 16 + 4 * lgrp + i <= qpos[rb]) ? s[kb][rb][i] : -INFINITY;
       }
-      float mx = s[0][rb][0];
+      float mx = fmaxf(fmaxf(s[0][rb][0], s[0][rb][1]), fmaxf(s[0][rb][2], s[0][rb][3]));
 #pragma unroll
-      for (int kb = 0; kb < 4; ++kb)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) mx = fmaxf(mx, s[kb][rb][i]);
+      for (int kb = 1; kb < 4; ++kb)
+        mx = fmaxf(mx, fmaxf(fmaxf(s[kb][rb][0], s[kb][rb][1]), fmaxf(s[kb][rb][2], s[kb][rb][3])));
       mx = fmaxf(mx, __shfl_xor(mx, 16));
       mx = fmaxf(mx, __shfl_xor(mx, 32));
       const float mxc = mx * c2;
       const bool up = mxc > mc[rb] + 8.f;
       const float mnew = up ? mxc : mc[rb];
-      const float alpha = up ? fast_exp2(mc[rb] - mnew) : 1.f;
+      alpha[rb] = up ? fast_exp2(mc[rb] - mnew) : 1.f;
       mc[rb] = mnew;
-      if (__any(up)) {
-        lsum[rb] *= alpha;
+      up_any = up_any || up;
+      muse[rb] = mnew == -INFINITY ? 0.f : mnew;
+    }
+    if (__any(up_any)) {
 #pragma unroll
-        for (int d = 0; d < kDb; ++d) o[d][rb] *= alpha;
-      }
-      const float muse = mnew == -INFINITY ? 0.f : mnew;
+      for (int rb = 0; rb < kPfRb; ++rb) {
+        lsum[rb] *= alpha[rb];
 #pragma unroll
-      for (int ks = 0; ks < 2; ++ks) {
-        bf16x8 p;
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          p[i] = static_cast<__bf16>(fast_exp2(fmaf(s[2 * ks][rb][i], c2, -muse)));
-          p[4 + i] = static_cast<__bf16>(fast_exp2(fmaf(s[2 * ks + 1][rb][i], c2, -muse)));
-        }
-        pk[rb][ks] = p;
-        lsum[rb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ones, p, lsum[rb], 0, 0, 0);
+        for (int d = 0; d < kDb; ++d) o[d][rb] *= alpha[rb];
       }
     }
 #pragma unroll
     for (int ks = 0; ks < 2; ++ks) {
+      bf16x8 pk[kPfRb];
+#pragma unroll
+      for (int rb = 0; rb < kPfRb; ++rb) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          pk[rb][i] = static_cast<__bf16>(fast_exp2(fmaf(s[2 * ks][rb][i], c2, -muse[rb])));
+          pk[rb][4 + i] = static_cast<__bf16>(fast_exp2(fmaf(s[2 * ks + 1][rb][i], c2, -muse[rb])));
+        }
+        lsum[rb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ones, pk[rb], lsum[rb], 0, 0, 0);
+      }
 #pragma unroll
       for (int d = 0; d < kDb; ++d) {
-        const char* vp = vt + v_lane + 32 * ks * kRowB + d * 32;
+        const char* vp = vt + v_lane + 32 * ks * kVRowB + d * 32;
         const bf16x4 v0 = lds_read_tr(vp);
-        const bf16x4 v1 = lds_read_tr(vp + 16 * kRowB);
+        const bf16x4 v1 = lds_read_tr(vp + 16 * kVRowB);
         const bf16x8 vf = __builtin_shufflevector(v0, v1, 0, 1, 2, 3, 4, 5, 6, 7);
 #pragma unroll
-        for (int rb = 0; rb < 2; ++rb)
-          o[d][rb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf, pk[rb][ks], o[d][rb], 0, 0, 0);
+        for (int rb = 0; rb < kPfRb; ++rb)
+          o[d][rb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf, pk[rb], o[d][rb], 0, 0, 0);
       }
     }
   };
@@ -1237,11 +1301,11 @@ __global__ __launch_bounds__(kThreads, 2) void paged_prefill_kernel(AttnArgs a,
     fetch_pages(t + 2);
     const int tb = k_lo + t * kPfKeys;
     if (w_active && tb <= w_qmax) {
-      const char* kt = smem + (t & 1) * 2 * kTileB;
+      const char* kt = smem + (t & 1) * kBufB;
       if (tb + kPfKeys - 1 <= w_qmin)
-        compute(kt, kt + kTileB, tb, std::integral_constant<bool, false>());
+        compute(kt, kt + kKTileB, tb, std::integral_constant<bool, false>());
       else
-        compute(kt, kt + kTileB, tb, std::integral_constant<bool, true>());
+        compute(kt, kt + kKTileB, tb, std::integral_constant<bool, true>());
     }
     stage((t + 1) & 1);
 #pragma unroll
@@ -1253,7 +1317,7 @@ __global__ __launch_bounds__(kThreads, 2) void paged_prefill_kernel(AttnArgs a,
   if (!w_active) return;
   const bool final_write = n_sp == 1;
 #pragma unroll
-  for (int rb = 0; rb < 2; ++rb) {
+  for (int rb = 0; rb < kPfRb; ++rb) {
     const int rr = wr0 + 16 * rb + lrow;
     if (qpos[rb] < 0) continue;
     const int qi = rr / group;
@@ -1280,42 +1344,17 @@ __global__ __launch_bounds__(kThreads, 2) void paged_prefill_kernel(AttnArgs a,
   }
 }
 
-// Log-sum-exp merge of the KV-split partials of one (query, head) row.  Grid:
-// (num_q_heads, max_q_per_seq, n_seqs), one wave per row.  RBW > 0: the
-// decode path, where rows whose sequence fits one chunk were written final
-// by the attention kernel; RBW = 0: the tile kernel, every split partial.
-template <typename T, int D, int RBW>
-__global__ __launch_bounds__(kWave) void merge_chunks_kernel(AttnArgs args) {
-  const int h = blockIdx.x;
-  const int qi = blockIdx.y;
-  const int b = blockIdx.z;
-  int q0, n_b;
-  int n_chunks = args.n_splits;
-  if constexpr (RBW > 0) {
-    const int kv_end = decode_kv_end<RBW>(args, b, &q0, &n_b);
-    n_chunks = kv_end > 0 ? min((kv_end + args.split_len - 1) / args.split_len, args.n_splits) : 0;
-    if (n_chunks <= 1) return;
-  } else {
-    if (args.cu_q) {
-      q0 = args.cu_q[b];
-      n_b = args.cu_q[b + 1] - q0;
-    } else {
-      q0 = b;
-      n_b = 1;
-    }
-  }
-  if (qi >= n_b) return;
-  const int tok = q0 + qi;
-  if (tok >= args.total_q || tok >= args.ws_tokens) return;
-  const int qpos = args.seq_lens[b] - n_b + qi;
-  const int ns = qpos < 0 ? 0 : min(n_chunks, qpos / args.split_len + 1);
+// Fold ns partial states of one output row: state k has its un-normalised
+// output at o[k * stride * D ..] and (max, sum) at ml[k * stride * 2 ..]
+// (log2 domain), and the result goes to row orow of out.  One wave; each lane
+// owns D / 64 dims; partial rows are read eight at a time.
+template <typename T, int D>
+__device__ __forceinline__ void merge_rows(const AttnArgs& args, const float* o, const float* ml, int stride,
+                                           int ns, int64_t orow) {
   const int lane = threadIdx.x;
-  const int64_t orow = static_cast<int64_t>(tok) * args.num_q_heads + h;
-  const int64_t base = orow * args.n_splits;
   constexpr int kPer = D / kWave;
-  // pass 1: global max; each lane holds the states of chunks lane, lane + 64, ...
   float mmax = -INFINITY;
-  for (int s = lane; s < ns; s += kWave) mmax = fmaxf(mmax, args.ws_ml[(base + s) * 2]);
+  for (int s = lane; s < ns; s += kWave) mmax = fmaxf(mmax, ml[static_cast<int64_t>(s) * stride * 2]);
 #pragma unroll
   for (int off = 32; off >= 1; off >>= 1) mmax = fmaxf(mmax, __shfl_xor(mmax, off));
   const float mref = mmax == -INFINITY ? 0.f : mmax;
@@ -1327,26 +1366,26 @@ __global__ __launch_bounds__(kWave) void merge_chunks_kernel(AttnArgs args) {
     const int sl = s0 + lane;
     float wt = 0.f;
     if (sl < ns) {
-      wt = fast_exp2(args.ws_ml[(base + sl) * 2] - mref);
-      lsum += wt * args.ws_ml[(base + sl) * 2 + 1];
+      const float* m = ml + static_cast<int64_t>(sl) * stride * 2;
+      wt = fast_exp2(m[0] - mref);
+      lsum += wt * m[1];
     }
     const int cnt = min(kWave, ns - s0);
-    // eight partial rows in flight at a time (indices clamped, weights zero)
     for (int k0 = 0; k0 < cnt; k0 += 8) {
       float part[8][kPer];
 #pragma unroll
-      for (int u = 0; u < 8; ++u) {
-        const int k = min(k0 + u, cnt - 1);
-        const float* o = args.ws_o + (base + s0 + k) * D + lane * kPer;
+      for (int v = 0; v < 8; ++v) {
+        const int k = min(k0 + v, cnt - 1);
+        const float* src = o + static_cast<int64_t>(s0 + k) * stride * D + lane * kPer;
 #pragma unroll
-        for (int j = 0; j < kPer; ++j) part[u][j] = o[j];
+        for (int j = 0; j < kPer; ++j) part[v][j] = src[j];
       }
 #pragma unroll
-      for (int u = 0; u < 8; ++u) {
-        const float wk = __shfl(wt, min(k0 + u, kWave - 1));
-        const float w_use = (k0 + u < cnt) ? wk : 0.f;
+      for (int v = 0; v < 8; ++v) {
+        const float wk = __shfl(wt, min(k0 + v, kWave - 1));
+        const float w_use = (k0 + v < cnt) ? wk : 0.f;
 #pragma unroll
-        for (int j = 0; j < kPer; ++j) acc[j] += w_use * part[u][j];
+        for (int j = 0; j < kPer; ++j) acc[j] += w_use * part[v][j];
       }
     }
   }
@@ -1362,6 +1401,54 @@ __global__ __launch_bounds__(kWave) void merge_chunks_kernel(AttnArgs args) {
     else
       static_cast<float*>(args.out)[e] = v;
   }
+}
+
+// Log-sum-exp merge of the KV-split partials of one (query, head) row of the
+// tile kernels.  Grid: (num_q_heads, max_q_per_seq, n_seqs), one wave per row.
+template <typename T, int D>
+__global__ __launch_bounds__(kWave) void merge_chunks_kernel(AttnArgs args) {
+  const int h = blockIdx.x;
+  const int qi = blockIdx.y;
+  const int b = blockIdx.z;
+  const int q0 = args.cu_q[b];
+  const int n_b = args.cu_q[b + 1] - q0;
+  if (qi >= n_b) return;
+  const int tok = q0 + qi;
+  if (tok >= args.total_q || tok >= args.ws_tokens) return;
+  const int qpos = args.seq_lens[b] - n_b + qi;
+  const int ns = qpos < 0 ? 0 : min(args.n_splits, qpos / args.split_len + 1);
+  const int64_t orow = static_cast<int64_t>(tok) * args.num_q_heads + h;
+  merge_rows<T, D>(args, args.ws_o + orow * args.n_splits * D, args.ws_ml + orow * args.n_splits * 2, 1, ns,
+                   orow);
+}
+
+// Log-sum-exp merge of the decode segments of one (unit, row): the slots
+// unit + w of the waves w whose block ranges cut the unit.  Grid: (units,
+// 16 * RBW), one wave each; units inside one wave's range were written final.
+template <typename T, int D, int RBW>
+__global__ __launch_bounds__(kWave) void merge_segments_kernel(AttnArgs a, const int32_t* __restrict__ seq_blk) {
+  constexpr int kRowsCap = 16 * RBW;
+  const int u = blockIdx.x;
+  const int r = blockIdx.y;
+  const int hkv = a.num_kv_heads;
+  const int b = u / hkv;
+  const int g = u - b * hkv;
+  const int nb = seq_blk[b + 1] - seq_blk[b];
+  if (nb == 0) return;
+  const int per = decode_per(seq_blk[a.n_seqs] * hkv, a.waves, a.split_len);
+  const int u0 = seq_blk[b] * hkv + g * nb;
+  const int f = u0 / per;
+  const int l = (u0 + nb - 1) / per;
+  if (f == l) return;
+  int q0, n_b, rows;
+  decode_kv_end<RBW>(a, b, &q0, &n_b, &rows);
+  if (r >= rows) return;
+  const int qi = r / a.group;
+  const int tok = q0 + qi;
+  if (tok >= a.total_q) return;
+  const int64_t orow = static_cast<int64_t>(tok) * a.num_q_heads + g * a.group + (r - qi * a.group);
+  const int64_t row0 = static_cast<int64_t>(u + f) * kRowsCap + r;
+  merge_rows<T, D>(a, a.ws_o + row0 * D, a.ws_ml + row0 * 2, kRowsCap, l - f + 1, orow);
 }
 
 // KV scatter: one thread per 16-byte chunk of a (token, KV head) row, K and
@@ -1439,13 +1526,6 @@ struct Plan {
 };
 
 // Decode-path tunables (overridable at build time for sweeps).
-#ifndef PKV_DECODE_WORKGROUPS
-#define PKV_DECODE_WORKGROUPS 512    // persistent decode workgroups (2 per CU)
-#endif
-#ifndef PKV_DECODE_MIN_CHUNK
-#define PKV_DECODE_MIN_CHUNK 256     // smallest work item, in positions
-#endif
-constexpr int kDecodeWorkgroups = PKV_DECODE_WORKGROUPS;
 
 // The launch shape is a pure function of host scalars, so the workspace size
 // and the split positions are reproducible from the same arguments.
@@ -1464,34 +1544,26 @@ int make_plan(const pkv_pool_desc* d, int n_seqs, int hq, int max_q, int max_seq
   const int ps = d->page_size;
   if (n_seqs == 0 || max_q == 0) return PKV_OK;  // nothing to launch, no workspace
   if (rows <= 48) {
-    // decode path: items of `chunk` positions.  Larger items for more rows
-    // keep the partials small next to the K/V they summarise; smaller ones
-    // keep enough items to balance the persistent workgroups.  An item spans
-    // at most 64 pages (its block-table slice sits in one register per lane).
+    // decode path: the units' 16-position blocks split evenly over at most
+    // kDecodeWaves one-wave workgroups, each taking at least
+    // PKV_DECODE_MIN_BLOCKS blocks.  Partial states: one slot per (unit,
+    // wave) pair that can meet, at most units + waves.
     p->decode = true;
     p->rbw = static_cast<int>(std::max<int64_t>(1, (rows + 15) / 16));
     p->epi_rows = static_cast<int>(std::max<int64_t>(1, std::min<int64_t>(16, rows)));
     p->tile_rows = 16 * p->rbw;
     p->q_tiles = 1;
-    int64_t chunk = std::max<int64_t>(PKV_DECODE_MIN_CHUNK, 64 * rows);
-    chunk = std::min<int64_t>(chunk, 4096);
-    const int64_t est_len = std::max<int64_t>(1, max_seq_len);
-    while (chunk > PKV_DECODE_MIN_CHUNK &&
-           static_cast<int64_t>(n_seqs) * d->num_kv_heads * ((est_len + chunk - 1) / chunk) < 4 * kDecodeWorkgroups)
-      chunk /= 2;
-    chunk = std::min<int64_t>(chunk, static_cast<int64_t>(63) * ps);
-    chunk = std::max<int64_t>(16, chunk & ~int64_t{15});
-    p->split_len = static_cast<int>(chunk);
-    p->n_splits = static_cast<int>(std::max<int64_t>(1, (est_len + chunk - 1) / chunk));
-    if (static_cast<int64_t>(n_seqs) * p->n_splits > (int64_t{1} << 30))
-      return fail(PKV_ERR_UNSUPPORTED, std::string(fn) + ": too many work items");
-    const int64_t items = static_cast<int64_t>(n_seqs) * p->n_splits * d->num_kv_heads;
-    p->grid = static_cast<int>(std::max<int64_t>(1, std::min<int64_t>(items, kDecodeWorkgroups)));
-    p->items_off = 256;
-    p->partial_off = p->items_off + static_cast<size_t>(n_seqs) * p->n_splits * 32;
-    p->ws_bytes = p->partial_off;
-    if (p->n_splits > 1)
-      p->ws_bytes += static_cast<size_t>(n_seqs) * max_q * hq * p->n_splits * (d->head_dim + 2) * sizeof(float);
+    const int64_t units = static_cast<int64_t>(n_seqs) * d->num_kv_heads;
+    const int64_t blocks_max = units * ((static_cast<int64_t>(std::max(1, max_seq_len)) + 15) / 16);
+    if (blocks_max > (int64_t{1} << 30)) return fail(PKV_ERR_UNSUPPORTED, std::string(fn) + ": too many KV blocks");
+    p->split_len = PKV_DECODE_MIN_BLOCKS;
+    p->grid = static_cast<int>(std::max<int64_t>(
+        1, std::min<int64_t>(kDecodeWaves, (blocks_max + PKV_DECODE_MIN_BLOCKS - 1) / PKV_DECODE_MIN_BLOCKS)));
+    p->n_splits = 2;   // partial slots are used
+    p->items_off = 0;
+    p->partial_off = (static_cast<size_t>(n_seqs + 1) * sizeof(int32_t) + 255) & ~size_t{255};
+    const size_t slots = static_cast<size_t>(units) + p->grid;
+    p->ws_bytes = p->partial_off + slots * (16 * p->rbw) * (d->head_dim + 2) * sizeof(float);
     return PKV_OK;
   }
   if (d->dtype == PKV_BF16) {
@@ -1553,23 +1625,17 @@ void launch_attention_t(const AttnArgs& a, const Plan& p, int n_seqs, int hkv, h
 
 template <typename T, int D, int RBW>
 void launch_decode_t(const AttnArgs& a, const Plan& p, int n_seqs, char* ws, hipStream_t st) {
-  DecodeQueue* queue = reinterpret_cast<DecodeQueue*>(ws);
-  DecodeItem* items = reinterpret_cast<DecodeItem*>(ws + p.items_off);
-  decode_schedule_kernel<RBW><<<1, kThreads, 0, st>>>(a, queue, items);
+  int32_t* seq_blk = reinterpret_cast<int32_t*>(ws + p.items_off);
   constexpr int kRowB = D * static_cast<int>(sizeof(T));
-  constexpr int kStage = 4 * 2 * 16 * (kRowB + (kRowB >= 512 ? 0 : 16));
-  const int epi = (4 * p.epi_rows * (D + 4) + 2 * 4 * p.epi_rows) * static_cast<int>(sizeof(float));
-  const int lds = std::max(kStage, epi);
+  constexpr int kLds = 16 * (2 * kRowB + (kRowB >= 512 ? 0 : 48));
   if (a.ps_shift >= 4)
-    paged_decode_kernel<T, D, RBW, 0><<<p.grid, dim3(kThreads), lds, st>>>(a, queue, items);
+    paged_decode_kernel<T, D, RBW, 0><<<p.grid, dim3(kWave), kLds, st>>>(a, seq_blk);
   else if (a.ps_shift >= 0)
-    paged_decode_kernel<T, D, RBW, 1><<<p.grid, dim3(kThreads), lds, st>>>(a, queue, items);
+    paged_decode_kernel<T, D, RBW, 1><<<p.grid, dim3(kWave), kLds, st>>>(a, seq_blk);
   else
-    paged_decode_kernel<T, D, RBW, 2><<<p.grid, dim3(kThreads), lds, st>>>(a, queue, items);
-  if (p.n_splits > 1) {
-    dim3 grid(a.num_q_heads, p.max_q, n_seqs);
-    merge_chunks_kernel<T, D, RBW><<<grid, dim3(kWave), 0, st>>>(a);
-  }
+    paged_decode_kernel<T, D, RBW, 2><<<p.grid, dim3(kWave), kLds, st>>>(a, seq_blk);
+  dim3 grid(n_seqs * a.num_kv_heads, 16 * RBW);
+  merge_segments_kernel<T, D, RBW><<<grid, dim3(kWave), 0, st>>>(a, seq_blk);
 }
 
 // Upper bound on the prefill tile-rows the schedule kernel can list, from
@@ -1582,20 +1648,20 @@ int64_t prefill_grid(const Plan& p, int n_seqs, int hkv, int group, int total_q)
   return 8 * rows * p.n_splits;
 }
 
-template <int D, bool kPow2>
+template <int D, int kPageMode>
 int launch_prefill_t(const AttnArgs& a, const Plan& p, char* ws, hipStream_t st) {
   constexpr int kLds = pf_lds_bytes<D>();
-  static const hipError_t attr = hipFuncSetAttribute(reinterpret_cast<const void*>(&paged_prefill_kernel<D, kPow2>),
+  static const hipError_t attr = hipFuncSetAttribute(reinterpret_cast<const void*>(&paged_prefill_kernel<D, kPageMode>),
                                                      hipFuncAttributeMaxDynamicSharedMemorySize, kLds);
   if (attr != hipSuccess) return fail(PKV_ERR_DEVICE, std::string("prefill: LDS attribute: ") + hipGetErrorString(attr));
   int32_t* row_off = reinterpret_cast<int32_t*>(ws + p.items_off);
   prefill_schedule_kernel<<<1, kThreads, 0, st>>>(a, row_off, p.n_blocks);
   const int64_t grid = prefill_grid(p, a.n_seqs, a.num_kv_heads, a.group, a.total_q);
   if (grid > INT32_MAX) return fail(PKV_ERR_UNSUPPORTED, "prefill: grid too large");
-  if (grid > 0) paged_prefill_kernel<D, kPow2><<<static_cast<int>(grid), dim3(kThreads), kLds, st>>>(a, row_off, p.n_blocks);
+  if (grid > 0) paged_prefill_kernel<D, kPageMode><<<static_cast<int>(grid), dim3(kThreads), kLds, st>>>(a, row_off, p.n_blocks);
   if (p.n_splits > 1) {
     dim3 mg(a.num_q_heads, p.max_q, a.n_seqs);
-    merge_chunks_kernel<uint16_t, D, 0><<<mg, dim3(kWave), 0, st>>>(a);
+    merge_chunks_kernel<uint16_t, D><<<mg, dim3(kWave), 0, st>>>(a);
   }
   return PKV_OK;
 }
@@ -1613,7 +1679,7 @@ void launch_attention_d(const AttnArgs& a, const Plan& p, int n_seqs, int hkv, c
   launch_attention_t<T, D, 4, 1>(a, p, n_seqs, hkv, st);
   if (p.n_splits > 1) {
     dim3 grid(a.num_q_heads, p.max_q, n_seqs);
-    merge_chunks_kernel<T, D, 0><<<grid, dim3(kWave), 0, st>>>(a);
+    merge_chunks_kernel<T, D><<<grid, dim3(kWave), 0, st>>>(a);
   }
 }
 
@@ -1663,7 +1729,12 @@ int run_attention(const char* fn, const pkv_pool_desc* desc, const void* k_pool,
   a.n_splits = p.n_splits;
   a.max_q = max_q;
   a.scale_log2 = scale * 1.4426950408889634f;
-  if (p.n_splits > 1) {
+  a.waves = p.grid;
+  if (p.decode) {
+    const size_t rows_out = (static_cast<size_t>(n_seqs) * desc->num_kv_heads + p.grid) * (16 * p.rbw);
+    a.ws_o = reinterpret_cast<float*>(static_cast<char*>(workspace) + p.partial_off);
+    a.ws_ml = a.ws_o + rows_out * desc->head_dim;
+  } else if (p.n_splits > 1) {
     const size_t rows_out = static_cast<size_t>(n_seqs) * max_q * hq * p.n_splits;
     a.ws_o = reinterpret_cast<float*>(static_cast<char*>(workspace) + p.partial_off);
     a.ws_ml = a.ws_o + rows_out * desc->head_dim;
@@ -1674,10 +1745,15 @@ int run_attention(const char* fn, const pkv_pool_desc* desc, const void* k_pool,
   (void)hipGetLastError();
   if (p.prefill) {
     const bool pow2 = a.ps_shift >= 0;
-    if (desc->head_dim == 128)
-      rc = pow2 ? launch_prefill_t<128, true>(a, p, ws, st) : launch_prefill_t<128, false>(a, p, ws, st);
-    else
-      rc = pow2 ? launch_prefill_t<64, true>(a, p, ws, st) : launch_prefill_t<64, false>(a, p, ws, st);
+    if (desc->head_dim == 128) {
+      const int mode = !pow2 ? 2 : a.page_size >= pf_wave_rows<128>() ? 0 : 1;
+      rc = mode == 0 ? launch_prefill_t<128, 0>(a, p, ws, st)
+                     : mode == 1 ? launch_prefill_t<128, 1>(a, p, ws, st) : launch_prefill_t<128, 2>(a, p, ws, st);
+    } else {
+      const int mode = !pow2 ? 2 : a.page_size >= pf_wave_rows<64>() ? 0 : 1;
+      rc = mode == 0 ? launch_prefill_t<64, 0>(a, p, ws, st)
+                     : mode == 1 ? launch_prefill_t<64, 1>(a, p, ws, st) : launch_prefill_t<64, 2>(a, p, ws, st);
+    }
     if (rc != PKV_OK) return rc;
   } else if (desc->dtype == PKV_BF16) {
     if (desc->head_dim == 128)
