@@ -533,7 +533,8 @@ typedef __attribute__((address_space(3))) dec_bf16x4 lds_dec_bf16x4;
 // one page); 1: a power of two < 16; 2: any other page size.
 template <typename T, int D, int RBW, int kPageMode>
 __global__ __launch_bounds__(kWave, RBW == 1 ? PKV_DECODE_WAVES_PER_SIMD : 1) void paged_decode_kernel(
-    AttnArgs args, int32_t* __restrict__ seq_blk) {
+    AttnArgs args, int32_t* __restrict__ seq_blk, const int32_t* __restrict__ seq_lens,
+    const int32_t* __restrict__ cu_q, const int32_t* __restrict__ block_tables) {
   constexpr int kEs = sizeof(T);
   constexpr int kRowBytes = D * kEs;
   constexpr int kCpr = kRowBytes / 16;                  // 16-byte chunks per row
@@ -570,9 +571,29 @@ __global__ __launch_bounds__(kWave, RBW == 1 ? PKV_DECODE_WAVES_PER_SIMD : 1) vo
   // nb(b) = 16-position blocks of sequence b per KV head.  Lane l of chunk c
   // handles sequence 64 c + l; wave 0 also writes the prefix seq_blk[] that
   // the merge kernel reads.
+  // Queries of sequence b seen here (at most 16 * RBW rows) and the positions
+  // they see, [0, kv_end) (the same rule as decode_kv_end, read through the
+  // read-only kernel arguments so uniform indices use scalar loads).
+  struct Unit {
+    int q0, start, rows, kv_end;
+  };
+  auto unit_of = [&](int b) __attribute__((always_inline)) {
+    Unit u;
+    int n_b;
+    if (cu_q) {
+      u.q0 = cu_q[b];
+      n_b = cu_q[b + 1] - u.q0;
+    } else {
+      u.q0 = b;
+      n_b = 1;
+    }
+    u.rows = max(0, min(min(n_b, args.max_q) * group, 16 * RBW));
+    u.start = seq_lens[b] - n_b;
+    u.kv_end = u.rows > 0 ? u.start + (u.rows - 1) / group + 1 : 0;
+    return u;
+  };
   auto nb_of = [&](int b) __attribute__((always_inline)) {
-    int q0, n_b, rows;
-    const int kv_end = decode_kv_end<RBW>(args, b, &q0, &n_b, &rows);
+    const int kv_end = unit_of(b).kv_end;
     return kv_end > 0 ? (kv_end + 15) >> 4 : 0;
   };
   int total_seq = 0;                       // blocks per KV head of all sequences
@@ -586,7 +607,7 @@ __global__ __launch_bounds__(kWave, RBW == 1 ? PKV_DECODE_WAVES_PER_SIMD : 1) vo
       if (lane >= off) incl += v;
     }
     if (blockIdx.x == 0 && b < n_seqs) seq_blk[b] = total_seq + incl - nb;
-    total_seq += __shfl(incl, kWave - 1);
+    total_seq += __builtin_amdgcn_readfirstlane(__shfl(incl, kWave - 1));
   }
   if (blockIdx.x == 0 && lane == 0) seq_blk[n_seqs] = total_seq;
 
@@ -619,12 +640,12 @@ __global__ __launch_bounds__(kWave, RBW == 1 ? PKV_DECODE_WAVES_PER_SIMD : 1) vo
       const unsigned long long hit = __ballot((base + incl) * hkv > i);
       if (hit) {
         const int l = __builtin_ctzll(hit);
-        c.b = c0 + l;
-        c.nb = __shfl(nb, l);
-        base += __shfl(incl, l) - c.nb;
+        c.b = __builtin_amdgcn_readfirstlane(c0 + l);
+        c.nb = __builtin_amdgcn_readfirstlane(__shfl(nb, l));
+        base += __builtin_amdgcn_readfirstlane(__shfl(incl, l)) - c.nb;
         break;
       }
-      base += __shfl(incl, kWave - 1);
+      base += __builtin_amdgcn_readfirstlane(__shfl(incl, kWave - 1));
     }
     const int r = i - base * hkv;
     c.g = r / c.nb;
@@ -637,27 +658,18 @@ __global__ __launch_bounds__(kWave, RBW == 1 ? PKV_DECODE_WAVES_PER_SIMD : 1) vo
     if (++c.g < hkv) return;
     c.g = 0;
     do {
-      ++c.b;
-      c.nb = nb_of(c.b);
+      c.b = __builtin_amdgcn_readfirstlane(c.b + 1);
+      c.nb = __builtin_amdgcn_readfirstlane(nb_of(c.b));
     } while (c.nb == 0 && c.b + 1 < n_seqs);
   };
 
-  // Per-unit scalars.
-  struct Unit {
-    int q0, start, rows, kv_end;
-  };
-  auto unit_of = [&](int b) __attribute__((always_inline)) {
-    Unit u;
-    int n_b;
-    u.kv_end = decode_kv_end<RBW>(args, b, &u.q0, &n_b, &u.rows);
-    u.start = args.seq_lens[b] - n_b;
-    return u;
-  };
 
   // Query rows (B operand of S^T = K Q^T): row r = (query r / group, head
   // g * group + r % group); this lane holds row rb * 16 + lrow, dims
-  // lgrp * kDl .. + kDl.  Branch-free: rows without a query read row 0 of the
-  // batch and are zeroed.
+  // lgrp * kDl .. + kDl.  Branch-free: a row without a query reads the
+  // batch's first query (finite values; its result is never written), and
+  // the loaded values are not touched until the unit is computed, so the
+  // loads stay in flight behind the K/V loads.
   auto load_q = [&](int b, int g, const Unit& u, QkFrag<T, kDl> (&qv)[RBW], int (&qpos)[RBW]) __attribute__((always_inline)) {
 #pragma unroll
     for (int rb = 0; rb < RBW; ++rb) {
@@ -667,12 +679,11 @@ __global__ __launch_bounds__(kWave, RBW == 1 ? PKV_DECODE_WAVES_PER_SIMD : 1) vo
       const bool ok = r < u.rows && tok < args.total_q;
       qpos[rb] = u.start + (r < u.rows ? qi : -1);
       const int tok_c = ok ? tok : 0;
-      const T* src = static_cast<const T*>(args.q) +
-                     (static_cast<int64_t>(tok_c) * args.num_q_heads + g * group + (r - qi * group)) * D +
+      const int hh = ok ? g * group + (r - qi * group) : 0;
+      const T* src = static_cast<const T*>(args.q) + (static_cast<int64_t>(tok_c) * args.num_q_heads + hh) * D +
                      lgrp * kDl;
-      const unsigned keep = ok ? ~0u : 0u;
 #pragma unroll
-      for (int c = 0; c < kFragChunks; ++c) qv[rb].load16(c, reinterpret_cast<const u32x4*>(src)[c] & keep);
+      for (int c = 0; c < kFragChunks; ++c) qv[rb].load16(c, reinterpret_cast<const u32x4*>(src)[c]);
     }
   };
 
@@ -683,7 +694,7 @@ __global__ __launch_bounds__(kWave, RBW == 1 ? PKV_DECODE_WAVES_PER_SIMD : 1) vo
   auto load_block = [&](const Cur& c, int kv_end, int page_hint, u32x4 (&kr)[kLoads], u32x4 (&vr)[kLoads],
                         uint32_t& okm) __attribute__((always_inline)) {
     const int pos0 = 16 * c.j;
-    const int32_t* bt_row = args.block_tables + static_cast<int64_t>(c.b) * args.bt_stride;
+    const int32_t* bt_row = block_tables + static_cast<int64_t>(c.b) * args.bt_stride;
     okm = 0;
     if constexpr (kPageMode == 0) {
       const uint32_t page = static_cast<uint32_t>(min(max(page_hint, 0), args.num_pages - 1));
@@ -716,7 +727,9 @@ __global__ __launch_bounds__(kWave, RBW == 1 ? PKV_DECODE_WAVES_PER_SIMD : 1) vo
   };
   // page of the block at cursor c (page mode 0: one page per block)
   auto page_of = [&](const Cur& c) __attribute__((always_inline)) {
-    return args.block_tables[static_cast<int64_t>(c.b) * args.bt_stride + ((16 * c.j) >> max(ps_shift, 0))];
+    const int b = __builtin_amdgcn_readfirstlane(c.b);
+    const int blk = __builtin_amdgcn_readfirstlane((16 * c.j) >> max(ps_shift, 0));
+    return block_tables[static_cast<int64_t>(b) * args.bt_stride + blk];
   };
 
   // Write a block's rows into the wave's LDS slices.  V rows past the unit
@@ -884,67 +897,45 @@ __global__ __launch_bounds__(kWave, RBW == 1 ? PKV_DECODE_WAVES_PER_SIMD : 1) vo
   issue(i0 + 1, kb, vb, okb);
 
   Unit uc = unit_of(cc.b);
-  QkFrag<T, kDl> q_cur[RBW], q_nxt[RBW];
-  int qpos_cur[RBW], qpos_nxt[RBW];
-  load_q(cc.b, cc.g, uc, q_cur, qpos_cur);
-  // the unit after the current one, if the range reaches it
-  Cur nc = cc;
+  // The unit's queries load at its start (a wave's range meets few units);
+  // they are first used by the next block's MFMAs, so the wait for them
+  // leaves that block's K/V loads in flight.
+  QkFrag<T, kDl> qv[RBW];
+  int qpos[RBW];
+  load_q(cc.b, cc.g, uc, qv, qpos);
   int seg_first = cc.j;             // block at which the current segment started
-  auto next_unit = [&]() __attribute__((always_inline)) {
-    Cur n = cc;
-    n.j = n.nb - 1;
-    advance(n);
-    return n;
-  };
-  const int rest0 = cc.nb - cc.j;   // blocks of the current unit left in the range
-  Unit un = uc;
-  bool has_next = i0 + rest0 < i1;
-  if (has_next) {
-    nc = next_unit();
-    un = unit_of(nc.b);
-    load_q(nc.b, nc.g, un, q_nxt, qpos_nxt);
-  }
   reset_state();
 
-  for (int i = i0; i < i1; i += 2) {
-#pragma unroll
-    for (int h = 0; h < 2; ++h) {
-      if (h == 1 && i + 1 >= i1) break;
-      const int ii = i + h;
-      if (h == 0) {
-        stage_block(ka, va, oka);
-        issue(ii + 2, ka, va, oka);
-      } else {
-        stage_block(kb, vb, okb);
-        issue(ii + 2, kb, vb, okb);
-      }
-      compute_block(16 * cc.j, uc.kv_end, q_cur, qpos_cur);
-      const bool unit_end = cc.j == cc.nb - 1;
-      if (unit_end || ii + 1 == i1) {
-        write_segment(cc.b, cc.g, uc, seg_first == 0 && unit_end);
-        if (ii + 1 < i1) {
-          // the next unit becomes current; fetch the one after it
-          cc = nc;
-          uc = un;
-#pragma unroll
-          for (int rb = 0; rb < RBW; ++rb) {
-            q_cur[rb] = q_nxt[rb];
-            qpos_cur[rb] = qpos_nxt[rb];
-          }
-          seg_first = 0;
-          reset_state();
-          has_next = ii + 1 + cc.nb < i1;
-          if (has_next) {
-            nc = next_unit();
-            un = unit_of(nc.b);
-            load_q(nc.b, nc.g, un, q_nxt, qpos_nxt);
-          }
-        }
-      } else {
+  // One step: stage block ii from its registers, issue block ii + 2 into
+  // them, compute block ii, and close the segment at a unit's or the range's
+  // end.
+  auto step = [&](int ii, u32x4 (&kr)[kLoads], u32x4 (&vr)[kLoads], uint32_t& okm) __attribute__((always_inline)) {
+    stage_block(kr, vr, okm);
+    issue(ii + 2, kr, vr, okm);
+    compute_block(16 * cc.j, uc.kv_end, qv, qpos);
+    const bool unit_end = cc.j == cc.nb - 1;
+    if (unit_end || ii + 1 == i1) {
+      write_segment(cc.b, cc.g, uc, seg_first == 0 && unit_end);
+      if (ii + 1 < i1) {            // on to the next unit
         advance(cc);
+        uc = unit_of(cc.b);
+        load_q(cc.b, cc.g, uc, qv, qpos);
+        seg_first = 0;
+        reset_state();
       }
+    } else {
+      advance(cc);
     }
+  };
+  // Whole pairs of steps, then an odd last one: every path back to the top
+  // of the loop has issued both buffers' loads, so each staging waits for
+  // the older buffer only.
+  int i = i0;
+  for (; i + 1 < i1; i += 2) {
+    step(i, ka, va, oka);
+    step(i + 1, kb, vb, okb);
   }
+  if (i < i1) step(i, ka, va, oka);
 }
 
 // ---------------------------------------------------------------------------
@@ -1629,11 +1620,11 @@ void launch_decode_t(const AttnArgs& a, const Plan& p, int n_seqs, char* ws, hip
   constexpr int kRowB = D * static_cast<int>(sizeof(T));
   constexpr int kLds = 16 * (2 * kRowB + (kRowB >= 512 ? 0 : 48));
   if (a.ps_shift >= 4)
-    paged_decode_kernel<T, D, RBW, 0><<<p.grid, dim3(kWave), kLds, st>>>(a, seq_blk);
+    paged_decode_kernel<T, D, RBW, 0><<<p.grid, dim3(kWave), kLds, st>>>(a, seq_blk, a.seq_lens, a.cu_q, a.block_tables);
   else if (a.ps_shift >= 0)
-    paged_decode_kernel<T, D, RBW, 1><<<p.grid, dim3(kWave), kLds, st>>>(a, seq_blk);
+    paged_decode_kernel<T, D, RBW, 1><<<p.grid, dim3(kWave), kLds, st>>>(a, seq_blk, a.seq_lens, a.cu_q, a.block_tables);
   else
-    paged_decode_kernel<T, D, RBW, 2><<<p.grid, dim3(kWave), kLds, st>>>(a, seq_blk);
+    paged_decode_kernel<T, D, RBW, 2><<<p.grid, dim3(kWave), kLds, st>>>(a, seq_blk, a.seq_lens, a.cu_q, a.block_tables);
   dim3 grid(n_seqs * a.num_kv_heads, 16 * RBW);
   merge_segments_kernel<T, D, RBW><<<grid, dim3(kWave), 0, st>>>(a, seq_blk);
 }
