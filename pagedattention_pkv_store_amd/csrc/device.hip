@@ -490,7 +490,7 @@ __global__ __launch_bounds__(kThreads) void paged_attention_kernel(AttnArgs args
 // ---------------------------------------------------------------------------
 
 #ifndef PKV_DECODE_WAVES
-#define PKV_DECODE_WAVES 2048          // one-wave workgroups (8 per CU)
+#define PKV_DECODE_WAVES 1024          // one-wave workgroups (4 per CU)
 #endif
 #ifndef PKV_DECODE_MIN_BLOCKS
 #define PKV_DECODE_MIN_BLOCKS 4        // smallest range of a wave, in blocks
@@ -498,7 +498,11 @@ __global__ __launch_bounds__(kThreads) void paged_attention_kernel(AttnArgs args
 #ifndef PKV_DECODE_WAVES_PER_SIMD
 #define PKV_DECODE_WAVES_PER_SIMD 2
 #endif
+#ifndef PKV_DECODE_DEPTH
+#define PKV_DECODE_DEPTH 2             // blocks in flight per wave
+#endif
 constexpr int kDecodeWaves = PKV_DECODE_WAVES;
+constexpr int kDecodeDepth = PKV_DECODE_DEPTH;
 
 // Queries of sequence b seen by the decode path (at most 16 * RBW rows) and
 // the positions they see: [0, kv_end).
@@ -880,8 +884,8 @@ __global__ __launch_bounds__(kWave, RBW == 1 ? PKV_DECODE_WAVES_PER_SIMD : 1) vo
   // ---- the walk ----
   Cur cc = locate(i0);              // block being computed
   Cur lc = cc;                      // block whose loads are issued next
-  u32x4 ka[kLoads], va[kLoads], kb[kLoads], vb[kLoads];
-  uint32_t oka, okb;
+  u32x4 kbuf[kDecodeDepth][kLoads], vbuf[kDecodeDepth][kLoads];
+  uint32_t okm[kDecodeDepth];
   Unit ul = unit_of(lc.b);          // unit of the load cursor
   int page_l = kPageMode == 0 ? page_of(lc) : 0;
   auto issue = [&](int li, u32x4 (&kr)[kLoads], u32x4 (&vr)[kLoads], uint32_t& okm) __attribute__((always_inline)) {
@@ -893,8 +897,8 @@ __global__ __launch_bounds__(kWave, RBW == 1 ? PKV_DECODE_WAVES_PER_SIMD : 1) vo
       if constexpr (kPageMode == 0) page_l = page_of(lc);
     }
   };
-  issue(i0, ka, va, oka);
-  issue(i0 + 1, kb, vb, okb);
+#pragma unroll
+  for (int d = 0; d < kDecodeDepth; ++d) issue(i0 + d, kbuf[d], vbuf[d], okm[d]);
 
   Unit uc = unit_of(cc.b);
   // The unit's queries load at its start (a wave's range meets few units);
@@ -906,12 +910,12 @@ __global__ __launch_bounds__(kWave, RBW == 1 ? PKV_DECODE_WAVES_PER_SIMD : 1) vo
   int seg_first = cc.j;             // block at which the current segment started
   reset_state();
 
-  // One step: stage block ii from its registers, issue block ii + 2 into
+  // One step: stage block ii from its registers, issue block ii + depth into
   // them, compute block ii, and close the segment at a unit's or the range's
   // end.
-  auto step = [&](int ii, u32x4 (&kr)[kLoads], u32x4 (&vr)[kLoads], uint32_t& okm) __attribute__((always_inline)) {
-    stage_block(kr, vr, okm);
-    issue(ii + 2, kr, vr, okm);
+  auto step = [&](int ii, u32x4 (&kr)[kLoads], u32x4 (&vr)[kLoads], uint32_t& om) __attribute__((always_inline)) {
+    stage_block(kr, vr, om);
+    issue(ii + kDecodeDepth, kr, vr, om);
     compute_block(16 * cc.j, uc.kv_end, qv, qpos);
     const bool unit_end = cc.j == cc.nb - 1;
     if (unit_end || ii + 1 == i1) {
@@ -927,15 +931,17 @@ __global__ __launch_bounds__(kWave, RBW == 1 ? PKV_DECODE_WAVES_PER_SIMD : 1) vo
       advance(cc);
     }
   };
-  // Whole pairs of steps, then an odd last one: every path back to the top
-  // of the loop has issued both buffers' loads, so each staging waits for
-  // the older buffer only.
+  // Whole groups of `depth` steps, then the last few: every path back to the
+  // top of the loop has issued all buffers' loads, so each staging waits for
+  // the oldest buffer only.
   int i = i0;
-  for (; i + 1 < i1; i += 2) {
-    step(i, ka, va, oka);
-    step(i + 1, kb, vb, okb);
+  for (; i + kDecodeDepth <= i1; i += kDecodeDepth) {
+#pragma unroll
+    for (int d = 0; d < kDecodeDepth; ++d) step(i + d, kbuf[d], vbuf[d], okm[d]);
   }
-  if (i < i1) step(i, ka, va, oka);
+#pragma unroll
+  for (int d = 0; d < kDecodeDepth - 1; ++d)
+    if (i + d < i1) step(i + d, kbuf[d], vbuf[d], okm[d]);
 }
 
 // ---------------------------------------------------------------------------
