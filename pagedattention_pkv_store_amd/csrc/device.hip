@@ -981,9 +981,20 @@ __global__ __launch_bounds__(kWave, RBW == 1 ? PKV_DECODE_WAVES_PER_SIMD : 1) vo
 #ifndef PKV_PREFILL_ROW_BLOCKS
 #define PKV_PREFILL_ROW_BLOCKS 2
 #endif
+#ifndef PKV_PREFILL_WAVES
+#define PKV_PREFILL_WAVES 8
+#endif
+#ifndef PKV_PREFILL_SETPRIO
+#define PKV_PREFILL_SETPRIO 0
+#endif
 constexpr int kPfRb = PKV_PREFILL_ROW_BLOCKS;   // 16-row MFMA blocks per wave
-constexpr int kPfRows = 64 * kPfRb;             // query rows per workgroup (4 waves)
-constexpr int kPfKeys = 64;    // positions per staged tile
+constexpr int kPfWaves = PKV_PREFILL_WAVES;     // waves per workgroup
+constexpr int kPfThreads = kPfWaves * 64;
+constexpr int kPfRows = 16 * kPfRb * kPfWaves;  // query rows per workgroup
+#ifndef PKV_PREFILL_KEYS
+#define PKV_PREFILL_KEYS 128
+#endif
+constexpr int kPfKeys = PKV_PREFILL_KEYS;   // positions per staged tile (computed 64 at a time)
 
 template <int D>
 constexpr int pf_k_row_bytes() { return D * 2 + 16; }
@@ -1052,14 +1063,14 @@ __device__ __forceinline__ bf16x4 lds_read_tr(const char* p) {
 // (those rows then share one page: scalar lookup); 1: other powers of two;
 // 2: any page size.
 template <int D, int kPageMode>
-__global__ __launch_bounds__(kThreads, kPfRb >= 3 ? 1 : 2) void paged_prefill_kernel(AttnArgs a,
+__global__ __launch_bounds__(kPfThreads, kPfRb >= 3 ? 1 : 2) void paged_prefill_kernel(AttnArgs a,
                                                                    const int32_t* __restrict__ row_off,
                                                                    int n_blocks) {
   constexpr int kKRowB = pf_k_row_bytes<D>();            // LDS row strides, bytes
   constexpr int kVRowB = pf_v_row_bytes<D>();
   constexpr int kCpr = D * 2 / 16;                      // 16-byte chunks per K/V row
-  constexpr int kChunks = kPfKeys * kCpr / kThreads;    // per thread per pool
-  constexpr int kRowsPerPass = kThreads / kCpr;         // rows staged per chunk index
+  constexpr int kChunks = kPfKeys * kCpr / kPfThreads;  // per thread per pool
+  constexpr int kRowsPerPass = kPfThreads / kCpr;       // rows staged per chunk index
   constexpr int kQk = D / 32;                           // MFMAs per 16x16 score block
   constexpr int kDb = D / 16;                           // 16-dim blocks of O^T
   constexpr int kKTileB = kPfKeys * kKRowB;             // bytes of one staged K tile
@@ -1209,6 +1220,7 @@ __global__ __launch_bounds__(kThreads, kPfRb >= 3 ? 1 : 2) void paged_prefill_ke
   auto compute = [&](const char* kt, const char* vt, int tb, auto mask_tag) __attribute__((always_inline)) {
     constexpr bool kMask = decltype(mask_tag)::value;
     f32x4 s[4][kPfRb];
+    if constexpr (PKV_PREFILL_SETPRIO) __builtin_amdgcn_s_setprio(1);
 #pragma unroll
     for (int kb = 0; kb < 4; ++kb) {
       bf16x8 kf[kQk];
@@ -1223,6 +1235,7 @@ __global__ __launch_bounds__(kThreads, kPfRb >= 3 ? 1 : 2) void paged_prefill_ke
         s[kb][rb] = acc;
       }
     }
+    if constexpr (PKV_PREFILL_SETPRIO) __builtin_amdgcn_s_setprio(0);
     // row maxima, then one (rarely taken) rescale branch for both row blocks
     float muse[kPfRb];
     bool up_any = false;
@@ -1296,13 +1309,17 @@ __global__ __launch_bounds__(kThreads, kPfRb >= 3 ? 1 : 2) void paged_prefill_ke
   for (int t = 0; t < n_tiles; ++t) {
     load_kv(t + 1);            // clamped: the last tile reloads itself
     fetch_pages(t + 2);
-    const int tb = k_lo + t * kPfKeys;
-    if (w_active && tb <= w_qmax) {
-      const char* kt = smem + (t & 1) * kBufB;
-      if (tb + kPfKeys - 1 <= w_qmin)
-        compute(kt, kt + kKTileB, tb, std::integral_constant<bool, false>());
-      else
-        compute(kt, kt + kKTileB, tb, std::integral_constant<bool, true>());
+#pragma unroll
+    for (int sub = 0; sub < kPfKeys / 64; ++sub) {
+      const int tb = k_lo + t * kPfKeys + 64 * sub;
+      if (w_active && tb <= w_qmax) {
+        const char* kt = smem + (t & 1) * kBufB + sub * 64 * kKRowB;
+        const char* vt = smem + (t & 1) * kBufB + kKTileB + sub * 64 * kVRowB;
+        if (tb + 63 <= w_qmin)
+          compute(kt, vt, tb, std::integral_constant<bool, false>());
+        else
+          compute(kt, vt, tb, std::integral_constant<bool, true>());
+      }
     }
     stage((t + 1) & 1);
 #pragma unroll
@@ -1655,7 +1672,7 @@ int launch_prefill_t(const AttnArgs& a, const Plan& p, char* ws, hipStream_t st)
   prefill_schedule_kernel<<<1, kThreads, 0, st>>>(a, row_off, p.n_blocks);
   const int64_t grid = prefill_grid(p, a.n_seqs, a.num_kv_heads, a.group, a.total_q);
   if (grid > INT32_MAX) return fail(PKV_ERR_UNSUPPORTED, "prefill: grid too large");
-  if (grid > 0) paged_prefill_kernel<D, kPageMode><<<static_cast<int>(grid), dim3(kThreads), kLds, st>>>(a, row_off, p.n_blocks);
+  if (grid > 0) paged_prefill_kernel<D, kPageMode><<<static_cast<int>(grid), dim3(kPfThreads), kLds, st>>>(a, row_off, p.n_blocks);
   if (p.n_splits > 1) {
     dim3 mg(a.num_q_heads, p.max_q, a.n_seqs);
     merge_chunks_kernel<uint16_t, D><<<mg, dim3(kWave), 0, st>>>(a);
