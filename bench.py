@@ -43,6 +43,28 @@ MFMA_BF16_PEAK_TFLOPS = 2500.0   # dense bf16 MFMA, MI355X
 METRIC = "paged-decode KV GB/s (% of HBM peak); prefill-append tokens/s (% MFMA peak)"
 
 
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
+KERNEL_SOURCE = os.path.join(ROOT, "pagedattention_pkv_store_amd", "csrc", "device.hip")
+
+
+def measured_traffic(name: str):
+    """HBM bytes per launch of one library call from the committed counter
+    summary (FETCH_SIZE / WRITE_SIZE passes, calibrated against a plain copy),
+    or None when the kernel source changed since the counters were taken."""
+    import hashlib
+    try:
+        with open(TRAFFIC_FILE) as f:
+            rec = json.load(f)
+        with open(KERNEL_SOURCE, "rb") as f:
+            sha = hashlib.sha256(f.read()).hexdigest()
+    except (OSError, ValueError):
+        return None
+    if rec.get("kernel_source_sha256") != sha or name not in rec:
+        return None
+    t = rec[name]
+    return int(t["read_bytes"] + t["write_bytes"])
+
+
 def kv_bytes_per_position(num_kv_heads: int, head_dim: int, elem_bytes: int) -> int:
     """K and V of one position across all KV heads (one layer)."""
     return 2 * num_kv_heads * head_dim * elem_bytes
@@ -166,7 +188,7 @@ def prefill_leg(args, torch, pkv, synth, dev: str) -> dict:
             "peak": MFMA_BF16_PEAK_TFLOPS,
             "unit": "TFLOP/s",
             "frac": round(achieved / MFMA_BF16_PEAK_TFLOPS, 4),
-            "traffic": None,
+            "traffic": measured_traffic("prefill_append"),
             "kernel": "pkv_prefill_append (prefill_schedule_kernel + paged_prefill_kernel)",
             "kernel_avg_us": round(attn_s * 1e6, 1),
             "kernel_median_us": round(float(np.median(attn_ms)) * 1e3, 1),
@@ -368,8 +390,8 @@ def main():
             "peak": HBM_PEAK_GBS,
             "unit": "GB/s",
             "frac": round(achieved / HBM_PEAK_GBS, 4),
-            "traffic": None,
-            "kernel": "pkv_decode (decode_schedule_kernel + paged_decode_kernel + merge_chunks_kernel)",
+            "traffic": measured_traffic("decode"),
+            "kernel": "pkv_decode (paged_decode_kernel + merge_segments_kernel)",
             "kernel_avg_us": round(dec_avg_s * 1e6, 2),
             "kernel_median_us": round(float(np.median(dec_ms)) * 1e3, 2),
             "algorithmic_bytes_per_launch": int(alg_per_launch),
