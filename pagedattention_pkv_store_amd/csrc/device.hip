@@ -988,20 +988,26 @@ __global__ __launch_bounds__(kWave, RBW == 1 ? PKV_DECODE_WAVES_PER_SIMD : 1) vo
 #define PKV_PREFILL_SETPRIO 0
 #endif
 constexpr int kPfRb = PKV_PREFILL_ROW_BLOCKS;   // 16-row MFMA blocks per wave
-constexpr int kPfWaves = PKV_PREFILL_WAVES;     // waves per workgroup
-constexpr int kPfThreads = kPfWaves * 64;
-constexpr int kPfRows = 16 * kPfRb * kPfWaves;  // query rows per workgroup
+// Two workgroup shapes: long contexts take PKV_PREFILL_WAVES waves and
+// PKV_PREFILL_KEYS-position tiles (one workgroup per CU); contexts up to
+// kPfShortCtx take 4 waves and 64-position tiles, two workgroups per CU, so
+// one workgroup's first loads overlap another's compute.
+constexpr int kPfWaves = PKV_PREFILL_WAVES;
+constexpr int kPfShortWaves = 4;
+constexpr int kPfShortKeys = 64;
+constexpr int kPfShortCtx = 2048;
 #ifndef PKV_PREFILL_KEYS
 #define PKV_PREFILL_KEYS 128
 #endif
 constexpr int kPfKeys = PKV_PREFILL_KEYS;   // positions per staged tile (computed 64 at a time)
+constexpr int kPfMaxRows = 16 * kPfRb * kPfWaves;   // rows of the larger workgroup shape
 
 template <int D>
 constexpr int pf_k_row_bytes() { return D * 2 + 16; }
 template <int D>
 constexpr int pf_v_row_bytes() { return D * 2 + 32; }
-template <int D>
-constexpr int pf_lds_bytes() { return 2 * kPfKeys * (pf_k_row_bytes<D>() + pf_v_row_bytes<D>()); }
+template <int D, int kKeys>
+constexpr int pf_lds_bytes() { return 2 * kKeys * (pf_k_row_bytes<D>() + pf_v_row_bytes<D>()); }
 // Rows one wave stages per pass (a pass = one 16-byte chunk per thread).
 template <int D>
 constexpr int pf_wave_rows() { return kWave / (D * 2 / 16); }
@@ -1009,7 +1015,7 @@ constexpr int pf_wave_rows() { return kWave / (D * 2 / 16); }
 // row_off[k] = sum over blocks < k of (q-tiles of the block) * n_splits,
 // where a block's q-tiles are the most any of its 8 units needs.
 __global__ __launch_bounds__(kThreads) void prefill_schedule_kernel(AttnArgs a, int32_t* row_off,
-                                                                    int n_blocks) {
+                                                                    int n_blocks, int tile_rows) {
   __shared__ int s_scan[kThreads];
   __shared__ int s_carry;
   const int tid = threadIdx.x;
@@ -1029,7 +1035,7 @@ __global__ __launch_bounds__(kThreads) void prefill_schedule_kernel(AttnArgs a, 
         if (b == prev) continue;
         prev = b;
         const int n_b = min(a.cu_q[b + 1] - a.cu_q[b], a.max_q);
-        tiles = max(tiles, (n_b * a.group + kPfRows - 1) / kPfRows);
+        tiles = max(tiles, (n_b * a.group + tile_rows - 1) / tile_rows);
       }
     }
     const int v = tiles * a.n_splits;
@@ -1062,10 +1068,11 @@ __device__ __forceinline__ bf16x4 lds_read_tr(const char* p) {
 // kPageMode 0: page_size a power of two >= the rows a wave stages per pass
 // (those rows then share one page: scalar lookup); 1: other powers of two;
 // 2: any page size.
-template <int D, int kPageMode>
+template <int D, int kPageMode, int kPfThreads, int kPfKeys>
 __global__ __launch_bounds__(kPfThreads, kPfRb >= 3 ? 1 : 2) void paged_prefill_kernel(AttnArgs a,
                                                                    const int32_t* __restrict__ row_off,
                                                                    int n_blocks) {
+  constexpr int kPfRows = 16 * kPfRb * (kPfThreads / kWave);   // query rows per workgroup
   constexpr int kKRowB = pf_k_row_bytes<D>();            // LDS row strides, bytes
   constexpr int kVRowB = pf_v_row_bytes<D>();
   constexpr int kCpr = D * 2 / 16;                      // 16-byte chunks per K/V row
@@ -1527,6 +1534,7 @@ struct Plan {
   int max_q = 0;
   bool decode = false;  // decode path (few rows) vs a tile kernel
   bool prefill = false; // bf16 tiles: paged_prefill_kernel, else paged_attention_kernel
+  bool pf_short = false; // prefill: the 4-wave, 64-position shape
   int n_blocks = 0;     // prefill: blocks of 8 (sequence, KV head) units
   int rbw = 1;          // decode: 16-row blocks each wave holds
   int epi_rows = 16;    // decode: rows of a block that carry queries
@@ -1584,17 +1592,19 @@ int make_plan(const pkv_pool_desc* d, int n_seqs, int hq, int max_q, int max_seq
     // paged_prefill_kernel: 128-row tiles; KV splits only when the units'
     // tiles alone cannot fill the chip.
     p->prefill = true;
-    p->tile_rows = kPfRows;
+    p->pf_short = max_seq_len <= kPfShortCtx;
+    const int keys = p->pf_short ? kPfShortKeys : kPfKeys;
+    p->tile_rows = p->pf_short ? 16 * kPfRb * kPfShortWaves : kPfMaxRows;
     if (rows > (int64_t{1} << 28)) return fail(PKV_ERR_UNSUPPORTED, std::string(fn) + ": too many queries per sequence");
-    const int64_t q_tiles = (rows + kPfRows - 1) / kPfRows;
+    const int64_t q_tiles = (rows + p->tile_rows - 1) / p->tile_rows;
     p->q_tiles = static_cast<int>(q_tiles);
     const int64_t units = static_cast<int64_t>(n_seqs) * d->num_kv_heads;
     p->n_blocks = static_cast<int>((units + 7) / 8);
-    const int64_t max_tiles = (static_cast<int64_t>(max_seq_len) + kPfKeys - 1) / kPfKeys;
+    const int64_t max_tiles = (static_cast<int64_t>(max_seq_len) + keys - 1) / keys;
     int64_t want = (kTargetWorkgroups + units * q_tiles - 1) / (units * q_tiles);
     want = std::max<int64_t>(1, std::min<int64_t>(want, (max_seq_len + kMinSplitKeys - 1) / kMinSplitKeys));
     const int64_t tiles_per_split = std::max<int64_t>(1, (max_tiles + want - 1) / want);
-    p->split_len = static_cast<int>(tiles_per_split * kPfKeys);
+    p->split_len = static_cast<int>(tiles_per_split * keys);
     p->n_splits = static_cast<int>(std::max<int64_t>(1, (max_tiles + tiles_per_split - 1) / tiles_per_split));
     const int64_t sched_rows = static_cast<int64_t>(p->n_blocks) * q_tiles * p->n_splits;
     if (sched_rows > (int64_t{1} << 27)) return fail(PKV_ERR_UNSUPPORTED, std::string(fn) + ": too many work items");
@@ -1656,28 +1666,35 @@ void launch_decode_t(const AttnArgs& a, const Plan& p, int n_seqs, char* ws, hip
 // host scalars: a block's q-tiles are at most its units' sequences' q-tiles
 // summed, and a sequence's units fall in at most hkv / 8 + 2 blocks.
 int64_t prefill_grid(const Plan& p, int n_seqs, int hkv, int group, int total_q) {
-  const int64_t tiles_all = (static_cast<int64_t>(total_q) * group + kPfRows - 1) / kPfRows + n_seqs;
+  const int64_t tiles_all = (static_cast<int64_t>(total_q) * group + p.tile_rows - 1) / p.tile_rows + n_seqs;
   const int64_t per_seq_blocks = hkv % 8 == 0 ? hkv / 8 : hkv / 8 + 2;
   const int64_t rows = std::min<int64_t>(static_cast<int64_t>(p.n_blocks) * p.q_tiles, per_seq_blocks * tiles_all);
   return 8 * rows * p.n_splits;
 }
 
-template <int D, int kPageMode>
+template <int D, int kPageMode, int kWaves, int kKeys>
 int launch_prefill_t(const AttnArgs& a, const Plan& p, char* ws, hipStream_t st) {
-  constexpr int kLds = pf_lds_bytes<D>();
-  static const hipError_t attr = hipFuncSetAttribute(reinterpret_cast<const void*>(&paged_prefill_kernel<D, kPageMode>),
+  constexpr int kLds = pf_lds_bytes<D, kKeys>();
+  auto* kern = &paged_prefill_kernel<D, kPageMode, kWaves * kWave, kKeys>;
+  static const hipError_t attr = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
                                                      hipFuncAttributeMaxDynamicSharedMemorySize, kLds);
   if (attr != hipSuccess) return fail(PKV_ERR_DEVICE, std::string("prefill: LDS attribute: ") + hipGetErrorString(attr));
   int32_t* row_off = reinterpret_cast<int32_t*>(ws + p.items_off);
-  prefill_schedule_kernel<<<1, kThreads, 0, st>>>(a, row_off, p.n_blocks);
+  prefill_schedule_kernel<<<1, kThreads, 0, st>>>(a, row_off, p.n_blocks, p.tile_rows);
   const int64_t grid = prefill_grid(p, a.n_seqs, a.num_kv_heads, a.group, a.total_q);
   if (grid > INT32_MAX) return fail(PKV_ERR_UNSUPPORTED, "prefill: grid too large");
-  if (grid > 0) paged_prefill_kernel<D, kPageMode><<<static_cast<int>(grid), dim3(kPfThreads), kLds, st>>>(a, row_off, p.n_blocks);
+  if (grid > 0) kern<<<static_cast<int>(grid), dim3(kWaves * kWave), kLds, st>>>(a, row_off, p.n_blocks);
   if (p.n_splits > 1) {
     dim3 mg(a.num_q_heads, p.max_q, a.n_seqs);
     merge_chunks_kernel<uint16_t, D><<<mg, dim3(kWave), 0, st>>>(a);
   }
   return PKV_OK;
+}
+
+template <int D, int kPageMode>
+int launch_prefill_shape(const AttnArgs& a, const Plan& p, char* ws, hipStream_t st) {
+  return p.pf_short ? launch_prefill_t<D, kPageMode, kPfShortWaves, kPfShortKeys>(a, p, ws, st)
+                    : launch_prefill_t<D, kPageMode, kPfWaves, kPfKeys>(a, p, ws, st);
 }
 
 template <typename T, int D>
@@ -1761,12 +1778,12 @@ int run_attention(const char* fn, const pkv_pool_desc* desc, const void* k_pool,
     const bool pow2 = a.ps_shift >= 0;
     if (desc->head_dim == 128) {
       const int mode = !pow2 ? 2 : a.page_size >= pf_wave_rows<128>() ? 0 : 1;
-      rc = mode == 0 ? launch_prefill_t<128, 0>(a, p, ws, st)
-                     : mode == 1 ? launch_prefill_t<128, 1>(a, p, ws, st) : launch_prefill_t<128, 2>(a, p, ws, st);
+      rc = mode == 0 ? launch_prefill_shape<128, 0>(a, p, ws, st)
+                     : mode == 1 ? launch_prefill_shape<128, 1>(a, p, ws, st) : launch_prefill_shape<128, 2>(a, p, ws, st);
     } else {
       const int mode = !pow2 ? 2 : a.page_size >= pf_wave_rows<64>() ? 0 : 1;
-      rc = mode == 0 ? launch_prefill_t<64, 0>(a, p, ws, st)
-                     : mode == 1 ? launch_prefill_t<64, 1>(a, p, ws, st) : launch_prefill_t<64, 2>(a, p, ws, st);
+      rc = mode == 0 ? launch_prefill_shape<64, 0>(a, p, ws, st)
+                     : mode == 1 ? launch_prefill_shape<64, 1>(a, p, ws, st) : launch_prefill_shape<64, 2>(a, p, ws, st);
     }
     if (rc != PKV_OK) return rc;
   } else if (desc->dtype == PKV_BF16) {
