@@ -111,6 +111,26 @@ template <int kDl> struct QkFrag<float, kDl> {
   }
 };
 
+// Pairwise reductions across lanes l and l ^ 16 (l ^ 32) without LDS:
+// v_permlane16_swap (v_permlane32_swap) with both operands x leaves, in
+// every lane, its own value in one result and its partner's in the other.
+__device__ __forceinline__ float max_xor16(float x) {
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float max_xor32(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float sum_xor16(float x) {
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+__device__ __forceinline__ float sum_xor32(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
 __device__ __forceinline__ f32x4 mfma_qk(bf16x8 a, bf16x8 b, f32x4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
 }
@@ -791,8 +811,7 @@ __global__ __launch_bounds__(kWave, RBW == 1 ? PKV_DECODE_WAVES_PER_SIMD : 1) vo
         s[rb][i] = (pos < kv_end && pos <= qpos[rb]) ? x : -INFINITY;
         mx = fmaxf(mx, s[rb][i]);
       }
-      mx = fmaxf(mx, __shfl_xor(mx, 16));
-      mx = fmaxf(mx, __shfl_xor(mx, 32));
+      mx = max_xor32(max_xor16(mx));
       const float m_new = fmaxf(m_run[rb], mx);
       const float m_use = m_new == -INFINITY ? 0.f : m_new;
       const float alpha = fast_exp2(m_run[rb] - m_use);
@@ -849,9 +868,7 @@ __global__ __launch_bounds__(kWave, RBW == 1 ? PKV_DECODE_WAVES_PER_SIMD : 1) vo
     const int slot = b * hkv + g + static_cast<int>(blockIdx.x);
 #pragma unroll
     for (int rb = 0; rb < RBW; ++rb) {
-      float l_row = l_part[rb];
-      l_row += __shfl_xor(l_row, 16);
-      l_row += __shfl_xor(l_row, 32);
+      const float l_row = sum_xor32(sum_xor16(l_part[rb]));
       const int r = rb * 16 + lrow;
       if (r >= u.rows) continue;
       const int qi = r / group;
@@ -1256,12 +1273,11 @@ __global__ __launch_bounds__(kPfThreads, kPfRb >= 3 ? 1 : 2) void paged_prefill_
           for (int i = 0; i < 4; ++i)
             s[kb][rb][i] = (tb + kb * 16 + 4 * lgrp + i <= qpos[rb]) ? s[kb][rb][i] : -INFINITY;
       }
-      float mx = fmaxf(fmaxf(s[0][rb][0], s[0][rb][1]), fmaxf(s[0][rb][2], s[0][rb][3]));
+      // a linear chain folds into three-input maxima (v_max3_f32)
+      float mx = fmaxf(s[0][rb][0], s[0][rb][1]);
 #pragma unroll
-      for (int kb = 1; kb < 4; ++kb)
-        mx = fmaxf(mx, fmaxf(fmaxf(s[kb][rb][0], s[kb][rb][1]), fmaxf(s[kb][rb][2], s[kb][rb][3])));
-      mx = fmaxf(mx, __shfl_xor(mx, 16));
-      mx = fmaxf(mx, __shfl_xor(mx, 32));
+      for (int e = 2; e < 16; e += 2) mx = fmaxf(fmaxf(mx, s[e >> 2][rb][e & 3]), s[e >> 2][rb][(e & 3) + 1]);
+      mx = max_xor32(max_xor16(mx));
       const float mxc = mx * c2;
       const bool up = mxc > mc[rb] + 8.f;
       const float mnew = up ? mxc : mc[rb];
@@ -1372,7 +1388,7 @@ __global__ __launch_bounds__(kPfThreads, kPfRb >= 3 ? 1 : 2) void paged_prefill_
 template <typename T, int D>
 __device__ __forceinline__ void merge_rows(const AttnArgs& args, const float* o, const float* ml, int stride,
                                            int ns, int64_t orow) {
-  const int lane = threadIdx.x;
+  const int lane = threadIdx.x & (kWave - 1);
   constexpr int kPer = D / kWave;
   float mmax = -INFINITY;
   for (int s = lane; s < ns; s += kWave) mmax = fmaxf(mmax, ml[static_cast<int64_t>(s) * stride * 2]);
@@ -1443,14 +1459,14 @@ __global__ __launch_bounds__(kWave) void merge_chunks_kernel(AttnArgs args) {
                    orow);
 }
 
-// Log-sum-exp merge of the decode segments of one (unit, row): the slots
-// unit + w of the waves w whose block ranges cut the unit.  Grid: (units,
-// 16 * RBW), one wave each; units inside one wave's range were written final.
+// Log-sum-exp merge of the decode segments of one unit: the slots unit + w
+// of the waves w whose block ranges cut the unit.  Grid: one 4-wave
+// workgroup per unit, wave v folding rows v, v + 4, ...; units inside one
+// wave's range were written final and exit at once.
 template <typename T, int D, int RBW>
-__global__ __launch_bounds__(kWave) void merge_segments_kernel(AttnArgs a, const int32_t* __restrict__ seq_blk) {
+__global__ __launch_bounds__(kThreads) void merge_segments_kernel(AttnArgs a, const int32_t* __restrict__ seq_blk) {
   constexpr int kRowsCap = 16 * RBW;
   const int u = blockIdx.x;
-  const int r = blockIdx.y;
   const int hkv = a.num_kv_heads;
   const int b = u / hkv;
   const int g = u - b * hkv;
@@ -1463,13 +1479,14 @@ __global__ __launch_bounds__(kWave) void merge_segments_kernel(AttnArgs a, const
   if (f == l) return;
   int q0, n_b, rows;
   decode_kv_end<RBW>(a, b, &q0, &n_b, &rows);
-  if (r >= rows) return;
-  const int qi = r / a.group;
-  const int tok = q0 + qi;
-  if (tok >= a.total_q) return;
-  const int64_t orow = static_cast<int64_t>(tok) * a.num_q_heads + g * a.group + (r - qi * a.group);
-  const int64_t row0 = static_cast<int64_t>(u + f) * kRowsCap + r;
-  merge_rows<T, D>(a, a.ws_o + row0 * D, a.ws_ml + row0 * 2, kRowsCap, l - f + 1, orow);
+  for (int r = threadIdx.x / kWave; r < rows; r += kThreads / kWave) {
+    const int qi = r / a.group;
+    const int tok = q0 + qi;
+    if (tok >= a.total_q) continue;
+    const int64_t orow = static_cast<int64_t>(tok) * a.num_q_heads + g * a.group + (r - qi * a.group);
+    const int64_t row0 = static_cast<int64_t>(u + f) * kRowsCap + r;
+    merge_rows<T, D>(a, a.ws_o + row0 * D, a.ws_ml + row0 * 2, kRowsCap, l - f + 1, orow);
+  }
 }
 
 // KV scatter: one thread per 16-byte chunk of a (token, KV head) row, K and
@@ -1658,8 +1675,7 @@ void launch_decode_t(const AttnArgs& a, const Plan& p, int n_seqs, char* ws, hip
     paged_decode_kernel<T, D, RBW, 1><<<p.grid, dim3(kWave), kLds, st>>>(a, seq_blk, a.seq_lens, a.cu_q, a.block_tables);
   else
     paged_decode_kernel<T, D, RBW, 2><<<p.grid, dim3(kWave), kLds, st>>>(a, seq_blk, a.seq_lens, a.cu_q, a.block_tables);
-  dim3 grid(n_seqs * a.num_kv_heads, 16 * RBW);
-  merge_segments_kernel<T, D, RBW><<<grid, dim3(kWave), 0, st>>>(a, seq_blk);
+  merge_segments_kernel<T, D, RBW><<<n_seqs * a.num_kv_heads, dim3(kThreads), 0, st>>>(a, seq_blk);
 }
 
 // Upper bound on the prefill tile-rows the schedule kernel can list, from
