@@ -23,6 +23,8 @@ planner     the sorted-adjacent-document prefix-sharing plan (Quail docs "KV",
 attention   softmax attention over a sequence's logical K/V, gathered through
             the block table ("KV Cache Management and PagedAttention",
             "Compute attention over scattered KV", Figure 4).
+quant       INT8 KV pages: per-vector symmetric codes and fp32 scales, and
+            attention over them (TileInfer.jl "KV cache", "INT8 cache").
 accounting  closed forms for KV bytes per position and per layer (TileInfer.jl
             "Sizing" table and "INT8 cache"; ReKV section 2.1 eqs. (1)-(2) and
             section 2.2 eq. (7)).
@@ -40,8 +42,12 @@ Pinning status (what each function is checked against, in ``tests/``):
               invariant: the pages' example never walks a link.
   attention   closed forms, fp64 SDPA library special case, scalar brute force,
               permutation invariance.
+  quant       hand-worked codes from the page's rule (incl. the ties-to-even
+              reading), zero vector, peak code +-127, the symmetric error
+              bound, placement by slot, brute force of the page's folded-scale
+              formulation, page-placement invariance.
   accounting  every cell of the TileInfer.jl sizing table and the ReKV byte
               figures.
 """
 
-from . import accounting, attention, paging, planner  # noqa: F401
+from . import accounting, attention, paging, planner, quant  # noqa: F401
