@@ -177,20 +177,40 @@ int pkv_plan_prefix(const int32_t* tokens, const int64_t* offsets, int32_t n_doc
  * [num_pages][num_kv_heads][page_size][head_dim] -- the TileInfer.jl pool
  * shape (head_dim, page_size, kv_heads, num_pages) in column-major order --
  * so one KV head's page is a contiguous page_size * head_dim block.
- * Supported: dtype PKV_F32 or PKV_BF16; head_dim 64 or 128;
+ * Supported: dtype PKV_F32, PKV_BF16 or PKV_I8; head_dim 64 or 128;
  * 1 <= page_size <= 256; num_q_heads a multiple of num_kv_heads with
  * group = num_q_heads / num_kv_heads <= 16; query head h reads KV head
  * h / group.  All device arrays must be 16-byte aligned.
+ *
+ * PKV_I8 (TileInfer.jl docs, "KV cache", section "INT8 cache"): each cached
+ * vector (one KV head at one position) is held as head_dim int8 codes and one
+ * fp32 scale, value ~ scale * code.  A pool is num_pages * num_kv_heads
+ * blocks of pkv_i8_block_bytes(page_size, head_dim) bytes, block
+ * (page, g) at byte (page * num_kv_heads + g) * block_bytes: first the codes
+ * of offsets 0..page_size-1 (head_dim bytes each), then their page_size fp32
+ * scales, then zero to 15 bytes of padding up to a multiple of 16.  So a
+ * vector costs head_dim + 4 bytes (132 for head_dim 128; the padding is 0
+ * when page_size is a multiple of 4).  New K/V, queries and outputs are bf16.
  * ------------------------------------------------------------------------- */
-enum { PKV_F32 = 0, PKV_BF16 = 1 };
+enum { PKV_F32 = 0, PKV_BF16 = 1, PKV_I8 = 2 };
 
 typedef struct {
-  int32_t dtype;        /* PKV_F32 or PKV_BF16: pools, new K/V, q and out */
+  int32_t dtype;        /* PKV_F32 or PKV_BF16: pools, new K/V, q and out;
+                           PKV_I8: INT8 pools, bf16 new K/V, q and out */
   int32_t num_pages;
   int32_t page_size;
   int32_t num_kv_heads;
   int32_t head_dim;
 } pkv_pool_desc;
+
+/* Bytes of one (page, KV head) block of a PKV_I8 pool:
+ * page_size * head_dim + (4 * page_size rounded up to a multiple of 16);
+ * 0 when page_size or head_dim is below 1. */
+size_t pkv_i8_block_bytes(int32_t page_size, int32_t head_dim);
+
+/* Bytes of one pool (K or V) for this descriptor; 0 when the descriptor is
+ * not supported. */
+size_t pkv_pool_bytes(const pkv_pool_desc* desc);
 
 /* Write each new token's keys and values into the pools at its slot
  * (TileInfer.jl "Pages and block tables": store_kv! writes the new keys and
@@ -199,7 +219,11 @@ typedef struct {
  * offset.  Token t's vector for KV head g goes to pool element
  * ((page * num_kv_heads + g) * page_size + offset) * head_dim.  A slot
  * outside [0, num_pages * page_size) is skipped (padding tokens may use -1).
- * Two tokens with the same slot race: the result is one of them. */
+ * Two tokens with the same slot race: the result is one of them.
+ * PKV_I8: each bf16 vector is quantized once, here ("INT8 cache"), in fp32:
+ * scale = max|x| / 127, code = x / scale rounded to nearest, ties to even,
+ * clamped to [-127, 127]; a zero vector gets scale 0 and codes 0.  Inputs
+ * must be finite. */
 int pkv_store_kv(const pkv_pool_desc* desc, void* k_pool, void* v_pool, const void* k_new,
                  const void* v_new, const int64_t* slots, int32_t n_tokens, void* stream);
 
@@ -221,6 +245,9 @@ size_t pkv_workspace_bytes(const pkv_pool_desc* desc, int32_t n_seqs, int32_t nu
  *   max_seq_len:  host upper bound of seq_lens (sizes the grid and the split)
  *   scale:        softmax scale (1/sqrt(head_dim) in the usual model)
  *   out:          device [n_seqs][num_q_heads][head_dim], dtype of q
+ *                 (q and out are bf16 for PKV_I8 pools, whose key scales
+ *                 multiply the scores and value scales the probabilities,
+ *                 "INT8 cache")
  *   workspace:    device, >= pkv_workspace_bytes(desc, n_seqs, num_q_heads, 1,
  *                 max_seq_len) bytes (may be NULL when that is 0)
  * Long contexts are split across workgroups at fixed logical positions and

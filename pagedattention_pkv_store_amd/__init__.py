@@ -17,12 +17,12 @@ from typing import Optional, Sequence, Tuple
 import numpy as np
 
 from . import _lib
-from ._lib import PKV_BF16, PKV_F32  # noqa: F401
+from ._lib import PKV_BF16, PKV_F32, PKV_I8  # noqa: F401
 
 __all__ = [
     "PkvError", "OutOfPagesError", "SharedPageError", "UnsupportedError",
     "PoolDesc", "Allocator", "plan_prefix", "store_kv", "decode", "prefill_append",
-    "workspace_bytes", "validate_tables", "PKV_F32", "PKV_BF16",
+    "workspace_bytes", "validate_tables", "PKV_F32", "PKV_BF16", "PKV_I8",
     "BoundCall", "bind_store_kv", "bind_decode", "bind_prefill_append",
 ]
 
@@ -231,7 +231,7 @@ def plan_prefix_packed(tokens: np.ndarray, offsets: np.ndarray, page_size: int
 # ---------------------------------------------------------------------------
 @dataclass(frozen=True)
 class PoolDesc:
-    dtype: int          # PKV_F32 or PKV_BF16
+    dtype: int          # PKV_F32, PKV_BF16 or PKV_I8
     num_pages: int
     page_size: int
     num_kv_heads: int
@@ -242,12 +242,43 @@ class PoolDesc:
                               self.head_dim)
 
     @property
-    def pool_shape(self) -> Tuple[int, int, int, int]:
+    def pool_shape(self) -> Tuple[int, ...]:
+        """Shape of one pool tensor: [num_pages][Hkv][page_size][D] elements,
+        or for PKV_I8 [num_pages][Hkv][block bytes] (codes, then scales)."""
+        if self.dtype == PKV_I8:
+            return (self.num_pages, self.num_kv_heads,
+                    int(_lib.lib().pkv_i8_block_bytes(self.page_size, self.head_dim)))
         return (self.num_pages, self.num_kv_heads, self.page_size, self.head_dim)
 
+    def pool_bytes(self) -> int:
+        n = int(_lib.lib().pkv_pool_bytes(ctypes.byref(self.c())))
+        if n == 0:
+            _check(_lib.PKV_ERR_UNSUPPORTED)
+        return n
+
     def torch_dtype(self):
+        """dtype of new K/V, queries and outputs (bf16 for INT8 pools)."""
         import torch
-        return torch.bfloat16 if self.dtype == PKV_BF16 else torch.float32
+        return torch.float32 if self.dtype == PKV_F32 else torch.bfloat16
+
+    def pool_torch_dtype(self):
+        import torch
+        return torch.int8 if self.dtype == PKV_I8 else self.torch_dtype()
+
+    def new_pools(self, device, fill=None):
+        """A (K, V) pair of pool tensors on ``device``.  ``fill``: a value for
+        every element (fp32 / bf16 pools) or byte (PKV_I8 pools), or None."""
+        import torch
+        pools = []
+        for _ in range(2):
+            t = torch.empty(self.pool_shape, dtype=self.pool_torch_dtype(), device=device)
+            if fill is not None:
+                if self.dtype == PKV_I8:
+                    t.view(torch.uint8).fill_(int(fill))
+                else:
+                    t.fill_(fill)
+            pools.append(t)
+        return pools[0], pools[1]
 
 
 def _dev(t, name, dtype=None):
@@ -292,9 +323,10 @@ def bind_store_kv(desc: PoolDesc, k_pool, v_pool, k_new, v_new, slots, stream=No
     """pkv_store_kv with its arguments bound (see store_kv)."""
     import torch
     dt = desc.torch_dtype()
+    pdt = desc.pool_torch_dtype()
     n = int(slots.numel())
     c_desc = desc.c()
-    args = (ctypes.byref(c_desc), _dev(k_pool, "k_pool", dt), _dev(v_pool, "v_pool", dt),
+    args = (ctypes.byref(c_desc), _dev(k_pool, "k_pool", pdt), _dev(v_pool, "v_pool", pdt),
             _dev(k_new, "k_new", dt), _dev(v_new, "v_new", dt), _dev(slots, "slots", torch.int64),
             n, _stream(stream))
     return BoundCall(_lib.lib().pkv_store_kv, args, (c_desc, k_pool, v_pool, k_new, v_new, slots))
@@ -326,10 +358,11 @@ def bind_decode(desc: PoolDesc, k_pool, v_pool, q, block_tables, seq_lens, max_s
     import torch
     dt = desc.torch_dtype()
     n_seqs, hq, _ = q.shape
+    pdt = desc.pool_torch_dtype()
     need = workspace_bytes(desc, n_seqs, hq, 1, max_seq_len)
     ws_ptr, ws_bytes = _workspace(workspace, need)
     c_desc = desc.c()
-    args = (ctypes.byref(c_desc), _dev(k_pool, "k_pool", dt), _dev(v_pool, "v_pool", dt),
+    args = (ctypes.byref(c_desc), _dev(k_pool, "k_pool", pdt), _dev(v_pool, "v_pool", pdt),
             _dev(q, "q", dt), n_seqs, hq, _dev(block_tables, "block_tables", torch.int32),
             int(block_tables.shape[1]), _dev(seq_lens, "seq_lens", torch.int32), max_seq_len,
             float(scale), _dev(out, "out", dt), ws_ptr, ws_bytes, _stream(stream))
@@ -352,10 +385,11 @@ def bind_prefill_append(desc: PoolDesc, k_pool, v_pool, q, cu_q, block_tables, s
     dt = desc.torch_dtype()
     total_q, hq, _ = q.shape
     n_seqs = int(cu_q.numel()) - 1
+    pdt = desc.pool_torch_dtype()
     need = workspace_bytes(desc, n_seqs, hq, max_q_per_seq, max_seq_len)
     ws_ptr, ws_bytes = _workspace(workspace, need)
     c_desc = desc.c()
-    args = (ctypes.byref(c_desc), _dev(k_pool, "k_pool", dt), _dev(v_pool, "v_pool", dt),
+    args = (ctypes.byref(c_desc), _dev(k_pool, "k_pool", pdt), _dev(v_pool, "v_pool", pdt),
             _dev(q, "q", dt), total_q, _dev(cu_q, "cu_q", torch.int32), n_seqs, hq,
             _dev(block_tables, "block_tables", torch.int32), int(block_tables.shape[1]),
             _dev(seq_lens, "seq_lens", torch.int32), max_q_per_seq, max_seq_len, float(scale),

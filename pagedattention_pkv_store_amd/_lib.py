@@ -22,6 +22,7 @@ PKV_ERR_SHARED_PAGE = -6
 
 PKV_F32 = 0
 PKV_BF16 = 1
+PKV_I8 = 2
 
 i32p = POINTER(c_int32)
 i64p = POINTER(ctypes.c_int64)
@@ -51,6 +52,8 @@ _SIGNATURES = {
     "pkv_plan_prefix": (c_int, [i32p, i64p, c_int32, c_int32, i32p, i32p, i32p]),
     "pkv_store_kv": (c_int, [POINTER(PoolDescC), c_void_p, c_void_p, c_void_p, c_void_p,
                              c_void_p, c_int32, c_void_p]),
+    "pkv_i8_block_bytes": (c_size_t, [c_int32, c_int32]),
+    "pkv_pool_bytes": (c_size_t, [POINTER(PoolDescC)]),
     "pkv_workspace_bytes": (c_size_t, [POINTER(PoolDescC), c_int32, c_int32, c_int32, c_int32]),
     "pkv_decode": (c_int, [POINTER(PoolDescC), c_void_p, c_void_p, c_void_p, c_int32, c_int32,
                            c_void_p, c_int32, c_void_p, c_int32, c_float, c_void_p, c_void_p,

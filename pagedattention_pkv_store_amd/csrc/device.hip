@@ -163,8 +163,30 @@ struct AttnArgs {
   int32_t n_splits;
   int32_t max_q;        // queries computed per sequence (later ones are not)
   int32_t waves;        // decode: one-wave workgroups of the launch
+  int32_t head_bytes;   // bytes of one (page, KV head) block of a pool
   float scale_log2;     // softmax scale * log2(e)
 };
+
+// INT8 pages: a (page, KV head) block holds page_size rows of head_dim codes,
+// then page_size fp32 scales, padded to a multiple of 16 bytes.
+__host__ __device__ constexpr int64_t i8_block_bytes(int64_t ps, int64_t d) { return ps * d + ((4 * ps + 15) & ~int64_t{15}); }
+
+// Sixteen int8 codes -> sixteen bf16 (exact: |code| <= 127 fits bf16's
+// 8-bit significand), as two 16-byte groups in code order.
+__device__ __forceinline__ void i8x16_to_bf16(u32x4 x, u32x4& lo, u32x4& hi) {
+  u32x4 o[2];
+#pragma unroll
+  for (int w = 0; w < 4; ++w) {
+    const uint32_t v = x[w];
+    const f32x4 f = {static_cast<float>(static_cast<int8_t>(v)), static_cast<float>(static_cast<int8_t>(v >> 8)),
+                     static_cast<float>(static_cast<int8_t>(v >> 16)), static_cast<float>(static_cast<int8_t>(v >> 24))};
+    const auto p = __builtin_bit_cast(uint2, pack_bf16x4(f));
+    o[w >> 1][2 * (w & 1)] = p.x;
+    o[w >> 1][2 * (w & 1) + 1] = p.y;
+  }
+  lo = o[0];
+  hi = o[1];
+}
 
 // Elements per LDS row of a staged K/V tile: a 16-byte pad staggers rows
 // across banks; 512-byte rows go unpadded so two tiles fit in 64 KiB.
@@ -553,16 +575,24 @@ __device__ __forceinline__ int decode_per(int total, int waves, int min_blocks) 
 typedef __bf16 dec_bf16x4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) dec_bf16x4 lds_dec_bf16x4;
 
+#ifndef PKV_DECODE_DEPTH_I8
+#define PKV_DECODE_DEPTH_I8 3          // INT8 blocks are half the bytes: more of them in flight
+#endif
+
 // kPageMode 0: page_size a power of two >= 16 (a 16-position block lies in
-// one page); 1: a power of two < 16; 2: any other page size.
-template <typename T, int D, int RBW, int kPageMode>
+// one page); 1: a power of two < 16; 2: any other page size.  kI8: INT8
+// pages (T is then the bf16 type of the queries and outputs).
+template <typename T, int D, int RBW, int kPageMode, bool kI8>
 __global__ __launch_bounds__(kWave, RBW == 1 ? PKV_DECODE_WAVES_PER_SIMD : 1) void paged_decode_kernel(
     AttnArgs args, int32_t* __restrict__ seq_blk, const int32_t* __restrict__ seq_lens,
     const int32_t* __restrict__ cu_q, const int32_t* __restrict__ block_tables) {
+  static_assert(!kI8 || sizeof(T) == 2, "INT8 pages take bf16 queries");
   constexpr int kEs = sizeof(T);
-  constexpr int kRowBytes = D * kEs;
-  constexpr int kCpr = kRowBytes / 16;                  // 16-byte chunks per row
-  constexpr int kLoads = 16 * kRowBytes / (16 * kWave); // 16-byte loads per lane per pool per block
+  constexpr int kRowBytes = D * kEs;                    // bytes of a staged (LDS) row
+  constexpr int kGRowBytes = kI8 ? D : kRowBytes;       // bytes of a pool row
+  constexpr int kCpr = kGRowBytes / 16;                 // 16-byte chunks per pool row
+  constexpr int kLoads = 16 * kGRowBytes / (16 * kWave); // 16-byte loads per lane per pool per block
+  constexpr int kDepth = kI8 ? PKV_DECODE_DEPTH_I8 : kDecodeDepth;
   constexpr int kDl = D / 4;                            // dims per lane in the QK operands
   constexpr int kFragChunks = kDl * kEs / 16;           // 16-byte chunks of one lane's K fragment
   constexpr int kQkMfmas = kDl / Elem<T>::kQkPerMfma;
@@ -574,7 +604,7 @@ __global__ __launch_bounds__(kWave, RBW == 1 ? PKV_DECODE_WAVES_PER_SIMD : 1) vo
   // unpadded.
   constexpr int kKRow = kRowBytes + (kRowBytes >= 512 ? 0 : 16);
   constexpr int kVRow = kRowBytes + (kRowBytes >= 512 ? 0 : 32);
-  static_assert(kLoads * kWave * 16 == 16 * kRowBytes, "block split");
+  static_assert(kLoads * kWave * 16 == 16 * kGRowBytes, "block split");
 
   extern __shared__ __align__(16) char smem[];
   char* kst = smem;
@@ -714,25 +744,48 @@ __global__ __launch_bounds__(kWave, RBW == 1 ? PKV_DECODE_WAVES_PER_SIMD : 1) vo
   // Issue the loads of the block at cursor c (kv_end: its unit's).  Load ci
   // of a lane covers 16-byte chunk q % kCpr of row q / kCpr (q = ci * 64 +
   // lane): consecutive lanes read consecutive bytes of whole rows.  okm marks
-  // the rows inside the unit.
+  // the rows inside the unit.  INT8 pages: the lane also loads the key and
+  // value scales of positions 4 lgrp .. 4 lgrp + 3 of the block, the rows
+  // its score and probability registers hold; they are issued first, so the
+  // wait for the block's rows covers them.
+  const uint32_t head_bytes = static_cast<uint32_t>(args.head_bytes);
+  const uint32_t scale_off = static_cast<uint32_t>(ps) * D;   // INT8: scales follow the codes
   auto load_block = [&](const Cur& c, int kv_end, int page_hint, u32x4 (&kr)[kLoads], u32x4 (&vr)[kLoads],
-                        uint32_t& okm) __attribute__((always_inline)) {
+                        uint32_t& okm, f32x4& ks, f32x4& vs) __attribute__((always_inline)) {
     const int pos0 = 16 * c.j;
     const int32_t* bt_row = block_tables + static_cast<int64_t>(c.b) * args.bt_stride;
     okm = 0;
     if constexpr (kPageMode == 0) {
       const uint32_t page = static_cast<uint32_t>(min(max(page_hint, 0), args.num_pages - 1));
-      const uint64_t base = (static_cast<uint64_t>(page * hkv + c.g) * ps + (pos0 & (ps - 1))) * kRowBytes;
+      const uint64_t head = static_cast<uint64_t>(page * hkv + c.g) * head_bytes;
+      const uint32_t row0 = pos0 & (ps - 1);
+      if constexpr (kI8) {
+        const uint32_t so = scale_off + 4 * (row0 + 4 * lgrp);
+        ks = *reinterpret_cast<const f32x4*>(kbytes + head + so);
+        vs = *reinterpret_cast<const f32x4*>(vbytes + head + so);
+      }
+      const uint64_t base = head + row0 * kGRowBytes;
 #pragma unroll
       for (int ci = 0; ci < kLoads; ++ci) {
         const int q = ci * kWave + lane;
         const int r = q / kCpr;
         okm |= (pos0 + r < kv_end) ? (1u << ci) : 0u;
-        const uint32_t off = r * kRowBytes + (q % kCpr) * 16;
+        const uint32_t off = r * kGRowBytes + (q % kCpr) * 16;
         kr[ci] = *reinterpret_cast<const u32x4*>(kbytes + base + off);
         vr[ci] = *reinterpret_cast<const u32x4*>(vbytes + base + off);
       }
     } else {
+      if constexpr (kI8) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int pos = min(pos0 + 4 * lgrp + i, kv_end - 1);
+          const int blk = kPageMode == 1 ? (pos >> ps_shift) : pos / ps;
+          const int page = min(max(bt_row[blk], 0), args.num_pages - 1);
+          const uint64_t e = static_cast<uint64_t>(page * hkv + c.g) * head_bytes + scale_off + 4 * (pos - blk * ps);
+          ks[i] = *reinterpret_cast<const float*>(kbytes + e);
+          vs[i] = *reinterpret_cast<const float*>(vbytes + e);
+        }
+      }
 #pragma unroll
       for (int ci = 0; ci < kLoads; ++ci) {
         const int q = ci * kWave + lane;
@@ -742,7 +795,7 @@ __global__ __launch_bounds__(kWave, RBW == 1 ? PKV_DECODE_WAVES_PER_SIMD : 1) vo
         const int blk = kPageMode == 1 ? (pos >> ps_shift) : pos / ps;
         const int page = min(max(bt_row[blk], 0), args.num_pages - 1);
         okm |= (pos_raw < kv_end) ? (1u << ci) : 0u;
-        const uint64_t e = (static_cast<uint64_t>(page * hkv + c.g) * ps + (pos - blk * ps)) * kRowBytes +
+        const uint64_t e = static_cast<uint64_t>(page * hkv + c.g) * head_bytes + (pos - blk * ps) * kGRowBytes +
                            (q % kCpr) * 16;
         kr[ci] = *reinterpret_cast<const u32x4*>(kbytes + e);
         vr[ci] = *reinterpret_cast<const u32x4*>(vbytes + e);
@@ -758,16 +811,28 @@ __global__ __launch_bounds__(kWave, RBW == 1 ? PKV_DECODE_WAVES_PER_SIMD : 1) vo
 
   // Write a block's rows into the wave's LDS slices.  V rows past the unit
   // are zeroed (their probability is 0, but stale slots may hold anything,
-  // NaN included); K rows need no zeroing, their scores are masked.
+  // NaN included); K rows need no zeroing, their scores are masked.  INT8
+  // codes are widened to bf16 here (every code is finite; a row past the
+  // unit gets value scale 0 instead).
   auto stage_block = [&](const u32x4 (&kr)[kLoads], const u32x4 (&vr)[kLoads], uint32_t okm) __attribute__((always_inline)) {
 #pragma unroll
     for (int ci = 0; ci < kLoads; ++ci) {
       const int q = ci * kWave + lane;
       const int r = q / kCpr;
       const int cc = q % kCpr;
-      const unsigned keep = 0u - ((okm >> ci) & 1u);   // all ones or zero
-      *reinterpret_cast<u32x4*>(kst + r * kKRow + cc * 16) = kr[ci];
-      *reinterpret_cast<u32x4*>(vst + r * kVRow + cc * 16) = vr[ci] & keep;
+      if constexpr (kI8) {
+        u32x4 lo, hi;
+        i8x16_to_bf16(kr[ci], lo, hi);
+        *reinterpret_cast<u32x4*>(kst + r * kKRow + cc * 32) = lo;
+        *reinterpret_cast<u32x4*>(kst + r * kKRow + cc * 32 + 16) = hi;
+        i8x16_to_bf16(vr[ci], lo, hi);
+        *reinterpret_cast<u32x4*>(vst + r * kVRow + cc * 32) = lo;
+        *reinterpret_cast<u32x4*>(vst + r * kVRow + cc * 32 + 16) = hi;
+      } else {
+        const unsigned keep = 0u - ((okm >> ci) & 1u);   // all ones or zero
+        *reinterpret_cast<u32x4*>(kst + r * kKRow + cc * 16) = kr[ci];
+        *reinterpret_cast<u32x4*>(vst + r * kVRow + cc * 16) = vr[ci] & keep;
+      }
     }
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
     __builtin_amdgcn_wave_barrier();
@@ -787,8 +852,11 @@ __global__ __launch_bounds__(kWave, RBW == 1 ? PKV_DECODE_WAVES_PER_SIMD : 1) vo
     }
   };
 
-  auto compute_block = [&](int pos0, int kv_end, const QkFrag<T, kDl> (&qv)[RBW], const int (&qpos)[RBW])
-      __attribute__((always_inline)) {
+  // ks, vs (INT8 pages): key and value scales of this lane's positions
+  // pos0 + 4 lgrp + i.  The key scale multiplies the scores, the value scale
+  // the probabilities entering O^T (not the row sums).
+  auto compute_block = [&](int pos0, int kv_end, const QkFrag<T, kDl> (&qv)[RBW], const int (&qpos)[RBW],
+                           f32x4 ks, f32x4 vs) __attribute__((always_inline)) {
     // K fragment: position lrow, dims lgrp * kDl .. + kDl
     QkFrag<T, kDl> kf;
 #pragma unroll
@@ -801,13 +869,16 @@ __global__ __launch_bounds__(kWave, RBW == 1 ? PKV_DECODE_WAVES_PER_SIMD : 1) vo
 #pragma unroll
       for (int kk = 0; kk < kQkMfmas; ++kk) s[rb] = mfma_qk(kf.v[kk], qv[rb].v[kk], s[rb]);
     }
+    f32x4 sc;                          // score scale of each of the lane's positions
+#pragma unroll
+    for (int i = 0; i < 4; ++i) sc[i] = kI8 ? ks[i] * args.scale_log2 : args.scale_log2;
 #pragma unroll
     for (int rb = 0; rb < RBW; ++rb) {
       float mx = -INFINITY;
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int pos = pos0 + lgrp * 4 + i;
-        const float x = s[rb][i] * args.scale_log2;
+        const float x = s[rb][i] * sc[i];
         s[rb][i] = (pos < kv_end && pos <= qpos[rb]) ? x : -INFINITY;
         mx = fmaxf(mx, s[rb][i]);
       }
@@ -831,8 +902,16 @@ __global__ __launch_bounds__(kWave, RBW == 1 ? PKV_DECODE_WAVES_PER_SIMD : 1) vo
     // O^T += V^T P^T
     if constexpr (sizeof(T) == 2) {
       i16x4 pb[RBW];
+      if constexpr (kI8) {
+        f32x4 vsm;                     // rows past the unit: scale 0 (stale scales may be NaN)
 #pragma unroll
-      for (int rb = 0; rb < RBW; ++rb) pb[rb] = pack_bf16x4(s[rb]);
+        for (int i = 0; i < 4; ++i) vsm[i] = pos0 + lgrp * 4 + i < kv_end ? vs[i] : 0.f;
+#pragma unroll
+        for (int rb = 0; rb < RBW; ++rb) pb[rb] = pack_bf16x4(s[rb] * vsm);
+      } else {
+#pragma unroll
+        for (int rb = 0; rb < RBW; ++rb) pb[rb] = pack_bf16x4(s[rb]);
+      }
       // lane k of a 16-lane group addresses row 4 lgrp + k / 4, dims 4 (k % 4)..;
       // it receives dim lrow of rows 4 lgrp .. 4 lgrp + 3
       const char* vl = vst + (4 * lgrp + (lrow >> 2)) * kVRow + (lrow & 3) * 8;
@@ -901,12 +980,14 @@ __global__ __launch_bounds__(kWave, RBW == 1 ? PKV_DECODE_WAVES_PER_SIMD : 1) vo
   // ---- the walk ----
   Cur cc = locate(i0);              // block being computed
   Cur lc = cc;                      // block whose loads are issued next
-  u32x4 kbuf[kDecodeDepth][kLoads], vbuf[kDecodeDepth][kLoads];
-  uint32_t okm[kDecodeDepth];
+  u32x4 kbuf[kDepth][kLoads], vbuf[kDepth][kLoads];
+  f32x4 ksb[kDepth] = {}, vsb[kDepth] = {};   // INT8 scales
+  uint32_t okm[kDepth];
   Unit ul = unit_of(lc.b);          // unit of the load cursor
   int page_l = kPageMode == 0 ? page_of(lc) : 0;
-  auto issue = [&](int li, u32x4 (&kr)[kLoads], u32x4 (&vr)[kLoads], uint32_t& okm) __attribute__((always_inline)) {
-    load_block(lc, ul.kv_end, page_l, kr, vr, okm);
+  auto issue = [&](int li, u32x4 (&kr)[kLoads], u32x4 (&vr)[kLoads], uint32_t& okm, f32x4& ks, f32x4& vs)
+      __attribute__((always_inline)) {
+    load_block(lc, ul.kv_end, page_l, kr, vr, okm, ks, vs);
     if (li + 1 < i1) {              // move the load cursor on (it stays on the last block)
       const int b_old = lc.b;
       advance(lc);
@@ -915,7 +996,7 @@ __global__ __launch_bounds__(kWave, RBW == 1 ? PKV_DECODE_WAVES_PER_SIMD : 1) vo
     }
   };
 #pragma unroll
-  for (int d = 0; d < kDecodeDepth; ++d) issue(i0 + d, kbuf[d], vbuf[d], okm[d]);
+  for (int d = 0; d < kDepth; ++d) issue(i0 + d, kbuf[d], vbuf[d], okm[d], ksb[d], vsb[d]);
 
   Unit uc = unit_of(cc.b);
   // The unit's queries load at its start (a wave's range meets few units);
@@ -930,10 +1011,12 @@ __global__ __launch_bounds__(kWave, RBW == 1 ? PKV_DECODE_WAVES_PER_SIMD : 1) vo
   // One step: stage block ii from its registers, issue block ii + depth into
   // them, compute block ii, and close the segment at a unit's or the range's
   // end.
-  auto step = [&](int ii, u32x4 (&kr)[kLoads], u32x4 (&vr)[kLoads], uint32_t& om) __attribute__((always_inline)) {
+  auto step = [&](int ii, u32x4 (&kr)[kLoads], u32x4 (&vr)[kLoads], uint32_t& om, f32x4& ks, f32x4& vs)
+      __attribute__((always_inline)) {
     stage_block(kr, vr, om);
-    issue(ii + kDecodeDepth, kr, vr, om);
-    compute_block(16 * cc.j, uc.kv_end, qv, qpos);
+    const f32x4 ks_c = ks, vs_c = vs;   // the buffer is refilled below
+    issue(ii + kDepth, kr, vr, om, ks, vs);
+    compute_block(16 * cc.j, uc.kv_end, qv, qpos, ks_c, vs_c);
     const bool unit_end = cc.j == cc.nb - 1;
     if (unit_end || ii + 1 == i1) {
       write_segment(cc.b, cc.g, uc, seg_first == 0 && unit_end);
@@ -952,13 +1035,13 @@ __global__ __launch_bounds__(kWave, RBW == 1 ? PKV_DECODE_WAVES_PER_SIMD : 1) vo
   // top of the loop has issued all buffers' loads, so each staging waits for
   // the oldest buffer only.
   int i = i0;
-  for (; i + kDecodeDepth <= i1; i += kDecodeDepth) {
+  for (; i + kDepth <= i1; i += kDepth) {
 #pragma unroll
-    for (int d = 0; d < kDecodeDepth; ++d) step(i + d, kbuf[d], vbuf[d], okm[d]);
+    for (int d = 0; d < kDepth; ++d) step(i + d, kbuf[d], vbuf[d], okm[d], ksb[d], vsb[d]);
   }
 #pragma unroll
-  for (int d = 0; d < kDecodeDepth - 1; ++d)
-    if (i + d < i1) step(i + d, kbuf[d], vbuf[d], okm[d]);
+  for (int d = 0; d < kDepth - 1; ++d)
+    if (i + d < i1) step(i + d, kbuf[d], vbuf[d], okm[d], ksb[d], vsb[d]);
 }
 
 // ---------------------------------------------------------------------------
@@ -1023,11 +1106,15 @@ template <int D>
 constexpr int pf_k_row_bytes() { return D * 2 + 16; }
 template <int D>
 constexpr int pf_v_row_bytes() { return D * 2 + 32; }
-template <int D, int kKeys>
-constexpr int pf_lds_bytes() { return 2 * kKeys * (pf_k_row_bytes<D>() + pf_v_row_bytes<D>()); }
+// LDS of one staged K + V buffer (INT8 pages add the tile's key and value
+// scales), two buffers per workgroup.
+template <int D, int kKeys, bool kI8>
+constexpr int pf_buf_bytes() { return kKeys * (pf_k_row_bytes<D>() + pf_v_row_bytes<D>() + (kI8 ? 8 : 0)); }
+template <int D, int kKeys, bool kI8>
+constexpr int pf_lds_bytes() { return 2 * pf_buf_bytes<D, kKeys, kI8>(); }
 // Rows one wave stages per pass (a pass = one 16-byte chunk per thread).
-template <int D>
-constexpr int pf_wave_rows() { return kWave / (D * 2 / 16); }
+template <int D, bool kI8>
+constexpr int pf_wave_rows() { return kWave / (D * (kI8 ? 1 : 2) / 16); }
 
 // row_off[k] = sum over blocks < k of (q-tiles of the block) * n_splits,
 // where a block's q-tiles are the most any of its 8 units needs.
@@ -1084,21 +1171,24 @@ __device__ __forceinline__ bf16x4 lds_read_tr(const char* p) {
 
 // kPageMode 0: page_size a power of two >= the rows a wave stages per pass
 // (those rows then share one page: scalar lookup); 1: other powers of two;
-// 2: any page size.
-template <int D, int kPageMode, int kPfThreads, int kPfKeys>
+// 2: any page size.  kI8: INT8 pages, widened to bf16 as they are staged;
+// each tile's key and value scales are staged beside it.
+template <int D, int kPageMode, int kPfThreads, int kPfKeys, bool kI8>
 __global__ __launch_bounds__(kPfThreads, kPfRb >= 3 ? 1 : 2) void paged_prefill_kernel(AttnArgs a,
                                                                    const int32_t* __restrict__ row_off,
                                                                    int n_blocks) {
   constexpr int kPfRows = 16 * kPfRb * (kPfThreads / kWave);   // query rows per workgroup
   constexpr int kKRowB = pf_k_row_bytes<D>();            // LDS row strides, bytes
   constexpr int kVRowB = pf_v_row_bytes<D>();
-  constexpr int kCpr = D * 2 / 16;                      // 16-byte chunks per K/V row
+  constexpr int kGRowB = D * (kI8 ? 1 : 2);             // bytes of a pool row
+  constexpr int kCpr = kGRowB / 16;                     // 16-byte chunks per pool row
   constexpr int kChunks = kPfKeys * kCpr / kPfThreads;  // per thread per pool
   constexpr int kRowsPerPass = kPfThreads / kCpr;       // rows staged per chunk index
   constexpr int kQk = D / 32;                           // MFMAs per 16x16 score block
   constexpr int kDb = D / 16;                           // 16-dim blocks of O^T
   constexpr int kKTileB = kPfKeys * kKRowB;             // bytes of one staged K tile
-  constexpr int kBufB = kPfKeys * (kKRowB + kVRowB);    // one K + V buffer
+  constexpr int kVTileB = kPfKeys * kVRowB;
+  constexpr int kBufB = pf_buf_bytes<D, kPfKeys, kI8>();  // one K + V buffer (+ scales)
   static_assert(kChunks * kRowsPerPass == kPfKeys, "tile split");
   extern __shared__ __align__(16) char smem[];
 
@@ -1144,7 +1234,8 @@ __global__ __launch_bounds__(kPfThreads, kPfRb >= 3 ? 1 : 2) void paged_prefill_
   const int ps = a.page_size;
   const int ps_shift = a.ps_shift;
   const int32_t* bt_row = a.block_tables + static_cast<int64_t>(b) * a.bt_stride;
-  const uint32_t head_bytes = static_cast<uint32_t>(ps) * D * 2;   // one (page, head) block
+  const uint32_t head_bytes = static_cast<uint32_t>(a.head_bytes);   // one (page, head) block
+  const uint32_t scale_off = static_cast<uint32_t>(ps) * D;           // INT8: scales follow the codes
   const char* kbytes = static_cast<const char*>(a.k_pool);
   const char* vbytes = static_cast<const char*>(a.v_pool);
   const int srow0 = tid / kCpr;
@@ -1154,6 +1245,7 @@ __global__ __launch_bounds__(kPfThreads, kPfRb >= 3 ? 1 : 2) void paged_prefill_
 
   int pg_next[kChunks], pg_next2[kChunks];
   u32x4 kr[kChunks], vr[kChunks];
+  float ksr[kChunks], vsr[kChunks];   // INT8: the staged rows' scales
   // position of staged row `row` of tile t (past the split's end: its last position)
   auto pos_of = [&](int t, int row) __attribute__((always_inline)) {
     return min(k_lo + t * kPfKeys + row, k_hi - 1);
@@ -1179,8 +1271,12 @@ __global__ __launch_bounds__(kPfThreads, kPfRb >= 3 ? 1 : 2) void paged_prefill_
       const int pos = pos_of(tl, srow0 + c * kRowsPerPass);
       const uint32_t page = static_cast<uint32_t>(min(max(pg_next[c], 0), a.num_pages - 1));
       const uint32_t off = kPageMode <= 1 ? (pos & (ps - 1)) : (pos - blk_of(pos) * ps);
-      const uint32_t voff = off * (D * 2) + spart * 16;
+      const uint32_t voff = off * kGRowB + spart * 16;
       const uint64_t base = static_cast<uint64_t>(page * hkv + g) * head_bytes;
+      if constexpr (kI8) {
+        ksr[c] = *reinterpret_cast<const float*>(kbytes + base + scale_off + 4 * off);
+        vsr[c] = *reinterpret_cast<const float*>(vbytes + base + scale_off + 4 * off);
+      }
       kr[c] = *reinterpret_cast<const u32x4*>(kbytes + base + voff);
       vr[c] = *reinterpret_cast<const u32x4*>(vbytes + base + voff);
     }
@@ -1191,8 +1287,23 @@ __global__ __launch_bounds__(kPfThreads, kPfRb >= 3 ? 1 : 2) void paged_prefill_
 #pragma unroll
     for (int c = 0; c < kChunks; ++c) {
       const int row = srow0 + c * kRowsPerPass;
-      *reinterpret_cast<u32x4*>(kb + row * kKRowB + spart * 16) = kr[c];
-      *reinterpret_cast<u32x4*>(vb + row * kVRowB + spart * 16) = vr[c];
+      if constexpr (kI8) {
+        u32x4 lo, hi;
+        i8x16_to_bf16(kr[c], lo, hi);
+        *reinterpret_cast<u32x4*>(kb + row * kKRowB + spart * 32) = lo;
+        *reinterpret_cast<u32x4*>(kb + row * kKRowB + spart * 32 + 16) = hi;
+        i8x16_to_bf16(vr[c], lo, hi);
+        *reinterpret_cast<u32x4*>(vb + row * kVRowB + spart * 32) = lo;
+        *reinterpret_cast<u32x4*>(vb + row * kVRowB + spart * 32 + 16) = hi;
+        if (spart == 0) {
+          float* sc = reinterpret_cast<float*>(vb + kVTileB);
+          sc[row] = ksr[c];
+          sc[kPfKeys + row] = vsr[c];
+        }
+      } else {
+        *reinterpret_cast<u32x4*>(kb + row * kKRowB + spart * 16) = kr[c];
+        *reinterpret_cast<u32x4*>(vb + row * kVRowB + spart * 16) = vr[c];
+      }
     }
   };
 
@@ -1241,7 +1352,10 @@ __global__ __launch_bounds__(kPfThreads, kPfRb >= 3 ? 1 : 2) void paged_prefill_
   const int k_lane = lrow * kKRowB + lgrp * (D / 4) * 2;
   const int v_lane = (4 * lgrp + (lrow >> 2)) * kVRowB + ((lrow & 3) >> 1) * 16 + (lrow & 1) * 8;
 
-  auto compute = [&](const char* kt, const char* vt, int tb, auto mask_tag) __attribute__((always_inline)) {
+  // kt, vt: the sub-tile's staged K and V rows; st (INT8): its key scales,
+  // value scales at st + kPfKeys.
+  auto compute = [&](const char* kt, const char* vt, const float* st, int tb, auto mask_tag)
+      __attribute__((always_inline)) {
     constexpr bool kMask = decltype(mask_tag)::value;
     f32x4 s[4][kPfRb];
     if constexpr (PKV_PREFILL_SETPRIO) __builtin_amdgcn_s_setprio(1);
@@ -1260,6 +1374,17 @@ __global__ __launch_bounds__(kPfThreads, kPfRb >= 3 ? 1 : 2) void paged_prefill_
       }
     }
     if constexpr (PKV_PREFILL_SETPRIO) __builtin_amdgcn_s_setprio(0);
+    // INT8: a key's scale multiplies its scores (rows 4 lgrp + i of block kb)
+    f32x4 vsc[4];
+    if constexpr (kI8) {
+#pragma unroll
+      for (int kb = 0; kb < 4; ++kb) {
+        const f32x4 ksc = *reinterpret_cast<const f32x4*>(st + kb * 16 + 4 * lgrp);
+        vsc[kb] = *reinterpret_cast<const f32x4*>(st + kPfKeys + kb * 16 + 4 * lgrp);
+#pragma unroll
+        for (int rb = 0; rb < kPfRb; ++rb) s[kb][rb] *= ksc;
+      }
+    }
     // row maxima, then one (rarely taken) rescale branch for both row blocks
     float muse[kPfRb];
     bool up_any = false;
@@ -1296,14 +1421,22 @@ __global__ __launch_bounds__(kPfThreads, kPfRb >= 3 ? 1 : 2) void paged_prefill_
     }
 #pragma unroll
     for (int ks = 0; ks < 2; ++ks) {
-      bf16x8 pk[kPfRb];
+      bf16x8 pk[kPfRb];   // probabilities: row sums (and PV for bf16 pages)
+      bf16x8 pv[kPfRb];   // INT8: probabilities times the value scales, for PV
 #pragma unroll
       for (int rb = 0; rb < kPfRb; ++rb) {
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          pk[rb][i] = static_cast<__bf16>(fast_exp2(fmaf(s[2 * ks][rb][i], c2, -muse[rb])));
-          pk[rb][4 + i] = static_cast<__bf16>(fast_exp2(fmaf(s[2 * ks + 1][rb][i], c2, -muse[rb])));
+          const float e0 = fast_exp2(fmaf(s[2 * ks][rb][i], c2, -muse[rb]));
+          const float e1 = fast_exp2(fmaf(s[2 * ks + 1][rb][i], c2, -muse[rb]));
+          pk[rb][i] = static_cast<__bf16>(e0);
+          pk[rb][4 + i] = static_cast<__bf16>(e1);
+          if constexpr (kI8) {
+            pv[rb][i] = static_cast<__bf16>(e0 * vsc[2 * ks][i]);
+            pv[rb][4 + i] = static_cast<__bf16>(e1 * vsc[2 * ks + 1][i]);
+          }
         }
+        if constexpr (!kI8) pv[rb] = pk[rb];
         lsum[rb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ones, pk[rb], lsum[rb], 0, 0, 0);
       }
 #pragma unroll
@@ -1314,7 +1447,7 @@ __global__ __launch_bounds__(kPfThreads, kPfRb >= 3 ? 1 : 2) void paged_prefill_
         const bf16x8 vf = __builtin_shufflevector(v0, v1, 0, 1, 2, 3, 4, 5, 6, 7);
 #pragma unroll
         for (int rb = 0; rb < kPfRb; ++rb)
-          o[d][rb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf, pk[rb], o[d][rb], 0, 0, 0);
+          o[d][rb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf, pv[rb], o[d][rb], 0, 0, 0);
       }
     }
   };
@@ -1338,10 +1471,11 @@ __global__ __launch_bounds__(kPfThreads, kPfRb >= 3 ? 1 : 2) void paged_prefill_
       if (w_active && tb <= w_qmax) {
         const char* kt = smem + (t & 1) * kBufB + sub * 64 * kKRowB;
         const char* vt = smem + (t & 1) * kBufB + kKTileB + sub * 64 * kVRowB;
+        const float* st = reinterpret_cast<const float*>(smem + (t & 1) * kBufB + kKTileB + kVTileB) + sub * 64;
         if (tb + 63 <= w_qmin)
-          compute(kt, vt, tb, std::integral_constant<bool, false>());
+          compute(kt, vt, st, tb, std::integral_constant<bool, false>());
         else
-          compute(kt, vt, tb, std::integral_constant<bool, true>());
+          compute(kt, vt, st, tb, std::integral_constant<bool, true>());
       }
     }
     stage((t + 1) & 1);
@@ -1517,6 +1651,61 @@ __global__ __launch_bounds__(kThreads) void store_kv_kernel(
   *reinterpret_cast<uint4*>((is_v ? v_pool : k_pool) + dst) = val;
 }
 
+// KV scatter into INT8 pages ("INT8 cache": a vector is quantized once, when
+// its position is written): kLpv = D / 8 consecutive lanes own one (token,
+// KV head) vector of K or V, 8 bf16 each.  Its absolute maximum is reduced
+// across those lanes; scale = max|x| / 127 and code = rint(x / scale), both
+// IEEE fp32 divisions, codes clamped to [-127, 127]; a zero vector stores
+// scale 0 and codes 0.  Each lane writes its 8 codes (8 bytes), the group's
+// first lane the scale.
+template <int D>
+__global__ __launch_bounds__(kThreads) void store_kv_i8_kernel(
+    char* __restrict__ k_pool, char* __restrict__ v_pool, const uint16_t* __restrict__ k_new,
+    const uint16_t* __restrict__ v_new, const int64_t* __restrict__ slots, int32_t n_tokens, int32_t hkv,
+    int32_t page_size, int32_t ps_shift, int64_t pool_slots, int32_t head_bytes) {
+  constexpr int kLpv = D / 8;
+  const int64_t per_pool = static_cast<int64_t>(n_tokens) * hkv;
+  const int64_t gid = static_cast<int64_t>(blockIdx.x) * kThreads + threadIdx.x;
+  int64_t vec = gid / kLpv;                          // vector index over both pools
+  const int part = static_cast<int>(gid % kLpv);
+  const bool live = vec < 2 * per_pool;              // whole groups are live or not
+  const bool is_v = vec >= per_pool;
+  if (is_v) vec -= per_pool;
+  if (!live) vec = 0;
+  const uint16_t* src = (is_v ? v_new : k_new) + vec * D + part * 8;
+  const u32x4 x = *reinterpret_cast<const u32x4*>(src);
+  float f[8];
+#pragma unroll
+  for (int w = 0; w < 4; ++w) {
+    f[2 * w] = __uint_as_float(x[w] << 16);
+    f[2 * w + 1] = __uint_as_float(x[w] & 0xffff0000u);
+  }
+  float amax = 0.f;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) amax = fmaxf(amax, fabsf(f[i]));
+#pragma unroll
+  for (int off = 1; off < kLpv; off <<= 1) amax = fmaxf(amax, __shfl_xor(amax, off));
+  const float scale = amax / 127.f;
+  uint32_t packed[2] = {0u, 0u};
+  if (scale > 0.f) {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const float c = fminf(fmaxf(rintf(f[i] / scale), -127.f), 127.f);
+      packed[i >> 2] |= (static_cast<uint32_t>(static_cast<int32_t>(c)) & 0xffu) << (8 * (i & 3));
+    }
+  }
+  if (!live) return;
+  const int64_t t = vec / hkv;
+  const int g = static_cast<int>(vec - t * hkv);
+  const int64_t slot = slots[t];
+  if (slot < 0 || slot >= pool_slots) return;
+  const int64_t page = ps_shift >= 0 ? (slot >> ps_shift) : slot / page_size;
+  const int64_t off = slot - page * page_size;
+  char* head = (is_v ? v_pool : k_pool) + (page * hkv + g) * static_cast<int64_t>(head_bytes);
+  *reinterpret_cast<uint2*>(head + off * D + part * 8) = make_uint2(packed[0], packed[1]);
+  if (part == 0) *reinterpret_cast<float*>(head + static_cast<int64_t>(page_size) * D + 4 * off) = scale;
+}
+
 // ---------------------------------------------------------------------------
 // host-side launch planning
 // ---------------------------------------------------------------------------
@@ -1531,8 +1720,8 @@ bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) ==
 
 int check_desc(const pkv_pool_desc* d, const char* fn) {
   if (!d) return fail(PKV_ERR_INVALID_ARG, std::string(fn) + ": NULL desc");
-  if (d->dtype != PKV_F32 && d->dtype != PKV_BF16)
-    return fail(PKV_ERR_UNSUPPORTED, std::string(fn) + ": dtype must be PKV_F32 or PKV_BF16");
+  if (d->dtype != PKV_F32 && d->dtype != PKV_BF16 && d->dtype != PKV_I8)
+    return fail(PKV_ERR_UNSUPPORTED, std::string(fn) + ": dtype must be PKV_F32, PKV_BF16 or PKV_I8");
   if (d->head_dim != 64 && d->head_dim != 128)
     return fail(PKV_ERR_UNSUPPORTED, std::string(fn) + ": head_dim must be 64 or 128");
   if (d->page_size < 1 || d->page_size > 256)
@@ -1545,6 +1734,12 @@ int check_desc(const pkv_pool_desc* d, const char* fn) {
   if (static_cast<int64_t>(d->num_pages) * d->num_kv_heads > INT32_MAX)
     return fail(PKV_ERR_UNSUPPORTED, std::string(fn) + ": num_pages * num_kv_heads above 2^31 - 1");
   return PKV_OK;
+}
+
+// Bytes of one (page, KV head) block of a pool of this descriptor.
+int64_t head_block_bytes(const pkv_pool_desc* d) {
+  if (d->dtype == PKV_I8) return i8_block_bytes(d->page_size, d->head_dim);
+  return static_cast<int64_t>(d->page_size) * d->head_dim * (d->dtype == PKV_BF16 ? 2 : 4);
 }
 
 struct Plan {
@@ -1605,7 +1800,7 @@ int make_plan(const pkv_pool_desc* d, int n_seqs, int hq, int max_q, int max_seq
     p->ws_bytes = p->partial_off + slots * (16 * p->rbw) * (d->head_dim + 2) * sizeof(float);
     return PKV_OK;
   }
-  if (d->dtype == PKV_BF16) {
+  if (d->dtype == PKV_BF16 || d->dtype == PKV_I8) {
     // paged_prefill_kernel: 128-row tiles; KV splits only when the units'
     // tiles alone cannot fill the chip.
     p->prefill = true;
@@ -1664,17 +1859,17 @@ void launch_attention_t(const AttnArgs& a, const Plan& p, int n_seqs, int hkv, h
   paged_attention_kernel<T, D, RB, KG><<<grid, dim3(kThreads), kLds, st>>>(a);
 }
 
-template <typename T, int D, int RBW>
+template <typename T, int D, int RBW, bool kI8>
 void launch_decode_t(const AttnArgs& a, const Plan& p, int n_seqs, char* ws, hipStream_t st) {
   int32_t* seq_blk = reinterpret_cast<int32_t*>(ws + p.items_off);
   constexpr int kRowB = D * static_cast<int>(sizeof(T));
   constexpr int kLds = 16 * (2 * kRowB + (kRowB >= 512 ? 0 : 48));
   if (a.ps_shift >= 4)
-    paged_decode_kernel<T, D, RBW, 0><<<p.grid, dim3(kWave), kLds, st>>>(a, seq_blk, a.seq_lens, a.cu_q, a.block_tables);
+    paged_decode_kernel<T, D, RBW, 0, kI8><<<p.grid, dim3(kWave), kLds, st>>>(a, seq_blk, a.seq_lens, a.cu_q, a.block_tables);
   else if (a.ps_shift >= 0)
-    paged_decode_kernel<T, D, RBW, 1><<<p.grid, dim3(kWave), kLds, st>>>(a, seq_blk, a.seq_lens, a.cu_q, a.block_tables);
+    paged_decode_kernel<T, D, RBW, 1, kI8><<<p.grid, dim3(kWave), kLds, st>>>(a, seq_blk, a.seq_lens, a.cu_q, a.block_tables);
   else
-    paged_decode_kernel<T, D, RBW, 2><<<p.grid, dim3(kWave), kLds, st>>>(a, seq_blk, a.seq_lens, a.cu_q, a.block_tables);
+    paged_decode_kernel<T, D, RBW, 2, kI8><<<p.grid, dim3(kWave), kLds, st>>>(a, seq_blk, a.seq_lens, a.cu_q, a.block_tables);
   merge_segments_kernel<T, D, RBW><<<n_seqs * a.num_kv_heads, dim3(kThreads), 0, st>>>(a, seq_blk);
 }
 
@@ -1688,10 +1883,10 @@ int64_t prefill_grid(const Plan& p, int n_seqs, int hkv, int group, int total_q)
   return 8 * rows * p.n_splits;
 }
 
-template <int D, int kPageMode, int kWaves, int kKeys>
+template <int D, int kPageMode, int kWaves, int kKeys, bool kI8>
 int launch_prefill_t(const AttnArgs& a, const Plan& p, char* ws, hipStream_t st) {
-  constexpr int kLds = pf_lds_bytes<D, kKeys>();
-  auto* kern = &paged_prefill_kernel<D, kPageMode, kWaves * kWave, kKeys>;
+  constexpr int kLds = pf_lds_bytes<D, kKeys, kI8>();
+  auto* kern = &paged_prefill_kernel<D, kPageMode, kWaves * kWave, kKeys, kI8>;
   static const hipError_t attr = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
                                                      hipFuncAttributeMaxDynamicSharedMemorySize, kLds);
   if (attr != hipSuccess) return fail(PKV_ERR_DEVICE, std::string("prefill: LDS attribute: ") + hipGetErrorString(attr));
@@ -1707,22 +1902,30 @@ int launch_prefill_t(const AttnArgs& a, const Plan& p, char* ws, hipStream_t st)
   return PKV_OK;
 }
 
-template <int D, int kPageMode>
+template <int D, int kPageMode, bool kI8>
 int launch_prefill_shape(const AttnArgs& a, const Plan& p, char* ws, hipStream_t st) {
-  return p.pf_short ? launch_prefill_t<D, kPageMode, kPfShortWaves, kPfShortKeys>(a, p, ws, st)
-                    : launch_prefill_t<D, kPageMode, kPfWaves, kPfKeys>(a, p, ws, st);
+  return p.pf_short ? launch_prefill_t<D, kPageMode, kPfShortWaves, kPfShortKeys, kI8>(a, p, ws, st)
+                    : launch_prefill_t<D, kPageMode, kPfWaves, kPfKeys, kI8>(a, p, ws, st);
 }
 
-template <typename T, int D>
+template <int D, bool kI8>
+int launch_prefill_d(const AttnArgs& a, const Plan& p, char* ws, hipStream_t st) {
+  const int mode = a.ps_shift < 0 ? 2 : a.page_size >= pf_wave_rows<D, kI8>() ? 0 : 1;
+  return mode == 0 ? launch_prefill_shape<D, 0, kI8>(a, p, ws, st)
+                   : mode == 1 ? launch_prefill_shape<D, 1, kI8>(a, p, ws, st) : launch_prefill_shape<D, 2, kI8>(a, p, ws, st);
+}
+
+template <typename T, int D, bool kI8 = false>
 void launch_attention_d(const AttnArgs& a, const Plan& p, int n_seqs, int hkv, char* ws, hipStream_t st) {
   if (p.decode) {
     switch (p.rbw) {
-      case 1: launch_decode_t<T, D, 1>(a, p, n_seqs, ws, st); break;
-      case 2: launch_decode_t<T, D, 2>(a, p, n_seqs, ws, st); break;
-      default: launch_decode_t<T, D, 3>(a, p, n_seqs, ws, st); break;
+      case 1: launch_decode_t<T, D, 1, kI8>(a, p, n_seqs, ws, st); break;
+      case 2: launch_decode_t<T, D, 2, kI8>(a, p, n_seqs, ws, st); break;
+      default: launch_decode_t<T, D, 3, kI8>(a, p, n_seqs, ws, st); break;
     }
     return;
   }
+  if constexpr (kI8) return;   // INT8 pages: the decode and prefill kernels cover every plan
   launch_attention_t<T, D, 4, 1>(a, p, n_seqs, hkv, st);
   if (p.n_splits > 1) {
     dim3 grid(a.num_q_heads, p.max_q, n_seqs);
@@ -1777,6 +1980,7 @@ int run_attention(const char* fn, const pkv_pool_desc* desc, const void* k_pool,
   a.max_q = max_q;
   a.scale_log2 = scale * 1.4426950408889634f;
   a.waves = p.grid;
+  a.head_bytes = static_cast<int32_t>(head_block_bytes(desc));
   if (p.decode) {
     const size_t rows_out = (static_cast<size_t>(n_seqs) * desc->num_kv_heads + p.grid) * (16 * p.rbw);
     a.ws_o = reinterpret_cast<float*>(static_cast<char*>(workspace) + p.partial_off);
@@ -1790,18 +1994,18 @@ int run_attention(const char* fn, const pkv_pool_desc* desc, const void* k_pool,
   const int hkv = desc->num_kv_heads;
   char* ws = static_cast<char*>(workspace);
   (void)hipGetLastError();
+  const bool i8 = desc->dtype == PKV_I8;
   if (p.prefill) {
-    const bool pow2 = a.ps_shift >= 0;
-    if (desc->head_dim == 128) {
-      const int mode = !pow2 ? 2 : a.page_size >= pf_wave_rows<128>() ? 0 : 1;
-      rc = mode == 0 ? launch_prefill_shape<128, 0>(a, p, ws, st)
-                     : mode == 1 ? launch_prefill_shape<128, 1>(a, p, ws, st) : launch_prefill_shape<128, 2>(a, p, ws, st);
-    } else {
-      const int mode = !pow2 ? 2 : a.page_size >= pf_wave_rows<64>() ? 0 : 1;
-      rc = mode == 0 ? launch_prefill_shape<64, 0>(a, p, ws, st)
-                     : mode == 1 ? launch_prefill_shape<64, 1>(a, p, ws, st) : launch_prefill_shape<64, 2>(a, p, ws, st);
-    }
+    if (desc->head_dim == 128)
+      rc = i8 ? launch_prefill_d<128, true>(a, p, ws, st) : launch_prefill_d<128, false>(a, p, ws, st);
+    else
+      rc = i8 ? launch_prefill_d<64, true>(a, p, ws, st) : launch_prefill_d<64, false>(a, p, ws, st);
     if (rc != PKV_OK) return rc;
+  } else if (i8) {
+    if (desc->head_dim == 128)
+      launch_attention_d<uint16_t, 128, true>(a, p, n_seqs, hkv, ws, st);
+    else
+      launch_attention_d<uint16_t, 64, true>(a, p, n_seqs, hkv, ws, st);
   } else if (desc->dtype == PKV_BF16) {
     if (desc->head_dim == 128)
       launch_attention_d<uint16_t, 128>(a, p, n_seqs, hkv, ws, st);
@@ -1834,30 +2038,57 @@ int pkv_store_kv(const pkv_pool_desc* desc, void* k_pool, void* v_pool, const vo
   if (!aligned16(k_pool) || !aligned16(v_pool) || !aligned16(k_new) || !aligned16(v_new) ||
       (reinterpret_cast<uintptr_t>(slots) & 7u))
     return fail(PKV_ERR_INVALID_ARG, "pkv_store_kv: misaligned device pointer");
-  const int es = desc->dtype == PKV_BF16 ? 2 : 4;
-  const int64_t chunks = 2 * static_cast<int64_t>(n_tokens) * desc->num_kv_heads *
-                         (desc->head_dim * es / 16);
-  const int64_t blocks = (chunks + kThreads - 1) / kThreads;
-  if (blocks > INT32_MAX) return fail(PKV_ERR_UNSUPPORTED, "pkv_store_kv: too many tokens");
   const int64_t pool_slots = static_cast<int64_t>(desc->num_pages) * desc->page_size;
+  const int ps_shift = log2_exact(desc->page_size);
   hipStream_t st = static_cast<hipStream_t>(stream);
   (void)hipGetLastError();
-  if (es == 2)
-    store_kv_kernel<2><<<dim3(static_cast<unsigned>(blocks)), dim3(kThreads), 0, st>>>(
-                       static_cast<char*>(k_pool), static_cast<char*>(v_pool),
-                       static_cast<const char*>(k_new), static_cast<const char*>(v_new), slots,
-                       n_tokens, desc->num_kv_heads, desc->head_dim, desc->page_size,
-                       log2_exact(desc->page_size), pool_slots);
-  else
-    store_kv_kernel<4><<<dim3(static_cast<unsigned>(blocks)), dim3(kThreads), 0, st>>>(
-                       static_cast<char*>(k_pool), static_cast<char*>(v_pool),
-                       static_cast<const char*>(k_new), static_cast<const char*>(v_new), slots,
-                       n_tokens, desc->num_kv_heads, desc->head_dim, desc->page_size,
-                       log2_exact(desc->page_size), pool_slots);
+  if (desc->dtype == PKV_I8) {
+    // one group of head_dim / 8 lanes per (token, KV head) vector of K or V
+    const int64_t threads = 2 * static_cast<int64_t>(n_tokens) * desc->num_kv_heads * (desc->head_dim / 8);
+    const int64_t blocks = (threads + kThreads - 1) / kThreads;
+    if (blocks > INT32_MAX) return fail(PKV_ERR_UNSUPPORTED, "pkv_store_kv: too many tokens");
+    const int32_t hb = static_cast<int32_t>(head_block_bytes(desc));
+    if (desc->head_dim == 128)
+      store_kv_i8_kernel<128><<<dim3(static_cast<unsigned>(blocks)), dim3(kThreads), 0, st>>>(
+          static_cast<char*>(k_pool), static_cast<char*>(v_pool), static_cast<const uint16_t*>(k_new),
+          static_cast<const uint16_t*>(v_new), slots, n_tokens, desc->num_kv_heads, desc->page_size, ps_shift,
+          pool_slots, hb);
+    else
+      store_kv_i8_kernel<64><<<dim3(static_cast<unsigned>(blocks)), dim3(kThreads), 0, st>>>(
+          static_cast<char*>(k_pool), static_cast<char*>(v_pool), static_cast<const uint16_t*>(k_new),
+          static_cast<const uint16_t*>(v_new), slots, n_tokens, desc->num_kv_heads, desc->page_size, ps_shift,
+          pool_slots, hb);
+  } else {
+    const int es = desc->dtype == PKV_BF16 ? 2 : 4;
+    const int64_t chunks = 2 * static_cast<int64_t>(n_tokens) * desc->num_kv_heads *
+                           (desc->head_dim * es / 16);
+    const int64_t blocks = (chunks + kThreads - 1) / kThreads;
+    if (blocks > INT32_MAX) return fail(PKV_ERR_UNSUPPORTED, "pkv_store_kv: too many tokens");
+    if (es == 2)
+      store_kv_kernel<2><<<dim3(static_cast<unsigned>(blocks)), dim3(kThreads), 0, st>>>(
+                         static_cast<char*>(k_pool), static_cast<char*>(v_pool),
+                         static_cast<const char*>(k_new), static_cast<const char*>(v_new), slots,
+                         n_tokens, desc->num_kv_heads, desc->head_dim, desc->page_size, ps_shift, pool_slots);
+    else
+      store_kv_kernel<4><<<dim3(static_cast<unsigned>(blocks)), dim3(kThreads), 0, st>>>(
+                         static_cast<char*>(k_pool), static_cast<char*>(v_pool),
+                         static_cast<const char*>(k_new), static_cast<const char*>(v_new), slots,
+                         n_tokens, desc->num_kv_heads, desc->head_dim, desc->page_size, ps_shift, pool_slots);
+  }
   hipError_t err = hipGetLastError();
   if (err != hipSuccess)
     return fail(PKV_ERR_DEVICE, std::string("pkv_store_kv: launch failed: ") + hipGetErrorString(err));
   return PKV_OK;
+}
+
+size_t pkv_i8_block_bytes(int32_t page_size, int32_t head_dim) {
+  if (page_size < 1 || head_dim < 1) return 0;
+  return static_cast<size_t>(i8_block_bytes(page_size, head_dim));
+}
+
+size_t pkv_pool_bytes(const pkv_pool_desc* desc) {
+  if (check_desc(desc, "pkv_pool_bytes") != PKV_OK) return 0;
+  return static_cast<size_t>(desc->num_pages) * desc->num_kv_heads * static_cast<size_t>(head_block_bytes(desc));
 }
 
 size_t pkv_workspace_bytes(const pkv_pool_desc* desc, int32_t n_seqs, int32_t num_q_heads,

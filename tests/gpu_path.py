@@ -33,16 +33,19 @@ def host_f64(t: torch.Tensor) -> np.ndarray:
     return t.detach().float().cpu().double().numpy()
 
 
-def desc_of(w) -> pkv.PoolDesc:
-    return pkv.PoolDesc(pkv.PKV_BF16 if w.dtype == synth.BF16 else pkv.PKV_F32,
-                        int(w.num_pages), int(w.page_size), int(w.num_kv_heads), int(w.head_dim))
+def desc_of(w, kv_int8: bool = False) -> pkv.PoolDesc:
+    if kv_int8:
+        assert w.dtype == synth.BF16, "INT8 pages take bf16 K/V and queries"
+        dt = pkv.PKV_I8
+    else:
+        dt = pkv.PKV_BF16 if w.dtype == synth.BF16 else pkv.PKV_F32
+    return pkv.PoolDesc(dt, int(w.num_pages), int(w.page_size), int(w.num_kv_heads), int(w.head_dim))
 
 
 def nan_pools(desc: pkv.PoolDesc):
-    dt = desc.torch_dtype()
-    k = torch.full(desc.pool_shape, float("nan"), dtype=dt, device=DEV)
-    v = torch.full(desc.pool_shape, float("nan"), dtype=dt, device=DEV)
-    return k, v
+    """Pools whose every unwritten slot reads as NaN: NaN elements, or for INT8
+    pages 0xFF bytes (codes -1, scales NaN)."""
+    return desc.new_pools(DEV, fill=0xFF if desc.dtype == pkv.PKV_I8 else float("nan"))
 
 
 def i32(a) -> torch.Tensor:
@@ -64,8 +67,8 @@ class Session:
     log: Dict[str, list] = field(default_factory=dict)   # tables / slots for checks
 
     @classmethod
-    def open(cls, w, free_order=None):
-        desc = desc_of(w)
+    def open(cls, w, free_order=None, kv_int8: bool = False):
+        desc = desc_of(w, kv_int8)
         order = w.free_order if free_order is None else free_order
         alloc = pkv.Allocator(desc.num_pages, desc.page_size, order)
         k, v = nan_pools(desc)
@@ -149,9 +152,9 @@ def run_tiny(w: synth.TinyBatch):
     return s, seqs, prefill, dec
 
 
-def run_decode(w: synth.DecodeBatch, free_order=None):
+def run_decode(w: synth.DecodeBatch, free_order=None, kv_int8: bool = False):
     """Setup stores positions 0..L-2; the step stores position L-1 and decodes."""
-    s = Session.open(w, free_order)
+    s = Session.open(w, free_order, kv_int8)
     seqs = [s.alloc.seq_new() for _ in w.lengths]
     items = []
     for b, seq in enumerate(seqs):
@@ -170,10 +173,10 @@ def run_decode(w: synth.DecodeBatch, free_order=None):
     return s, seqs, out
 
 
-def run_prefix(w: synth.PrefixTraces):
+def run_prefix(w: synth.PrefixTraces, kv_int8: bool = False):
     """Plan, adopt shared pages in planned order, store every unshared suffix,
     then one prefill/append over all rows' suffixes (rows in id order)."""
-    s = Session.open(w)
+    s = Session.open(w, kv_int8=kv_int8)
     n = len(w.row_len)
     order, parent, shared = pkv.plan_prefix([w.row_tokens(r) for r in range(n)], w.page_size)
     seqs = [-1] * n
@@ -193,10 +196,10 @@ def run_prefix(w: synth.PrefixTraces):
     return s, (order, parent, shared), seqs, n_new, out
 
 
-def run_rewind(w: synth.RewindDocs):
+def run_rewind(w: synth.RewindDocs, kv_int8: bool = False):
     """Documents cached; question 1 appended and answered; truncated back to the
     document; question 2 appended and answered on the kept pages."""
-    s = Session.open(w)
+    s = Session.open(w, kv_int8=kv_int8)
     n = w.doc_k.shape[0]
     seqs = [s.alloc.seq_new() for _ in range(n)]
     items = []
@@ -219,10 +222,10 @@ def run_rewind(w: synth.RewindDocs):
     return s, seqs, outs
 
 
-def run_spec(w: synth.SpecDecode, steps: Optional[int] = None):
+def run_spec(w: synth.SpecDecode, steps: Optional[int] = None, kv_int8: bool = False):
     """Each step: reserve the drafts, store them, 5-query causal append, keep a
     prefix of the drafts via truncate."""
-    s = Session.open(w)
+    s = Session.open(w, kv_int8=kv_int8)
     B = len(w.ctx_len)
     seqs = [s.alloc.seq_new() for _ in range(B)]
     items = []

@@ -16,10 +16,18 @@ import synth
 from oracle.attention import attend, attend_row
 from oracle.paging import Allocator
 from oracle.planner import plan_prefix
+from oracle.quant import dequantize, quantize
 
 
 def f64(values, dtype):
     return synth.to_f64(values, dtype)
+
+
+def kv_f64(values, dtype, kv_int8: bool = False):
+    """Logical K or V as attention sees them: the stored values, or for an
+    INT8 cache the dequantized codes of each (position, head) vector."""
+    x = synth.to_f64(values, dtype)
+    return dequantize(*quantize(x)) if kv_int8 else x
 
 
 def tiny_reference(w: synth.TinyBatch, scale: float):
@@ -49,7 +57,8 @@ def decode_allocator(w, free_order=None):
     return alloc, seqs
 
 
-def decode_reference(w: synth.DecodeBatch, scale: float, rows=None) -> Dict[Tuple[int, int], np.ndarray]:
+def decode_reference(w: synth.DecodeBatch, scale: float, rows=None,
+                     kv_int8: bool = False) -> Dict[Tuple[int, int], np.ndarray]:
     """rows: iterable of (b, h); default all.  Returns {(b, h): o [D]}."""
     B, hq = len(w.lengths), w.num_q_heads
     grp = hq // w.num_kv_heads
@@ -59,8 +68,8 @@ def decode_reference(w: synth.DecodeBatch, scale: float, rows=None) -> Dict[Tupl
     for b, h in rows:
         lo, L = int(w.offsets[b]), int(w.lengths[b])
         g = h // grp
-        k = f64(w.k[lo:lo + L, g], w.dtype)
-        v = f64(w.v[lo:lo + L, g], w.dtype)
+        k = kv_f64(w.k[lo:lo + L, g], w.dtype, kv_int8)
+        v = kv_f64(w.v[lo:lo + L, g], w.dtype, kv_int8)
         out[(b, h)] = attend_row(f64(w.q[b, h], w.dtype), k, v, L - 1, scale)
     return out
 
@@ -82,17 +91,18 @@ def prefix_reference_rows(w: synth.PrefixTraces, shared: List[int], scale: float
     return out
 
 
-def prefix_reference_full(w: synth.PrefixTraces, shared: List[int], scale: float) -> np.ndarray:
+def prefix_reference_full(w: synth.PrefixTraces, shared: List[int], scale: float,
+                          kv_int8: bool = False) -> np.ndarray:
     """All rows' suffix outputs, packed in row-id order."""
     outs = []
     for d in range(len(w.row_len)):
         t, L, sh = int(w.row_trace[d]), int(w.row_len[d]), int(shared[d])
-        outs.append(attend(f64(w.q[t, sh:L], w.dtype), f64(w.k[t, :L], w.dtype),
-                           f64(w.v[t, :L], w.dtype), scale))
+        outs.append(attend(f64(w.q[t, sh:L], w.dtype), kv_f64(w.k[t, :L], w.dtype, kv_int8),
+                           kv_f64(w.v[t, :L], w.dtype, kv_int8), scale))
     return np.concatenate(outs)
 
 
-def rewind_reference(w: synth.RewindDocs, scale: float, docs=None):
+def rewind_reference(w: synth.RewindDocs, scale: float, docs=None, kv_int8: bool = False):
     """[pass1, pass2] outputs [n_docs][q_len][Hq][D] for the listed docs."""
     n = w.doc_k.shape[0]
     docs = range(n) if docs is None else docs
@@ -100,24 +110,28 @@ def rewind_reference(w: synth.RewindDocs, scale: float, docs=None):
     for qq, qk, qv in ((w.q1_q, w.q1_k, w.q1_v), (w.q2_q, w.q2_k, w.q2_v)):
         per = {}
         for d in docs:
-            k = np.concatenate([f64(w.doc_k[d], w.dtype), f64(qk[d], w.dtype)])
-            v = np.concatenate([f64(w.doc_v[d], w.dtype), f64(qv[d], w.dtype)])
+            k = np.concatenate([kv_f64(w.doc_k[d], w.dtype, kv_int8), kv_f64(qk[d], w.dtype, kv_int8)])
+            v = np.concatenate([kv_f64(w.doc_v[d], w.dtype, kv_int8), kv_f64(qv[d], w.dtype, kv_int8)])
             per[d] = attend(f64(qq[d], w.dtype), k, v, scale)
         res.append(per)
     return res
 
 
-def spec_reference(w: synth.SpecDecode, scale: float, steps: int, seqs_checked=None):
+def spec_reference(w: synth.SpecDecode, scale: float, steps: int, seqs_checked=None,
+                   kv_int8: bool = False):
     """Per step, {b: [drafts][Hq][D]} over each sequence's kept logical K/V."""
     B = len(w.ctx_len)
     seqs_checked = range(B) if seqs_checked is None else seqs_checked
-    kept_k = {b: [f64(w.ctx_k[w.ctx_offsets[b]:w.ctx_offsets[b + 1]], w.dtype)] for b in seqs_checked}
-    kept_v = {b: [f64(w.ctx_v[w.ctx_offsets[b]:w.ctx_offsets[b + 1]], w.dtype)] for b in seqs_checked}
+    kept_k = {b: [kv_f64(w.ctx_k[w.ctx_offsets[b]:w.ctx_offsets[b + 1]], w.dtype, kv_int8)]
+              for b in seqs_checked}
+    kept_v = {b: [kv_f64(w.ctx_v[w.ctx_offsets[b]:w.ctx_offsets[b + 1]], w.dtype, kv_int8)]
+              for b in seqs_checked}
     res = []
     for st in range(steps):
         per = {}
         for b in seqs_checked:
-            dk, dv = f64(w.draft_k[st, b], w.dtype), f64(w.draft_v[st, b], w.dtype)
+            dk = kv_f64(w.draft_k[st, b], w.dtype, kv_int8)
+            dv = kv_f64(w.draft_v[st, b], w.dtype, kv_int8)
             k = np.concatenate(kept_k[b] + [dk])
             v = np.concatenate(kept_v[b] + [dv])
             per[b] = attend(f64(w.draft_q[st, b], w.dtype), k, v, scale)

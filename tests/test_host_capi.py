@@ -200,6 +200,29 @@ def test_workspace_and_descriptor_checks(pkv_lib):
     assert pkv.workspace_bytes(pkv.PoolDesc(pkv.PKV_BF16, 10, 16, 1, 128), 4, 32, 1, 100) == 0  # group 32
 
 
+def test_int8_pool_layout_sizes(pkv_lib, golden):
+    """INT8 pages cost head_dim + 4 bytes per vector (TileInfer.jl "INT8 cache":
+    132 bytes instead of 256 at head_dim 128); a (page, head) block is padded
+    to 16 bytes only when page_size is not a multiple of 4."""
+    fixture = golden("tileinfer_sizing.json")
+    assert pkv_lib.pkv_i8_block_bytes(16, 128) == 16 * fixture["int8_vector_bytes"]
+    assert pkv_lib.pkv_i8_block_bytes(1, 128) == 128 + 16
+    assert pkv_lib.pkv_i8_block_bytes(3, 64) == 3 * 64 + 16
+    assert pkv_lib.pkv_i8_block_bytes(64, 128) == 64 * 132
+    assert pkv_lib.pkv_i8_block_bytes(0, 128) == 0
+    d8 = pkv.PoolDesc(pkv.PKV_I8, 300_000, 16, 8, 128)
+    d16 = pkv.PoolDesc(pkv.PKV_BF16, 300_000, 16, 8, 128)
+    assert d8.pool_shape == (300_000, 8, 2112)
+    assert d8.pool_bytes() == 300_000 * 8 * 16 * 132
+    assert d16.pool_bytes() == 300_000 * 8 * 16 * 256
+    assert pkv.PoolDesc(pkv.PKV_F32, 10, 4, 1, 64).pool_bytes() == 10 * 4 * 64 * 4
+    with pytest.raises(pkv.UnsupportedError):
+        pkv.PoolDesc(7, 10, 16, 8, 128).pool_bytes()
+    # the same launch plans (and workspace) as bf16 pages
+    for args in [(64, 32, 1, 4096), (256, 32, 8000, 8000), (8, 64, 5, 131_072)]:
+        assert pkv.workspace_bytes(d8, *args) == pkv.workspace_bytes(d16, *args) > 0
+
+
 @pytest.mark.parametrize("seed", range(10))
 def test_prepare_step_matches_oracle_and_is_atomic(pkv_lib, seed):
     rnd = random.Random(seed)
