@@ -81,6 +81,8 @@ def parse():
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--prefill-reps", type=int, default=10,
                     help="timed repetitions of the prefix-shared prefill leg (0 disables it)")
+    ap.add_argument("--int8", type=int, default=1,
+                    help="also time the decode batch on INT8 pages (1) or not (0)")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="finally copy a buffer of this many MiB three times (a plain copy of known "
                          "size, the reference for the FETCH_SIZE / WRITE_SIZE counters)")
@@ -233,27 +235,14 @@ def cpu_baseline(w, scale: float, budget_s: float):
     }
 
 
-def main():
-    args = parse()
-    world = int(os.environ.get("WORLD_SIZE", "1"))
-    if args.gpus != 1 or world != 1:
-        print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}, WORLD_SIZE {world}); "
-              "the paged path is not sharded across GPUs in this build.", file=sys.stderr)
-        sys.exit(2)
-
-    import torch
-
-    import pagedattention_pkv_store_amd as pkv
-    import synth
-
-    assert torch.cuda.is_available(), "bench.py needs a HIP device"
-    dev = "cuda:0"
-    torch.cuda.set_device(0)
-    w = synth.decode_batch(seed=args.seed)
+def decode_leg(args, torch, pkv, synth, w, dev: str, kv_int8: bool) -> dict:
+    """The paged-decode batch stepped ``args.steps`` times after
+    ``args.warmup`` untimed steps (see the module docstring); bf16 pools, or
+    INT8 pages (bf16 queries, one fp32 scale per cached vector)."""
     B, hq, hkv, D, ps = len(w.lengths), w.num_q_heads, w.num_kv_heads, w.head_dim, w.page_size
-    desc = pkv.PoolDesc(pkv.PKV_BF16, w.num_pages, ps, hkv, D)
+    desc = pkv.PoolDesc(pkv.PKV_I8 if kv_int8 else pkv.PKV_BF16, w.num_pages, ps, hkv, D)
     scale = 1.0 / float(np.sqrt(D))
-    per_pos = kv_bytes_per_position(hkv, D, 2)
+    per_pos = 2 * hkv * (D + 4) if kv_int8 else kv_bytes_per_position(hkv, D, 2)
     R = args.instances
     total_steps = args.warmup + args.steps
     uses = -(-total_steps // R)
@@ -262,8 +251,7 @@ def main():
         return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).to(dev).view(torch.bfloat16)
 
     # ---- setup (untimed): pools, R copies of the batch with L-1 positions stored ----
-    k_pool = torch.full(desc.pool_shape, float("nan"), dtype=torch.bfloat16, device=dev)
-    v_pool = torch.full_like(k_pool, float("nan"))
+    k_pool, v_pool = desc.new_pools(dev, fill=0xFF if kv_int8 else float("nan"))
     alloc = pkv.Allocator(w.num_pages, ps, w.free_order)
     k_all, v_all = bf16(w.k), bf16(w.v)
     inst = []
@@ -278,6 +266,7 @@ def main():
         inst.append(seqs)
     last_rows = torch.from_numpy(w.offsets[1:] - 1).to(dev)
     k_new, v_new = k_all[last_rows].contiguous(), v_all[last_rows].contiguous()
+    del k_all, v_all
     q = bf16(w.q)
     out = torch.empty_like(q)
     max_len = int(w.lengths.max()) + uses
@@ -355,22 +344,49 @@ def main():
         a, b = ev[k % EV_RING]
         dec_ms.append(a.elapsed_time(b))
     dec_ms = np.array(dec_ms)
+    assert torch.isfinite(out.float()).all(), "non-finite decode output"
     total_kv = float(sum(kv_bytes))
     qo_bytes = 2 * B * hq * D * 2                      # q read + out written per launch
-    alg_per_launch = total_kv / args.steps + qo_bytes
     dec_avg_s = float(dec_ms.mean()) / 1e3
-    achieved = alg_per_launch / dec_avg_s / 1e9
-    value = total_kv / wall / 1e9
-    assert torch.isfinite(out.float()).all(), "non-finite decode output"
+    res = {
+        "per_pos": per_pos, "total_kv": total_kv, "wall": wall, "dec_ms": dec_ms,
+        "alg_per_launch": total_kv / args.steps + qo_bytes, "dec_avg_s": dec_avg_s,
+        "B": B, "hq": hq, "hkv": hkv, "D": D, "ps": ps, "scale": scale,
+    }
+    res["achieved"] = res["alg_per_launch"] / dec_avg_s / 1e9
+    del k_pool, v_pool, ws, pinned, d_buf
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
+    return res
 
+
+def main():
+    args = parse()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}, WORLD_SIZE {world}); "
+              "the paged path is not sharded across GPUs in this build.", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import pagedattention_pkv_store_amd as pkv
+    import synth
+
+    assert torch.cuda.is_available(), "bench.py needs a HIP device"
+    dev = "cuda:0"
+    torch.cuda.set_device(0)
+    w = synth.decode_batch(seed=args.seed)
+    d = decode_leg(args, torch, pkv, synth, w, dev, kv_int8=False)
+    B, hq, hkv, D, ps, per_pos = d["B"], d["hq"], d["hkv"], d["D"], d["ps"], d["per_pos"]
     rec = {
         "metric": METRIC,
-        "value": round(value, 2),
+        "value": round(d["total_kv"] / d["wall"] / 1e9, 2),
         "unit": "GB/s",
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
-        "ms_per_step": round(wall / args.steps * 1e3, 4),
+        "ms_per_step": round(d["wall"] / args.steps * 1e3, 4),
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
@@ -381,24 +397,46 @@ def main():
                         "300k-page pool, 32 q heads / 8 KV heads, head_dim 128, bf16 KV, fp32 accumulate; "
                         "step = prepare_step + H2D + store_kv + decode (+LSE merge)",
             "n_seqs": B, "page_size": ps, "num_pages": w.num_pages, "num_q_heads": hq,
-            "num_kv_heads": hkv, "head_dim": D, "instances_rotated": R,
-            "mean_seq_len": round(float(total_kv / per_pos / args.steps / B), 1),
+            "num_kv_heads": hkv, "head_dim": D, "instances_rotated": args.instances,
+            "mean_seq_len": round(float(d["total_kv"] / per_pos / args.steps / B), 1),
         },
         "roofline": {
             "bound": "hbm",
-            "achieved": round(achieved, 1),
+            "achieved": round(d["achieved"], 1),
             "peak": HBM_PEAK_GBS,
             "unit": "GB/s",
-            "frac": round(achieved / HBM_PEAK_GBS, 4),
+            "frac": round(d["achieved"] / HBM_PEAK_GBS, 4),
             "traffic": measured_traffic("decode"),
             "kernel": "pkv_decode (paged_decode_kernel + merge_segments_kernel)",
-            "kernel_avg_us": round(dec_avg_s * 1e6, 2),
-            "kernel_median_us": round(float(np.median(dec_ms)) * 1e3, 2),
-            "algorithmic_bytes_per_launch": int(alg_per_launch),
+            "kernel_avg_us": round(d["dec_avg_s"] * 1e6, 2),
+            "kernel_median_us": round(float(np.median(d["dec_ms"])) * 1e3, 2),
+            "algorithmic_bytes_per_launch": int(d["alg_per_launch"]),
         },
     }
-    del k_pool, v_pool
-    torch.cuda.empty_cache()
+    if args.int8:
+        d8 = decode_leg(args, torch, pkv, synth, w, dev, kv_int8=True)
+        rec["int8_decode"] = {
+            "workload": "the same decode batch with INT8 pages (int8 codes + one fp32 scale per cached "
+                        "vector: 132 bytes per 128-element vector); bf16 queries and outputs",
+            "value": round(d8["total_kv"] / d8["wall"] / 1e9, 2),
+            "unit": "GB/s",
+            "ms_per_step": round(d8["wall"] / args.steps * 1e3, 4),
+            "tokens_per_s": round(B * args.steps / d8["wall"], 1),
+            "speedup_vs_bf16_step": round(d["wall"] / d8["wall"], 3),
+            "roofline": {
+                "bound": "hbm",
+                "achieved": round(d8["achieved"], 1),
+                "peak": HBM_PEAK_GBS,
+                "unit": "GB/s",
+                "frac": round(d8["achieved"] / HBM_PEAK_GBS, 4),
+                "traffic": measured_traffic("decode_int8"),
+                "kernel": "pkv_decode on PKV_I8 pools (paged_decode_kernel + merge_segments_kernel)",
+                "kernel_avg_us": round(d8["dec_avg_s"] * 1e6, 2),
+                "kernel_median_us": round(float(np.median(d8["dec_ms"])) * 1e3, 2),
+                "algorithmic_bytes_per_launch": int(d8["alg_per_launch"]),
+                "speedup_vs_bf16_kernel": round(d["dec_avg_s"] / d8["dec_avg_s"], 3),
+            },
+        }
     if args.prefill_reps > 0:
         rec["prefill_append"] = prefill_leg(args, torch, pkv, synth, dev)
     if args.copy_calibration_mib > 0:
@@ -411,7 +449,7 @@ def main():
         rec["copy_calibration_bytes"] = n_f32 * 4
         del src, dst
     if args.cpu_seconds > 0:
-        rec["cpu_baseline"] = cpu_baseline(w, scale, args.cpu_seconds)
+        rec["cpu_baseline"] = cpu_baseline(w, d["scale"], args.cpu_seconds)
     print(json.dumps(rec), flush=True)
 
 

@@ -575,15 +575,24 @@ __device__ __forceinline__ int decode_per(int total, int waves, int min_blocks) 
 typedef __bf16 dec_bf16x4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) dec_bf16x4 lds_dec_bf16x4;
 
+// INT8 pages: a block is half the bytes, so a wave spends relatively longer
+// waiting; twice the waves keep the same bytes in flight.
 #ifndef PKV_DECODE_DEPTH_I8
-#define PKV_DECODE_DEPTH_I8 3          // INT8 blocks are half the bytes: more of them in flight
+#define PKV_DECODE_DEPTH_I8 2
+#endif
+#ifndef PKV_DECODE_WAVES_I8
+#define PKV_DECODE_WAVES_I8 2048
+#endif
+#ifndef PKV_DECODE_WAVES_PER_SIMD_I8
+#define PKV_DECODE_WAVES_PER_SIMD_I8 2
 #endif
 
 // kPageMode 0: page_size a power of two >= 16 (a 16-position block lies in
 // one page); 1: a power of two < 16; 2: any other page size.  kI8: INT8
 // pages (T is then the bf16 type of the queries and outputs).
 template <typename T, int D, int RBW, int kPageMode, bool kI8>
-__global__ __launch_bounds__(kWave, RBW == 1 ? PKV_DECODE_WAVES_PER_SIMD : 1) void paged_decode_kernel(
+__global__ __launch_bounds__(kWave, RBW == 1 ? (kI8 ? PKV_DECODE_WAVES_PER_SIMD_I8 : PKV_DECODE_WAVES_PER_SIMD)
+                                             : 1) void paged_decode_kernel(
     AttnArgs args, int32_t* __restrict__ seq_blk, const int32_t* __restrict__ seq_lens,
     const int32_t* __restrict__ cu_q, const int32_t* __restrict__ block_tables) {
   static_assert(!kI8 || sizeof(T) == 2, "INT8 pages take bf16 queries");
@@ -1791,8 +1800,9 @@ int make_plan(const pkv_pool_desc* d, int n_seqs, int hq, int max_q, int max_seq
     const int64_t blocks_max = units * ((static_cast<int64_t>(std::max(1, max_seq_len)) + 15) / 16);
     if (blocks_max > (int64_t{1} << 30)) return fail(PKV_ERR_UNSUPPORTED, std::string(fn) + ": too many KV blocks");
     p->split_len = PKV_DECODE_MIN_BLOCKS;
+    const int64_t waves = d->dtype == PKV_I8 ? PKV_DECODE_WAVES_I8 : kDecodeWaves;
     p->grid = static_cast<int>(std::max<int64_t>(
-        1, std::min<int64_t>(kDecodeWaves, (blocks_max + PKV_DECODE_MIN_BLOCKS - 1) / PKV_DECODE_MIN_BLOCKS)));
+        1, std::min<int64_t>(waves, (blocks_max + PKV_DECODE_MIN_BLOCKS - 1) / PKV_DECODE_MIN_BLOCKS)));
     p->n_splits = 2;   // partial slots are used
     p->items_off = 0;
     p->partial_off = (static_cast<size_t>(n_seqs + 1) * sizeof(int32_t) + 255) & ~size_t{255};
