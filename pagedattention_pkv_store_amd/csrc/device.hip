@@ -171,22 +171,26 @@ struct AttnArgs {
 // then page_size fp32 scales, padded to a multiple of 16 bytes.
 __host__ __device__ constexpr int64_t i8_block_bytes(int64_t ps, int64_t d) { return ps * d + ((4 * ps + 15) & ~int64_t{15}); }
 
-// Sixteen int8 codes -> sixteen bf16 (exact: |code| <= 127 fits bf16's
-// 8-bit significand), as two 16-byte groups in code order.
-__device__ __forceinline__ void i8x16_to_bf16(u32x4 x, u32x4& lo, u32x4& hi) {
-  u32x4 o[2];
+// Eight int8 codes -> eight bf16 in code order (exact: |code| <= 127 fits
+// bf16's 8-bit significand).
+__device__ __forceinline__ u32x4 i8x8_to_bf16(uint2 x) {
+  u32x4 o;
 #pragma unroll
-  for (int w = 0; w < 4; ++w) {
-    const uint32_t v = x[w];
+  for (int w = 0; w < 2; ++w) {
+    const uint32_t v = w ? x.y : x.x;
     const f32x4 f = {static_cast<float>(static_cast<int8_t>(v)), static_cast<float>(static_cast<int8_t>(v >> 8)),
                      static_cast<float>(static_cast<int8_t>(v >> 16)), static_cast<float>(static_cast<int8_t>(v >> 24))};
     const auto p = __builtin_bit_cast(uint2, pack_bf16x4(f));
-    o[w >> 1][2 * (w & 1)] = p.x;
-    o[w >> 1][2 * (w & 1) + 1] = p.y;
+    o[2 * w] = p.x;
+    o[2 * w + 1] = p.y;
   }
-  lo = o[0];
-  hi = o[1];
+  return o;
 }
+
+// Unit of the K/V loads: 16 bytes of bf16 / fp32 rows, or 8 INT8 codes (which
+// widen to 16 bytes of bf16, so staged rows are written in the same pattern).
+template <bool kI8>
+using KvLoad = std::conditional_t<kI8, uint2, u32x4>;
 
 // Elements per LDS row of a staged K/V tile: a 16-byte pad staggers rows
 // across banks; 512-byte rows go unpadded so two tiles fit in 64 KiB.
@@ -597,10 +601,12 @@ __global__ __launch_bounds__(kWave, RBW == 1 ? (kI8 ? PKV_DECODE_WAVES_PER_SIMD_
     const int32_t* __restrict__ cu_q, const int32_t* __restrict__ block_tables) {
   static_assert(!kI8 || sizeof(T) == 2, "INT8 pages take bf16 queries");
   constexpr int kEs = sizeof(T);
+  using Ld = KvLoad<kI8>;
+  constexpr int kLdB = sizeof(Ld);
   constexpr int kRowBytes = D * kEs;                    // bytes of a staged (LDS) row
   constexpr int kGRowBytes = kI8 ? D : kRowBytes;       // bytes of a pool row
-  constexpr int kCpr = kGRowBytes / 16;                 // 16-byte chunks per pool row
-  constexpr int kLoads = 16 * kGRowBytes / (16 * kWave); // 16-byte loads per lane per pool per block
+  constexpr int kCpr = kGRowBytes / kLdB;               // load units per pool row
+  constexpr int kLoads = 16 * kGRowBytes / (kLdB * kWave); // loads per lane per pool per block
   constexpr int kDepth = kI8 ? PKV_DECODE_DEPTH_I8 : kDecodeDepth;
   constexpr int kDl = D / 4;                            // dims per lane in the QK operands
   constexpr int kFragChunks = kDl * kEs / 16;           // 16-byte chunks of one lane's K fragment
@@ -613,7 +619,7 @@ __global__ __launch_bounds__(kWave, RBW == 1 ? (kI8 ? PKV_DECODE_WAVES_PER_SIMD_
   // unpadded.
   constexpr int kKRow = kRowBytes + (kRowBytes >= 512 ? 0 : 16);
   constexpr int kVRow = kRowBytes + (kRowBytes >= 512 ? 0 : 32);
-  static_assert(kLoads * kWave * 16 == 16 * kGRowBytes, "block split");
+  static_assert(kLoads * kWave * kLdB == 16 * kGRowBytes, "block split");
 
   extern __shared__ __align__(16) char smem[];
   char* kst = smem;
@@ -751,7 +757,7 @@ __global__ __launch_bounds__(kWave, RBW == 1 ? (kI8 ? PKV_DECODE_WAVES_PER_SIMD_
   };
 
   // Issue the loads of the block at cursor c (kv_end: its unit's).  Load ci
-  // of a lane covers 16-byte chunk q % kCpr of row q / kCpr (q = ci * 64 +
+  // of a lane covers load unit q % kCpr of row q / kCpr (q = ci * 64 +
   // lane): consecutive lanes read consecutive bytes of whole rows.  okm marks
   // the rows inside the unit.  INT8 pages: the lane also loads the key and
   // value scales of positions 4 lgrp .. 4 lgrp + 3 of the block, the rows
@@ -759,7 +765,7 @@ __global__ __launch_bounds__(kWave, RBW == 1 ? (kI8 ? PKV_DECODE_WAVES_PER_SIMD_
   // wait for the block's rows covers them.
   const uint32_t head_bytes = static_cast<uint32_t>(args.head_bytes);
   const uint32_t scale_off = static_cast<uint32_t>(ps) * D;   // INT8: scales follow the codes
-  auto load_block = [&](const Cur& c, int kv_end, int page_hint, u32x4 (&kr)[kLoads], u32x4 (&vr)[kLoads],
+  auto load_block = [&](const Cur& c, int kv_end, int page_hint, Ld (&kr)[kLoads], Ld (&vr)[kLoads],
                         uint32_t& okm, f32x4& ks, f32x4& vs) __attribute__((always_inline)) {
     const int pos0 = 16 * c.j;
     const int32_t* bt_row = block_tables + static_cast<int64_t>(c.b) * args.bt_stride;
@@ -779,9 +785,9 @@ __global__ __launch_bounds__(kWave, RBW == 1 ? (kI8 ? PKV_DECODE_WAVES_PER_SIMD_
         const int q = ci * kWave + lane;
         const int r = q / kCpr;
         okm |= (pos0 + r < kv_end) ? (1u << ci) : 0u;
-        const uint32_t off = r * kGRowBytes + (q % kCpr) * 16;
-        kr[ci] = *reinterpret_cast<const u32x4*>(kbytes + base + off);
-        vr[ci] = *reinterpret_cast<const u32x4*>(vbytes + base + off);
+        const uint32_t off = r * kGRowBytes + (q % kCpr) * kLdB;
+        kr[ci] = *reinterpret_cast<const Ld*>(kbytes + base + off);
+        vr[ci] = *reinterpret_cast<const Ld*>(vbytes + base + off);
       }
     } else {
       if constexpr (kI8) {
@@ -805,9 +811,9 @@ __global__ __launch_bounds__(kWave, RBW == 1 ? (kI8 ? PKV_DECODE_WAVES_PER_SIMD_
         const int page = min(max(bt_row[blk], 0), args.num_pages - 1);
         okm |= (pos_raw < kv_end) ? (1u << ci) : 0u;
         const uint64_t e = static_cast<uint64_t>(page * hkv + c.g) * head_bytes + (pos - blk * ps) * kGRowBytes +
-                           (q % kCpr) * 16;
-        kr[ci] = *reinterpret_cast<const u32x4*>(kbytes + e);
-        vr[ci] = *reinterpret_cast<const u32x4*>(vbytes + e);
+                           (q % kCpr) * kLdB;
+        kr[ci] = *reinterpret_cast<const Ld*>(kbytes + e);
+        vr[ci] = *reinterpret_cast<const Ld*>(vbytes + e);
       }
     }
   };
@@ -823,20 +829,15 @@ __global__ __launch_bounds__(kWave, RBW == 1 ? (kI8 ? PKV_DECODE_WAVES_PER_SIMD_
   // NaN included); K rows need no zeroing, their scores are masked.  INT8
   // codes are widened to bf16 here (every code is finite; a row past the
   // unit gets value scale 0 instead).
-  auto stage_block = [&](const u32x4 (&kr)[kLoads], const u32x4 (&vr)[kLoads], uint32_t okm) __attribute__((always_inline)) {
+  auto stage_block = [&](const Ld (&kr)[kLoads], const Ld (&vr)[kLoads], uint32_t okm) __attribute__((always_inline)) {
 #pragma unroll
     for (int ci = 0; ci < kLoads; ++ci) {
       const int q = ci * kWave + lane;
       const int r = q / kCpr;
       const int cc = q % kCpr;
       if constexpr (kI8) {
-        u32x4 lo, hi;
-        i8x16_to_bf16(kr[ci], lo, hi);
-        *reinterpret_cast<u32x4*>(kst + r * kKRow + cc * 32) = lo;
-        *reinterpret_cast<u32x4*>(kst + r * kKRow + cc * 32 + 16) = hi;
-        i8x16_to_bf16(vr[ci], lo, hi);
-        *reinterpret_cast<u32x4*>(vst + r * kVRow + cc * 32) = lo;
-        *reinterpret_cast<u32x4*>(vst + r * kVRow + cc * 32 + 16) = hi;
+        *reinterpret_cast<u32x4*>(kst + r * kKRow + cc * 16) = i8x8_to_bf16(kr[ci]);
+        *reinterpret_cast<u32x4*>(vst + r * kVRow + cc * 16) = i8x8_to_bf16(vr[ci]);
       } else {
         const unsigned keep = 0u - ((okm >> ci) & 1u);   // all ones or zero
         *reinterpret_cast<u32x4*>(kst + r * kKRow + cc * 16) = kr[ci];
@@ -989,12 +990,12 @@ __global__ __launch_bounds__(kWave, RBW == 1 ? (kI8 ? PKV_DECODE_WAVES_PER_SIMD_
   // ---- the walk ----
   Cur cc = locate(i0);              // block being computed
   Cur lc = cc;                      // block whose loads are issued next
-  u32x4 kbuf[kDepth][kLoads], vbuf[kDepth][kLoads];
+  Ld kbuf[kDepth][kLoads], vbuf[kDepth][kLoads];
   f32x4 ksb[kDepth] = {}, vsb[kDepth] = {};   // INT8 scales
   uint32_t okm[kDepth];
   Unit ul = unit_of(lc.b);          // unit of the load cursor
   int page_l = kPageMode == 0 ? page_of(lc) : 0;
-  auto issue = [&](int li, u32x4 (&kr)[kLoads], u32x4 (&vr)[kLoads], uint32_t& okm, f32x4& ks, f32x4& vs)
+  auto issue = [&](int li, Ld (&kr)[kLoads], Ld (&vr)[kLoads], uint32_t& okm, f32x4& ks, f32x4& vs)
       __attribute__((always_inline)) {
     load_block(lc, ul.kv_end, page_l, kr, vr, okm, ks, vs);
     if (li + 1 < i1) {              // move the load cursor on (it stays on the last block)
@@ -1020,7 +1021,7 @@ __global__ __launch_bounds__(kWave, RBW == 1 ? (kI8 ? PKV_DECODE_WAVES_PER_SIMD_
   // One step: stage block ii from its registers, issue block ii + depth into
   // them, compute block ii, and close the segment at a unit's or the range's
   // end.
-  auto step = [&](int ii, u32x4 (&kr)[kLoads], u32x4 (&vr)[kLoads], uint32_t& om, f32x4& ks, f32x4& vs)
+  auto step = [&](int ii, Ld (&kr)[kLoads], Ld (&vr)[kLoads], uint32_t& om, f32x4& ks, f32x4& vs)
       __attribute__((always_inline)) {
     stage_block(kr, vr, om);
     const f32x4 ks_c = ks, vs_c = vs;   // the buffer is refilled below
@@ -1123,7 +1124,7 @@ template <int D, int kKeys, bool kI8>
 constexpr int pf_lds_bytes() { return 2 * pf_buf_bytes<D, kKeys, kI8>(); }
 // Rows one wave stages per pass (a pass = one 16-byte chunk per thread).
 template <int D, bool kI8>
-constexpr int pf_wave_rows() { return kWave / (D * (kI8 ? 1 : 2) / 16); }
+constexpr int pf_wave_rows() { return kWave / (D * (kI8 ? 1 : 2) / static_cast<int>(sizeof(KvLoad<kI8>))); }
 
 // row_off[k] = sum over blocks < k of (q-tiles of the block) * n_splits,
 // where a block's q-tiles are the most any of its 8 units needs.
@@ -1189,8 +1190,10 @@ __global__ __launch_bounds__(kPfThreads, kPfRb >= 3 ? 1 : 2) void paged_prefill_
   constexpr int kPfRows = 16 * kPfRb * (kPfThreads / kWave);   // query rows per workgroup
   constexpr int kKRowB = pf_k_row_bytes<D>();            // LDS row strides, bytes
   constexpr int kVRowB = pf_v_row_bytes<D>();
+  using Ld = KvLoad<kI8>;
+  constexpr int kLdB = sizeof(Ld);
   constexpr int kGRowB = D * (kI8 ? 1 : 2);             // bytes of a pool row
-  constexpr int kCpr = kGRowB / 16;                     // 16-byte chunks per pool row
+  constexpr int kCpr = kGRowB / kLdB;                   // load units per pool row
   constexpr int kChunks = kPfKeys * kCpr / kPfThreads;  // per thread per pool
   constexpr int kRowsPerPass = kPfThreads / kCpr;       // rows staged per chunk index
   constexpr int kQk = D / 32;                           // MFMAs per 16x16 score block
@@ -1239,7 +1242,7 @@ __global__ __launch_bounds__(kPfThreads, kPfRb >= 3 ? 1 : 2) void paged_prefill_
   const int k_hi = min(k_lo + a.split_len, kv_end);
   const int n_tiles = (k_hi - k_lo + kPfKeys - 1) / kPfKeys;
 
-  // ---- staging: this thread's rows srow0 + c * kRowsPerPass, chunk spart ----
+  // ---- staging: this thread's rows srow0 + c * kRowsPerPass, load unit spart ----
   const int ps = a.page_size;
   const int ps_shift = a.ps_shift;
   const int32_t* bt_row = a.block_tables + static_cast<int64_t>(b) * a.bt_stride;
@@ -1253,7 +1256,7 @@ __global__ __launch_bounds__(kPfThreads, kPfRb >= 3 ? 1 : 2) void paged_prefill_
   const int wrow0 = __builtin_amdgcn_readfirstlane(srow0);
 
   int pg_next[kChunks], pg_next2[kChunks];
-  u32x4 kr[kChunks], vr[kChunks];
+  Ld kr[kChunks], vr[kChunks];
   float ksr[kChunks], vsr[kChunks];   // INT8: the staged rows' scales
   // position of staged row `row` of tile t (past the split's end: its last position)
   auto pos_of = [&](int t, int row) __attribute__((always_inline)) {
@@ -1280,14 +1283,14 @@ __global__ __launch_bounds__(kPfThreads, kPfRb >= 3 ? 1 : 2) void paged_prefill_
       const int pos = pos_of(tl, srow0 + c * kRowsPerPass);
       const uint32_t page = static_cast<uint32_t>(min(max(pg_next[c], 0), a.num_pages - 1));
       const uint32_t off = kPageMode <= 1 ? (pos & (ps - 1)) : (pos - blk_of(pos) * ps);
-      const uint32_t voff = off * kGRowB + spart * 16;
+      const uint32_t voff = off * kGRowB + spart * kLdB;
       const uint64_t base = static_cast<uint64_t>(page * hkv + g) * head_bytes;
       if constexpr (kI8) {
         ksr[c] = *reinterpret_cast<const float*>(kbytes + base + scale_off + 4 * off);
         vsr[c] = *reinterpret_cast<const float*>(vbytes + base + scale_off + 4 * off);
       }
-      kr[c] = *reinterpret_cast<const u32x4*>(kbytes + base + voff);
-      vr[c] = *reinterpret_cast<const u32x4*>(vbytes + base + voff);
+      kr[c] = *reinterpret_cast<const Ld*>(kbytes + base + voff);
+      vr[c] = *reinterpret_cast<const Ld*>(vbytes + base + voff);
     }
   };
   auto stage = [&](int buf) __attribute__((always_inline)) {
@@ -1297,13 +1300,8 @@ __global__ __launch_bounds__(kPfThreads, kPfRb >= 3 ? 1 : 2) void paged_prefill_
     for (int c = 0; c < kChunks; ++c) {
       const int row = srow0 + c * kRowsPerPass;
       if constexpr (kI8) {
-        u32x4 lo, hi;
-        i8x16_to_bf16(kr[c], lo, hi);
-        *reinterpret_cast<u32x4*>(kb + row * kKRowB + spart * 32) = lo;
-        *reinterpret_cast<u32x4*>(kb + row * kKRowB + spart * 32 + 16) = hi;
-        i8x16_to_bf16(vr[c], lo, hi);
-        *reinterpret_cast<u32x4*>(vb + row * kVRowB + spart * 32) = lo;
-        *reinterpret_cast<u32x4*>(vb + row * kVRowB + spart * 32 + 16) = hi;
+        *reinterpret_cast<u32x4*>(kb + row * kKRowB + spart * 16) = i8x8_to_bf16(kr[c]);
+        *reinterpret_cast<u32x4*>(vb + row * kVRowB + spart * 16) = i8x8_to_bf16(vr[c]);
         if (spart == 0) {
           float* sc = reinterpret_cast<float*>(vb + kVTileB);
           sc[row] = ksr[c];
