@@ -269,32 +269,41 @@ def decode_leg(args, torch, pkv, synth, w, dev: str, kv_int8: bool) -> dict:
     del k_all, v_all
     q = bf16(w.q)
     out = torch.empty_like(q)
-    max_len = int(w.lengths.max()) + uses
+    max_len = int(w.lengths.max()) + uses + 1     # + 1: the upload one step ahead
     stride = -(-max_len // ps)
     ws = torch.empty(max(16, pkv.workspace_bytes(desc, B, hq, 1, max_len)), dtype=torch.uint8, device=dev)
     torch.cuda.synchronize()
 
-    # pinned staging, double-buffered: the host fills set k%2 while the copy
-    # of the previous step's set may still be in flight.  One buffer per set
-    # holds slots (int64 [B]), block tables (int32 [B][stride]) and lengths
-    # (int32 [B]), so a step uploads them with one copy.
+    # Upload, double-buffered: step k's slots (int64 [B]), block tables (int32
+    # [B][stride]) and lengths (int32 [B]) go from pinned set k%2 to device
+    # set k%2 in one copy, issued on a copy stream while the previous step's
+    # decode runs; the compute stream waits for it with an event that has
+    # normally fired long before (a copy in line with the kernels costs the
+    # copy engine's two hand-offs, about 30 us per step in a kernel trace).
     nbytes = B * 8 + B * stride * 4 + B * 4
 
     def views(buf):
         return (buf[:B * 8].view(torch.int64), buf[B * 8:B * 8 + B * stride * 4].view(torch.int32).view(B, stride),
                 buf[B * 8 + B * stride * 4:nbytes].view(torch.int32))
 
-    pinned = []
+    stream = torch.cuda.current_stream()
+    copy_stream = torch.cuda.Stream(device=dev)          # default priority
+    ones = np.ones(B, np.int32)
+    sets = []
     for _ in range(2):
         hb = torch.empty(nbytes, dtype=torch.uint8, pin_memory=True)
+        db = torch.empty(nbytes, dtype=torch.uint8, device=dev)
         hs, hbt, hl = views(hb)
-        pinned.append({"buf": hb, "np": (hs.numpy(), hbt.numpy(), hl.numpy()), "done": torch.cuda.Event()})
-    d_buf = torch.empty(nbytes, dtype=torch.uint8, device=dev)
-    d_slots, d_bt, d_lens = views(d_buf)
-    ones = np.ones(B, np.int32)
-    stream = torch.cuda.current_stream()
-    store_call = pkv.bind_store_kv(desc, k_pool, v_pool, k_new, v_new, d_slots, stream)
-    decode_call = pkv.bind_decode(desc, k_pool, v_pool, q, d_bt, d_lens, max_len, scale, out, ws, stream)
+        d_slots, d_bt, d_lens = views(db)
+        sets.append({
+            "host": hb, "dev": db, "np": (hs.numpy(), hbt.numpy(), hl.numpy()),
+            "uploaded": torch.cuda.Event(), "consumed": torch.cuda.Event(),
+            "store": pkv.bind_store_kv(desc, k_pool, v_pool, k_new, v_new, d_slots, stream),
+            "decode": pkv.bind_decode(desc, k_pool, v_pool, q, d_bt, d_lens, max_len, scale, out, ws, stream),
+        })
+    # prepare_step of instance r into pinned set j, marshalled once
+    prep = [[alloc.bind_prepare_step(inst[r], ones, stride, *sets[j]["np"]) for j in range(2)]
+            for r in range(R)]
     # A small ring of timing-event pairs, read back before reuse (a pair is
     # reused EV_RING steps later, long after it completed): many live timing
     # events slow down every record.
@@ -304,27 +313,36 @@ def decode_leg(args, torch, pkv, synth, w, dev: str, kv_int8: bool) -> dict:
     dec_ms = []
     kv_bytes = []
 
-    def step(k: int, timed_idx: int):
-        r = k % R
-        buf = pinned[k % 2]
+    def upload(k: int):
+        st = sets[k % 2]
         if k >= 2:
-            buf["done"].synchronize()
-        s_np, bt_np, l_np = buf["np"]
-        alloc.prepare_step(inst[r], ones, stride, s_np, bt_np, l_np)
-        d_buf.copy_(buf["buf"], non_blocking=True)
-        buf["done"].record(stream)
-        store_call()
+            st["uploaded"].synchronize()      # the host copy of step k - 2 was read
+        prep[k % R][k % 2]()
+        with torch.cuda.stream(copy_stream):
+            if k >= 2:
+                copy_stream.wait_event(st["consumed"])   # step k - 2's kernels are done with it
+            st["dev"].copy_(st["host"], non_blocking=True)
+            st["uploaded"].record(copy_stream)
+
+    def step(k: int, timed_idx: int):
+        st = sets[k % 2]
+        l_np = st["np"][2]
+        stream.wait_event(st["uploaded"])
+        st["store"]()
         pair = ev[timed_idx % EV_RING] if timed_idx >= 0 else None
         if pair is not None:
             if timed_idx >= EV_RING:
                 pair[1].synchronize()
                 dec_ms.append(pair[0].elapsed_time(pair[1]))
             pair[0].record(stream)
-        decode_call()
+        st["decode"]()
         if pair is not None:
             pair[1].record(stream)
             kv_bytes.append(int(l_np.astype(np.int64).sum()) * per_pos)
+        st["consumed"].record(stream)
+        upload(k + 1)                         # the next step's tables, during this decode
 
+    upload(0)
     for k in range(args.warmup):
         step(k, -1)
     torch.cuda.synchronize()
@@ -354,7 +372,8 @@ def decode_leg(args, torch, pkv, synth, w, dev: str, kv_int8: bool) -> dict:
         "B": B, "hq": hq, "hkv": hkv, "D": D, "ps": ps, "scale": scale,
     }
     res["achieved"] = res["alg_per_launch"] / dec_avg_s / 1e9
-    del k_pool, v_pool, ws, pinned, d_buf
+    torch.cuda.synchronize()
+    del k_pool, v_pool, ws, sets, prep
     torch.cuda.synchronize()
     torch.cuda.empty_cache()
     return res

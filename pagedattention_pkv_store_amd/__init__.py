@@ -186,6 +186,27 @@ class Allocator:
                                         _ptr(lens_out, ctypes.c_int32)))
         return slots_out[:total], bt_out.reshape(-1)[: n * bt_stride].reshape(n, bt_stride), lens_out[:n]
 
+    def bind_prepare_step(self, seqs: Sequence[int], n_new: Sequence[int], bt_stride: int,
+                          slots_out: np.ndarray, bt_out: Optional[np.ndarray], lens_out: np.ndarray) -> "BoundCall":
+        """pkv_prepare_step with its arguments marshalled once, for a serving
+        loop that repeats it on fixed (e.g. pinned) output arrays: each call
+        reserves n_new[b] more positions for seqs[b] and rewrites the outputs
+        (see prepare_step).  bt_out may be None (no block tables)."""
+        seqs_a = _i32(seqs)
+        n_a = _i32(n_new)
+        n = seqs_a.size
+        total = int(n_a.sum())
+        if (slots_out.dtype != np.int64 or slots_out.size < total or lens_out.dtype != np.int32
+                or lens_out.size < n or not (slots_out.flags.c_contiguous and lens_out.flags.c_contiguous)
+                or (bt_out is not None and (bt_out.dtype != np.int32 or bt_out.size < n * bt_stride
+                                            or not bt_out.flags.c_contiguous))):
+            raise PkvError(_lib.PKV_ERR_INVALID_ARG, "prepare_step: output arrays too small or wrong dtype")
+        bt_ptr = _ptr(bt_out, ctypes.c_int32) if bt_out is not None and bt_stride > 0 else None
+        args = (self._h, _ptr(seqs_a, ctypes.c_int32), n, _ptr(n_a, ctypes.c_int32),
+                bt_stride if bt_ptr is not None else 0, _ptr(slots_out, ctypes.c_int64), bt_ptr,
+                _ptr(lens_out, ctypes.c_int32))
+        return BoundCall(self._L.pkv_prepare_step, args, (self, seqs_a, n_a, slots_out, bt_out, lens_out))
+
     def slots(self, seq: int, start: int, n: int, out: Optional[np.ndarray] = None) -> np.ndarray:
         if out is None:
             out = np.empty(n, dtype=np.int64)

@@ -200,6 +200,25 @@ def test_workspace_and_descriptor_checks(pkv_lib):
     assert pkv.workspace_bytes(pkv.PoolDesc(pkv.PKV_BF16, 10, 16, 1, 128), 4, 32, 1, 100) == 0  # group 32
 
 
+def test_bound_prepare_step_matches_prepare_step(pkv_lib):
+    """The bound form (arguments marshalled once, outputs rewritten in place)
+    gives what repeated prepare_step calls give on an identical allocator."""
+    order = np.random.default_rng(5).permutation(200).astype(np.int32)
+    a, b = pkv.Allocator(200, 4, order), pkv.Allocator(200, 4, order)
+    sa = [a.seq_new() for _ in range(5)]
+    sb = [b.seq_new() for _ in range(5)]
+    n_new = [3, 1, 0, 7, 2]
+    slots, bt, lens = np.empty(13, np.int64), np.empty((5, 40), np.int32), np.empty(5, np.int32)
+    call = a.bind_prepare_step(sa, n_new, 40, slots, bt, lens)
+    for _ in range(6):
+        call()
+        e_slots, e_bt, e_lens = b.prepare_step(sb, n_new, 40)
+        assert slots.tolist() == e_slots.tolist()
+        assert np.array_equal(bt, e_bt) and lens.tolist() == e_lens.tolist()
+    with pytest.raises(pkv.PkvError):
+        a.bind_prepare_step(sa, n_new, 40, np.empty(3, np.int64), bt, lens)   # slots too small
+
+
 def test_int8_pool_layout_sizes(pkv_lib, golden):
     """INT8 pages cost head_dim + 4 bytes per vector (TileInfer.jl "INT8 cache":
     132 bytes instead of 256 at head_dim 128); a (page, head) block is padded
