@@ -31,13 +31,20 @@ notes):
   pushed last-logical-block first, so truncate followed by reserve hands back
   the same pages in the same order.
 * Every allocator call is all-or-nothing: on error the state is unchanged.
-* Writing a new position into a page that another sequence also references is
-  refused (``SharedPageWrite``); copy-on-write is not part of this model.
+* ``reserve`` refuses to write a new position into a page that another
+  sequence also references (``SharedPageWrite``).  ``reserve_cow`` is the
+  copy-on-write form ("KV Cache Management and PagedAttention", "Split shared
+  blocks when a write is needed", Figure 6): the writing sequence first gets
+  a fresh page holding a copy of the shared one (popped before any page the
+  growth needs), the shared page loses that reference, and the copy is
+  returned for the device to perform.  The whole page is copied.
+* ``fork`` makes an empty sequence reference every page of another one, the
+  partial last page included ("Share common KV across responses", Figure 5).
 """
 
 from __future__ import annotations
 
-from typing import Dict, List, Optional, Sequence
+from typing import Dict, List, Optional, Sequence, Tuple
 
 
 class AllocatorError(Exception):
@@ -184,6 +191,47 @@ class Allocator:
         self._tables[child] = list(pages)
         self._lens[child] = n_tokens
 
+    def fork(self, child: int, parent: int) -> None:
+        """Make an empty ``child`` reference all of the parent's pages (two
+        responses to one input share its blocks, the last partial one too)."""
+        self._check(child)
+        self._check(parent)
+        if child == parent:
+            raise InvalidArgument("child and parent must differ")
+        if self._lens[child] != 0:
+            raise InvalidArgument("child must be empty")
+        for page in self._tables[parent]:
+            self.refcount[page] += 1
+        self._tables[child] = list(self._tables[parent])
+        self._lens[child] = self._lens[parent]
+
+    def reserve_cow(self, seq: int, n: int) -> Optional[Tuple[int, int]]:
+        """reserve() with copy-on-write: when the first new position falls in
+        a partially filled page that other sequences also reference, ``seq``
+        first takes a fresh page, its table points there, and (shared page,
+        fresh page) is returned: the device must copy the shared page into the
+        fresh one before anything is written to it.  All-or-nothing."""
+        self._check(seq)
+        if n < 0:
+            raise InvalidArgument("n must be >= 0")
+        length = self._lens[seq]
+        table = self._tables[seq]
+        ps = self.page_size
+        copy_needed = n > 0 and length % ps != 0 and self.refcount[table[length // ps]] > 1
+        need = ceil_div(length + n, ps) - len(table) + (1 if copy_needed else 0)
+        if need > len(self._free):
+            raise OutOfPages(f"need {need} pages, {len(self._free)} free")
+        copy = None
+        if copy_needed:
+            shared = table[length // ps]
+            fresh = self._free.pop()
+            self.refcount[shared] -= 1
+            self.refcount[fresh] = 1
+            table[length // ps] = fresh
+            copy = (shared, fresh)
+        self.reserve(seq, n)
+        return copy
+
     def _check(self, seq: int) -> None:
         if seq not in self._tables:
             raise InvalidArgument(f"unknown sequence {seq}")
@@ -202,3 +250,11 @@ def store_rows(pool, slots: Sequence[int], rows) -> None:
         slot = int(slot)
         if 0 <= slot < limit:
             pool[slot // page_size, :, slot % page_size, :] = rows[t]
+
+
+def copy_pages(pool, copies: Sequence[Tuple[int, int]]) -> None:
+    """The device half of copy-on-write: page dst of ``pool`` (every KV head,
+    every offset) becomes a copy of page src, for each (src, dst)."""
+    for src, dst in copies:
+        pool[int(dst)] = pool[int(src)]
+
