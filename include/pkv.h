@@ -114,6 +114,26 @@ int pkv_release(pkv_alloc* a, int32_t seq);
  * one reference; nothing is copied (Quail docs "KV", "Execution"). */
 int pkv_share_prefix(pkv_alloc* a, int32_t child, int32_t parent, int32_t n_tokens);
 
+/* Make the empty sequence `child` reference every page of `parent`, its
+ * partially filled last page included, each page gaining one reference; the
+ * child's length becomes the parent's.  Two responses to one input then share
+ * the input's KV ("KV Cache Management and PagedAttention", "Share common KV
+ * across responses", Figure 5).  A later write into the shared partial page
+ * needs pkv_reserve_cow. */
+int pkv_fork(pkv_alloc* a, int32_t child, int32_t parent);
+
+/* pkv_reserve with copy-on-write ("KV Cache Management and PagedAttention",
+ * "Split shared blocks when a write is needed", Figure 6): when the first new
+ * position falls in a partially filled page that other sequences also
+ * reference, the sequence first takes a fresh page (popped before any page
+ * the growth needs), its block table points there, and the shared page loses
+ * this reference.  copy_out[0] = the shared page, copy_out[1] = the fresh
+ * one, *n_copies = 1; the caller must copy the page on the device
+ * (pkv_copy_pages) before storing into it.  Otherwise *n_copies = 0.  A
+ * shared page that is already full stays shared.  All-or-nothing:
+ * OUT_OF_PAGES (counting the copy's page) leaves the allocator unchanged. */
+int pkv_reserve_cow(pkv_alloc* a, int32_t seq, int32_t n, int32_t* copy_out, int32_t* n_copies);
+
 int pkv_seq_len(const pkv_alloc* a, int32_t seq, int32_t* len);
 int pkv_num_free(const pkv_alloc* a, int32_t* n);
 /* Reference count of one page (0 = free). */
@@ -226,6 +246,17 @@ size_t pkv_pool_bytes(const pkv_pool_desc* desc);
  * must be finite. */
 int pkv_store_kv(const pkv_pool_desc* desc, void* k_pool, void* v_pool, const void* k_new,
                  const void* v_new, const int64_t* slots, int32_t n_tokens, void* stream);
+
+/* The device half of copy-on-write: for each i < n_copies, page
+ * copies[2 i + 1] of both pools becomes a byte copy of page copies[2 i] (every
+ * KV head and offset; for PKV_I8 pools codes and scales).  copies: device
+ * int32 [n_copies][2] = (source, destination), as pkv_reserve_cow returns
+ * them.  A pair with a page outside [0, num_pages) or source == destination
+ * is skipped.  Destination pages must differ from each other and from every
+ * source page of the same call (pages fresh from pkv_reserve_cow do);
+ * otherwise the result is undefined. */
+int pkv_copy_pages(const pkv_pool_desc* desc, void* k_pool, void* v_pool, const int32_t* copies,
+                   int32_t n_copies, void* stream);
 
 /* Bytes of device workspace pkv_decode / pkv_prefill_append need for these
  * sizes (0 when a launch needs none).  Pass the same scalars to the call.

@@ -21,7 +21,7 @@ from ._lib import PKV_BF16, PKV_F32, PKV_I8  # noqa: F401
 
 __all__ = [
     "PkvError", "OutOfPagesError", "SharedPageError", "UnsupportedError",
-    "PoolDesc", "Allocator", "plan_prefix", "store_kv", "decode", "prefill_append",
+    "PoolDesc", "Allocator", "plan_prefix", "store_kv", "copy_pages", "decode", "prefill_append",
     "workspace_bytes", "validate_tables", "PKV_F32", "PKV_BF16", "PKV_I8",
     "BoundCall", "bind_store_kv", "bind_decode", "bind_prefill_append",
 ]
@@ -121,6 +121,19 @@ class Allocator:
 
     def share_prefix(self, child: int, parent: int, n_tokens: int) -> None:
         _check(self._L.pkv_share_prefix(self._h, child, parent, n_tokens))
+
+    def fork(self, child: int, parent: int) -> None:
+        """Empty ``child`` references all of ``parent``'s pages (pkv_fork)."""
+        _check(self._L.pkv_fork(self._h, child, parent))
+
+    def reserve_cow(self, seq: int, n: int) -> Optional[Tuple[int, int]]:
+        """pkv_reserve with copy-on-write: returns (shared page, fresh page)
+        when the device must copy a page before the new positions are stored
+        (copy_pages), else None."""
+        cp = (ctypes.c_int32 * 2)()
+        nc = ctypes.c_int32()
+        _check(self._L.pkv_reserve_cow(self._h, seq, n, cp, ctypes.byref(nc)))
+        return (cp[0], cp[1]) if nc.value else None
 
     def seq_len(self, seq: int) -> int:
         out = ctypes.c_int32()
@@ -356,6 +369,19 @@ def bind_store_kv(desc: PoolDesc, k_pool, v_pool, k_new, v_new, slots, stream=No
 def store_kv(desc: PoolDesc, k_pool, v_pool, k_new, v_new, slots, stream=None) -> None:
     """Scatter new K/V rows [T][Hkv][D] into the pools at int64 ``slots``."""
     bind_store_kv(desc, k_pool, v_pool, k_new, v_new, slots, stream)()
+
+
+def copy_pages(desc: PoolDesc, k_pool, v_pool, copies, stream=None) -> None:
+    """Copy whole pages in both pools: ``copies`` is a device int32 tensor
+    [n][2] of (source, destination) page ids (pkv_copy_pages)."""
+    import torch
+    pdt = desc.pool_torch_dtype()
+    n = int(copies.shape[0]) if copies.dim() == 2 else 0
+    if copies.dim() != 2 or copies.shape[1] != 2:
+        raise ValueError("copies must be [n][2]")
+    c_desc = desc.c()
+    _check(_lib.lib().pkv_copy_pages(ctypes.byref(c_desc), _dev(k_pool, "k_pool", pdt), _dev(v_pool, "v_pool", pdt),
+                                     _dev(copies, "copies", torch.int32), n, _stream(stream)))
 
 
 def workspace_bytes(desc: PoolDesc, n_seqs: int, num_q_heads: int, max_q_per_seq: int,

@@ -42,6 +42,9 @@ _SIGNATURES = {
     "pkv_truncate": (c_int, [c_void_p, c_int32, c_int32]),
     "pkv_release": (c_int, [c_void_p, c_int32]),
     "pkv_share_prefix": (c_int, [c_void_p, c_int32, c_int32, c_int32]),
+    "pkv_fork": (c_int, [c_void_p, c_int32, c_int32]),
+    "pkv_reserve_cow": (c_int, [c_void_p, c_int32, c_int32, i32p, i32p]),
+    "pkv_copy_pages": (c_int, [POINTER(PoolDescC), c_void_p, c_void_p, c_void_p, c_int32, c_void_p]),
     "pkv_seq_len": (c_int, [c_void_p, c_int32, i32p]),
     "pkv_num_free": (c_int, [c_void_p, i32p]),
     "pkv_page_refcount": (c_int, [c_void_p, c_int32, i32p]),

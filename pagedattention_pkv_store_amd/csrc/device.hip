@@ -1713,6 +1713,26 @@ __global__ __launch_bounds__(kThreads) void store_kv_i8_kernel(
   if (part == 0) *reinterpret_cast<float*>(head + static_cast<int64_t>(page_size) * D + 4 * off) = scale;
 }
 
+// Page copy for copy-on-write: one thread moves 16 bytes of one (source,
+// destination) pair in both pools; a page is num_kv_heads contiguous
+// (page, KV head) blocks, so a pair copies one contiguous run per pool.
+__global__ __launch_bounds__(kThreads) void copy_pages_kernel(char* __restrict__ k_pool, char* __restrict__ v_pool,
+                                                              const int32_t* __restrict__ copies, int32_t n_copies,
+                                                              int64_t page_chunks, int32_t num_pages) {
+  const int64_t idx = static_cast<int64_t>(blockIdx.x) * kThreads + threadIdx.x;
+  const int64_t pair = idx / (2 * page_chunks);
+  if (pair >= n_copies) return;
+  int64_t chunk = idx - pair * 2 * page_chunks;
+  const bool is_v = chunk >= page_chunks;
+  if (is_v) chunk -= page_chunks;
+  const int32_t src = copies[2 * pair];
+  const int32_t dst = copies[2 * pair + 1];
+  if (src < 0 || src >= num_pages || dst < 0 || dst >= num_pages || src == dst) return;
+  char* pool = is_v ? v_pool : k_pool;
+  const u32x4 x = *reinterpret_cast<const u32x4*>(pool + (static_cast<int64_t>(src) * page_chunks + chunk) * 16);
+  *reinterpret_cast<u32x4*>(pool + (static_cast<int64_t>(dst) * page_chunks + chunk) * 16) = x;
+}
+
 // ---------------------------------------------------------------------------
 // host-side launch planning
 // ---------------------------------------------------------------------------
@@ -2086,6 +2106,29 @@ int pkv_store_kv(const pkv_pool_desc* desc, void* k_pool, void* v_pool, const vo
   hipError_t err = hipGetLastError();
   if (err != hipSuccess)
     return fail(PKV_ERR_DEVICE, std::string("pkv_store_kv: launch failed: ") + hipGetErrorString(err));
+  return PKV_OK;
+}
+
+int pkv_copy_pages(const pkv_pool_desc* desc, void* k_pool, void* v_pool, const int32_t* copies,
+                   int32_t n_copies, void* stream) {
+  int rc = check_desc(desc, "pkv_copy_pages");
+  if (rc != PKV_OK) return rc;
+  if (n_copies < 0) return fail(PKV_ERR_INVALID_ARG, "pkv_copy_pages: n_copies < 0");
+  if (n_copies == 0) return PKV_OK;
+  if (!k_pool || !v_pool || !copies) return fail(PKV_ERR_INVALID_ARG, "pkv_copy_pages: NULL device pointer");
+  if (!aligned16(k_pool) || !aligned16(v_pool) || (reinterpret_cast<uintptr_t>(copies) & 3u))
+    return fail(PKV_ERR_INVALID_ARG, "pkv_copy_pages: misaligned device pointer");
+  const int64_t page_bytes = head_block_bytes(desc) * desc->num_kv_heads;   // a multiple of 16
+  const int64_t page_chunks = page_bytes / 16;
+  const int64_t blocks = (2 * page_chunks * n_copies + kThreads - 1) / kThreads;
+  if (blocks > INT32_MAX) return fail(PKV_ERR_UNSUPPORTED, "pkv_copy_pages: too many pages");
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  (void)hipGetLastError();
+  copy_pages_kernel<<<dim3(static_cast<unsigned>(blocks)), dim3(kThreads), 0, st>>>(
+      static_cast<char*>(k_pool), static_cast<char*>(v_pool), copies, n_copies, page_chunks, desc->num_pages);
+  hipError_t err = hipGetLastError();
+  if (err != hipSuccess)
+    return fail(PKV_ERR_DEVICE, std::string("pkv_copy_pages: launch failed: ") + hipGetErrorString(err));
   return PKV_OK;
 }
 

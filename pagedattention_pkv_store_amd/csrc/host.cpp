@@ -173,6 +173,51 @@ int pkv_share_prefix(pkv_alloc* a, int32_t child, int32_t parent, int32_t n_toke
   return PKV_OK;
 }
 
+int pkv_fork(pkv_alloc* a, int32_t child, int32_t parent) {
+  if (!a) return fail(PKV_ERR_INVALID_ARG, "pkv_fork: NULL allocator");
+  pkv_alloc::Seq* c = a->find(child);
+  const pkv_alloc::Seq* p = a->find(parent);
+  if (!c || !p) return fail(PKV_ERR_INVALID_ARG, "pkv_fork: unknown sequence");
+  if (child == parent) return fail(PKV_ERR_INVALID_ARG, "pkv_fork: child == parent");
+  if (c->len != 0) return fail(PKV_ERR_INVALID_ARG, "pkv_fork: child is not empty");
+  c->table = p->table;
+  for (int32_t page : c->table) ++a->refcount[page];
+  c->len = p->len;
+  return PKV_OK;
+}
+
+int pkv_reserve_cow(pkv_alloc* a, int32_t seq, int32_t n, int32_t* copy_out, int32_t* n_copies) {
+  if (!a) return fail(PKV_ERR_INVALID_ARG, "pkv_reserve_cow: NULL allocator");
+  if (!copy_out || !n_copies) return fail(PKV_ERR_INVALID_ARG, "pkv_reserve_cow: NULL output");
+  pkv_alloc::Seq* s = a->find(seq);
+  if (!s) return fail(PKV_ERR_INVALID_ARG, "pkv_reserve_cow: unknown sequence " + std::to_string(seq));
+  if (n < 0) return fail(PKV_ERR_INVALID_ARG, "pkv_reserve_cow: n < 0");
+  const int32_t ps = a->page_size;
+  const int64_t new_len = static_cast<int64_t>(s->len) + n;
+  if (new_len > INT32_MAX) return fail(PKV_ERR_INVALID_ARG, "pkv_reserve_cow: length overflows int32");
+  const bool copy = n > 0 && s->len % ps != 0 && a->refcount[s->table[s->len / ps]] > 1;
+  const int64_t need =
+      pkv_alloc::blocks_for(new_len, ps) - static_cast<int64_t>(s->table.size()) + (copy ? 1 : 0);
+  if (need > static_cast<int64_t>(a->free_stack.size()))
+    return fail(PKV_ERR_OUT_OF_PAGES, "pkv_reserve_cow: need " + std::to_string(need) + " pages, " +
+                                          std::to_string(a->free_stack.size()) + " free");
+  *n_copies = 0;
+  if (copy) {
+    // the writer takes a fresh page first; the shared one loses its reference
+    const size_t blk = static_cast<size_t>(s->len / ps);
+    const int32_t shared = s->table[blk];
+    const int32_t fresh = a->free_stack.back();
+    a->free_stack.pop_back();
+    --a->refcount[shared];
+    a->refcount[fresh] = 1;
+    s->table[blk] = fresh;
+    copy_out[0] = shared;
+    copy_out[1] = fresh;
+    *n_copies = 1;
+  }
+  return pkv_reserve(a, seq, n);   // cannot fail now: pages were counted above
+}
+
 int pkv_seq_len(const pkv_alloc* a, int32_t seq, int32_t* len) {
   if (!a || !len) return fail(PKV_ERR_INVALID_ARG, "pkv_seq_len: NULL argument");
   const pkv_alloc::Seq* s = a->find(seq);

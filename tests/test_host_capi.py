@@ -125,6 +125,48 @@ def test_allocator_matches_oracle_on_random_ops(pkv_lib, seed):
         _same_state(c, o, live)
 
 
+@pytest.mark.parametrize("seed", range(25))
+def test_copy_on_write_matches_oracle_on_random_ops(pkv_lib, seed):
+    """fork / reserve_cow / reserve / truncate / release through the C ABI
+    against the oracle, including the copies reported and OOM atomicity."""
+    rnd = random.Random(7000 + seed)
+    ps = rnd.choice([1, 3, 4, 16])
+    n = rnd.choice([10, 40])
+    order = rnd.sample(range(n), n)
+    c, o = _pair(n, ps, order)
+    live = []
+    for _ in range(250):
+        op_ = rnd.random()
+        if op_ < 0.1 or not live:
+            s_c, s_o = c.seq_new(), o.seq_new()
+            assert s_c == s_o
+            live.append(s_o)
+        elif op_ < 0.5:
+            s, k = rnd.choice(live), rnd.randrange(0, 2 * ps + 3)
+            res = _both(lambda: c.reserve_cow(s, k), lambda: o.reserve_cow(s, k))
+            if res != "err":
+                assert res[0] == res[1]         # the same copy, or none
+        elif op_ < 0.6:
+            s, k = rnd.choice(live), rnd.randrange(0, ps + 2)
+            _both(lambda: c.reserve(s, k), lambda: o.reserve(s, k))
+        elif op_ < 0.72:
+            s = rnd.choice(live)
+            k = rnd.randrange(0, o.seq_len(s) + 1)
+            _both(lambda: c.truncate(s, k), lambda: o.truncate(s, k))
+        elif op_ < 0.8:
+            s = rnd.choice(live)
+            _both(lambda: c.release(s), lambda: o.release(s))
+            live.remove(s)
+        else:
+            p = rnd.choice(live)
+            ch_c, ch_o = c.seq_new(), o.seq_new()
+            live.append(ch_o)
+            if rnd.random() < 0.2:           # a non-empty child is refused
+                _both(lambda: c.reserve(ch_c, 1), lambda: o.reserve(ch_o, 1))
+            _both(lambda: c.fork(ch_c, p), lambda: o.fork(ch_o, p))
+        _same_state(c, o, live)
+
+
 @pytest.mark.parametrize("seed", range(30))
 def test_planner_matches_oracle_random(pkv_lib, seed):
     rnd = random.Random(seed)
