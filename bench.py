@@ -83,6 +83,8 @@ def parse():
                     help="timed repetitions of the prefix-shared prefill leg (0 disables it)")
     ap.add_argument("--int8", type=int, default=1,
                     help="also time the decode batch on INT8 pages (1) or not (0)")
+    ap.add_argument("--copy-pairs", type=int, default=4096,
+                    help="page pairs of the copy-on-write page-copy leg (0 disables it)")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="finally copy a buffer of this many MiB three times (a plain copy of known "
                          "size, the reference for the FETCH_SIZE / WRITE_SIZE counters)")
@@ -197,6 +199,70 @@ def prefill_leg(args, torch, pkv, synth, dev: str) -> dict:
             "algorithmic_flops_per_launch": flops,
             "unmasked_pairs": pairs,
         },
+    }
+
+
+def copy_pages_leg(args, torch, pkv, dev: str) -> dict:
+    """Copy-on-write page copies: ``args.copy_pairs`` (shared, fresh) page
+    pairs drawn without repetition from a shuffled 32,768-page pool of the
+    decode shape (16 positions x 8 KV heads x 128, bf16), copied in K and V
+    by one pkv_copy_pages launch.  HBM bytes per launch = 2 pools x (read +
+    write) x 32 KiB x pairs."""
+    ps, hkv, D, num_pages = 16, 8, 128, 32_768
+    desc = pkv.PoolDesc(pkv.PKV_BF16, num_pages, ps, hkv, D)
+    k_pool, v_pool = desc.new_pools(dev, fill=1.0)
+    perm = np.random.default_rng(args.seed + 77).permutation(num_pages)[: 2 * args.copy_pairs]
+    copies = torch.from_numpy(perm.reshape(2, -1).T.copy().astype(np.int32)).to(dev)
+    for _ in range(3):
+        pkv.copy_pages(desc, k_pool, v_pool, copies)
+    torch.cuda.synchronize()
+    reps = 20
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
+    for a, b in evs:
+        a.record()
+        pkv.copy_pages(desc, k_pool, v_pool, copies)
+        b.record()
+    torch.cuda.synchronize()
+    ms = np.array([a.elapsed_time(b) for a, b in evs])
+    page_bytes = hkv * ps * D * 2
+    alg = 2 * 2 * page_bytes * args.copy_pairs
+    avg_s = float(ms.mean()) / 1e3
+    achieved = alg / avg_s / 1e9
+    del k_pool, v_pool
+    torch.cuda.empty_cache()
+    # context: torch's contiguous device-to-device copy reading and writing
+    # the same bytes (alg / 2 each way)
+    src = torch.ones(alg // 2, dtype=torch.uint8, device=dev)
+    dst = torch.empty_like(src)
+    dst.copy_(src)
+    torch.cuda.synchronize()
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
+    for a, b in evs:
+        a.record()
+        dst.copy_(src)
+        b.record()
+    torch.cuda.synchronize()
+    ref_s = float(np.mean([a.elapsed_time(b) for a, b in evs])) / 1e3
+    del src, dst
+    torch.cuda.empty_cache()
+    return {
+        "workload": f"copy-on-write page copies: {args.copy_pairs} distinct (shared, fresh) page pairs of a shuffled "
+                    "32,768-page bf16 pool (16 positions x 8 KV heads x 128), K and V, one pkv_copy_pages launch",
+        "pairs": args.copy_pairs,
+        "reps": reps,
+        "roofline": {
+            "bound": "hbm",
+            "achieved": round(achieved, 1),
+            "peak": HBM_PEAK_GBS,
+            "unit": "GB/s",
+            "frac": round(achieved / HBM_PEAK_GBS, 4),
+            "traffic": measured_traffic("copy_pages"),
+            "kernel": "pkv_copy_pages (copy_pages_kernel)",
+            "kernel_avg_us": round(avg_s * 1e6, 2),
+            "kernel_median_us": round(float(np.median(ms)) * 1e3, 2),
+            "algorithmic_bytes_per_launch": alg,
+        },
+        "contiguous_copy_same_bytes_gbs": round(alg / ref_s / 1e9, 1),
     }
 
 
@@ -456,6 +522,8 @@ def main():
                 "speedup_vs_bf16_kernel": round(d["dec_avg_s"] / d8["dec_avg_s"], 3),
             },
         }
+    if args.copy_pairs > 0:
+        rec["copy_pages"] = copy_pages_leg(args, torch, pkv, dev)
     if args.prefill_reps > 0:
         rec["prefill_append"] = prefill_leg(args, torch, pkv, synth, dev)
     if args.copy_calibration_mib > 0:

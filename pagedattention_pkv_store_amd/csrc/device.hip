@@ -538,6 +538,9 @@ __global__ __launch_bounds__(kThreads) void paged_attention_kernel(AttnArgs args
 #ifndef PKV_DECODE_WAVES
 #define PKV_DECODE_WAVES 1024          // one-wave workgroups (4 per CU)
 #endif
+#ifndef PKV_COPY_CHUNKS
+#define PKV_COPY_CHUNKS 1              // 16-byte chunks per thread of the page copy
+#endif
 #ifndef PKV_DECODE_MIN_BLOCKS
 #define PKV_DECODE_MIN_BLOCKS 4        // smallest range of a wave, in blocks
 #endif
@@ -1713,24 +1716,37 @@ __global__ __launch_bounds__(kThreads) void store_kv_i8_kernel(
   if (part == 0) *reinterpret_cast<float*>(head + static_cast<int64_t>(page_size) * D + 4 * off) = scale;
 }
 
-// Page copy for copy-on-write: one thread moves 16 bytes of one (source,
-// destination) pair in both pools; a page is num_kv_heads contiguous
-// (page, KV head) blocks, so a pair copies one contiguous run per pool.
+// Page copy for copy-on-write.  A page is num_kv_heads contiguous (page, KV
+// head) blocks, so a (source, destination) pair copies one contiguous run per
+// pool.  Grid: x = pair (its page ids are scalar loads), y = a tile of
+// kCopyPer * 256 of the pair's 16-byte chunks (K chunks, then V chunks); each
+// thread issues its kCopyPer loads before its stores.
+constexpr int kCopyPer = PKV_COPY_CHUNKS;
 __global__ __launch_bounds__(kThreads) void copy_pages_kernel(char* __restrict__ k_pool, char* __restrict__ v_pool,
-                                                              const int32_t* __restrict__ copies, int32_t n_copies,
-                                                              int64_t page_chunks, int32_t num_pages) {
-  const int64_t idx = static_cast<int64_t>(blockIdx.x) * kThreads + threadIdx.x;
-  const int64_t pair = idx / (2 * page_chunks);
-  if (pair >= n_copies) return;
-  int64_t chunk = idx - pair * 2 * page_chunks;
-  const bool is_v = chunk >= page_chunks;
-  if (is_v) chunk -= page_chunks;
+                                                              const int32_t* __restrict__ copies, int32_t page_chunks,
+                                                              int32_t num_pages) {
+  const int64_t pair = blockIdx.x;
   const int32_t src = copies[2 * pair];
   const int32_t dst = copies[2 * pair + 1];
   if (src < 0 || src >= num_pages || dst < 0 || dst >= num_pages || src == dst) return;
-  char* pool = is_v ? v_pool : k_pool;
-  const u32x4 x = *reinterpret_cast<const u32x4*>(pool + (static_cast<int64_t>(src) * page_chunks + chunk) * 16);
-  *reinterpret_cast<u32x4*>(pool + (static_cast<int64_t>(dst) * page_chunks + chunk) * 16) = x;
+  const int c0 = static_cast<int>(blockIdx.y) * kThreads * kCopyPer + threadIdx.x;
+  u32x4 x[kCopyPer];
+#pragma unroll
+  for (int j = 0; j < kCopyPer; ++j) {
+    const int c = c0 + j * kThreads;
+    if (c >= 2 * page_chunks) continue;
+    const bool is_v = c >= page_chunks;
+    const char* pool = is_v ? v_pool : k_pool;
+    x[j] = *reinterpret_cast<const u32x4*>(pool + (static_cast<int64_t>(src) * page_chunks + (is_v ? c - page_chunks : c)) * 16);
+  }
+#pragma unroll
+  for (int j = 0; j < kCopyPer; ++j) {
+    const int c = c0 + j * kThreads;
+    if (c >= 2 * page_chunks) continue;
+    const bool is_v = c >= page_chunks;
+    char* pool = is_v ? v_pool : k_pool;
+    *reinterpret_cast<u32x4*>(pool + (static_cast<int64_t>(dst) * page_chunks + (is_v ? c - page_chunks : c)) * 16) = x[j];
+  }
 }
 
 // ---------------------------------------------------------------------------
@@ -2120,12 +2136,15 @@ int pkv_copy_pages(const pkv_pool_desc* desc, void* k_pool, void* v_pool, const 
     return fail(PKV_ERR_INVALID_ARG, "pkv_copy_pages: misaligned device pointer");
   const int64_t page_bytes = head_block_bytes(desc) * desc->num_kv_heads;   // a multiple of 16
   const int64_t page_chunks = page_bytes / 16;
-  const int64_t blocks = (2 * page_chunks * n_copies + kThreads - 1) / kThreads;
-  if (blocks > INT32_MAX) return fail(PKV_ERR_UNSUPPORTED, "pkv_copy_pages: too many pages");
+  const int64_t per_block = static_cast<int64_t>(kThreads) * kCopyPer;
+  const int64_t tiles = (2 * page_chunks + per_block - 1) / per_block;
+  if (page_chunks > INT32_MAX / 4 || tiles > 65535)
+    return fail(PKV_ERR_UNSUPPORTED, "pkv_copy_pages: pages too large");
   hipStream_t st = static_cast<hipStream_t>(stream);
   (void)hipGetLastError();
-  copy_pages_kernel<<<dim3(static_cast<unsigned>(blocks)), dim3(kThreads), 0, st>>>(
-      static_cast<char*>(k_pool), static_cast<char*>(v_pool), copies, n_copies, page_chunks, desc->num_pages);
+  copy_pages_kernel<<<dim3(static_cast<unsigned>(n_copies), static_cast<unsigned>(tiles)), dim3(kThreads), 0, st>>>(
+      static_cast<char*>(k_pool), static_cast<char*>(v_pool), copies, static_cast<int32_t>(page_chunks),
+      desc->num_pages);
   hipError_t err = hipGetLastError();
   if (err != hipSuccess)
     return fail(PKV_ERR_DEVICE, std::string("pkv_copy_pages: launch failed: ") + hipGetErrorString(err));
