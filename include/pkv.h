@@ -57,9 +57,9 @@ enum {
   PKV_ERR_UNSUPPORTED = -3,      /* dtype / head_dim / page_size / head counts not built */
   PKV_ERR_DEVICE = -4,           /* a HIP launch failed */
   PKV_ERR_BUFFER_TOO_SMALL = -5, /* workspace or output array too small */
-  PKV_ERR_SHARED_PAGE = -6       /* a reserve would write into a page another
-                                    sequence references (copy-on-write is not
-                                    provided) */
+  PKV_ERR_SHARED_PAGE = -6       /* pkv_reserve would write into a page another
+                                    sequence references (pkv_reserve_cow copies
+                                    the page instead) */
 };
 
 /* Message describing the last failing call on this thread ("" if none). */
@@ -95,7 +95,8 @@ int pkv_seq_new(pkv_alloc* a, int32_t* seq_out);
 /* Extend a sequence by n positions (n >= 0), popping a page from the free
  * stack only when the last page is full.  All-or-nothing: OUT_OF_PAGES when
  * fewer pages are free than needed; SHARED_PAGE when position len would be
- * written into a partially filled page whose reference count exceeds 1. */
+ * written into a partially filled page whose reference count exceeds 1 (see
+ * pkv_reserve_cow). */
 int pkv_reserve(pkv_alloc* a, int32_t seq, int32_t n);
 
 /* Keep the first n_keep positions (0 <= n_keep <= len).  Pages of logical

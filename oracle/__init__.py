@@ -30,6 +30,10 @@ accounting  closed forms for KV bytes per position and per layer (TileInfer.jl
             section 2.2 eq. (7)).
 
 Pinning status (what each function is checked against, in ``tests/``):
+  paging      copy-on-write (fork, reserve_cow, copy_pages): the blog's Figure 6
+              walk-through (golden fixture), the full-shared-block rule,
+              all-or-nothing, and every forked response reading exactly its
+              prompt and its own tokens after random writes and page copies.
   paging      the worked example of "KV Cache Management and PagedAttention"
               (block counts; B in physical blocks 3, 0 and C in 1, 4; growth
               into block 5),
