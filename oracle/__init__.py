@@ -23,6 +23,9 @@ planner     the sorted-adjacent-document prefix-sharing plan (Quail docs "KV",
 attention   softmax attention over a sequence's logical K/V, gathered through
             the block table ("KV Cache Management and PagedAttention",
             "Compute attention over scattered KV", Figure 4).
+retention   the KV retention pool: priority = probability_of_reuse *
+            recompute_seconds / pages, lowest evicted first (Quail docs "KV",
+            "KV retention").
 quant       INT8 KV pages: per-vector symmetric codes and fp32 scales, and
             attention over them (TileInfer.jl "KV cache", "INT8 cache").
 accounting  closed forms for KV bytes per position and per layer (TileInfer.jl
@@ -46,6 +49,9 @@ Pinning status (what each function is checked against, in ``tests/``):
               invariant: the pages' example never walks a link.
   attention   closed forms, fp64 SDPA library special case, scalar brute force,
               permutation invariance.
+  retention   hand-worked priorities and eviction orders from the page's
+              formula; ties, per-page value, take-back, shared pages
+              surviving, the two-forward-pass limit.
   quant       hand-worked codes from the page's rule (incl. the ties-to-even
               reading), zero vector, peak code +-127, the symmetric error
               bound, placement by slot, brute force of the page's folded-scale
@@ -54,4 +60,4 @@ Pinning status (what each function is checked against, in ``tests/``):
               figures.
 """
 
-from . import accounting, attention, paging, planner, quant  # noqa: F401
+from . import accounting, attention, paging, planner, quant, retention  # noqa: F401
