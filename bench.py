@@ -85,6 +85,8 @@ def parse():
                     help="also time the decode batch on INT8 pages (1) or not (0)")
     ap.add_argument("--copy-pairs", type=int, default=4096,
                     help="page pairs of the copy-on-write page-copy leg (0 disables it)")
+    ap.add_argument("--retention-docs", type=int, default=100_000,
+                    help="documents of the host retention-pool leg (0 disables it)")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="finally copy a buffer of this many MiB three times (a plain copy of known "
                          "size, the reference for the FETCH_SIZE / WRITE_SIZE counters)")
@@ -263,6 +265,38 @@ def copy_pages_leg(args, torch, pkv, dev: str) -> dict:
             "algorithmic_bytes_per_launch": alg,
         },
         "contiguous_copy_same_bytes_gbs": round(alg / ref_s / 1e9, 1),
+    }
+
+
+def retention_leg(args, pkv) -> dict:
+    """Host-side KV retention pool: ``args.retention_docs`` documents of
+    U{1..64} pages (page size 16) retained with probability_of_reuse ~
+    U[0, 1) and recompute_seconds ~ U[0.01, 1), then one eviction down to
+    half of their pages (lowest probability * seconds / pages first)."""
+    n = args.retention_docs
+    rng = np.random.default_rng(args.seed + 99)
+    pages = rng.integers(1, 65, size=n)
+    prob = rng.random(n)
+    secs = 0.01 + 0.99 * rng.random(n)
+    alloc = pkv.Allocator(int(pages.sum()), 16)
+    seqs = [alloc.seq_new() for _ in range(n)]
+    for s_, p_ in zip(seqs, pages.tolist()):
+        alloc.reserve(s_, 16 * p_)
+    t0 = time.perf_counter()
+    for s_, p_, t_ in zip(seqs, prob.tolist(), secs.tolist()):
+        alloc.retention_add(s_, p_, t_)
+    add_s = time.perf_counter() - t0
+    total = alloc.retention_pages()
+    t0 = time.perf_counter()
+    evicted = alloc.retention_evict(total // 2)
+    evict_s = time.perf_counter() - t0
+    return {
+        "workload": f"host KV retention pool: {n} documents of U{{1..64}} pages, evicted to half their "
+                    "pages in one pkv_retention_evict call",
+        "retained_pages": int(total),
+        "evicted_docs": int(evicted.size),
+        "evict_ms": round(evict_s * 1e3, 3),
+        "add_us_per_doc_incl_python": round(add_s / n * 1e6, 3),
     }
 
 
@@ -524,6 +558,8 @@ def main():
         }
     if args.copy_pairs > 0:
         rec["copy_pages"] = copy_pages_leg(args, torch, pkv, dev)
+    if args.retention_docs > 0:
+        rec["retention"] = retention_leg(args, pkv)
     if args.prefill_reps > 0:
         rec["prefill_append"] = prefill_leg(args, torch, pkv, synth, dev)
     if args.copy_calibration_mib > 0:

@@ -135,6 +135,39 @@ int pkv_fork(pkv_alloc* a, int32_t child, int32_t parent);
  * OUT_OF_PAGES (counting the copy's page) leaves the allocator unchanged. */
 int pkv_reserve_cow(pkv_alloc* a, int32_t seq, int32_t n, int32_t* copy_out, int32_t* n_copies);
 
+/* ---------------------------------------------------------------------------
+ * KV retention pool (on the allocator)
+ *
+ * Source: Quail docs "KV", section "KV retention".  KV that a later consumer
+ * may reuse is retained within a memory limit; when the pool is over its
+ * limit the KV with the lowest priority = probability_of_reuse *
+ * recompute_seconds / pages (estimated compute saved per page) is removed
+ * first, and a consumer that finds its KV removed computes it again.  Here a
+ * retained unit is a sequence; `pages` is its page count when it enters the
+ * pool; equal priorities leave in entry order; removal is pkv_release.
+ * ------------------------------------------------------------------------- */
+
+/* Retain a live, non-empty sequence (not already retained).  INVALID_ARG for
+ * a negative or non-finite probability or time.  The caller keeps the
+ * sequence unchanged while it is retained. */
+int pkv_retention_add(pkv_alloc* a, int32_t seq, double probability_of_reuse, double recompute_seconds);
+
+/* Release lowest-priority retained sequences until the retained page count
+ * is at most limit_pages (the caller's limit: for instance the pool's pages
+ * minus the pages two forward passes need).  Their ids go to evicted[],
+ * eviction order, and their count to *n_evicted.  All-or-nothing:
+ * BUFFER_TOO_SMALL when more than max_evicted would leave. */
+int pkv_retention_evict(pkv_alloc* a, int64_t limit_pages, int32_t* evicted, int32_t max_evicted,
+                        int32_t* n_evicted);
+
+/* A consumer reuses `seq`: *available = 1 when its KV is still retained (it
+ * leaves the pool and stays live), 0 when it was evicted or never retained
+ * (the consumer recomputes it). */
+int pkv_retention_take(pkv_alloc* a, int32_t seq, int32_t* available);
+
+/* Sum of the retained sequences' page counts. */
+int pkv_retention_pages(const pkv_alloc* a, int64_t* pages);
+
 int pkv_seq_len(const pkv_alloc* a, int32_t seq, int32_t* len);
 int pkv_num_free(const pkv_alloc* a, int32_t* n);
 /* Reference count of one page (0 = free). */

@@ -135,6 +135,30 @@ class Allocator:
         _check(self._L.pkv_reserve_cow(self._h, seq, n, cp, ctypes.byref(nc)))
         return (cp[0], cp[1]) if nc.value else None
 
+    # -- KV retention pool -------------------------------------------------
+    def retention_add(self, seq: int, probability_of_reuse: float, recompute_seconds: float) -> None:
+        _check(self._L.pkv_retention_add(self._h, seq, float(probability_of_reuse), float(recompute_seconds)))
+
+    def retention_evict(self, limit_pages: int, max_evicted: Optional[int] = None) -> np.ndarray:
+        """Release lowest-priority retained sequences until at most limit_pages
+        remain retained; returns their ids in eviction order."""
+        cap = self.retention_pages() if max_evicted is None else max_evicted
+        out = np.empty(max(1, cap), np.int32)
+        n = ctypes.c_int32()
+        _check(self._L.pkv_retention_evict(self._h, int(limit_pages), _ptr(out, ctypes.c_int32), cap,
+                                           ctypes.byref(n)))
+        return out[: n.value]
+
+    def retention_take(self, seq: int) -> bool:
+        avail = ctypes.c_int32()
+        _check(self._L.pkv_retention_take(self._h, seq, ctypes.byref(avail)))
+        return bool(avail.value)
+
+    def retention_pages(self) -> int:
+        n = ctypes.c_int64()
+        _check(self._L.pkv_retention_pages(self._h, ctypes.byref(n)))
+        return n.value
+
     def seq_len(self, seq: int) -> int:
         out = ctypes.c_int32()
         _check(self._L.pkv_seq_len(self._h, seq, ctypes.byref(out)))

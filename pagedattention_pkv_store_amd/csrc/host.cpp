@@ -16,9 +16,12 @@
 // and produces the int32/int64 arrays the kernels consume.
 
 #include <algorithm>
+#include <cmath>
 #include <cstdint>
 #include <numeric>
+#include <set>
 #include <string>
+#include <tuple>
 #include <vector>
 
 #include "../../include/pkv.h"
@@ -48,6 +51,21 @@ struct pkv_alloc {
   std::vector<int32_t> free_stack;  // top = back()
   std::vector<int32_t> refcount;
   std::vector<Seq> seqs;            // index = sequence id
+
+  // KV retention pool: (priority, entry order, sequence), lowest first, and
+  // each retained sequence's page count at entry (0 = not retained).
+  std::set<std::tuple<double, int64_t, int32_t>> retained;
+  std::vector<int32_t> ret_pages_of;
+  std::vector<std::pair<double, int64_t>> ret_key_of;
+  int64_t ret_pages = 0;
+  int64_t ret_order = 0;
+  void retention_drop(int32_t seq) {
+    if (seq < static_cast<int32_t>(ret_pages_of.size()) && ret_pages_of[seq] > 0) {
+      retained.erase(std::make_tuple(ret_key_of[seq].first, ret_key_of[seq].second, seq));
+      ret_pages -= ret_pages_of[seq];
+      ret_pages_of[seq] = 0;
+    }
+  }
 
   const Seq* find(int32_t id) const {
     if (id < 0 || id >= static_cast<int32_t>(seqs.size()) || !seqs[id].live) return nullptr;
@@ -151,6 +169,7 @@ int pkv_truncate(pkv_alloc* a, int32_t seq, int32_t n_keep) {
 int pkv_release(pkv_alloc* a, int32_t seq) {
   int rc = pkv_truncate(a, seq, 0);
   if (rc != PKV_OK) return rc;
+  a->retention_drop(seq);
   a->seqs[seq].live = false;
   a->seqs[seq].table.shrink_to_fit();
   return PKV_OK;
@@ -216,6 +235,66 @@ int pkv_reserve_cow(pkv_alloc* a, int32_t seq, int32_t n, int32_t* copy_out, int
     *n_copies = 1;
   }
   return pkv_reserve(a, seq, n);   // cannot fail now: pages were counted above
+}
+
+int pkv_retention_add(pkv_alloc* a, int32_t seq, double probability_of_reuse, double recompute_seconds) {
+  if (!a) return fail(PKV_ERR_INVALID_ARG, "pkv_retention_add: NULL allocator");
+  const pkv_alloc::Seq* s = a->find(seq);
+  if (!s) return fail(PKV_ERR_INVALID_ARG, "pkv_retention_add: unknown sequence " + std::to_string(seq));
+  if (seq < static_cast<int32_t>(a->ret_pages_of.size()) && a->ret_pages_of[seq] > 0)
+    return fail(PKV_ERR_INVALID_ARG, "pkv_retention_add: sequence already retained");
+  if (s->table.empty()) return fail(PKV_ERR_INVALID_ARG, "pkv_retention_add: an empty sequence holds no KV");
+  if (!(probability_of_reuse >= 0.0) || !(recompute_seconds >= 0.0) || !std::isfinite(probability_of_reuse) ||
+      !std::isfinite(recompute_seconds))
+    return fail(PKV_ERR_INVALID_ARG, "pkv_retention_add: probability and seconds must be finite and >= 0");
+  const int32_t pages = static_cast<int32_t>(s->table.size());
+  const double prio = probability_of_reuse * recompute_seconds / pages;   // saving per page
+  if (a->ret_pages_of.size() < a->seqs.size()) {
+    a->ret_pages_of.resize(a->seqs.size(), 0);
+    a->ret_key_of.resize(a->seqs.size());
+  }
+  const int64_t order = a->ret_order++;
+  a->retained.emplace(prio, order, seq);
+  a->ret_key_of[seq] = {prio, order};
+  a->ret_pages_of[seq] = pages;
+  a->ret_pages += pages;
+  return PKV_OK;
+}
+
+int pkv_retention_evict(pkv_alloc* a, int64_t limit_pages, int32_t* evicted, int32_t max_evicted,
+                        int32_t* n_evicted) {
+  if (!a || !n_evicted) return fail(PKV_ERR_INVALID_ARG, "pkv_retention_evict: NULL argument");
+  if (limit_pages < 0 || max_evicted < 0) return fail(PKV_ERR_INVALID_ARG, "pkv_retention_evict: negative size");
+  // choose first, so a too-small output array leaves everything unchanged
+  std::vector<int32_t> chosen;
+  int64_t pages = a->ret_pages;
+  for (auto it = a->retained.begin(); it != a->retained.end() && pages > limit_pages; ++it) {
+    const int32_t seq = std::get<2>(*it);
+    chosen.push_back(seq);
+    pages -= a->ret_pages_of[seq];
+  }
+  if (static_cast<int64_t>(chosen.size()) > max_evicted || (!chosen.empty() && !evicted))
+    return fail(PKV_ERR_BUFFER_TOO_SMALL, "pkv_retention_evict: " + std::to_string(chosen.size()) +
+                                              " sequences to evict");
+  for (size_t i = 0; i < chosen.size(); ++i) {
+    evicted[i] = chosen[i];
+    pkv_release(a, chosen[i]);   // drops it from the pool too
+  }
+  *n_evicted = static_cast<int32_t>(chosen.size());
+  return PKV_OK;
+}
+
+int pkv_retention_take(pkv_alloc* a, int32_t seq, int32_t* available) {
+  if (!a || !available) return fail(PKV_ERR_INVALID_ARG, "pkv_retention_take: NULL argument");
+  *available = (seq >= 0 && seq < static_cast<int32_t>(a->ret_pages_of.size()) && a->ret_pages_of[seq] > 0) ? 1 : 0;
+  if (*available) a->retention_drop(seq);
+  return PKV_OK;
+}
+
+int pkv_retention_pages(const pkv_alloc* a, int64_t* pages) {
+  if (!a || !pages) return fail(PKV_ERR_INVALID_ARG, "pkv_retention_pages: NULL argument");
+  *pages = a->ret_pages;
+  return PKV_OK;
 }
 
 int pkv_seq_len(const pkv_alloc* a, int32_t seq, int32_t* len) {

@@ -167,6 +167,57 @@ def test_copy_on_write_matches_oracle_on_random_ops(pkv_lib, seed):
         _same_state(c, o, live)
 
 
+@pytest.mark.parametrize("seed", range(20))
+def test_retention_pool_matches_oracle_on_random_ops(pkv_lib, seed):
+    """pkv_retention_add / evict / take (and release of retained sequences)
+    against the oracle's retention pool: same evictions in the same order,
+    same takes, same allocator state."""
+    from oracle.retention import RetentionPool
+    rnd = random.Random(9000 + seed)
+    ps = rnd.choice([1, 4, 16])
+    n = 120
+    order = rnd.sample(range(n), n)
+    c, o = _pair(n, ps, order)
+    pool = RetentionPool(o)
+    live = []
+    for _ in range(200):
+        op_ = rnd.random()
+        if op_ < 0.3 or not live:
+            s_c, s_o = c.seq_new(), o.seq_new()
+            k = rnd.randrange(1, 4 * ps + 2)
+            if _both(lambda: c.reserve(s_c, k), lambda: o.reserve(s_o, k)) == "err":
+                continue
+            live.append(s_o)
+            # coarse values make exact priority ties common
+            p, t = rnd.choice([0.0, 0.25, 0.5, 1.0]), rnd.choice([0.5, 1.0, 2.0])
+            _both(lambda: c.retention_add(s_c, p, t), lambda: pool.add(s_o, p, t))
+        elif op_ < 0.5:
+            limit = rnd.randrange(0, max(1, pool.pages() + 2))
+            res = _both(lambda: c.retention_evict(limit).tolist(), lambda: pool.evict(limit))
+            assert res != "err" and res[0] == res[1]
+            for s in res[1]:
+                live.remove(s)
+        elif op_ < 0.65:
+            s = rnd.choice(live)
+            assert c.retention_take(s) == pool.take(s)
+        elif op_ < 0.75:
+            s = rnd.choice(live)
+            pool.take(s)                      # the oracle pool forgets a released sequence
+            _both(lambda: c.release(s), lambda: o.release(s))
+            live.remove(s)
+        else:
+            s, k = rnd.choice(live), rnd.randrange(0, ps + 2)
+            if s not in pool.retained():      # retained sequences stay unchanged
+                _both(lambda: c.reserve(s, k), lambda: o.reserve(s, k))
+        assert c.retention_pages() == pool.pages()
+        _same_state(c, o, live)
+    if pool.pages() > 0:                      # all-or-nothing when the output array is too small
+        with pytest.raises(pkv.BufferTooSmallError):
+            c.retention_evict(0, max_evicted=0)
+        assert c.retention_pages() == pool.pages()
+        _same_state(c, o, live)
+
+
 @pytest.mark.parametrize("seed", range(30))
 def test_planner_matches_oracle_random(pkv_lib, seed):
     rnd = random.Random(seed)
