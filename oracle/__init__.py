@@ -28,6 +28,8 @@ retention   the KV retention pool: priority = probability_of_reuse *
             "KV retention").
 quant       INT8 KV pages: per-vector symmetric codes and fp32 scales, and
             attention over them (TileInfer.jl "KV cache", "INT8 cache").
+codec       group-wise Q8/Q4 KV codec: groups of 64, fp16 scales, packed
+            payloads (ReKV section 2.2).
 accounting  closed forms for KV bytes per position and per layer (TileInfer.jl
             "Sizing" table and "INT8 cache"; ReKV section 2.1 eqs. (1)-(2) and
             section 2.2 eq. (7)).
@@ -56,8 +58,11 @@ Pinning status (what each function is checked against, in ``tests/``):
               reading), zero vector, peak code +-127, the symmetric error
               bound, placement by slot, brute force of the page's folded-scale
               formulation, page-placement invariance.
+  codec       payload size = eq. (7) and the page's 8.25 / 179.75 / 231 MiB
+              figures; hand-worked Q8 and Q4 groups (ties, nibble order);
+              the error bound; zero groups; pack/unpack and layout inverses.
   accounting  every cell of the TileInfer.jl sizing table and the ReKV byte
               figures.
 """
 
-from . import accounting, attention, paging, planner, quant, retention  # noqa: F401
+from . import accounting, attention, codec, paging, planner, quant, retention  # noqa: F401
