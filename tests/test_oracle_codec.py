@@ -5,8 +5,8 @@
   layer, 179.75 MiB for a 15-layer Q8 prefix plus the 56 MiB boundary, 231 MiB
   for all 28 layers (tests/golden/rekv_bytes.json).
 * Codes worked out by hand from the reading (symmetric groups of 64, fp16
-  scale = max|x| / q_max, codes from the stored scale, ties to even, Q4 low
-  nibble first).
+  scale = max|x| / q_max, codes from the stored scale's fp32 reciprocal, ties
+  to even, Q4 low nibble first).
 * The symmetric quantizer's error bound, zero groups, pack/unpack inverses,
   and the payload layout decoding back to the same values.
 """
@@ -40,7 +40,8 @@ def test_payload_size_is_eq7_and_the_pages_figures(golden):
 
 def test_q8_hand_worked_group():
     # max|x| = fp32(1.27); / 127 = 0.0099999998 -> fp16 0.01000213623046875;
-    # 1.27 / s = 126.97 -> 127, -0.5 / s = -49.99 -> -50, 0.02 / s = 2.00 -> 2
+    # 1 / s = 99.9786; 1.27 * that = 126.97 -> 127, -0.5 * = -49.99 -> -50,
+    # 0.02 * = 2.00 -> 2
     x = np.zeros(64, np.float32)
     x[:3] = [1.27, -0.5, 0.02]
     codes, scales = quantize_groups(x, 8)
