@@ -85,6 +85,7 @@ def parse():
                     help="also time the decode batch on INT8 pages (1) or not (0)")
     ap.add_argument("--copy-pairs", type=int, default=4096,
                     help="page pairs of the copy-on-write page-copy leg (0 disables it)")
+    ap.add_argument("--codec", type=int, default=1, help="time the Q8 / Q4 KV codec leg (1) or not (0)")
     ap.add_argument("--retention-docs", type=int, default=100_000,
                     help="documents of the host retention-pool leg (0 disables it)")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
@@ -266,6 +267,53 @@ def copy_pages_leg(args, torch, pkv, dev: str) -> dict:
         },
         "contiguous_copy_same_bytes_gbs": round(alg / ref_s / 1e9, 1),
     }
+
+
+def codec_leg(args, torch, pkv, dev: str) -> dict:
+    """Group-wise Q8 / Q4 codec of one long prefix: 131,072 positions of 8 KV
+    heads x 128 (bf16, 16-position pages scattered over a shuffled pool),
+    encoded into a payload and restored into other scattered pages.  HBM
+    bytes: encode reads the K/V (2 x n x 8 x 128 x 2) and writes the payload;
+    restore reads the payload and writes the K/V."""
+    n, hkv, D, ps = 131_072, 8, 128, 16
+    pages = n // ps
+    num_pages = 2 * pages + 64
+    desc = pkv.PoolDesc(pkv.PKV_BF16, num_pages, ps, hkv, D)
+    k_pool, v_pool = desc.new_pools(dev)
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(args.seed + 5)
+    k_pool.normal_(generator=gen)
+    v_pool.normal_(generator=gen)
+    order = np.random.default_rng(args.seed + 6).permutation(num_pages).astype(np.int32)
+    src_bt = torch.from_numpy(order[:pages].copy()).to(dev)
+    dst_bt = torch.from_numpy(order[pages:2 * pages].copy()).to(dev)
+    kv_bytes = 2 * n * hkv * D * 2
+    out = {"workload": "one 131,072-position prefix, 8 KV heads x 128, bf16, 16-position pages scattered over a "
+                       "shuffled pool: encode into a packed payload (groups of 64, fp16 scales) and restore into "
+                       "other scattered pages"}
+    reps = 20
+    for bits in (8, 4):
+        pay = torch.empty(pkv.codec_payload_bytes(n, hkv, D, bits), dtype=torch.uint8, device=dev)
+        res = {}
+        for name, call in (("encode", lambda: pkv.codec_encode(desc, k_pool, v_pool, src_bt, n, bits, pay)),
+                           ("restore", lambda: pkv.codec_decode(desc, k_pool, v_pool, dst_bt, n, bits, pay))):
+            call()
+            torch.cuda.synchronize()
+            evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
+            for a, b in evs:
+                a.record()
+                call()
+                b.record()
+            torch.cuda.synchronize()
+            t = float(np.mean([a.elapsed_time(b) for a, b in evs])) / 1e3
+            alg = kv_bytes + pay.numel()
+            res[name] = {"kernel_avg_us": round(t * 1e6, 2), "achieved_gbs": round(alg / t / 1e9, 1),
+                         "frac": round(alg / t / 1e9 / HBM_PEAK_GBS, 4), "algorithmic_bytes_per_launch": alg}
+        out[f"q{bits}"] = res
+        del pay
+    del k_pool, v_pool
+    torch.cuda.empty_cache()
+    return out
 
 
 def retention_leg(args, pkv) -> dict:
@@ -558,6 +606,8 @@ def main():
         }
     if args.copy_pairs > 0:
         rec["copy_pages"] = copy_pages_leg(args, torch, pkv, dev)
+    if args.codec:
+        rec["kv_codec"] = codec_leg(args, torch, pkv, dev)
     if args.retention_docs > 0:
         rec["retention"] = retention_leg(args, pkv)
     if args.prefill_reps > 0:

@@ -292,6 +292,38 @@ int pkv_store_kv(const pkv_pool_desc* desc, void* k_pool, void* v_pool, const vo
 int pkv_copy_pages(const pkv_pool_desc* desc, void* k_pool, void* v_pool, const int32_t* copies,
                    int32_t n_copies, void* stream);
 
+/* ---------------------------------------------------------------------------
+ * Group-wise low-bit KV codec (ReKV, section 2.2: the prefix KV is quantized
+ * in groups of 64 elements along the last dimension and sent as packed codes
+ * with one FP16 scale per group, eq. (7); the receiver dequantizes it)
+ *
+ * Symmetric groups: scale = fp16(max|x| / q_max), q_max = 127 (bits 8) or 7
+ * (bits 4); code = x * (1 / scale) rounded to nearest (ties to even) in
+ * fp32, one reciprocal per group, clamped to [-q_max, q_max]; a zero scale
+ * gives zero codes.  Restoring
+ * writes bf16(scale * code).  Payload: the codes of K then V (position,
+ * KV head, element order; bits 8: one byte each; bits 4: two's-complement
+ * nibbles, element 2i in the low nibble of byte i), then the fp16 scales of
+ * K then V in the same order.  bf16 pools; head_dim 64 or 128.
+ * ------------------------------------------------------------------------- */
+
+/* Payload bytes of n_positions positions: 2 n Hkv D bits/8 + 2 (2 n Hkv D /
+ * 64); 0 for unsupported arguments. */
+size_t pkv_codec_payload_bytes(int32_t n_positions, int32_t num_kv_heads, int32_t head_dim, int32_t bits);
+
+/* Encode positions 0..n_positions-1 of one sequence, read in place through
+ * its device block table (>= ceil(n_positions / page_size) entries), into
+ * `payload` (device, 16-byte aligned, pkv_codec_payload_bytes).  Errors:
+ * INVALID_ARG, UNSUPPORTED (dtype other than PKV_BF16, bits), DEVICE. */
+int pkv_codec_encode(const pkv_pool_desc* desc, const void* k_pool, const void* v_pool, const int32_t* block_table,
+                     int32_t n_positions, int32_t bits, void* payload, void* stream);
+
+/* Restore a payload written by pkv_codec_encode into positions
+ * 0..n_positions-1 of a sequence whose block table names the destination
+ * pages (bf16(scale * code) per element; other slots untouched). */
+int pkv_codec_decode(const pkv_pool_desc* desc, void* k_pool, void* v_pool, const int32_t* block_table,
+                     int32_t n_positions, int32_t bits, const void* payload, void* stream);
+
 /* Bytes of device workspace pkv_decode / pkv_prefill_append need for these
  * sizes (0 when a launch needs none).  Pass the same scalars to the call.
  * Returns 0 for unsupported descriptors as well; the call then reports it. */

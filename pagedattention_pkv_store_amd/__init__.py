@@ -22,6 +22,7 @@ from ._lib import PKV_BF16, PKV_F32, PKV_I8  # noqa: F401
 __all__ = [
     "PkvError", "OutOfPagesError", "SharedPageError", "UnsupportedError",
     "PoolDesc", "Allocator", "plan_prefix", "store_kv", "copy_pages", "decode", "prefill_append",
+    "codec_payload_bytes", "codec_encode", "codec_decode",
     "workspace_bytes", "validate_tables", "PKV_F32", "PKV_BF16", "PKV_I8",
     "BoundCall", "bind_store_kv", "bind_decode", "bind_prefill_append",
 ]
@@ -406,6 +407,34 @@ def copy_pages(desc: PoolDesc, k_pool, v_pool, copies, stream=None) -> None:
     c_desc = desc.c()
     _check(_lib.lib().pkv_copy_pages(ctypes.byref(c_desc), _dev(k_pool, "k_pool", pdt), _dev(v_pool, "v_pool", pdt),
                                      _dev(copies, "copies", torch.int32), n, _stream(stream)))
+
+
+def codec_payload_bytes(n_positions: int, num_kv_heads: int, head_dim: int, bits: int) -> int:
+    n = int(_lib.lib().pkv_codec_payload_bytes(n_positions, num_kv_heads, head_dim, bits))
+    if n == 0 and n_positions > 0:
+        _check(_lib.PKV_ERR_UNSUPPORTED)
+    return n
+
+
+def codec_encode(desc: PoolDesc, k_pool, v_pool, block_table, n_positions: int, bits: int, payload,
+                 stream=None) -> None:
+    """Quantize a sequence's first n_positions K/V (read through its device
+    block table) into a device uint8 payload (pkv_codec_encode)."""
+    import torch
+    pdt = desc.pool_torch_dtype()
+    _check(_lib.lib().pkv_codec_encode(ctypes.byref(desc.c()), _dev(k_pool, "k_pool", pdt),
+                                       _dev(v_pool, "v_pool", pdt), _dev(block_table, "block_table", torch.int32),
+                                       n_positions, bits, _dev(payload, "payload", torch.uint8), _stream(stream)))
+
+
+def codec_decode(desc: PoolDesc, k_pool, v_pool, block_table, n_positions: int, bits: int, payload,
+                 stream=None) -> None:
+    """Restore a payload into a sequence's first n_positions (pkv_codec_decode)."""
+    import torch
+    pdt = desc.pool_torch_dtype()
+    _check(_lib.lib().pkv_codec_decode(ctypes.byref(desc.c()), _dev(k_pool, "k_pool", pdt),
+                                       _dev(v_pool, "v_pool", pdt), _dev(block_table, "block_table", torch.int32),
+                                       n_positions, bits, _dev(payload, "payload", torch.uint8), _stream(stream)))
 
 
 def workspace_bytes(desc: PoolDesc, n_seqs: int, num_q_heads: int, max_q_per_seq: int,

@@ -61,6 +61,11 @@ _SIGNATURES = {
                              c_void_p, c_int32, c_void_p]),
     "pkv_i8_block_bytes": (c_size_t, [c_int32, c_int32]),
     "pkv_pool_bytes": (c_size_t, [POINTER(PoolDescC)]),
+    "pkv_codec_payload_bytes": (c_size_t, [c_int32, c_int32, c_int32, c_int32]),
+    "pkv_codec_encode": (c_int, [POINTER(PoolDescC), c_void_p, c_void_p, c_void_p, c_int32, c_int32, c_void_p,
+                                 c_void_p]),
+    "pkv_codec_decode": (c_int, [POINTER(PoolDescC), c_void_p, c_void_p, c_void_p, c_int32, c_int32, c_void_p,
+                                 c_void_p]),
     "pkv_workspace_bytes": (c_size_t, [POINTER(PoolDescC), c_int32, c_int32, c_int32, c_int32]),
     "pkv_decode": (c_int, [POINTER(PoolDescC), c_void_p, c_void_p, c_void_p, c_int32, c_int32,
                            c_void_p, c_int32, c_void_p, c_int32, c_float, c_void_p, c_void_p,

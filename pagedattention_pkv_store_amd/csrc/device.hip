@@ -1749,6 +1749,131 @@ __global__ __launch_bounds__(kThreads) void copy_pages_kernel(char* __restrict__
   }
 }
 
+// Group-wise low-bit codec of a prefix's K and V (the quantize / restore half
+// of a KV handoff, ReKV section 2.2): groups of 64 elements along head_dim,
+// one fp16 scale each, Q8 bytes or Q4 nibbles.  Eight consecutive lanes own
+// one group, 8 elements each; the payload holds the codes of K then V
+// (position, KV head, element order), then the scales in the same order.
+// Scale = fp16(max|x| / q_max); codes = rint(x * (1 / scale16)) clamped to
+// [-q_max, q_max], with one IEEE fp32 reciprocal per group; a zero scale
+// gives zero codes.  Restoring writes bf16(scale16 * code).
+struct CodecArgs {
+  const int32_t* block_table;
+  int32_t n_positions;
+  int32_t hkv;
+  int32_t head_dim;
+  int32_t page_size;
+  int32_t ps_shift;
+  int32_t num_pages;
+  int64_t groups_per_tensor;   // n_positions * hkv * head_dim / 64
+};
+
+// Pool element offset of the 8 elements of (tensor-local) group gi, part.
+// Index arithmetic is 32-bit: the host keeps 2 * groups_per_tensor * 8 below
+// 2^31.  head_dim is 64 or 128, so a vector holds 1 or 2 groups.
+__device__ __forceinline__ int64_t codec_pool_elem(const CodecArgs& a, int gi, int part) {
+  const int gshift = a.head_dim == 128 ? 1 : 0;      // log2(groups per (position, head) vector)
+  const int vec = gi >> gshift;
+  const int d0 = (gi - (vec << gshift)) * 64 + part * 8;
+  const int pos = static_cast<int>(static_cast<unsigned>(vec) / static_cast<unsigned>(a.hkv));
+  const int head = vec - pos * a.hkv;
+  const int blk = a.ps_shift >= 0 ? (pos >> a.ps_shift) : pos / a.page_size;
+  const int off = pos - blk * a.page_size;
+  const int page = min(max(a.block_table[blk], 0), a.num_pages - 1);
+  return ((static_cast<int64_t>(page) * a.hkv + head) * a.page_size + off) * a.head_dim + d0;
+}
+
+template <int kBits>
+__global__ __launch_bounds__(kThreads) void codec_encode_kernel(CodecArgs a, const uint16_t* __restrict__ k_pool,
+                                                                const uint16_t* __restrict__ v_pool,
+                                                                uint8_t* __restrict__ codes,
+                                                                uint16_t* __restrict__ scales) {
+  constexpr float kQMax = kBits == 8 ? 127.f : 7.f;
+  const int gid = static_cast<int>(blockIdx.x) * kThreads + static_cast<int>(threadIdx.x);
+  const int gpt = static_cast<int>(a.groups_per_tensor);
+  int group = gid >> 3;
+  const int part = gid & 7;
+  const bool live = group < 2 * gpt;                 // whole 8-lane groups are live or not
+  if (!live) group = 0;
+  const bool is_v = group >= gpt;
+  const int gi = is_v ? group - gpt : group;
+  const u32x4 x = *reinterpret_cast<const u32x4*>((is_v ? v_pool : k_pool) + codec_pool_elem(a, gi, part));
+  float f[8];
+#pragma unroll
+  for (int w = 0; w < 4; ++w) {
+    f[2 * w] = __uint_as_float(x[w] << 16);
+    f[2 * w + 1] = __uint_as_float(x[w] & 0xffff0000u);
+  }
+  float amax = 0.f;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) amax = fmaxf(amax, fabsf(f[i]));
+  amax = fmaxf(amax, __shfl_xor(amax, 1));
+  amax = fmaxf(amax, __shfl_xor(amax, 2));
+  amax = fmaxf(amax, __shfl_xor(amax, 4));
+  const _Float16 s16 = static_cast<_Float16>(amax / kQMax);
+  const float sf = static_cast<float>(s16);
+  const float inv = 1.f / (sf > 0.f ? sf : 1.f);      // correctly rounded, once per lane
+  int c[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i)
+    c[i] = sf > 0.f ? static_cast<int>(fminf(fmaxf(rintf(f[i] * inv), -kQMax), kQMax)) : 0;
+  if (!live) return;
+  const int64_t e = static_cast<int64_t>(group) * 64 + part * 8;   // element index in the payload
+  if constexpr (kBits == 8) {
+    uint32_t lo = 0, hi = 0;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      lo |= (static_cast<uint32_t>(c[i]) & 0xffu) << (8 * i);
+      hi |= (static_cast<uint32_t>(c[4 + i]) & 0xffu) << (8 * i);
+    }
+    *reinterpret_cast<uint2*>(codes + e) = make_uint2(lo, hi);
+  } else {
+    uint32_t w = 0;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) w |= (static_cast<uint32_t>(c[i]) & 0xfu) << (4 * i);
+    *reinterpret_cast<uint32_t*>(codes + e / 2) = w;
+  }
+  if (part == 0) scales[group] = __builtin_bit_cast(uint16_t, s16);
+}
+
+template <int kBits>
+__global__ __launch_bounds__(kThreads) void codec_decode_kernel(CodecArgs a, uint16_t* __restrict__ k_pool,
+                                                                uint16_t* __restrict__ v_pool,
+                                                                const uint8_t* __restrict__ codes,
+                                                                const uint16_t* __restrict__ scales) {
+  const int gid = static_cast<int>(blockIdx.x) * kThreads + static_cast<int>(threadIdx.x);
+  const int gpt = static_cast<int>(a.groups_per_tensor);
+  const int group = gid >> 3;
+  const int part = gid & 7;
+  if (group >= 2 * gpt) return;
+  const bool is_v = group >= gpt;
+  const int gi = is_v ? group - gpt : group;
+  const int64_t e = static_cast<int64_t>(group) * 64 + part * 8;
+  int c[8];
+  if constexpr (kBits == 8) {
+    const uint2 w = *reinterpret_cast<const uint2*>(codes + e);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      c[i] = static_cast<int8_t>(w.x >> (8 * i));
+      c[4 + i] = static_cast<int8_t>(w.y >> (8 * i));
+    }
+  } else {
+    const uint32_t w = *reinterpret_cast<const uint32_t*>(codes + e / 2);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) c[i] = static_cast<int>(static_cast<int32_t>(w << (28 - 4 * i)) >> 28);
+  }
+  const float sf = static_cast<float>(__builtin_bit_cast(_Float16, scales[group]));
+  f32x4 lo, hi;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    lo[i] = sf * static_cast<float>(c[i]);
+    hi[i] = sf * static_cast<float>(c[4 + i]);
+  }
+  const uint2 plo = __builtin_bit_cast(uint2, pack_bf16x4(lo));
+  const uint2 phi = __builtin_bit_cast(uint2, pack_bf16x4(hi));
+  *reinterpret_cast<u32x4*>((is_v ? v_pool : k_pool) + codec_pool_elem(a, gi, part)) = u32x4{plo.x, plo.y, phi.x, phi.y};
+}
+
 // ---------------------------------------------------------------------------
 // host-side launch planning
 // ---------------------------------------------------------------------------
@@ -2067,6 +2192,32 @@ int run_attention(const char* fn, const pkv_pool_desc* desc, const void* k_pool,
   return PKV_OK;
 }
 
+int codec_setup(const char* fn, const pkv_pool_desc* desc, const void* k_pool, const void* v_pool,
+                const int32_t* block_table, int32_t n_positions, int32_t bits, const void* payload, CodecArgs* a,
+                int64_t* blocks) {
+  int rc = check_desc(desc, fn);
+  if (rc != PKV_OK) return rc;
+  if (desc->dtype != PKV_BF16) return fail(PKV_ERR_UNSUPPORTED, std::string(fn) + ": bf16 pools only");
+  if (bits != 4 && bits != 8) return fail(PKV_ERR_UNSUPPORTED, std::string(fn) + ": bits must be 4 or 8");
+  if (n_positions < 0) return fail(PKV_ERR_INVALID_ARG, std::string(fn) + ": n_positions < 0");
+  if (n_positions > 0 && (!k_pool || !v_pool || !block_table || !payload))
+    return fail(PKV_ERR_INVALID_ARG, std::string(fn) + ": NULL device pointer");
+  if (!aligned16(k_pool) || !aligned16(v_pool) || !aligned16(payload))
+    return fail(PKV_ERR_INVALID_ARG, std::string(fn) + ": pools and payload must be 16-byte aligned");
+  a->block_table = block_table;
+  a->n_positions = n_positions;
+  a->hkv = desc->num_kv_heads;
+  a->head_dim = desc->head_dim;
+  a->page_size = desc->page_size;
+  a->ps_shift = log2_exact(desc->page_size);
+  a->num_pages = desc->num_pages;
+  a->groups_per_tensor = static_cast<int64_t>(n_positions) * desc->num_kv_heads * (desc->head_dim / 64);
+  if (2 * a->groups_per_tensor * 8 + kThreads > INT32_MAX)
+    return fail(PKV_ERR_UNSUPPORTED, std::string(fn) + ": prefix too long");
+  *blocks = (2 * a->groups_per_tensor * 8 + kThreads - 1) / kThreads;
+  return PKV_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -2148,6 +2299,57 @@ int pkv_copy_pages(const pkv_pool_desc* desc, void* k_pool, void* v_pool, const 
   hipError_t err = hipGetLastError();
   if (err != hipSuccess)
     return fail(PKV_ERR_DEVICE, std::string("pkv_copy_pages: launch failed: ") + hipGetErrorString(err));
+  return PKV_OK;
+}
+
+size_t pkv_codec_payload_bytes(int32_t n_positions, int32_t num_kv_heads, int32_t head_dim, int32_t bits) {
+  if (n_positions < 0 || num_kv_heads < 1 || head_dim < 64 || head_dim % 64 || (bits != 4 && bits != 8)) return 0;
+  const size_t elems = 2 * static_cast<size_t>(n_positions) * num_kv_heads * head_dim;
+  return elems * bits / 8 + 2 * (elems / 64);
+}
+
+
+int pkv_codec_encode(const pkv_pool_desc* desc, const void* k_pool, const void* v_pool, const int32_t* block_table,
+                     int32_t n_positions, int32_t bits, void* payload, void* stream) {
+  CodecArgs a{};
+  int64_t blocks = 0;
+  int rc = codec_setup("pkv_codec_encode", desc, k_pool, v_pool, block_table, n_positions, bits, payload, &a, &blocks);
+  if (rc != PKV_OK || n_positions == 0) return rc;
+  uint8_t* codes = static_cast<uint8_t*>(payload);
+  uint16_t* scales = reinterpret_cast<uint16_t*>(codes + 2 * a.groups_per_tensor * 64 * bits / 8);
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  (void)hipGetLastError();
+  if (bits == 8)
+    codec_encode_kernel<8><<<dim3(static_cast<unsigned>(blocks)), dim3(kThreads), 0, st>>>(
+        a, static_cast<const uint16_t*>(k_pool), static_cast<const uint16_t*>(v_pool), codes, scales);
+  else
+    codec_encode_kernel<4><<<dim3(static_cast<unsigned>(blocks)), dim3(kThreads), 0, st>>>(
+        a, static_cast<const uint16_t*>(k_pool), static_cast<const uint16_t*>(v_pool), codes, scales);
+  hipError_t err = hipGetLastError();
+  if (err != hipSuccess)
+    return fail(PKV_ERR_DEVICE, std::string("pkv_codec_encode: launch failed: ") + hipGetErrorString(err));
+  return PKV_OK;
+}
+
+int pkv_codec_decode(const pkv_pool_desc* desc, void* k_pool, void* v_pool, const int32_t* block_table,
+                     int32_t n_positions, int32_t bits, const void* payload, void* stream) {
+  CodecArgs a{};
+  int64_t blocks = 0;
+  int rc = codec_setup("pkv_codec_decode", desc, k_pool, v_pool, block_table, n_positions, bits, payload, &a, &blocks);
+  if (rc != PKV_OK || n_positions == 0) return rc;
+  const uint8_t* codes = static_cast<const uint8_t*>(payload);
+  const uint16_t* scales = reinterpret_cast<const uint16_t*>(codes + 2 * a.groups_per_tensor * 64 * bits / 8);
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  (void)hipGetLastError();
+  if (bits == 8)
+    codec_decode_kernel<8><<<dim3(static_cast<unsigned>(blocks)), dim3(kThreads), 0, st>>>(
+        a, static_cast<uint16_t*>(k_pool), static_cast<uint16_t*>(v_pool), codes, scales);
+  else
+    codec_decode_kernel<4><<<dim3(static_cast<unsigned>(blocks)), dim3(kThreads), 0, st>>>(
+        a, static_cast<uint16_t*>(k_pool), static_cast<uint16_t*>(v_pool), codes, scales);
+  hipError_t err = hipGetLastError();
+  if (err != hipSuccess)
+    return fail(PKV_ERR_DEVICE, std::string("pkv_codec_decode: launch failed: ") + hipGetErrorString(err));
   return PKV_OK;
 }
 

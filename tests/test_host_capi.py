@@ -312,6 +312,14 @@ def test_bound_prepare_step_matches_prepare_step(pkv_lib):
         a.bind_prepare_step(sa, n_new, 40, np.empty(3, np.int64), bt, lens)   # slots too small
 
 
+def test_codec_payload_bytes_match_oracle(pkv_lib):
+    from oracle.codec import payload_bytes
+    for n, hkv, d, bits in [(1, 1, 64, 8), (53, 8, 128, 4), (8192, 4, 128, 8), (0, 2, 64, 4)]:
+        assert pkv.codec_payload_bytes(n, hkv, d, bits) == payload_bytes(2 * n * hkv * d, bits)
+    assert pkv_lib.pkv_codec_payload_bytes(10, 8, 128, 6) == 0
+    assert pkv_lib.pkv_codec_payload_bytes(10, 8, 96, 8) == 0
+
+
 def test_int8_pool_layout_sizes(pkv_lib, golden):
     """INT8 pages cost head_dim + 4 bytes per vector (TileInfer.jl "INT8 cache":
     132 bytes instead of 256 at head_dim 128); a (page, head) block is padded
