@@ -339,7 +339,9 @@ size_t pkv_workspace_bytes(const pkv_pool_desc* desc, int32_t n_seqs, int32_t nu
  *   block_tables: device int32 [n_seqs][bt_stride]
  *   seq_lens:     device int32 [n_seqs], positions stored, the new one included
  *                 (>= 1, <= bt_stride * page_size)
- *   max_seq_len:  host upper bound of seq_lens (sizes the grid and the split)
+ *   max_seq_len:  host upper bound of seq_lens (sizes the grid and the split);
+ *                 positions at or past min(max_seq_len, bt_stride * page_size)
+ *                 are never read, whatever seq_lens holds
  *   scale:        softmax scale (1/sqrt(head_dim) in the usual model)
  *   out:          device [n_seqs][num_q_heads][head_dim], dtype of q
  *                 (q and out are bf16 for PKV_I8 pools, whose key scales

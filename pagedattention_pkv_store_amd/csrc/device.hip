@@ -164,6 +164,10 @@ struct AttnArgs {
   int32_t max_q;        // queries computed per sequence (later ones are not)
   int32_t waves;        // decode: one-wave workgroups of the launch
   int32_t head_bytes;   // bytes of one (page, KV head) block of a pool
+  int32_t kv_cap;       // min(bt_stride * page_size, max_seq_len): positions at
+                        // or past it are never read, so a seq_lens entry past
+                        // its block-table row (or the planned length) cannot
+                        // index beyond the row
   float scale_log2;     // softmax scale * log2(e)
 };
 
@@ -316,7 +320,7 @@ __global__ __launch_bounds__(kThreads) void paged_attention_kernel(AttnArgs args
   const int seq_len = args.seq_lens[b];
   const int start = seq_len - n_b;                    // position of new query 0
   const int row_last = min(row0 + kTileRows, rows_total) - 1;
-  const int kv_end = start + row_last / group + 1;    // positions this tile can see
+  const int kv_end = min(start + row_last / group + 1, args.kv_cap);   // positions this tile can see
   const int k_lo = blockIdx.x * args.split_len;
   if (k_lo >= kv_end) return;
   const int k_hi = min(k_lo + args.split_len, kv_end);
@@ -571,7 +575,7 @@ __device__ __forceinline__ int decode_kv_end(const AttnArgs& a, int b, int* q0_o
   const int rows = max(0, min(min(n_b, a.max_q) * a.group, 16 * RBW));
   *rows_out = rows;
   if (rows <= 0) return 0;
-  return a.seq_lens[b] - n_b + (rows - 1) / a.group + 1;
+  return min(a.seq_lens[b] - n_b + (rows - 1) / a.group + 1, a.kv_cap);
 }
 
 // Blocks per wave: the same in the attention and merge kernels.
@@ -661,7 +665,7 @@ __global__ __launch_bounds__(kWave, RBW == 1 ? (kI8 ? PKV_DECODE_WAVES_PER_SIMD_
     }
     u.rows = max(0, min(min(n_b, args.max_q) * group, 16 * RBW));
     u.start = seq_lens[b] - n_b;
-    u.kv_end = u.rows > 0 ? u.start + (u.rows - 1) / group + 1 : 0;
+    u.kv_end = u.rows > 0 ? min(u.start + (u.rows - 1) / group + 1, args.kv_cap) : 0;
     return u;
   };
   auto nb_of = [&](int b) __attribute__((always_inline)) {
@@ -1239,7 +1243,7 @@ __global__ __launch_bounds__(kPfThreads, kPfRb >= 3 ? 1 : 2) void paged_prefill_
   const int row0 = qt * kPfRows;
   if (row0 >= rows_total) return;
   const int start = a.seq_lens[b] - n_b;                 // position of new query 0
-  const int kv_end = start + (min(row0 + kPfRows, rows_total) - 1) / group + 1;
+  const int kv_end = min(start + (min(row0 + kPfRows, rows_total) - 1) / group + 1, a.kv_cap);
   const int k_lo = split * a.split_len;
   if (k_lo >= kv_end) return;
   const int k_hi = min(k_lo + a.split_len, kv_end);
@@ -1329,7 +1333,7 @@ __global__ __launch_bounds__(kPfThreads, kPfRb >= 3 ? 1 : 2) void paged_prefill_
     const int rr = wr0 + 16 * rb + lrow;
     const int qi = rr / group;
     const bool ok = rr < rows_total && q0 + qi < a.total_q;
-    qpos[rb] = ok ? start + qi : -1;
+    qpos[rb] = ok ? min(start + qi, kv_end - 1) : -1;   // keys past kv_end are clamped copies: masked
     const uint16_t* src = static_cast<const uint16_t*>(a.q) +
                           (static_cast<int64_t>(q0 + qi) * a.num_q_heads + g * group + (rr - qi * group)) * D +
                           lgrp * (D / 4);
@@ -1342,8 +1346,8 @@ __global__ __launch_bounds__(kPfThreads, kPfRb >= 3 ? 1 : 2) void paged_prefill_
   }
 
   const bool w_active = wr0 < rows_total;
-  const int w_qmin = start + wr0 / group;
-  const int w_qmax = start + (min(wr0 + kWr - 1, rows_total - 1)) / group;
+  const int w_qmin = min(start + wr0 / group, kv_end - 1);
+  const int w_qmax = min(start + (min(wr0 + kWr - 1, rows_total - 1)) / group, kv_end - 1);
   const float c2 = a.scale_log2;
 
   f32x4 o[kDb][kPfRb];
@@ -1596,7 +1600,7 @@ __global__ __launch_bounds__(kWave) void merge_chunks_kernel(AttnArgs args) {
   if (qi >= n_b) return;
   const int tok = q0 + qi;
   if (tok >= args.total_q || tok >= args.ws_tokens) return;
-  const int qpos = args.seq_lens[b] - n_b + qi;
+  const int qpos = min(args.seq_lens[b] - n_b + qi, args.kv_cap - 1);   // last position read
   const int ns = qpos < 0 ? 0 : min(args.n_splits, qpos / args.split_len + 1);
   const int64_t orow = static_cast<int64_t>(tok) * args.num_q_heads + h;
   merge_rows<T, D>(args, args.ws_o + orow * args.n_splits * D, args.ws_ml + orow * args.n_splits * 2, 1, ns,
@@ -2150,6 +2154,7 @@ int run_attention(const char* fn, const pkv_pool_desc* desc, const void* k_pool,
   a.scale_log2 = scale * 1.4426950408889634f;
   a.waves = p.grid;
   a.head_bytes = static_cast<int32_t>(head_block_bytes(desc));
+  a.kv_cap = static_cast<int32_t>(std::min<int64_t>(static_cast<int64_t>(bt_stride) * desc->page_size, max_seq_len));
   if (p.decode) {
     const size_t rows_out = (static_cast<size_t>(n_seqs) * desc->num_kv_heads + p.grid) * (16 * p.rbw);
     a.ws_o = reinterpret_cast<float*>(static_cast<char*>(workspace) + p.partial_off);

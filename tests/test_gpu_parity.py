@@ -21,11 +21,12 @@ import oracle_path as ref
 import pagedattention_pkv_store_amd as pkv
 import synth
 from conftest import ensure_library
-from gpu_path import (DEV, Session, dev_tensor, host_f64, i64, run_decode, run_prefix,
+from gpu_path import (DEV, Session, dev_tensor, host_f64, i32, i64, run_decode, run_prefix,
                       run_rewind, run_spec, run_tiny)
 from oracle.attention import attend, attend_row, paged_attention
 from oracle.paging import Allocator as OracleAllocator
 from oracle.paging import store_rows
+from oracle.quant import dequantize, quantize
 
 pytestmark = pytest.mark.gpu
 
@@ -265,6 +266,74 @@ def test_truncated_slots_are_never_read():
                            synth.to_f64(w.v[lo:lo + L, h // 4], w.dtype), L - 1, s.scale)
             assert np.isfinite(out[b, h]).all()
             assert np.abs(out[b, h] - e).max() <= BF16_MAX
+
+
+@pytest.mark.parametrize("dtype,kv_int8,D", [(synth.F32, False, 64), (synth.BF16, False, 128),
+                                         (synth.BF16, True, 128)])
+def test_positions_past_the_table_row_are_not_read(dtype, kv_int8, D):
+    """seq_lens entries past bt_stride * page_size, or past max_seq_len, read
+    only the positions the row and the bound cover.  The table buffer runs on
+    past the last row into entries naming never-written (NaN) pages, and rows
+    sit back to back, so a read past a row would show as a NaN or as another
+    sequence's keys."""
+    print(f"positions past the row {dtype} int8={kv_int8} D={D}", flush=True)
+    rng = np.random.default_rng(D + 5 * kv_int8)
+    ps, stride, n, hq, hkv = 4, 5, 3, 16, 2
+    cap = ps * stride
+    pools = _Pools(dtype, D, ps, hkv, n * stride + 4, seed=9)
+    s = Session.open(pools, kv_int8=kv_int8)
+    seqs = [s.alloc.seq_new() for _ in range(n)]
+    kv = synth.normal_values(rng, (n, 2, cap, hkv, D), dtype)
+    for b, seq in enumerate(seqs):
+        s.alloc.reserve(seq, cap)
+        s.store(seq, 0, kv[b, 0], kv[b, 1], dtype)
+    bt = s.alloc.block_tables(seqs, stride)
+    unused = sorted(set(range(pools.num_pages)) - set(bt.ravel().tolist()))
+    buf = i32(np.concatenate([bt.ravel(), np.resize(np.array(unused, np.int32), 64)]))
+    d_bt = buf[: n * stride].view(n, stride)
+
+    def logical(b, n_pos):
+        k = synth.to_f64(kv[b, 0, :n_pos], dtype)
+        v = synth.to_f64(kv[b, 1, :n_pos], dtype)
+        if kv_int8:
+            k, v = dequantize(*quantize(k)), dequantize(*quantize(v))
+        return k, v
+
+    def run_decode_call(lens, max_len):
+        q = synth.normal_values(rng, (n, hq, D), dtype)
+        out = torch.empty((n, hq, D), dtype=s.desc.torch_dtype(), device=DEV)
+        ws = torch.empty(max(16, pkv.workspace_bytes(s.desc, n, hq, 1, max_len)), dtype=torch.uint8, device=DEV)
+        pkv.decode(s.desc, s.k_pool, s.v_pool, dev_tensor(q, dtype), d_bt, i32(lens), max_len, s.scale, out, ws)
+        return q, host_f64(out)
+
+    # past the row: every query sees the row's cap positions
+    lens = np.array([cap + 7, cap + 100, cap], np.int32)
+    q, o = run_decode_call(lens, int(lens.max()))
+    for b in range(n):
+        k, v = logical(b, cap)
+        check_close(o[b:b + 1], attend(synth.to_f64(q[b:b + 1], dtype), k, v, s.scale), dtype, f"decode row {b}")
+    # past max_seq_len: the first 13 positions only
+    q, o = run_decode_call(np.full(n, cap, np.int32), 13)
+    for b in range(n):
+        k, v = logical(b, 13)
+        check_close(o[b:b + 1], attend(synth.to_f64(q[b:b + 1], dtype), k, v, s.scale), dtype, f"bounded row {b}")
+    # append: 8, 7 and 2 queries (64 rows per KV head: the multi-query tiles)
+    n_new = np.array([8, 7, 2], np.int32)
+    cu = np.concatenate([[0], np.cumsum(n_new)]).astype(np.int32)
+    q = synth.normal_values(rng, (int(cu[-1]), hq, D), dtype)
+    out = torch.empty((int(cu[-1]), hq, D), dtype=s.desc.torch_dtype(), device=DEV)
+    max_len = int(lens.max())
+    ws = torch.empty(max(16, pkv.workspace_bytes(s.desc, n, hq, 8, max_len)), dtype=torch.uint8, device=DEV)
+    pkv.prefill_append(s.desc, s.k_pool, s.v_pool, dev_tensor(q, dtype), i32(cu), d_bt, i32(lens), 8, max_len,
+                       s.scale, out, ws)
+    o = host_f64(out)
+    for b in range(n):
+        qb = synth.to_f64(q[cu[b]:cu[b + 1]], dtype)
+        e = []
+        for i in range(n_new[b]):        # query i at position lens - n_new + i sees at most cap positions
+            k, v = logical(b, min(int(lens[b] - n_new[b]) + i + 1, cap))
+            e.append(attend(qb[i:i + 1], k, v, s.scale))
+        check_close(o[cu[b]:cu[b + 1]], np.concatenate(e), dtype, f"append row {b}")
 
 
 # ---------------------------------------------------------------------------
