@@ -308,7 +308,8 @@ def codec_leg(args, torch, pkv, dev: str) -> dict:
             t = float(np.mean([a.elapsed_time(b) for a, b in evs])) / 1e3
             alg = kv_bytes + pay.numel()
             res[name] = {"kernel_avg_us": round(t * 1e6, 2), "achieved_gbs": round(alg / t / 1e9, 1),
-                         "frac": round(alg / t / 1e9 / HBM_PEAK_GBS, 4), "algorithmic_bytes_per_launch": alg}
+                         "frac": round(alg / t / 1e9 / HBM_PEAK_GBS, 4), "algorithmic_bytes_per_launch": alg,
+                         "traffic": measured_traffic(f"codec_q{bits}_{name}")}
         out[f"q{bits}"] = res
         del pay
     del k_pool, v_pool
