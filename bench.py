@@ -446,7 +446,7 @@ def decode_leg(args, torch, pkv, synth, w, dev: str, kv_int8: bool) -> dict:
         d_slots, d_bt, d_lens = views(db)
         sets.append({
             "host": hb, "dev": db, "np": (hs.numpy(), hbt.numpy(), hl.numpy()),
-            "uploaded": torch.cuda.Event(), "consumed": torch.cuda.Event(),
+            "uploaded": torch.cuda.Event(), "consumed": torch.cuda.Event(), "consumed_at": None,
             "store": pkv.bind_store_kv(desc, k_pool, v_pool, k_new, v_new, d_slots, stream),
             "decode": pkv.bind_decode(desc, k_pool, v_pool, q, d_bt, d_lens, max_len, scale, out, ws, stream),
         })
@@ -469,7 +469,7 @@ def decode_leg(args, torch, pkv, synth, w, dev: str, kv_int8: bool) -> dict:
         prep[k % R][k % 2]()
         with torch.cuda.stream(copy_stream):
             if k >= 2:
-                copy_stream.wait_event(st["consumed"])   # step k - 2's kernels are done with it
+                copy_stream.wait_event(st["consumed_at"])   # step k - 2's kernels are done with it
             st["dev"].copy_(st["host"], non_blocking=True)
             st["uploaded"].record(copy_stream)
 
@@ -485,10 +485,16 @@ def decode_leg(args, torch, pkv, synth, w, dev: str, kv_int8: bool) -> dict:
                 dec_ms.append(pair[0].elapsed_time(pair[1]))
             pair[0].record(stream)
         st["decode"]()
+        # one marker after the decode: the timing end event doubles as the
+        # point after which the copy stream may overwrite this set (each
+        # marker on the stream costs a few microseconds of idle GPU)
         if pair is not None:
             pair[1].record(stream)
+            st["consumed_at"] = pair[1]
             kv_bytes.append(int(l_np.astype(np.int64).sum()) * per_pos)
-        st["consumed"].record(stream)
+        else:
+            st["consumed"].record(stream)
+            st["consumed_at"] = st["consumed"]
         upload(k + 1)                         # the next step's tables, during this decode
 
     upload(0)
