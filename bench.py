@@ -19,7 +19,8 @@ Printed: one JSON line.  ``value`` = KV bytes the decode steps must read
 (sum of lengths x 2 x 8 heads x 128 x 2 bytes) / wall time of the timed steps
 (host work and copies included).  ``roofline`` = the decode kernels' own
 algorithmic bytes per launch / their average duration from HIP events on the
-launch stream, against the 8 TB/s HBM peak.  ``cpu_baseline`` = the fp64 CPU
+launch stream (every 4th timed step carries the event pair, 50 of the
+default 200), against the 8 TB/s HBM peak.  ``cpu_baseline`` = the fp64 CPU
 oracle on a bounded sample of the same sequences.
 """
 
@@ -423,12 +424,18 @@ def decode_leg(args, torch, pkv, synth, w, dev: str, kv_int8: bool) -> dict:
     ws = torch.empty(max(16, pkv.workspace_bytes(desc, B, hq, 1, max_len)), dtype=torch.uint8, device=dev)
     torch.cuda.synchronize()
 
-    # Upload, double-buffered: step k's slots (int64 [B]), block tables (int32
-    # [B][stride]) and lengths (int32 [B]) go from pinned set k%2 to device
-    # set k%2 in one copy, issued on a copy stream while the previous step's
-    # decode runs; the compute stream waits for it with an event that has
-    # normally fired long before (a copy in line with the kernels costs the
-    # copy engine's two hand-offs, about 30 us per step in a kernel trace).
+    # Upload: step k's slots (int64 [B]), block tables (int32 [B][stride]) and
+    # lengths (int32 [B]) go from pinned set k % NSETS to device set k % NSETS
+    # in one copy, issued on a copy stream while the previous step's decode
+    # runs; the compute stream waits for it with an event that has normally
+    # fired long before (a copy in line with the kernels costs the copy
+    # engine's two hand-offs, about 30 us per step in a kernel trace).
+    # Before a set is refilled the host waits for a timing event recorded
+    # after the decode that last read it (at least 5 steps back, so it has
+    # long completed): the compute stream then carries one marker per step
+    # (the upload wait) plus the timing pair on every TIME_EVERY-th step.
+    # Each marker leaves the GPU idle for a few microseconds.
+    NSETS, TIME_EVERY = 8, 4
     nbytes = B * 8 + B * stride * 4 + B * 4
 
     def views(buf):
@@ -439,67 +446,74 @@ def decode_leg(args, torch, pkv, synth, w, dev: str, kv_int8: bool) -> dict:
     copy_stream = torch.cuda.Stream(device=dev)          # default priority
     ones = np.ones(B, np.int32)
     sets = []
-    for _ in range(2):
+    for _ in range(NSETS):
         hb = torch.empty(nbytes, dtype=torch.uint8, pin_memory=True)
         db = torch.empty(nbytes, dtype=torch.uint8, device=dev)
         hs, hbt, hl = views(hb)
         d_slots, d_bt, d_lens = views(db)
         sets.append({
             "host": hb, "dev": db, "np": (hs.numpy(), hbt.numpy(), hl.numpy()),
-            "uploaded": torch.cuda.Event(), "consumed": torch.cuda.Event(), "consumed_at": None,
+            "uploaded": torch.cuda.Event(),
             "store": pkv.bind_store_kv(desc, k_pool, v_pool, k_new, v_new, d_slots, stream),
             "decode": pkv.bind_decode(desc, k_pool, v_pool, q, d_bt, d_lens, max_len, scale, out, ws, stream),
         })
     # prepare_step of instance r into pinned set j, marshalled once
-    prep = [[alloc.bind_prepare_step(inst[r], ones, stride, *sets[j]["np"]) for j in range(2)]
+    prep = [[alloc.bind_prepare_step(inst[r], ones, stride, *sets[j]["np"]) for j in range(NSETS)]
             for r in range(R)]
-    # A small ring of timing-event pairs, read back before reuse (a pair is
-    # reused EV_RING steps later, long after it completed): many live timing
-    # events slow down every record.
+    # A small ring of timing-event pairs, read back before reuse (a slot is
+    # reused EV_RING marked steps later, long after it completed): many live
+    # timing events slow down every record.
     EV_RING = 32
     ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
           for _ in range(EV_RING)]
+    slot_timed = [False] * EV_RING        # the slot's last pair belongs to a timed step, unread
     dec_ms = []
-    kv_bytes = []
+    kv_bytes = []                         # every timed step: KV bytes its decode reads
+    kv_bytes_timed_calls = []             # the steps whose decode call was timed
+
+    def read_slot(slot: int):
+        if slot_timed[slot]:
+            a, b = ev[slot]
+            b.synchronize()
+            dec_ms.append(a.elapsed_time(b))
+            slot_timed[slot] = False
 
     def upload(k: int):
-        st = sets[k % 2]
-        if k >= 2:
-            st["uploaded"].synchronize()      # the host copy of step k - 2 was read
-        prep[k % R][k % 2]()
+        j = k % NSETS
+        st = sets[j]
+        if k >= NSETS:
+            st["uploaded"].synchronize()      # the copy of step k - NSETS has read the pinned set
+            m = k - NSETS + (-(k - NSETS)) % TIME_EVERY   # the marked step in [k - NSETS, k - NSETS + 3]
+            ev[(m // TIME_EVERY) % EV_RING][1].synchronize()   # its decode, and step k - NSETS's, are done
+        prep[k % R][j]()
         with torch.cuda.stream(copy_stream):
-            if k >= 2:
-                copy_stream.wait_event(st["consumed_at"])   # step k - 2's kernels are done with it
             st["dev"].copy_(st["host"], non_blocking=True)
             st["uploaded"].record(copy_stream)
 
-    def step(k: int, timed_idx: int):
-        st = sets[k % 2]
+    def step(k: int, timed: bool):
+        st = sets[k % NSETS]
         l_np = st["np"][2]
         stream.wait_event(st["uploaded"])
         st["store"]()
-        pair = ev[timed_idx % EV_RING] if timed_idx >= 0 else None
-        if pair is not None:
-            if timed_idx >= EV_RING:
-                pair[1].synchronize()
-                dec_ms.append(pair[0].elapsed_time(pair[1]))
-            pair[0].record(stream)
+        marked = k % TIME_EVERY == 0
+        if marked:
+            slot = (k // TIME_EVERY) % EV_RING
+            read_slot(slot)
+            ev[slot][0].record(stream)
         st["decode"]()
-        # one marker after the decode: the timing end event doubles as the
-        # point after which the copy stream may overwrite this set (each
-        # marker on the stream costs a few microseconds of idle GPU)
-        if pair is not None:
-            pair[1].record(stream)
-            st["consumed_at"] = pair[1]
-            kv_bytes.append(int(l_np.astype(np.int64).sum()) * per_pos)
-        else:
-            st["consumed"].record(stream)
-            st["consumed_at"] = st["consumed"]
+        if marked:
+            ev[slot][1].record(stream)
+            slot_timed[slot] = timed
+        if timed:
+            b = int(l_np.astype(np.int64).sum()) * per_pos
+            kv_bytes.append(b)
+            if marked:
+                kv_bytes_timed_calls.append(b)
         upload(k + 1)                         # the next step's tables, during this decode
 
     upload(0)
     for k in range(args.warmup):
-        step(k, -1)
+        step(k, False)
     torch.cuda.synchronize()
     # Keep the garbage collector out of the timed loop: with the workload's
     # arrays alive a full collection takes tens of milliseconds.
@@ -508,22 +522,23 @@ def decode_leg(args, torch, pkv, synth, w, dev: str, kv_int8: bool) -> dict:
     gc.disable()
     t0 = time.perf_counter()
     for i in range(args.steps):
-        step(args.warmup + i, i)
+        step(args.warmup + i, True)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     gc.enable()
 
-    for k in range(max(0, args.steps - EV_RING), args.steps):
-        a, b = ev[k % EV_RING]
-        dec_ms.append(a.elapsed_time(b))
+    for slot in range(EV_RING):
+        read_slot(slot)
     dec_ms = np.array(dec_ms)
     assert torch.isfinite(out.float()).all(), "non-finite decode output"
     total_kv = float(sum(kv_bytes))
     qo_bytes = 2 * B * hq * D * 2                      # q read + out written per launch
+    assert len(dec_ms) == len(kv_bytes_timed_calls) > 0, "no timed decode call"
     dec_avg_s = float(dec_ms.mean()) / 1e3
     res = {
         "per_pos": per_pos, "total_kv": total_kv, "wall": wall, "dec_ms": dec_ms,
-        "alg_per_launch": total_kv / args.steps + qo_bytes, "dec_avg_s": dec_avg_s,
+        "alg_per_launch": float(np.mean(kv_bytes_timed_calls)) + qo_bytes, "dec_avg_s": dec_avg_s,
+        "timed_calls": len(dec_ms),
         "B": B, "hq": hq, "hkv": hkv, "D": D, "ps": ps, "scale": scale,
     }
     res["achieved"] = res["alg_per_launch"] / dec_avg_s / 1e9
@@ -584,6 +599,7 @@ def main():
             "kernel": "pkv_decode (paged_decode_kernel + merge_segments_kernel)",
             "kernel_avg_us": round(d["dec_avg_s"] * 1e6, 2),
             "kernel_median_us": round(float(np.median(d["dec_ms"])) * 1e3, 2),
+            "timed_launches": d["timed_calls"],
             "algorithmic_bytes_per_launch": int(d["alg_per_launch"]),
         },
     }
@@ -607,6 +623,7 @@ def main():
                 "kernel": "pkv_decode on PKV_I8 pools (paged_decode_kernel + merge_segments_kernel)",
                 "kernel_avg_us": round(d8["dec_avg_s"] * 1e6, 2),
                 "kernel_median_us": round(float(np.median(d8["dec_ms"])) * 1e3, 2),
+                "timed_launches": d8["timed_calls"],
                 "algorithmic_bytes_per_launch": int(d8["alg_per_launch"]),
                 "speedup_vs_bf16_kernel": round(d["dec_avg_s"] / d8["dec_avg_s"], 3),
             },
