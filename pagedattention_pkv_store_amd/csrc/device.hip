@@ -1755,8 +1755,8 @@ __global__ __launch_bounds__(kThreads) void copy_pages_kernel(char* __restrict__
 
 // Group-wise low-bit codec of a prefix's K and V (the quantize / restore half
 // of a KV handoff, ReKV section 2.2): groups of 64 elements along head_dim,
-// one fp16 scale each, Q8 bytes or Q4 nibbles.  Eight consecutive lanes own
-// one group, 8 elements each; the payload holds the codes of K then V
+// one fp16 scale each, Q8 bytes or Q4 nibbles.  Four consecutive lanes own
+// one group, 16 elements each; the payload holds the codes of K then V
 // (position, KV head, element order), then the scales in the same order.
 // Scale = fp16(max|x| / q_max); codes = rint(x * (1 / scale16)) clamped to
 // [-q_max, q_max], with one IEEE fp32 reciprocal per group; a zero scale
@@ -1787,95 +1787,132 @@ __device__ __forceinline__ int64_t codec_pool_elem(const CodecArgs& a, int gi, i
   return ((static_cast<int64_t>(page) * a.hkv + head) * a.page_size + off) * a.head_dim + d0;
 }
 
+// Encode: four consecutive lanes own one group of 64 elements; lane p reads
+// 16-byte chunks p and p + 4 (each load instruction of the four lanes covers
+// 64 contiguous bytes), so the group's maximum takes two shuffles and the
+// per-group work (address, scale, reciprocal) is shared by 16 elements.
+// A code is rint(clamp(x * inv, -q_max, q_max)): the clamped product plus
+// 1.5 * 2^23 rounds it to the nearest integer, ties to even, and the low
+// bits of the sum are the two's complement code.  With a zero scale inv is
+// 1 and every element is below 2^-18 in magnitude (a nonzero max / q_max
+// that rounds to fp16 zero is below 2^-25), so its code is 0.
+constexpr int kCodecLanes = 4;   // lanes per group of 64, both directions
+
 template <int kBits>
 __global__ __launch_bounds__(kThreads) void codec_encode_kernel(CodecArgs a, const uint16_t* __restrict__ k_pool,
                                                                 const uint16_t* __restrict__ v_pool,
                                                                 uint8_t* __restrict__ codes,
                                                                 uint16_t* __restrict__ scales) {
   constexpr float kQMax = kBits == 8 ? 127.f : 7.f;
+  constexpr float kRound = 12582912.f;               // 1.5 * 2^23
   const int gid = static_cast<int>(blockIdx.x) * kThreads + static_cast<int>(threadIdx.x);
   const int gpt = static_cast<int>(a.groups_per_tensor);
-  int group = gid >> 3;
-  const int part = gid & 7;
-  const bool live = group < 2 * gpt;                 // whole 8-lane groups are live or not
+  int group = gid >> 2;
+  const int part = gid & 3;
+  const bool live = group < 2 * gpt;                 // whole 4-lane groups are live or not
   if (!live) group = 0;
   const bool is_v = group >= gpt;
   const int gi = is_v ? group - gpt : group;
-  const u32x4 x = *reinterpret_cast<const u32x4*>((is_v ? v_pool : k_pool) + codec_pool_elem(a, gi, part));
-  float f[8];
+  const uint16_t* src = (is_v ? v_pool : k_pool) + codec_pool_elem(a, gi, part);
+  const u32x4 x0 = *reinterpret_cast<const u32x4*>(src);        // elements 8 part ..
+  const u32x4 x1 = *reinterpret_cast<const u32x4*>(src + 32);   // elements 32 + 8 part ..
+  float f[16];
 #pragma unroll
   for (int w = 0; w < 4; ++w) {
-    f[2 * w] = __uint_as_float(x[w] << 16);
-    f[2 * w + 1] = __uint_as_float(x[w] & 0xffff0000u);
+    f[2 * w] = __uint_as_float(x0[w] << 16);
+    f[2 * w + 1] = __uint_as_float(x0[w] & 0xffff0000u);
+    f[8 + 2 * w] = __uint_as_float(x1[w] << 16);
+    f[8 + 2 * w + 1] = __uint_as_float(x1[w] & 0xffff0000u);
   }
   float amax = 0.f;
 #pragma unroll
-  for (int i = 0; i < 8; ++i) amax = fmaxf(amax, fabsf(f[i]));
+  for (int i = 0; i < 16; ++i) amax = fmaxf(amax, fabsf(f[i]));
   amax = fmaxf(amax, __shfl_xor(amax, 1));
   amax = fmaxf(amax, __shfl_xor(amax, 2));
-  amax = fmaxf(amax, __shfl_xor(amax, 4));
   const _Float16 s16 = static_cast<_Float16>(amax / kQMax);
   const float sf = static_cast<float>(s16);
   const float inv = 1.f / (sf > 0.f ? sf : 1.f);      // correctly rounded, once per lane
-  int c[8];
+  uint32_t c[16];                                     // low bits: the codes
 #pragma unroll
-  for (int i = 0; i < 8; ++i)
-    c[i] = sf > 0.f ? static_cast<int>(fminf(fmaxf(rintf(f[i] * inv), -kQMax), kQMax)) : 0;
+  for (int i = 0; i < 16; ++i)
+    c[i] = __float_as_uint(__builtin_amdgcn_fmed3f(f[i] * inv, -kQMax, kQMax) + kRound);
   if (!live) return;
-  const int64_t e = static_cast<int64_t>(group) * 64 + part * 8;   // element index in the payload
+  const int64_t e = static_cast<int64_t>(group) * 64;   // first element of the group in the payload
   if constexpr (kBits == 8) {
-    uint32_t lo = 0, hi = 0;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      lo |= (static_cast<uint32_t>(c[i]) & 0xffu) << (8 * i);
-      hi |= (static_cast<uint32_t>(c[4 + i]) & 0xffu) << (8 * i);
+    for (int h = 0; h < 2; ++h) {
+      const uint32_t* q = c + 8 * h;
+      uint32_t lo = 0, hi = 0;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        lo |= (q[i] & 0xffu) << (8 * i);
+        hi |= (q[4 + i] & 0xffu) << (8 * i);
+      }
+      *reinterpret_cast<uint2*>(codes + e + 32 * h + 8 * part) = make_uint2(lo, hi);
     }
-    *reinterpret_cast<uint2*>(codes + e) = make_uint2(lo, hi);
   } else {
-    uint32_t w = 0;
 #pragma unroll
-    for (int i = 0; i < 8; ++i) w |= (static_cast<uint32_t>(c[i]) & 0xfu) << (4 * i);
-    *reinterpret_cast<uint32_t*>(codes + e / 2) = w;
+    for (int h = 0; h < 2; ++h) {
+      uint32_t w = 0;
+#pragma unroll
+      for (int i = 0; i < 8; ++i) w |= (c[8 * h + i] & 0xfu) << (4 * i);
+      *reinterpret_cast<uint32_t*>(codes + e / 2 + 16 * h + 4 * part) = w;
+    }
   }
   if (part == 0) scales[group] = __builtin_bit_cast(uint16_t, s16);
 }
 
-template <int kBits>
+// Restore: kL consecutive lanes own one group; lane p writes the group's
+// 16-byte chunks p, p + kL, ... (each store instruction of the kL lanes
+// covers 16 kL contiguous bytes).
+#ifndef PKV_RESTORE_LANES_Q8
+#define PKV_RESTORE_LANES_Q8 8
+#endif
+#ifndef PKV_RESTORE_LANES_Q4
+#define PKV_RESTORE_LANES_Q4 4
+#endif
+template <int kBits, int kL>
 __global__ __launch_bounds__(kThreads) void codec_decode_kernel(CodecArgs a, uint16_t* __restrict__ k_pool,
                                                                 uint16_t* __restrict__ v_pool,
                                                                 const uint8_t* __restrict__ codes,
                                                                 const uint16_t* __restrict__ scales) {
+  static_assert(kL == 4 || kL == 8, "4 or 8 lanes per group");
   const int gid = static_cast<int>(blockIdx.x) * kThreads + static_cast<int>(threadIdx.x);
   const int gpt = static_cast<int>(a.groups_per_tensor);
-  const int group = gid >> 3;
-  const int part = gid & 7;
+  const int group = gid / kL;
+  const int part = gid % kL;
   if (group >= 2 * gpt) return;
   const bool is_v = group >= gpt;
   const int gi = is_v ? group - gpt : group;
-  const int64_t e = static_cast<int64_t>(group) * 64 + part * 8;
-  int c[8];
-  if constexpr (kBits == 8) {
-    const uint2 w = *reinterpret_cast<const uint2*>(codes + e);
+  const int64_t e = static_cast<int64_t>(group) * 64;   // first element of the group in the payload
+  const float sf = static_cast<float>(__builtin_bit_cast(_Float16, scales[group]));
+  uint16_t* dst = (is_v ? v_pool : k_pool) + codec_pool_elem(a, gi, part);
+#pragma unroll
+  for (int h = 0; h < 8 / kL; ++h) {
+    const int chunk = part + kL * h;
+    int c[8];
+    if constexpr (kBits == 8) {
+      const uint2 w = *reinterpret_cast<const uint2*>(codes + e + 8 * chunk);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        c[i] = static_cast<int8_t>(w.x >> (8 * i));
+        c[4 + i] = static_cast<int8_t>(w.y >> (8 * i));
+      }
+    } else {
+      const uint32_t w = *reinterpret_cast<const uint32_t*>(codes + e / 2 + 4 * chunk);
+#pragma unroll
+      for (int i = 0; i < 8; ++i) c[i] = static_cast<int>(static_cast<int32_t>(w << (28 - 4 * i)) >> 28);
+    }
+    f32x4 lo, hi;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      c[i] = static_cast<int8_t>(w.x >> (8 * i));
-      c[4 + i] = static_cast<int8_t>(w.y >> (8 * i));
+      lo[i] = sf * static_cast<float>(c[i]);
+      hi[i] = sf * static_cast<float>(c[4 + i]);
     }
-  } else {
-    const uint32_t w = *reinterpret_cast<const uint32_t*>(codes + e / 2);
-#pragma unroll
-    for (int i = 0; i < 8; ++i) c[i] = static_cast<int>(static_cast<int32_t>(w << (28 - 4 * i)) >> 28);
+    const uint2 plo = __builtin_bit_cast(uint2, pack_bf16x4(lo));
+    const uint2 phi = __builtin_bit_cast(uint2, pack_bf16x4(hi));
+    *reinterpret_cast<u32x4*>(dst + 8 * kL * h) = u32x4{plo.x, plo.y, phi.x, phi.y};
   }
-  const float sf = static_cast<float>(__builtin_bit_cast(_Float16, scales[group]));
-  f32x4 lo, hi;
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    lo[i] = sf * static_cast<float>(c[i]);
-    hi[i] = sf * static_cast<float>(c[4 + i]);
-  }
-  const uint2 plo = __builtin_bit_cast(uint2, pack_bf16x4(lo));
-  const uint2 phi = __builtin_bit_cast(uint2, pack_bf16x4(hi));
-  *reinterpret_cast<u32x4*>((is_v ? v_pool : k_pool) + codec_pool_elem(a, gi, part)) = u32x4{plo.x, plo.y, phi.x, phi.y};
 }
 
 // ---------------------------------------------------------------------------
@@ -2199,7 +2236,7 @@ int run_attention(const char* fn, const pkv_pool_desc* desc, const void* k_pool,
 
 int codec_setup(const char* fn, const pkv_pool_desc* desc, const void* k_pool, const void* v_pool,
                 const int32_t* block_table, int32_t n_positions, int32_t bits, const void* payload, CodecArgs* a,
-                int64_t* blocks) {
+                int64_t* groups) {
   int rc = check_desc(desc, fn);
   if (rc != PKV_OK) return rc;
   if (desc->dtype != PKV_BF16) return fail(PKV_ERR_UNSUPPORTED, std::string(fn) + ": bf16 pools only");
@@ -2219,7 +2256,7 @@ int codec_setup(const char* fn, const pkv_pool_desc* desc, const void* k_pool, c
   a->groups_per_tensor = static_cast<int64_t>(n_positions) * desc->num_kv_heads * (desc->head_dim / 64);
   if (2 * a->groups_per_tensor * 8 + kThreads > INT32_MAX)
     return fail(PKV_ERR_UNSUPPORTED, std::string(fn) + ": prefix too long");
-  *blocks = (2 * a->groups_per_tensor * 8 + kThreads - 1) / kThreads;
+  *groups = 2 * a->groups_per_tensor;   // K and V groups; each kernel sizes its grid by its lanes per group
   return PKV_OK;
 }
 
@@ -2317,13 +2354,14 @@ size_t pkv_codec_payload_bytes(int32_t n_positions, int32_t num_kv_heads, int32_
 int pkv_codec_encode(const pkv_pool_desc* desc, const void* k_pool, const void* v_pool, const int32_t* block_table,
                      int32_t n_positions, int32_t bits, void* payload, void* stream) {
   CodecArgs a{};
-  int64_t blocks = 0;
-  int rc = codec_setup("pkv_codec_encode", desc, k_pool, v_pool, block_table, n_positions, bits, payload, &a, &blocks);
+  int64_t groups = 0;
+  int rc = codec_setup("pkv_codec_encode", desc, k_pool, v_pool, block_table, n_positions, bits, payload, &a, &groups);
   if (rc != PKV_OK || n_positions == 0) return rc;
   uint8_t* codes = static_cast<uint8_t*>(payload);
   uint16_t* scales = reinterpret_cast<uint16_t*>(codes + 2 * a.groups_per_tensor * 64 * bits / 8);
   hipStream_t st = static_cast<hipStream_t>(stream);
   (void)hipGetLastError();
+  const int64_t blocks = (groups * kCodecLanes + kThreads - 1) / kThreads;
   if (bits == 8)
     codec_encode_kernel<8><<<dim3(static_cast<unsigned>(blocks)), dim3(kThreads), 0, st>>>(
         a, static_cast<const uint16_t*>(k_pool), static_cast<const uint16_t*>(v_pool), codes, scales);
@@ -2339,19 +2377,21 @@ int pkv_codec_encode(const pkv_pool_desc* desc, const void* k_pool, const void* 
 int pkv_codec_decode(const pkv_pool_desc* desc, void* k_pool, void* v_pool, const int32_t* block_table,
                      int32_t n_positions, int32_t bits, const void* payload, void* stream) {
   CodecArgs a{};
-  int64_t blocks = 0;
-  int rc = codec_setup("pkv_codec_decode", desc, k_pool, v_pool, block_table, n_positions, bits, payload, &a, &blocks);
+  int64_t groups = 0;
+  int rc = codec_setup("pkv_codec_decode", desc, k_pool, v_pool, block_table, n_positions, bits, payload, &a, &groups);
   if (rc != PKV_OK || n_positions == 0) return rc;
   const uint8_t* codes = static_cast<const uint8_t*>(payload);
   const uint16_t* scales = reinterpret_cast<const uint16_t*>(codes + 2 * a.groups_per_tensor * 64 * bits / 8);
   hipStream_t st = static_cast<hipStream_t>(stream);
   (void)hipGetLastError();
   if (bits == 8)
-    codec_decode_kernel<8><<<dim3(static_cast<unsigned>(blocks)), dim3(kThreads), 0, st>>>(
-        a, static_cast<uint16_t*>(k_pool), static_cast<uint16_t*>(v_pool), codes, scales);
+    codec_decode_kernel<8, PKV_RESTORE_LANES_Q8>
+        <<<dim3(static_cast<unsigned>((groups * PKV_RESTORE_LANES_Q8 + kThreads - 1) / kThreads)), dim3(kThreads), 0,
+            st>>>(a, static_cast<uint16_t*>(k_pool), static_cast<uint16_t*>(v_pool), codes, scales);
   else
-    codec_decode_kernel<4><<<dim3(static_cast<unsigned>(blocks)), dim3(kThreads), 0, st>>>(
-        a, static_cast<uint16_t*>(k_pool), static_cast<uint16_t*>(v_pool), codes, scales);
+    codec_decode_kernel<4, PKV_RESTORE_LANES_Q4>
+        <<<dim3(static_cast<unsigned>((groups * PKV_RESTORE_LANES_Q4 + kThreads - 1) / kThreads)), dim3(kThreads), 0,
+            st>>>(a, static_cast<uint16_t*>(k_pool), static_cast<uint16_t*>(v_pool), codes, scales);
   hipError_t err = hipGetLastError();
   if (err != hipSuccess)
     return fail(PKV_ERR_DEVICE, std::string("pkv_codec_decode: launch failed: ") + hipGetErrorString(err));
