@@ -87,6 +87,11 @@ def parse():
     ap.add_argument("--copy-pairs", type=int, default=4096,
                     help="page pairs of the copy-on-write page-copy leg (0 disables it)")
     ap.add_argument("--codec", type=int, default=1, help="time the Q8 / Q4 KV codec leg (1) or not (0)")
+    ap.add_argument("--read-probe", type=int, default=1,
+                    help="measure the streaming HBM read ceiling with pkv_stream_read (1) or not (0)")
+    ap.add_argument("--rewind", type=int, default=1, help="time the KV rewind append workload (1) or not (0)")
+    ap.add_argument("--spec", type=int, default=1,
+                    help="time the long-context speculative-rollback workload (1) or not (0)")
     ap.add_argument("--retention-docs", type=int, default=100_000,
                     help="documents of the host retention-pool leg (0 disables it)")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
@@ -203,6 +208,185 @@ def prefill_leg(args, torch, pkv, synth, dev: str) -> dict:
             "algorithmic_flops_per_launch": flops,
             "unmasked_pairs": pairs,
         },
+    }
+
+
+def read_probe_leg(args, torch, pkv, dev: str) -> dict:
+    """Practical HBM read ceiling: pkv_stream_read (a plain grid-stride
+    streaming read with 16-byte loads, eight in flight per thread) over a
+    4 GiB buffer, far beyond the 256 MB Infinity Cache, for a few grid sizes;
+    the best is reported beside the 8 TB/s nominal peak."""
+    nbytes = 4 << 30
+    buf = torch.zeros(nbytes // 4, dtype=torch.int32, device=dev)
+    best = None
+    for grid in (2048, 4096, 8192, 16384, 32768, 65535):
+        sums = torch.empty(grid, dtype=torch.int32, device=dev)
+        call = pkv.bind_stream_read(buf, sums)
+        for _ in range(2):
+            call()
+        torch.cuda.synchronize()
+        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(10)]
+        for a, b in evs:
+            a.record()
+            call()
+            b.record()
+        torch.cuda.synchronize()
+        t = float(np.median([a.elapsed_time(b) for a, b in evs])) / 1e3
+        if best is None or t < best[1]:
+            best = (grid, t)
+    del buf
+    torch.cuda.empty_cache()
+    grid, t = best
+    return {"kernel": "pkv_stream_read (stream_read_kernel)", "bytes": nbytes, "grid": grid,
+            "kernel_median_us": round(t * 1e6, 1), "gbs": round(nbytes / t / 1e9, 1),
+            "frac_of_nominal": round(nbytes / t / 1e9 / HBM_PEAK_GBS, 4)}
+
+
+def _append_roofline(kv_bytes: int, qo_bytes: int, t_s: float, traffic_key, kernel: str, timed_ms) -> dict:
+    alg = kv_bytes + qo_bytes
+    achieved = alg / t_s / 1e9
+    return {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+            "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": measured_traffic(traffic_key) if traffic_key else None,
+            "kernel": kernel, "kernel_avg_us": round(t_s * 1e6, 1),
+            "kernel_median_us": round(float(np.median(timed_ms)) * 1e3, 1), "algorithmic_bytes_per_launch": alg}
+
+
+def rewind_leg(args, torch, pkv, dev: str) -> dict:
+    """KV rewind: 1,000 documents of 300 cached positions (16-position pages
+    over a shuffled 32,768-page pool, 32 / 8 heads of 128, bf16).  One pass
+    reserves 50 positions per document, stores the question's K/V (store_kv,
+    50,000 tokens) and runs a causal 50-query append per document against its
+    300 cached positions (prefill_append); the documents are then truncated
+    back to 300 on the host (untimed), which hands the same pages back.
+    Values are N(0,1) drawn on the device; lengths and placement come from
+    the allocator."""
+    n_docs, doc_len, q_len, ps, hq, hkv, D, num_pages = 1000, 300, 50, 16, 32, 8, 128, 32_768
+    desc = pkv.PoolDesc(pkv.PKV_BF16, num_pages, ps, hkv, D)
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(4000 + args.seed)
+    k_pool = torch.randn(desc.pool_shape, generator=gen, device=dev).to(torch.bfloat16)
+    v_pool = torch.randn(desc.pool_shape, generator=gen, device=dev).to(torch.bfloat16)
+    order = np.random.default_rng(4100 + args.seed).permutation(num_pages).astype(np.int32)
+    alloc = pkv.Allocator(num_pages, ps, order)
+    seqs = np.array([alloc.seq_new() for _ in range(n_docs)], np.int32)
+    alloc.prepare_step(seqs, np.full(n_docs, doc_len, np.int32), 0)      # the cached documents
+    n_new = np.full(n_docs, q_len, np.int32)
+    stride = -(-(doc_len + q_len) // ps)
+    slots, bt, lens = alloc.prepare_step(seqs, n_new, stride)
+    d_slots, d_bt, d_lens = (torch.from_numpy(x.copy()).to(dev) for x in (slots, bt, lens))
+    cu = torch.from_numpy(np.concatenate([[0], np.cumsum(n_new)]).astype(np.int32)).to(dev)
+    q = torch.randn((n_docs * q_len, hq, D), generator=gen, device=dev).to(torch.bfloat16)
+    k_new = torch.randn((n_docs * q_len, hkv, D), generator=gen, device=dev).to(torch.bfloat16)
+    v_new = torch.randn((n_docs * q_len, hkv, D), generator=gen, device=dev).to(torch.bfloat16)
+    out = torch.empty_like(q)
+    max_len = doc_len + q_len
+    ws = torch.empty(max(16, pkv.workspace_bytes(desc, n_docs, hq, q_len, max_len)), dtype=torch.uint8, device=dev)
+    scale = 1.0 / float(np.sqrt(D))
+    store = pkv.bind_store_kv(desc, k_pool, v_pool, k_new, v_new, d_slots)
+    append = pkv.bind_prefill_append(desc, k_pool, v_pool, q, cu, d_bt, d_lens, q_len, max_len, scale, out, ws)
+    reps = 12
+    evs = [tuple(torch.cuda.Event(enable_timing=True) for _ in range(3)) for _ in range(reps)]
+    for i in range(reps + 2):
+        ev = evs[i - 2] if i >= 2 else None
+        if ev:
+            ev[0].record()
+        store()
+        if ev:
+            ev[1].record()
+        append()
+        if ev:
+            ev[2].record()
+        torch.cuda.synchronize()
+        # rewind to the documents, last first, so the free stack hands document
+        # 0's pages back first and the next question reuses the same pages
+        for x in seqs[::-1].tolist():
+            alloc.truncate(x, doc_len)
+        s2, b2, l2 = alloc.prepare_step(seqs, n_new, stride)
+        assert np.array_equal(s2, slots) and np.array_equal(b2, bt), "truncate then reserve must reuse the pages"
+    store_ms = np.array([a.elapsed_time(b) for a, b, _ in evs])
+    attn_ms = np.array([b.elapsed_time(c) for _, b, c in evs])
+    assert torch.isfinite(out.float()).all(), "non-finite append output"
+    attn_s = float(attn_ms.mean()) / 1e3
+    pass_s = attn_s + float(store_ms.mean()) / 1e3
+    kv = n_docs * max_len * kv_bytes_per_position(hkv, D, 2)
+    qo = 2 * q.numel() * 2
+    return {
+        "workload": "KV rewind: 1,000 documents x 300 cached positions, page_size 16, 32,768-page shuffled pool, "
+                    "32 q / 8 KV heads, head_dim 128, bf16; pass = store_kv of 50,000 question tokens + one causal "
+                    "50-query prefill_append per document over its 350 positions",
+        "value": round(n_docs * q_len / pass_s, 1), "unit": "tokens/s", "reps": reps,
+        "new_tokens_per_pass": n_docs * q_len, "tokens_if_recomputed": n_docs * max_len,
+        "store_kv_avg_us": round(float(store_ms.mean()) * 1e3, 1),
+        "roofline": _append_roofline(kv, qo, attn_s, None,
+                                     "pkv_prefill_append (prefill_schedule_kernel + paged_prefill_kernel)", attn_ms),
+    }
+
+
+def spec_leg(args, torch, pkv, synth, dev: str) -> dict:
+    """Long-context decode with speculative rollback: 8 sequences with
+    contexts U{32K..128K} (the lengths of the seeded workload), 64-position
+    pages over a shuffled pool twice the live size, 64 q / 8 KV heads of 128,
+    bf16.  A step reserves 5 drafts per sequence, stores their K/V (40
+    tokens) and runs a 5-query causal append (the split decode kernel and its
+    merge); then each sequence keeps a random 0..5 drafts (host truncate,
+    untimed).  16 steps."""
+    B, drafts, steps, ps, hq, hkv, D = 8, 5, 16, 64, 64, 8, 128
+    ctx = synth.generator(5, "lengths", args.seed).integers(32_768, 131_072, size=B, endpoint=True).astype(np.int64)
+    keep = np.random.default_rng(5100 + args.seed).integers(0, drafts + 1, size=(steps, B))
+    num_pages = int(2 * sum(-(-int(x + steps * drafts) // ps) for x in ctx))
+    desc = pkv.PoolDesc(pkv.PKV_BF16, num_pages, ps, hkv, D)
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(5000 + args.seed)
+    k_pool = torch.randn(desc.pool_shape, generator=gen, device=dev).to(torch.bfloat16)
+    v_pool = torch.randn(desc.pool_shape, generator=gen, device=dev).to(torch.bfloat16)
+    order = np.random.default_rng(5200 + args.seed).permutation(num_pages).astype(np.int32)
+    alloc = pkv.Allocator(num_pages, ps, order)
+    seqs = np.array([alloc.seq_new() for _ in range(B)], np.int32)
+    alloc.prepare_step(seqs, ctx.astype(np.int32), 0)
+    max_len = int(ctx.max()) + steps * drafts
+    stride = -(-max_len // ps)
+    n_new = np.full(B, drafts, np.int32)
+    cu = torch.from_numpy(np.arange(0, (B + 1) * drafts, drafts, dtype=np.int32)).to(dev)
+    q = torch.randn((B * drafts, hq, D), generator=gen, device=dev).to(torch.bfloat16)
+    k_new = torch.randn((B * drafts, hkv, D), generator=gen, device=dev).to(torch.bfloat16)
+    v_new = torch.randn((B * drafts, hkv, D), generator=gen, device=dev).to(torch.bfloat16)
+    out = torch.empty_like(q)
+    ws = torch.empty(max(16, pkv.workspace_bytes(desc, B, hq, drafts, max_len)), dtype=torch.uint8, device=dev)
+    scale = 1.0 / float(np.sqrt(D))
+    store_ms, attn_ms, kv = [], [], []
+    for st in range(steps + 2):                 # two untimed warm-up steps, then 16
+        slots, bt, lens = alloc.prepare_step(seqs, n_new, stride)
+        d_slots, d_bt, d_lens = (torch.from_numpy(x.copy()).to(dev) for x in (slots, bt, lens))
+        ev = tuple(torch.cuda.Event(enable_timing=True) for _ in range(3))
+        ev[0].record()
+        pkv.store_kv(desc, k_pool, v_pool, k_new, v_new, d_slots)
+        ev[1].record()
+        pkv.prefill_append(desc, k_pool, v_pool, q, cu, d_bt, d_lens, drafts, max_len, scale, out, ws)
+        ev[2].record()
+        torch.cuda.synchronize()
+        if st >= 2:
+            store_ms.append(ev[0].elapsed_time(ev[1]))
+            attn_ms.append(ev[1].elapsed_time(ev[2]))
+            kv.append(int(lens.astype(np.int64).sum()) * kv_bytes_per_position(hkv, D, 2))
+        k = keep[(st - 2) % steps] if st >= 2 else np.zeros(B, np.int64)
+        for b, x in enumerate(seqs.tolist()):
+            alloc.truncate(x, int(lens[b]) - drafts + int(k[b]))
+    assert torch.isfinite(out.float()).all(), "non-finite append output"
+    attn_ms = np.array(attn_ms)
+    attn_s = float(attn_ms.mean()) / 1e3
+    step_s = attn_s + float(np.mean(store_ms)) / 1e3
+    qo = 2 * q.numel() * 2
+    return {
+        "workload": "long-context decode + speculative rollback: 8 sequences, contexts U{32K..128K}, page_size 64, "
+                    f"{num_pages:,}-page shuffled pool, 64 q / 8 KV heads, head_dim 128, bf16; step = store_kv of 5 "
+                    "drafts per sequence + one 5-query causal prefill_append (split decode kernel + merge), then "
+                    "keep 0..5 drafts",
+        "value": round(float(np.mean(kv)) / step_s / 1e9, 1), "unit": "GB/s", "steps": steps,
+        "ms_per_step": round(step_s * 1e3, 3), "mean_context": round(float(np.mean(kv)) / 4096 / B, 1),
+        "store_kv_avg_us": round(float(np.mean(store_ms)) * 1e3, 1),
+        "roofline": _append_roofline(int(np.mean(kv)), qo, attn_s, None,
+                                     "pkv_prefill_append, 5 queries per sequence (paged_decode_kernel + "
+                                     "merge_segments_kernel)", attn_ms),
     }
 
 
@@ -636,6 +820,17 @@ def main():
         rec["retention"] = retention_leg(args, pkv)
     if args.prefill_reps > 0:
         rec["prefill_append"] = prefill_leg(args, torch, pkv, synth, dev)
+    if args.rewind:
+        rec["rewind_append"] = rewind_leg(args, torch, pkv, dev)
+    if args.spec:
+        rec["spec_rollback"] = spec_leg(args, torch, pkv, synth, dev)
+    if args.read_probe:
+        probe = read_probe_leg(args, torch, pkv, dev)
+        rec["hbm_read_probe"] = probe
+        for obj in [rec] + [rec[k] for k in ("int8_decode", "copy_pages", "rewind_append", "spec_rollback") if k in rec]:
+            r = obj.get("roofline")
+            if r and r.get("bound") == "hbm":
+                r["frac_of_measured_read"] = round(r["achieved"] / probe["gbs"], 4)
     if args.copy_calibration_mib > 0:
         n_f32 = args.copy_calibration_mib * (1 << 20) // 4
         src = torch.ones(n_f32, dtype=torch.float32, device=dev)

@@ -388,6 +388,21 @@ int pkv_validate_tables(const pkv_pool_desc* desc, const int32_t* block_tables, 
                         int32_t bt_stride, const int32_t* seq_lens, const int32_t* cu_q,
                         int32_t max_q_per_seq);
 
+/* ---------------------------------------------------------------------------
+ * Measurement aid (not part of the paged method): the HBM read bandwidth a
+ * plain streaming kernel reaches on this device, the practical ceiling the
+ * memory-bound kernels above are compared with.
+ *
+ * Reads `bytes` (a multiple of 16) of device memory at `buf` (16-byte
+ * aligned) once, with coalesced 16-byte loads from a grid-stride loop of
+ * n_partials workgroups (1..65535).  Workgroup i writes partial_sums[i] =
+ * the sum modulo 2^32 of the 32-bit words it read, so the sum of all
+ * partials is the sum of every word of the buffer modulo 2^32 (which keeps
+ * the loads from being elided and lets a test check that every byte was
+ * read once).  partial_sums: device uint32 [n_partials], caller-owned.
+ * Errors: INVALID_ARG, DEVICE. */
+int pkv_stream_read(const void* buf, size_t bytes, uint32_t* partial_sums, int32_t n_partials, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -409,6 +409,22 @@ def copy_pages(desc: PoolDesc, k_pool, v_pool, copies, stream=None) -> None:
                                      _dev(copies, "copies", torch.int32), n, _stream(stream)))
 
 
+def bind_stream_read(buf, partial_sums, stream=None) -> BoundCall:
+    """pkv_stream_read with its arguments bound: read every byte of the device
+    tensor ``buf`` once; ``partial_sums`` (device int32/uint32 [n]) receives the
+    per-workgroup sums modulo 2^32 of its 32-bit words."""
+    nbytes = buf.numel() * buf.element_size()
+    if partial_sums.element_size() != 4 or not partial_sums.is_contiguous():
+        raise ValueError("partial_sums must be a contiguous 32-bit tensor")
+    args = (_dev(buf, "buf"), nbytes, _dev(partial_sums, "partial_sums"), int(partial_sums.numel()), _stream(stream))
+    return BoundCall(_lib.lib().pkv_stream_read, args, (buf, partial_sums))
+
+
+def stream_read(buf, partial_sums, stream=None) -> None:
+    """Streaming read of a device buffer (a bandwidth measurement aid)."""
+    bind_stream_read(buf, partial_sums, stream)()
+
+
 def codec_payload_bytes(n_positions: int, num_kv_heads: int, head_dim: int, bits: int) -> int:
     n = int(_lib.lib().pkv_codec_payload_bytes(n_positions, num_kv_heads, head_dim, bits))
     if n == 0 and n_positions > 0:

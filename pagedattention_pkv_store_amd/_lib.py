@@ -45,6 +45,7 @@ _SIGNATURES = {
     "pkv_fork": (c_int, [c_void_p, c_int32, c_int32]),
     "pkv_reserve_cow": (c_int, [c_void_p, c_int32, c_int32, i32p, i32p]),
     "pkv_copy_pages": (c_int, [POINTER(PoolDescC), c_void_p, c_void_p, c_void_p, c_int32, c_void_p]),
+    "pkv_stream_read": (c_int, [c_void_p, c_size_t, c_void_p, c_int32, c_void_p]),
     "pkv_retention_add": (c_int, [c_void_p, c_int32, ctypes.c_double, ctypes.c_double]),
     "pkv_retention_evict": (c_int, [c_void_p, ctypes.c_int64, i32p, c_int32, i32p]),
     "pkv_retention_take": (c_int, [c_void_p, c_int32, i32p]),

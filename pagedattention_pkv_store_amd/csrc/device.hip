@@ -1112,7 +1112,10 @@ constexpr int kPfRb = PKV_PREFILL_ROW_BLOCKS;   // 16-row MFMA blocks per wave
 constexpr int kPfWaves = PKV_PREFILL_WAVES;
 constexpr int kPfShortWaves = 4;
 constexpr int kPfShortKeys = 64;
-constexpr int kPfShortCtx = 2048;
+#ifndef PKV_PREFILL_SHORT_CTX
+#define PKV_PREFILL_SHORT_CTX 2048
+#endif
+constexpr int kPfShortCtx = PKV_PREFILL_SHORT_CTX;
 #ifndef PKV_PREFILL_KEYS
 #define PKV_PREFILL_KEYS 128
 #endif
@@ -1915,6 +1918,38 @@ __global__ __launch_bounds__(kThreads) void codec_decode_kernel(CodecArgs a, uin
   }
 }
 
+// Streaming read of n16 16-byte chunks: a grid-stride loop, eight loads in
+// flight per thread; workgroup i writes the sum modulo 2^32 of the words it
+// read to sums[i].
+__global__ __launch_bounds__(kThreads) void stream_read_kernel(const u32x4* __restrict__ src, int64_t n16,
+                                                                uint32_t* __restrict__ sums) {
+  __shared__ uint32_t s_part[kThreads / kWave];
+  const int64_t stride = static_cast<int64_t>(gridDim.x) * kThreads;
+  int64_t i = static_cast<int64_t>(blockIdx.x) * kThreads + threadIdx.x;
+  uint32_t acc = 0;
+  for (; i + 7 * stride < n16; i += 8 * stride) {
+    u32x4 v[8];
+#pragma unroll
+    for (int k = 0; k < 8; ++k) v[k] = src[i + k * stride];
+#pragma unroll
+    for (int k = 0; k < 8; ++k) acc += v[k][0] + v[k][1] + v[k][2] + v[k][3];
+  }
+  for (; i < n16; i += stride) {
+    const u32x4 v = src[i];
+    acc += v[0] + v[1] + v[2] + v[3];
+  }
+#pragma unroll
+  for (int off = kWave / 2; off >= 1; off >>= 1) acc += __shfl_xor(acc, off);
+  if ((threadIdx.x & (kWave - 1)) == 0) s_part[threadIdx.x / kWave] = acc;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    uint32_t t = 0;
+#pragma unroll
+    for (int w = 0; w < kThreads / kWave; ++w) t += s_part[w];
+    sums[blockIdx.x] = t;
+  }
+}
+
 // ---------------------------------------------------------------------------
 // host-side launch planning
 // ---------------------------------------------------------------------------
@@ -2341,6 +2376,23 @@ int pkv_copy_pages(const pkv_pool_desc* desc, void* k_pool, void* v_pool, const 
   hipError_t err = hipGetLastError();
   if (err != hipSuccess)
     return fail(PKV_ERR_DEVICE, std::string("pkv_copy_pages: launch failed: ") + hipGetErrorString(err));
+  return PKV_OK;
+}
+
+int pkv_stream_read(const void* buf, size_t bytes, uint32_t* partial_sums, int32_t n_partials, void* stream) {
+  if (n_partials < 1 || n_partials > 65535)
+    return fail(PKV_ERR_INVALID_ARG, "pkv_stream_read: n_partials must be in 1..65535");
+  if (bytes % 16) return fail(PKV_ERR_INVALID_ARG, "pkv_stream_read: bytes must be a multiple of 16");
+  if (!partial_sums || (bytes > 0 && !buf)) return fail(PKV_ERR_INVALID_ARG, "pkv_stream_read: NULL device pointer");
+  if (!aligned16(buf) || (reinterpret_cast<uintptr_t>(partial_sums) & 3u))
+    return fail(PKV_ERR_INVALID_ARG, "pkv_stream_read: misaligned device pointer");
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  (void)hipGetLastError();
+  stream_read_kernel<<<dim3(static_cast<unsigned>(n_partials)), dim3(kThreads), 0, st>>>(
+      static_cast<const u32x4*>(buf), static_cast<int64_t>(bytes / 16), partial_sums);
+  hipError_t err = hipGetLastError();
+  if (err != hipSuccess)
+    return fail(PKV_ERR_DEVICE, std::string("pkv_stream_read: launch failed: ") + hipGetErrorString(err));
   return PKV_OK;
 }
 

@@ -268,6 +268,20 @@ def test_error_paths(pkv_lib):
     assert "stride" in _lib.last_error()
 
 
+def test_stream_read_argument_checks(pkv_lib):
+    """Rejected before any device work: a bad workgroup count, a size that is
+    not whole 16-byte chunks, NULL or misaligned pointers."""
+    lib = pkv_lib
+    fake = 1 << 20                                    # never dereferenced: every call is rejected
+    assert lib.pkv_stream_read(fake, 64, fake, 0, None) == _lib.PKV_ERR_INVALID_ARG
+    assert lib.pkv_stream_read(fake, 64, fake, 65536, None) == _lib.PKV_ERR_INVALID_ARG
+    assert lib.pkv_stream_read(fake, 63, fake, 4, None) == _lib.PKV_ERR_INVALID_ARG
+    assert lib.pkv_stream_read(None, 64, fake, 4, None) == _lib.PKV_ERR_INVALID_ARG
+    assert lib.pkv_stream_read(fake, 64, None, 4, None) == _lib.PKV_ERR_INVALID_ARG
+    assert lib.pkv_stream_read(fake + 8, 64, fake, 4, None) == _lib.PKV_ERR_INVALID_ARG
+    assert "pkv_stream_read" in _lib.last_error()
+
+
 def test_validate_tables(pkv_lib):
     d = pkv.PoolDesc(pkv.PKV_BF16, 10, 4, 2, 128)
     bt = np.array([[1, 2, 0], [9, 0, 0]], np.int32)
