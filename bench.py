@@ -238,6 +238,7 @@ def read_probe_leg(args, torch, pkv, dev: str) -> dict:
     torch.cuda.empty_cache()
     grid, t = best
     return {"kernel": "pkv_stream_read (stream_read_kernel)", "bytes": nbytes, "grid": grid,
+            "traffic": measured_traffic("stream_read"),
             "kernel_median_us": round(t * 1e6, 1), "gbs": round(nbytes / t / 1e9, 1),
             "frac_of_nominal": round(nbytes / t / 1e9 / HBM_PEAK_GBS, 4)}
 
@@ -317,7 +318,7 @@ def rewind_leg(args, torch, pkv, dev: str) -> dict:
         "value": round(n_docs * q_len / pass_s, 1), "unit": "tokens/s", "reps": reps,
         "new_tokens_per_pass": n_docs * q_len, "tokens_if_recomputed": n_docs * max_len,
         "store_kv_avg_us": round(float(store_ms.mean()) * 1e3, 1),
-        "roofline": _append_roofline(kv, qo, attn_s, None,
+        "roofline": _append_roofline(kv, qo, attn_s, "rewind_append",
                                      "pkv_prefill_append (prefill_schedule_kernel + paged_prefill_kernel)", attn_ms),
     }
 
@@ -384,7 +385,7 @@ def spec_leg(args, torch, pkv, synth, dev: str) -> dict:
         "value": round(float(np.mean(kv)) / step_s / 1e9, 1), "unit": "GB/s", "steps": steps,
         "ms_per_step": round(step_s * 1e3, 3), "mean_context": round(float(np.mean(kv)) / 4096 / B, 1),
         "store_kv_avg_us": round(float(np.mean(store_ms)) * 1e3, 1),
-        "roofline": _append_roofline(int(np.mean(kv)), qo, attn_s, None,
+        "roofline": _append_roofline(int(np.mean(kv)), qo, attn_s, "spec_rollback",
                                      "pkv_prefill_append, 5 queries per sequence (paged_decode_kernel + "
                                      "merge_segments_kernel)", attn_ms),
     }

@@ -1611,12 +1611,19 @@ __global__ __launch_bounds__(kWave) void merge_chunks_kernel(AttnArgs args) {
 }
 
 // Log-sum-exp merge of the decode segments of one unit: the slots unit + w
-// of the waves w whose block ranges cut the unit.  Grid: one 4-wave
-// workgroup per unit, wave v folding rows v, v + 4, ...; units inside one
-// wave's range were written final and exit at once.
+// of the waves w whose block ranges cut the unit.  Grid: (units, row
+// groups); the 4-wave workgroup (u, y) folds rows y * kMergeRows + v,
+// + 4, ... below (y + 1) * kMergeRows with wave v; units inside one wave's
+// range were written final and exit at once.  One row block takes one row
+// group; more row blocks (many query rows, few units, many segments each)
+// spread each unit over 4 rows per workgroup.
+template <int RBW>
+constexpr int merge_rows_per_group() { return RBW == 1 ? 16 : 4; }
+
 template <typename T, int D, int RBW>
 __global__ __launch_bounds__(kThreads) void merge_segments_kernel(AttnArgs a, const int32_t* __restrict__ seq_blk) {
   constexpr int kRowsCap = 16 * RBW;
+  constexpr int kMergeRows = merge_rows_per_group<RBW>();
   const int u = blockIdx.x;
   const int hkv = a.num_kv_heads;
   const int b = u / hkv;
@@ -1630,7 +1637,8 @@ __global__ __launch_bounds__(kThreads) void merge_segments_kernel(AttnArgs a, co
   if (f == l) return;
   int q0, n_b, rows;
   decode_kv_end<RBW>(a, b, &q0, &n_b, &rows);
-  for (int r = threadIdx.x / kWave; r < rows; r += kThreads / kWave) {
+  const int r_end = min(rows, static_cast<int>(blockIdx.y + 1) * kMergeRows);
+  for (int r = static_cast<int>(blockIdx.y) * kMergeRows + threadIdx.x / kWave; r < r_end; r += kThreads / kWave) {
     const int qi = r / a.group;
     const int tok = q0 + qi;
     if (tok >= a.total_q) continue;
@@ -2115,7 +2123,9 @@ void launch_decode_t(const AttnArgs& a, const Plan& p, int n_seqs, char* ws, hip
     paged_decode_kernel<T, D, RBW, 1, kI8><<<p.grid, dim3(kWave), kLds, st>>>(a, seq_blk, a.seq_lens, a.cu_q, a.block_tables);
   else
     paged_decode_kernel<T, D, RBW, 2, kI8><<<p.grid, dim3(kWave), kLds, st>>>(a, seq_blk, a.seq_lens, a.cu_q, a.block_tables);
-  merge_segments_kernel<T, D, RBW><<<n_seqs * a.num_kv_heads, dim3(kThreads), 0, st>>>(a, seq_blk);
+  const dim3 merge_grid(static_cast<unsigned>(n_seqs * a.num_kv_heads),
+                        static_cast<unsigned>(16 * RBW / merge_rows_per_group<RBW>()));
+  merge_segments_kernel<T, D, RBW><<<merge_grid, dim3(kThreads), 0, st>>>(a, seq_blk);
 }
 
 // Upper bound on the prefill tile-rows the schedule kernel can list, from
