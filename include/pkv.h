@@ -12,8 +12,10 @@
  *   Host:   a page allocator (free stack, block tables, reference counts,
  *           reserve / truncate / release / share) and the prefix-sharing
  *           planner.  Pure C++ on the CPU; never touches the GPU.
- *   Device: pkv_store_kv, pkv_decode and pkv_prefill_append, hand-written
- *           HIP kernels for gfx950, enqueued on a caller-provided stream.
+ *   Device: pkv_store_kv, pkv_decode and pkv_prefill_append (plus
+ *           pkv_copy_pages, the group-wise codec and a streaming-read
+ *           probe), hand-written HIP kernels for gfx950, enqueued on a
+ *           caller-provided stream.
  *
  * Conventions for every function:
  *   - Every function returns int (PKV_OK = 0 or a negative PKV_ERR_* code),
