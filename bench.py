@@ -100,7 +100,7 @@ def parse():
     return ap.parse_args()
 
 
-def prefill_leg(args, torch, pkv, synth, dev: str) -> dict:
+def prefill_leg(args, torch, pkv, synth, dev: str, kv_int8: bool = False) -> dict:
     """The prefix-shared prefill workload: 256 agent-trace rows (the first
     three 1,000 / 1,400 / 1,900 tokens of one trace, the rest U{1000..8000}
     tokens of 31 others), 16-position pages over a shuffled 100,000-page pool,
@@ -116,9 +116,8 @@ def prefill_leg(args, torch, pkv, synth, dev: str) -> dict:
     t0 = time.perf_counter()
     order, parent, shared = pkv.plan_prefix([w.row_tokens(r) for r in range(n)], ps)
     plan_ms = (time.perf_counter() - t0) * 1e3
-    desc = pkv.PoolDesc(pkv.PKV_BF16, w.num_pages, ps, hkv, D)
-    k_pool = torch.full(desc.pool_shape, float("nan"), dtype=torch.bfloat16, device=dev)
-    v_pool = torch.full_like(k_pool, float("nan"))
+    desc = pkv.PoolDesc(pkv.PKV_I8 if kv_int8 else pkv.PKV_BF16, w.num_pages, ps, hkv, D)
+    k_pool, v_pool = desc.new_pools(dev, fill=0xFF if kv_int8 else float("nan"))
     alloc = pkv.Allocator(w.num_pages, ps, w.free_order)
     seqs = [-1] * n
     lens = w.row_len.astype(np.int64)
@@ -201,7 +200,7 @@ def prefill_leg(args, torch, pkv, synth, dev: str) -> dict:
             "peak": MFMA_BF16_PEAK_TFLOPS,
             "unit": "TFLOP/s",
             "frac": round(achieved / MFMA_BF16_PEAK_TFLOPS, 4),
-            "traffic": measured_traffic("prefill_append"),
+            "traffic": measured_traffic("prefill_append_int8" if kv_int8 else "prefill_append"),
             "kernel": "pkv_prefill_append (prefill_schedule_kernel + paged_prefill_kernel)",
             "kernel_avg_us": round(attn_s * 1e6, 1),
             "kernel_median_us": round(float(np.median(attn_ms)) * 1e3, 1),
@@ -821,6 +820,12 @@ def main():
         rec["retention"] = retention_leg(args, pkv)
     if args.prefill_reps > 0:
         rec["prefill_append"] = prefill_leg(args, torch, pkv, synth, dev)
+        if args.int8:
+            p8 = prefill_leg(args, torch, pkv, synth, dev, kv_int8=True)
+            p8["workload"] = ("the same prefix-shared prefill on INT8 pages (codes widened to bf16 as they are staged, "
+                              "key scales on the scores, value scales on the probabilities); bf16 queries and outputs")
+            p8["roofline"]["kernel"] = "pkv_prefill_append on PKV_I8 pools (prefill_schedule_kernel + paged_prefill_kernel)"
+            rec["int8_prefill_append"] = p8
     if args.rewind:
         rec["rewind_append"] = rewind_leg(args, torch, pkv, dev)
     if args.spec:
