@@ -48,7 +48,8 @@ Pinning status (what each function is checked against, in ``tests/``):
               tokens);
               brute force on tiny alphabets (maximal sharing, page identity).
               The parent-link chase is pinned only by the page-identity
-              invariant: the pages' example never walks a link.
+              invariant: the pages' example never walks a link, so the
+              choice among equivalent parents is parity unpinned.
   attention   closed forms, fp64 SDPA library special case, scalar brute force,
               permutation invariance.
   retention   hand-worked priorities and eviction orders from the page's

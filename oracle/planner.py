@@ -23,7 +23,9 @@ Readings (also listed in the design notes):
   current candidate has a parent and shares at least the new prefix length s,
   move to its parent.  The pages' example never walks a link, so this loop is
   pinned only by the invariant that the chosen parent's first s/page_size
-  pages are the very pages the preceding document holds.
+  pages are the very pages the preceding document holds: which of several
+  equivalent parents is chosen is parity unpinned (no attention output can
+  depend on it).
 * The cost rule ("savings exceed additional KV write costs") gives no
   constants; the plainest reading shares whenever at least one page is whole.
 """
