@@ -611,14 +611,14 @@ def decode_leg(args, torch, pkv, synth, w, dev: str, kv_int8: bool) -> dict:
     # Upload: step k's slots (int64 [B]), block tables (int32 [B][stride]) and
     # lengths (int32 [B]) go from pinned set k % NSETS to device set k % NSETS
     # in one copy, issued on a copy stream while the previous step's decode
-    # runs; the compute stream waits for it with an event that has normally
-    # fired long before (a copy in line with the kernels costs the copy
-    # engine's two hand-offs, about 30 us per step in a kernel trace).
-    # Before a set is refilled the host waits for a timing event recorded
-    # after the decode that last read it (at least 5 steps back, so it has
-    # long completed): the compute stream then carries one marker per step
-    # (the upload wait) plus the timing pair on every TIME_EVERY-th step.
-    # Each marker leaves the GPU idle for a few microseconds.
+    # runs; the host waits for its event, which has normally fired long
+    # before, before launching step k (a copy in line with the kernels costs
+    # the copy engine's two hand-offs, about 30 us per step in a kernel
+    # trace).  Before a set is refilled the host waits for a timing event
+    # recorded after the decode that last read it (at least 5 steps back, so
+    # it has long completed).  The compute stream then carries no marker but
+    # the timing pair on every TIME_EVERY-th step: each marker leaves the GPU
+    # idle for a few microseconds.
     NSETS, TIME_EVERY = 8, 4
     nbytes = B * 8 + B * stride * 4 + B * 4
 
@@ -677,7 +677,11 @@ def decode_leg(args, torch, pkv, synth, w, dev: str, kv_int8: bool) -> dict:
     def step(k: int, timed: bool):
         st = sets[k % NSETS]
         l_np = st["np"][2]
-        stream.wait_event(st["uploaded"])
+        # The host waits for this step's copy, which has normally completed
+        # during the previous decode; kernels launched after an event is
+        # observed complete see what the copy wrote, so the compute stream
+        # needs no cross-stream wait (a marker that idles the GPU ~6 us).
+        st["uploaded"].synchronize()
         st["store"]()
         marked = k % TIME_EVERY == 0
         if marked:
@@ -713,6 +717,17 @@ def decode_leg(args, torch, pkv, synth, w, dev: str, kv_int8: bool) -> dict:
 
     for slot in range(EV_RING):
         read_slot(slot)
+
+    # The last step's decode once more, its tables copied in stream order into
+    # a fresh buffer: the timed steps must have read exactly what they uploaded.
+    last = sets[(args.warmup + args.steps - 1) % NSETS]
+    fresh = torch.empty_like(last["dev"])
+    fresh.copy_(last["host"])
+    _, f_bt, f_lens = views(fresh)
+    out_check = torch.empty_like(out)
+    pkv.decode(desc, k_pool, v_pool, q, f_bt, f_lens, max_len, scale, out_check, ws)
+    torch.cuda.synchronize()
+    assert torch.equal(out, out_check), "the timed steps' decode differs from a stream-ordered rerun"
     dec_ms = np.array(dec_ms)
     assert torch.isfinite(out.float()).all(), "non-finite decode output"
     total_kv = float(sum(kv_bytes))
