@@ -133,6 +133,52 @@ def test_decode_bf16(n_seqs, len_lo, len_hi):
     _decode_full_check(w, s, seqs, out)
 
 
+@pytest.mark.parametrize("kv_int8", [False, True])
+def test_decode_many_sequences(kv_int8):
+    """300 sequences: each wave scans the block counts in five 64-sequence
+    chunks, and ranges start in every chunk."""
+    print(f"decode 300 sequences int8={kv_int8}", flush=True)
+    w = synth.decode_batch(n_seqs=300, len_lo=1, len_hi=400, num_pages=300 * 25 + 64, seed=300)
+    s, seqs, out = run_decode(w, kv_int8=kv_int8)
+    if kv_int8:
+        expect = ref.decode_reference(w, s.scale, kv_int8=True)
+        o = host_f64(out)
+        e = np.stack([np.stack([expect[(b, h)] for h in range(w.num_q_heads)]) for b in range(len(seqs))])
+        check_close(o, e, w.dtype, "int8 decode, 300 sequences")
+    else:
+        _decode_full_check(w, s, seqs, out)
+
+
+def test_short_append_many_sequences():
+    """Prefill/append with at most 3 new queries per sequence (the decode
+    kernel family) over 200 sequences, some with none, including those on
+    64-sequence chunk boundaries."""
+    rng = np.random.default_rng(200)
+    n = 200
+    hq, hkv, D = 32, 8, 128
+    n_new = rng.integers(0, 4, size=n)
+    for b in (0, 63, 64, 127, 128, 199):
+        n_new[b] = 0
+    n_new[1] = 3
+    lens = [int(x) for x in rng.integers(1, 300, size=n) + n_new]
+    pages = sum(-(-L // 16) for L in lens) + 8
+    s = Session.open(_Pools(synth.BF16, D, 16, hkv, pages, seed=7))
+    seqs = [s.alloc.seq_new() for _ in lens]
+    kv = [synth.normal_values(rng, (2, L, hkv, D), synth.BF16) for L in lens]
+    for b, seq in enumerate(seqs):
+        s.alloc.reserve(seq, lens[b])
+        s.store(seq, 0, kv[b][0], kv[b][1], synth.BF16)
+    qs = [synth.normal_values(rng, (int(k), hq, D), synth.BF16) for k in n_new]
+    out = host_f64(s.append(seqs, [int(k) for k in n_new], dev_tensor(np.concatenate(qs), synth.BF16)))
+    row = 0
+    for b in range(n):
+        if n_new[b]:
+            e = attend(synth.to_f64(qs[b], synth.BF16), synth.to_f64(kv[b][0], synth.BF16),
+                       synth.to_f64(kv[b][1], synth.BF16), s.scale)
+            check_close(out[row:row + n_new[b]], e, synth.BF16, f"short append seq {b}")
+        row += int(n_new[b])
+
+
 def test_decode_gather_form_equals_logical():
     """A host copy of the device pools, read through the oracle's block tables,
     reproduces the logical K/V bit for bit (store_kv + slots placed every row)."""
@@ -389,10 +435,12 @@ class _Pools:
     (synth.BF16, 128, 1, 1, 1, [3000], [60]),
     (synth.BF16, 64, 16, 6, 3, [2500, 700], [100, 20]),
     (synth.F32, 64, 4, 4, 2, [100, 30], [70, 40]),
+    (synth.BF16, 128, 256, 16, 1, [600, 0], [100, 40]),
+    (synth.BF16, 64, 256, 32, 2, [2500], [33]),
 ])
 def test_prefill_variants(dtype, D, ps, hq, hkv, ctx, news):
     """Append of several queries per sequence over cached positions: GQA groups
-    1..16, page sizes 1..64 (power of two or not), one or several KV splits,
+    1..16, page sizes 1..256 (power of two or not), one or several KV splits,
     KV-head counts that do or do not fill blocks of 8 units."""
     print(f"prefill variant {dtype} D={D} ps={ps} hq={hq} hkv={hkv} ctx={ctx} new={news}", flush=True)
     rng = np.random.default_rng(D * 7 + ps)
