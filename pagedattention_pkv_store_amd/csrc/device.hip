@@ -191,6 +191,24 @@ __device__ __forceinline__ u32x4 i8x8_to_bf16(uint2 x) {
   return o;
 }
 
+// Eight int8 codes times their vector's scale -> eight bf16 (each product
+// rounded once, to nearest even).
+__device__ __forceinline__ u32x4 i8x8_scaled_to_bf16(uint2 x, float scale) {
+  u32x4 o;
+#pragma unroll
+  for (int w = 0; w < 2; ++w) {
+    const uint32_t v = w ? x.y : x.x;
+    const f32x4 f = {static_cast<float>(static_cast<int8_t>(v)) * scale,
+                     static_cast<float>(static_cast<int8_t>(v >> 8)) * scale,
+                     static_cast<float>(static_cast<int8_t>(v >> 16)) * scale,
+                     static_cast<float>(static_cast<int8_t>(v >> 24)) * scale};
+    const auto p = __builtin_bit_cast(uint2, pack_bf16x4(f));
+    o[2 * w] = p.x;
+    o[2 * w + 1] = p.y;
+  }
+  return o;
+}
+
 // Unit of the K/V loads: 16 bytes of bf16 / fp32 rows, or 8 INT8 codes (which
 // widen to 16 bytes of bf16, so staged rows are written in the same pattern).
 template <bool kI8>
@@ -1126,10 +1144,10 @@ template <int D>
 constexpr int pf_k_row_bytes() { return D * 2 + 16; }
 template <int D>
 constexpr int pf_v_row_bytes() { return D * 2 + 32; }
-// LDS of one staged K + V buffer (INT8 pages add the tile's key and value
-// scales), two buffers per workgroup.
+// LDS of one staged K + V buffer (INT8 pages add the tile's key scales),
+// two buffers per workgroup.
 template <int D, int kKeys, bool kI8>
-constexpr int pf_buf_bytes() { return kKeys * (pf_k_row_bytes<D>() + pf_v_row_bytes<D>() + (kI8 ? 8 : 0)); }
+constexpr int pf_buf_bytes() { return kKeys * (pf_k_row_bytes<D>() + pf_v_row_bytes<D>() + (kI8 ? 4 : 0)); }
 template <int D, int kKeys, bool kI8>
 constexpr int pf_lds_bytes() { return 2 * pf_buf_bytes<D, kKeys, kI8>(); }
 // Rows one wave stages per pass (a pass = one 16-byte chunk per thread).
@@ -1310,12 +1328,13 @@ __global__ __launch_bounds__(kPfThreads, kPfRb >= 3 ? 1 : 2) void paged_prefill_
     for (int c = 0; c < kChunks; ++c) {
       const int row = srow0 + c * kRowsPerPass;
       if constexpr (kI8) {
+        // keys stay exact codes (their scale multiplies the scores); values
+        // are staged dequantized, so the probabilities need no second copy
         *reinterpret_cast<u32x4*>(kb + row * kKRowB + spart * 16) = i8x8_to_bf16(kr[c]);
-        *reinterpret_cast<u32x4*>(vb + row * kVRowB + spart * 16) = i8x8_to_bf16(vr[c]);
+        *reinterpret_cast<u32x4*>(vb + row * kVRowB + spart * 16) = i8x8_scaled_to_bf16(vr[c], vsr[c]);
         if (spart == 0) {
           float* sc = reinterpret_cast<float*>(vb + kVTileB);
           sc[row] = ksr[c];
-          sc[kPfKeys + row] = vsr[c];
         }
       } else {
         *reinterpret_cast<u32x4*>(kb + row * kKRowB + spart * 16) = kr[c];
@@ -1369,8 +1388,8 @@ __global__ __launch_bounds__(kPfThreads, kPfRb >= 3 ? 1 : 2) void paged_prefill_
   const int k_lane = lrow * kKRowB + lgrp * (D / 4) * 2;
   const int v_lane = (4 * lgrp + (lrow >> 2)) * kVRowB + ((lrow & 3) >> 1) * 16 + (lrow & 1) * 8;
 
-  // kt, vt: the sub-tile's staged K and V rows; st (INT8): its key scales,
-  // value scales at st + kPfKeys.
+  // kt, vt: the sub-tile's staged K and V rows; st (INT8): its key scales
+  // (the values are staged already scaled).
   auto compute = [&](const char* kt, const char* vt, const float* st, int tb, auto mask_tag)
       __attribute__((always_inline)) {
     constexpr bool kMask = decltype(mask_tag)::value;
@@ -1392,12 +1411,10 @@ __global__ __launch_bounds__(kPfThreads, kPfRb >= 3 ? 1 : 2) void paged_prefill_
     }
     if constexpr (PKV_PREFILL_SETPRIO) __builtin_amdgcn_s_setprio(0);
     // INT8: a key's scale multiplies its scores (rows 4 lgrp + i of block kb)
-    f32x4 vsc[4];
     if constexpr (kI8) {
 #pragma unroll
       for (int kb = 0; kb < 4; ++kb) {
         const f32x4 ksc = *reinterpret_cast<const f32x4*>(st + kb * 16 + 4 * lgrp);
-        vsc[kb] = *reinterpret_cast<const f32x4*>(st + kPfKeys + kb * 16 + 4 * lgrp);
 #pragma unroll
         for (int rb = 0; rb < kPfRb; ++rb) s[kb][rb] *= ksc;
       }
@@ -1438,8 +1455,7 @@ __global__ __launch_bounds__(kPfThreads, kPfRb >= 3 ? 1 : 2) void paged_prefill_
     }
 #pragma unroll
     for (int ks = 0; ks < 2; ++ks) {
-      bf16x8 pk[kPfRb];   // probabilities: row sums (and PV for bf16 pages)
-      bf16x8 pv[kPfRb];   // INT8: probabilities times the value scales, for PV
+      bf16x8 pk[kPfRb];   // probabilities: row sums and PV
 #pragma unroll
       for (int rb = 0; rb < kPfRb; ++rb) {
 #pragma unroll
@@ -1448,12 +1464,7 @@ __global__ __launch_bounds__(kPfThreads, kPfRb >= 3 ? 1 : 2) void paged_prefill_
           const float e1 = fast_exp2(fmaf(s[2 * ks + 1][rb][i], c2, -muse[rb]));
           pk[rb][i] = static_cast<__bf16>(e0);
           pk[rb][4 + i] = static_cast<__bf16>(e1);
-          if constexpr (kI8) {
-            pv[rb][i] = static_cast<__bf16>(e0 * vsc[2 * ks][i]);
-            pv[rb][4 + i] = static_cast<__bf16>(e1 * vsc[2 * ks + 1][i]);
-          }
         }
-        if constexpr (!kI8) pv[rb] = pk[rb];
         lsum[rb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ones, pk[rb], lsum[rb], 0, 0, 0);
       }
 #pragma unroll
@@ -1464,7 +1475,7 @@ __global__ __launch_bounds__(kPfThreads, kPfRb >= 3 ? 1 : 2) void paged_prefill_
         const bf16x8 vf = __builtin_shufflevector(v0, v1, 0, 1, 2, 3, 4, 5, 6, 7);
 #pragma unroll
         for (int rb = 0; rb < kPfRb; ++rb)
-          o[d][rb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf, pv[rb], o[d][rb], 0, 0, 0);
+          o[d][rb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf, pk[rb], o[d][rb], 0, 0, 0);
       }
     }
   };
