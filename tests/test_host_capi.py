@@ -36,6 +36,60 @@ def test_library_exports_every_declared_function(pkv_lib):
     assert sorted(_lib.EXPORTED) == declared
 
 
+def _header_prototypes():
+    """{name: (return type, [parameter declarations])} of every function in pkv.h."""
+    with open(os.path.join(ROOT, "include", "pkv.h")) as f:
+        text = f.read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    text = re.sub(r"^\s*#.*$", "", text, flags=re.M)
+    protos = {}
+    for m in re.finditer(r"([A-Za-z_][\w\s\*]*?)\b(pkv_[a-z0-9_]+)\s*\(([^)]*)\)\s*;", text):
+        ret = " ".join(m.group(1).split())
+        params = [p.strip() for p in m.group(3).split(",") if p.strip() and p.strip() != "void"]
+        protos[m.group(2)] = (ret.split("\n")[-1], params)
+    return protos
+
+
+def test_binding_signatures_match_the_header():
+    """Every ctypes signature has the header's parameter count, and integer,
+    size and pointer parameters and results line up kind for kind."""
+    import ctypes
+    protos = _header_prototypes()
+    assert sorted(protos) == _header_functions()
+
+    def kind_c(decl):
+        if "*" in decl:
+            return "ptr"
+        if "size_t" in decl:
+            return "size"
+        if "double" in decl:
+            return "double"
+        if "float" in decl:
+            return "float"
+        return "int"
+
+    def kind_py(t):
+        if t is None:
+            return "void"
+        if t in (ctypes.c_size_t,):
+            return "size"
+        if t in (ctypes.c_double,):
+            return "double"
+        if t in (ctypes.c_float,):
+            return "float"
+        if t in (ctypes.c_int, ctypes.c_int32, ctypes.c_int64, ctypes.c_uint32):
+            return "int"
+        return "ptr"
+
+    for name, (ret, params) in protos.items():
+        res, args = _lib._SIGNATURES[name]
+        assert len(args) == len(params), (name, len(args), len(params))
+        for decl, t in zip(params, args):
+            assert kind_c(decl) == kind_py(t), (name, decl, t)
+        want = "void" if ret.endswith("void") and "*" not in ret else kind_c(ret)
+        assert kind_py(res) == want, (name, ret, res)
+
+
 def test_blog_example_through_capi(pkv_lib, golden):
     ex = golden("blog_block_example.json")
     a = pkv.Allocator(ex["capacity_blocks"], ex["block_size"], ex["free_order_reading"])
