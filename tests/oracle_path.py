@@ -78,7 +78,8 @@ def prefix_plan(w: synth.PrefixTraces):
     return plan_prefix([w.row_tokens(r).tolist() for r in range(len(w.row_len))], w.page_size)
 
 
-def prefix_reference_rows(w: synth.PrefixTraces, shared: List[int], scale: float, rows):
+def prefix_reference_rows(w: synth.PrefixTraces, shared: List[int], scale: float, rows,
+                          kv_int8: bool = False):
     """rows: iterable of (doc, i, h) with i the index among the doc's new queries."""
     grp = w.num_q_heads // w.num_kv_heads
     out = {}
@@ -86,8 +87,8 @@ def prefix_reference_rows(w: synth.PrefixTraces, shared: List[int], scale: float
         t = int(w.row_trace[d])
         pos = int(shared[d]) + i
         g = h // grp
-        out[(d, i, h)] = attend_row(f64(w.q[t, pos, h], w.dtype), f64(w.k[t, :pos + 1, g], w.dtype),
-                                    f64(w.v[t, :pos + 1, g], w.dtype), pos, scale)
+        out[(d, i, h)] = attend_row(f64(w.q[t, pos, h], w.dtype), kv_f64(w.k[t, :pos + 1, g], w.dtype, kv_int8),
+                                    kv_f64(w.v[t, :pos + 1, g], w.dtype, kv_int8), pos, scale)
     return out
 
 
