@@ -373,7 +373,10 @@ int pkv_decode(const pkv_pool_desc* desc, const void* k_pool, const void* v_pool
  *   cu_q:         device int32 [n_seqs + 1], non-decreasing, cu_q[0] = 0
  *   max_q_per_seq: host upper bound of n_b (queries beyond it are not computed)
  *   other arguments as for pkv_decode; workspace >= pkv_workspace_bytes(desc,
- *   n_seqs, num_q_heads, max_q_per_seq, max_seq_len).
+ *   n_seqs, num_q_heads, max_q_per_seq, max_seq_len).  On PKV_I8 pools the
+ *   MFMA kernel for more than 48 query rows per (sequence, KV head) attends
+ *   over bf16(code x scale) keys and values (the same product as the
+ *   page's folded scales, with the rounding on the staged vector).
  * Errors: INVALID_ARG, UNSUPPORTED, BUFFER_TOO_SMALL, DEVICE. */
 int pkv_prefill_append(const pkv_pool_desc* desc, const void* k_pool, const void* v_pool,
                        const void* q, int32_t total_q, const int32_t* cu_q, int32_t n_seqs,

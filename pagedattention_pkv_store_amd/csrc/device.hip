@@ -1144,10 +1144,10 @@ template <int D>
 constexpr int pf_k_row_bytes() { return D * 2 + 16; }
 template <int D>
 constexpr int pf_v_row_bytes() { return D * 2 + 32; }
-// LDS of one staged K + V buffer (INT8 pages add the tile's key scales),
-// two buffers per workgroup.
+// LDS of one staged K + V buffer (INT8 pages are staged dequantized, in the
+// same layout), two buffers per workgroup.
 template <int D, int kKeys, bool kI8>
-constexpr int pf_buf_bytes() { return kKeys * (pf_k_row_bytes<D>() + pf_v_row_bytes<D>() + (kI8 ? 4 : 0)); }
+constexpr int pf_buf_bytes() { return kKeys * (pf_k_row_bytes<D>() + pf_v_row_bytes<D>()); }
 template <int D, int kKeys, bool kI8>
 constexpr int pf_lds_bytes() { return 2 * pf_buf_bytes<D, kKeys, kI8>(); }
 // Rows one wave stages per pass (a pass = one 16-byte chunk per thread).
@@ -1209,8 +1209,9 @@ __device__ __forceinline__ bf16x4 lds_read_tr(const char* p) {
 
 // kPageMode 0: page_size a power of two >= the rows a wave stages per pass
 // (those rows then share one page: scalar lookup); 1: other powers of two;
-// 2: any page size.  kI8: INT8 pages, widened to bf16 as they are staged;
-// each tile's key and value scales are staged beside it.
+// 2: any page size.  kI8: INT8 pages, staged dequantized as bf16(code x
+// scale) in the bf16 tile layout, so the scores and probabilities take the
+// bf16 path unchanged.
 template <int D, int kPageMode, int kPfThreads, int kPfKeys, bool kI8>
 __global__ __launch_bounds__(kPfThreads, kPfRb >= 3 ? 1 : 2) void paged_prefill_kernel(AttnArgs a,
                                                                    const int32_t* __restrict__ row_off,
@@ -1227,8 +1228,7 @@ __global__ __launch_bounds__(kPfThreads, kPfRb >= 3 ? 1 : 2) void paged_prefill_
   constexpr int kQk = D / 32;                           // MFMAs per 16x16 score block
   constexpr int kDb = D / 16;                           // 16-dim blocks of O^T
   constexpr int kKTileB = kPfKeys * kKRowB;             // bytes of one staged K tile
-  constexpr int kVTileB = kPfKeys * kVRowB;
-  constexpr int kBufB = pf_buf_bytes<D, kPfKeys, kI8>();  // one K + V buffer (+ scales)
+  constexpr int kBufB = pf_buf_bytes<D, kPfKeys, kI8>();  // one K + V buffer
   static_assert(kChunks * kRowsPerPass == kPfKeys, "tile split");
   extern __shared__ __align__(16) char smem[];
 
@@ -1328,14 +1328,10 @@ __global__ __launch_bounds__(kPfThreads, kPfRb >= 3 ? 1 : 2) void paged_prefill_
     for (int c = 0; c < kChunks; ++c) {
       const int row = srow0 + c * kRowsPerPass;
       if constexpr (kI8) {
-        // keys stay exact codes (their scale multiplies the scores); values
-        // are staged dequantized, so the probabilities need no second copy
-        *reinterpret_cast<u32x4*>(kb + row * kKRowB + spart * 16) = i8x8_to_bf16(kr[c]);
+        // keys and values are staged dequantized, bf16(code x scale): the
+        // scores and probabilities then take the bf16 path unchanged
+        *reinterpret_cast<u32x4*>(kb + row * kKRowB + spart * 16) = i8x8_scaled_to_bf16(kr[c], ksr[c]);
         *reinterpret_cast<u32x4*>(vb + row * kVRowB + spart * 16) = i8x8_scaled_to_bf16(vr[c], vsr[c]);
-        if (spart == 0) {
-          float* sc = reinterpret_cast<float*>(vb + kVTileB);
-          sc[row] = ksr[c];
-        }
       } else {
         *reinterpret_cast<u32x4*>(kb + row * kKRowB + spart * 16) = kr[c];
         *reinterpret_cast<u32x4*>(vb + row * kVRowB + spart * 16) = vr[c];
@@ -1388,9 +1384,8 @@ __global__ __launch_bounds__(kPfThreads, kPfRb >= 3 ? 1 : 2) void paged_prefill_
   const int k_lane = lrow * kKRowB + lgrp * (D / 4) * 2;
   const int v_lane = (4 * lgrp + (lrow >> 2)) * kVRowB + ((lrow & 3) >> 1) * 16 + (lrow & 1) * 8;
 
-  // kt, vt: the sub-tile's staged K and V rows; st (INT8): its key scales
-  // (the values are staged already scaled).
-  auto compute = [&](const char* kt, const char* vt, const float* st, int tb, auto mask_tag)
+  // kt, vt: the sub-tile's staged K and V rows.
+  auto compute = [&](const char* kt, const char* vt, int tb, auto mask_tag)
       __attribute__((always_inline)) {
     constexpr bool kMask = decltype(mask_tag)::value;
     f32x4 s[4][kPfRb];
@@ -1410,15 +1405,6 @@ __global__ __launch_bounds__(kPfThreads, kPfRb >= 3 ? 1 : 2) void paged_prefill_
       }
     }
     if constexpr (PKV_PREFILL_SETPRIO) __builtin_amdgcn_s_setprio(0);
-    // INT8: a key's scale multiplies its scores (rows 4 lgrp + i of block kb)
-    if constexpr (kI8) {
-#pragma unroll
-      for (int kb = 0; kb < 4; ++kb) {
-        const f32x4 ksc = *reinterpret_cast<const f32x4*>(st + kb * 16 + 4 * lgrp);
-#pragma unroll
-        for (int rb = 0; rb < kPfRb; ++rb) s[kb][rb] *= ksc;
-      }
-    }
     // row maxima, then one (rarely taken) rescale branch for both row blocks
     float muse[kPfRb];
     bool up_any = false;
@@ -1499,11 +1485,10 @@ __global__ __launch_bounds__(kPfThreads, kPfRb >= 3 ? 1 : 2) void paged_prefill_
       if (w_active && tb <= w_qmax) {
         const char* kt = smem + (t & 1) * kBufB + sub * 64 * kKRowB;
         const char* vt = smem + (t & 1) * kBufB + kKTileB + sub * 64 * kVRowB;
-        const float* st = reinterpret_cast<const float*>(smem + (t & 1) * kBufB + kKTileB + kVTileB) + sub * 64;
         if (tb + 63 <= w_qmin)
-          compute(kt, vt, st, tb, std::integral_constant<bool, false>());
+          compute(kt, vt, tb, std::integral_constant<bool, false>());
         else
-          compute(kt, vt, st, tb, std::integral_constant<bool, true>());
+          compute(kt, vt, tb, std::integral_constant<bool, true>());
       }
     }
     stage((t + 1) & 1);
