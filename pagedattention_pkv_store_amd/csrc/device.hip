@@ -632,7 +632,8 @@ __global__ __launch_bounds__(kWave, RBW == 1 ? (kI8 ? PKV_DECODE_WAVES_PER_SIMD_
   constexpr int kGRowBytes = kI8 ? D : kRowBytes;       // bytes of a pool row
   constexpr int kCpr = kGRowBytes / kLdB;               // load units per pool row
   constexpr int kLoads = 16 * kGRowBytes / (kLdB * kWave); // loads per lane per pool per block
-  constexpr int kDepth = kI8 ? PKV_DECODE_DEPTH_I8 : kDecodeDepth;
+  // fp32 rows of 128 elements: one block in flight (two would spill)
+  constexpr int kDepth = kI8 ? PKV_DECODE_DEPTH_I8 : (kGRowBytes >= 512 ? 1 : kDecodeDepth);
   constexpr int kDl = D / 4;                            // dims per lane in the QK operands
   constexpr int kFragChunks = kDl * kEs / 16;           // 16-byte chunks of one lane's K fragment
   constexpr int kQkMfmas = kDl / Elem<T>::kQkPerMfma;
