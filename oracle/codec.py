@@ -13,8 +13,8 @@ Readings (also listed in the design notes):
 * Symmetric groups (one scale, no zero point, as the two bytes per group in
   eq. (7) allow): scale = max|x| / q_max with q_max = 2^(b-1) - 1 (127 for
   Q8, 7 for Q4), computed in fp32 and rounded to fp16 (nearest, ties to
-  even).  Codes use the stored scale through its fp32 reciprocal, one per
-  group: inv = 1 / scale16 (fp32), code = x * inv in fp32, rounded to nearest
+  even).  Codes use the stored scale: code = x / scale16, one IEEE fp32
+  division per element (correctly rounded), rounded to the nearest integer
   (ties to even), clamped to [-q_max, q_max]; a zero scale gives zero codes.
   Restoring computes scale16 * code in fp32 (exact) and rounds it to the
   pool's bf16.
@@ -61,8 +61,8 @@ def quantize_groups(x, bits: int) -> Tuple[np.ndarray, np.ndarray]:
     amax = np.max(np.abs(g), axis=-1)
     scale16 = (amax / qm).astype(np.float32).astype(np.float16)
     sf = scale16.astype(np.float32)[..., None]
-    inv = (np.float32(1) / np.where(sf > 0, sf, np.float32(1))).astype(np.float32)   # one per group
-    codes = np.rint((g * inv).astype(np.float32))
+    safe = np.where(sf > 0, sf, np.float32(1))
+    codes = np.rint((g / safe).astype(np.float32))
     codes = np.clip(codes, -qm, qm)
     codes = np.where(sf > 0, codes, 0.0)
     return codes.astype(np.int8).reshape(x32.shape), scale16

@@ -5,8 +5,11 @@
   layer, 179.75 MiB for a 15-layer Q8 prefix plus the 56 MiB boundary, 231 MiB
   for all 28 layers (tests/golden/rekv_bytes.json).
 * Codes worked out by hand from the reading (symmetric groups of 64, fp16
-  scale = max|x| / q_max, codes from the stored scale's fp32 reciprocal, ties
-  to even, Q4 low nibble first).
+  scale = max|x| / q_max, codes x / scale rounded to nearest with ties to
+  even, Q4 low nibble first), including an exact tie that a per-group
+  reciprocal would round the other way.
+* Codes equal the nearest integer to the exact rational quotient x / scale
+  wherever that quotient is not within fp32 rounding of a half-integer.
 * The symmetric quantizer's error bound, zero groups, pack/unpack inverses,
   and the payload layout decoding back to the same values.
 """
@@ -40,8 +43,7 @@ def test_payload_size_is_eq7_and_the_pages_figures(golden):
 
 def test_q8_hand_worked_group():
     # max|x| = fp32(1.27); / 127 = 0.0099999998 -> fp16 0.01000213623046875;
-    # 1 / s = 99.9786; 1.27 * that = 126.97 -> 127, -0.5 * = -49.99 -> -50,
-    # 0.02 * = 2.00 -> 2
+    # 1.27 / s = 126.97 -> 127, -0.5 / s = -49.99 -> -50, 0.02 / s = 2.00 -> 2
     x = np.zeros(64, np.float32)
     x[:3] = [1.27, -0.5, 0.02]
     codes, scales = quantize_groups(x, 8)
@@ -58,6 +60,54 @@ def test_q4_hand_worked_group_and_packing():
     packed = pack(codes, 4)
     assert packed.size == 32 and packed[0] == 0xC7 and packed[1] == 0x01   # low nibble first
     assert unpack(packed, 4, 64).tolist() == codes.tolist()
+
+
+def test_exact_tie_is_divided_not_multiplied_by_a_reciprocal():
+    # max 1.53125 -> scale 1.53125 / 7 = 0.21875 = 7/32 exactly (fp16 exact);
+    # 1.421875 = 6.5 * 7/32 exactly, an exact tie -> 6 (even).  The fp32
+    # reciprocal 1/0.21875 = 4.5714285... is rounded up, and 1.421875 times it
+    # lands above 6.5, so a reciprocal-based code would be 7.  Likewise
+    # 0.65625 = 3 * 7/32 -> 3 and -1.421875 -> -6.
+    x = np.zeros(64, np.float32)
+    x[:4] = [1.53125, 1.421875, 0.65625, -1.421875]
+    codes, scales = quantize_groups(x, 4)
+    assert float(scales[0]) == 0.21875
+    assert codes[:4].tolist() == [7, 6, 3, -6]
+    inv = np.float32(1) / np.float32(0.21875)
+    assert np.rint(np.float32(np.float32(1.421875) * inv)) == 7       # the other reading differs here
+
+
+@pytest.mark.parametrize("bits", [4, 8])
+def test_codes_round_the_exact_quotient(bits):
+    """Where the exact quotient x / scale16 (rational arithmetic) lies more
+    than 2^-16 from a half-integer, fp32 rounding cannot move it across one,
+    so the code must be its nearest integer, clamped."""
+    from fractions import Fraction
+    rng = np.random.default_rng(100 + bits)
+    x = (rng.standard_normal((24, 128)) * rng.uniform(0.05, 30, size=(24, 1))).astype(np.float32)
+    x = synth_bf16(x)
+    codes, scales = quantize_groups(x, bits)
+    qm = q_max(bits)
+    checked = 0
+    for r in range(x.shape[0]):
+        for j in range(x.shape[1]):
+            s = Fraction(float(np.float32(scales[r, j // GROUP])))
+            t = Fraction(float(x[r, j])) / s
+            frac = t - (t.numerator // t.denominator)
+            if abs(frac - Fraction(1, 2)) <= Fraction(1, 1 << 16):
+                continue
+            near = t.numerator // t.denominator + (1 if frac > Fraction(1, 2) else 0)
+            assert codes[r, j] == max(-qm, min(qm, near)), (r, j)
+            checked += 1
+    assert checked > 0.99 * x.size
+
+
+def synth_bf16(x):
+    """Round fp32 values to bf16 (nearest, ties to even) and back, so the
+    inputs are bf16 pool values."""
+    b = np.asarray(x, np.float32).view(np.uint32).astype(np.uint64)
+    b = ((b + 0x7FFF + ((b >> 16) & 1)) >> 16) << 16
+    return b.astype(np.uint32).view(np.float32)
 
 
 def test_zero_group_and_clamp():
