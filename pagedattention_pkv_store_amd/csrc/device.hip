@@ -8,26 +8,30 @@
 //    sequence, read in place through the block table ("KV Cache Management
 //    and PagedAttention", "Compute attention over scattered KV", Figure 4).
 //
-// Kernel design (MI355X-first, not a translation of any page's design):
-//  * One workgroup (4 waves) owns one (sequence, KV head, query tile, KV
-//    split).  Its query rows are (query, head-in-group) pairs of one GQA
-//    group, so every K/V byte a workgroup reads serves the whole group.
-//  * K/V are staged 64 positions at a time in LDS, gathered page by page
-//    through the block table with 16-byte coalesced loads; the next tile's
-//    loads are in flight while the current tile is computed.
-//  * Scores are computed transposed, S^T = K Q^T, on MFMA (bf16:
-//    v_mfma_f32_16x16x32_bf16; fp32: v_mfma_f32_16x16x4_f32).  In that layout
-//    each lane holds one query row and four key positions, so the running
-//    max / sum of the online softmax need only in-lane work plus two
-//    wavefront shuffles, and the probabilities are already in the MFMA
-//    operand layout of O^T = V^T P^T (bf16: v_mfma_f32_16x16x16_bf16).  V is
-//    read transposed out of LDS.
-//  * Waves either split the query tile (long prefill tiles) or split the
-//    staged keys (decode, few rows); partial softmax states of waves are
-//    combined in LDS.  Long contexts are split across workgroups at fixed
-//    logical positions and merged with log-sum-exp by a second kernel, so
-//    the result depends only on the logical sequence, never on which
-//    physical pages hold it.
+// Kernels (MI355X-first, not a translation of any page's design):
+//  * store_kv_kernel / store_kv_i8_kernel: one 16-byte chunk of a (token,
+//    KV head) row per thread, coalesced; INT8 pages quantize on the way.
+//  * paged_decode_kernel (decode and appends of at most 48 rows per unit):
+//    one-wave workgroups split the list of 16-position blocks of all
+//    (sequence, KV head) units into equal contiguous ranges ("stream-K").
+//    A wave keeps two blocks in flight in registers, stages them in LDS and
+//    runs S^T = K Q^T and O^T += V^T P^T on bf16 MFMA, with each lane
+//    holding one query row, so the online softmax is in-lane work plus two
+//    shuffles.  merge_segments_kernel folds the partial states of units that
+//    a range boundary split, by log-sum-exp.
+//  * paged_prefill_kernel (bf16 and INT8 pages, longer appends): a
+//    workgroup owns 32 query rows per wave of one (sequence, KV head) unit
+//    (8 waves and 128-position K/V tiles, or 4 waves and 64-position tiles
+//    when no context exceeds 2048 positions), stages K/V tiles in two LDS
+//    buffers through the block table, and runs both products on
+//    v_mfma_f32_16x16x32_bf16 with V^T read by ds_read_b64_tr_b16.
+//  * paged_attention_kernel: the fp32 prefill (4 waves, 64-position tiles,
+//    v_mfma_f32_16x16x4_f32), kept for the fp32 parity cases.
+//  * copy_pages_kernel, codec_encode_kernel / codec_decode_kernel,
+//    stream_read_kernel: page copies, the group-wise codec and a read probe.
+// Long contexts are split at fixed logical positions and merged with
+// log-sum-exp, so every result depends only on the logical sequence, never
+// on which physical pages hold it.
 
 #include <hip/hip_runtime.h>
 
@@ -542,8 +546,8 @@ __global__ __launch_bounds__(kThreads) void paged_attention_kernel(AttnArgs args
 //    (each instruction reads 1 KB of whole rows) into registers, two blocks
 //    ahead, then written to the wave's LDS slices (K rows padded by 16 bytes,
 //    V rows by 32, so the operand reads below are free of bank conflicts);
-//  * S^T = K Q^T runs on MFMA with the unit's queries held in registers (the
-//    next unit's are fetched one unit ahead); a lane then holds one query row
+//  * S^T = K Q^T runs on MFMA with the unit's queries held in registers
+//    (loaded when the wave enters the unit); a lane then holds one query row
 //    and 4 positions, so the online softmax takes in-lane work and two
 //    wavefront shuffles; O^T += V^T P^T takes V^T straight out of LDS with
 //    ds_read_b64_tr_b16 (bf16);
@@ -1083,11 +1087,14 @@ __global__ __launch_bounds__(kWave, RBW == 1 ? (kI8 ? PKV_DECODE_WAVES_PER_SIMD_
 // ---------------------------------------------------------------------------
 // Paged prefill/append in bf16 for more than 48 query rows per sequence and
 // KV head.
-//  * A workgroup owns 128 query rows of one (sequence, KV head) unit; rows are
-//    (query, head-in-group) pairs, so every K/V byte it stages serves the
-//    whole GQA group.  Wave w owns rows 32w..32w+31 as two 16-row MFMA
-//    blocks and keeps its own softmax state: no cross-wave combine.
-//  * K/V tiles of 64 positions are gathered through the block table with
+//  * A workgroup of W waves owns 32 W query rows of one (sequence, KV head)
+//    unit: 8 waves (256 rows) with 128-position tiles, one workgroup per CU;
+//    or, when no context exceeds kPfShortCtx positions, 4 waves (128 rows)
+//    with 64-position tiles, two workgroups per CU.  Rows are (query,
+//    head-in-group) pairs, so every K/V byte it stages serves the whole GQA
+//    group.  Wave w owns rows 32w..32w+31 as two 16-row MFMA blocks and keeps
+//    its own softmax state: no cross-wave combine.
+//  * K/V tiles are gathered through the block table with
 //    16-byte loads into registers one tile ahead and written to one of two
 //    LDS buffers.  K rows are padded to D*2 + 16 bytes and V rows to
 //    D*2 + 32, which keeps both operand reads below free of bank conflicts.
@@ -1673,8 +1680,8 @@ __global__ __launch_bounds__(kThreads) void store_kv_kernel(
   *reinterpret_cast<uint4*>((is_v ? v_pool : k_pool) + dst) = val;
 }
 
-// KV scatter into INT8 pages ("INT8 cache": a vector is quantized once, when
-// its position is written): kLpv = D / 8 consecutive lanes own one (token,
+// KV scatter into INT8 pages ("INT8 cache": quantization happens here, at
+// write time, and a stored scale is never revised): kLpv = D / 8 consecutive lanes own one (token,
 // KV head) vector of K or V, 8 bf16 each.  Its absolute maximum is reduced
 // across those lanes; scale = max|x| / 127 and code = rint(x / scale), both
 // IEEE fp32 divisions, codes clamped to [-127, 127]; a zero vector stores
@@ -1780,10 +1787,13 @@ struct CodecArgs {
   int64_t groups_per_tensor;   // n_positions * hkv * head_dim / 64
 };
 
-// Pool element offset of the 8 elements of (tensor-local) group gi, part.
-// Index arithmetic is 32-bit: the host keeps 2 * groups_per_tensor * 8 below
-// 2^31.  head_dim is 64 or 128, so a vector holds 1 or 2 groups.
-__device__ __forceinline__ int64_t codec_pool_elem(const CodecArgs& a, int gi, int part) {
+// Pool element offset of the 8 elements of (tensor-local) group gi, part;
+// *valid is false when the block-table entry is not a page of the pool (the
+// offset then names page 0, so address arithmetic never leaves the pool and
+// takes no branch).  Index arithmetic is 32-bit: the host keeps
+// 2 * groups_per_tensor * 8 below 2^31.  head_dim is 64 or 128, so a vector
+// holds 1 or 2 groups.
+__device__ __forceinline__ int64_t codec_pool_elem(const CodecArgs& a, int gi, int part, bool* valid) {
   const int gshift = a.head_dim == 128 ? 1 : 0;      // log2(groups per (position, head) vector)
   const int vec = gi >> gshift;
   const int d0 = (gi - (vec << gshift)) * 64 + part * 8;
@@ -1791,7 +1801,9 @@ __device__ __forceinline__ int64_t codec_pool_elem(const CodecArgs& a, int gi, i
   const int head = vec - pos * a.hkv;
   const int blk = a.ps_shift >= 0 ? (pos >> a.ps_shift) : pos / a.page_size;
   const int off = pos - blk * a.page_size;
-  const int page = min(max(a.block_table[blk], 0), a.num_pages - 1);
+  const int entry = a.block_table[blk];
+  *valid = entry >= 0 && entry < a.num_pages;
+  const int page = *valid ? entry : 0;
   return ((static_cast<int64_t>(page) * a.hkv + head) * a.page_size + off) * a.head_dim + d0;
 }
 
@@ -1799,11 +1811,27 @@ __device__ __forceinline__ int64_t codec_pool_elem(const CodecArgs& a, int gi, i
 // 16-byte chunks p and p + 4 (each load instruction of the four lanes covers
 // 64 contiguous bytes), so the group's maximum takes two shuffles and the
 // per-group work (address, scale, reciprocal) is shared by 16 elements.
-// A code is rint(clamp(x * inv, -q_max, q_max)): the clamped product plus
-// 1.5 * 2^23 rounds it to the nearest integer, ties to even, and the low
-// bits of the sum are the two's complement code.  With a zero scale inv is
-// 1 and every element is below 2^-18 in magnitude (a nonzero max / q_max
-// that rounds to fp16 zero is below 2^-25), so its code is 0.
+// A code is rint(clamp(x / scale, -q_max, q_max)) with x / scale the
+// correctly rounded fp32 quotient.  For a bf16 x and an fp16 scale that
+// quotient never rounds onto a half-integer h unless x / scale is exactly h:
+// a nonzero x - h * scale is at least 2^-12 relative to the scale, far above
+// half an fp32 ulp of h (|h| < 128).  So the code is the exact quotient
+// rounded to nearest, ties to even, and it is found without a division:
+//  * c = rint(x * inv) with inv = 1 / scale rounded once per group; adding
+//    1.5 * 2^23 to the clamped product rounds it to an integer (the low
+//    bits of the sum are the two's complement code, its lowest bit the
+//    parity), and c is within 1 of the answer;
+//  * e = x - c * scale by one fma, exact (all terms are short multiples of a
+//    common quantum); |e| > scale / 2 moves c one step toward e's sign, and
+//    |e| = scale / 2 (an exact tie) moves it only when c is odd.
+// The correction is needed only where the product lies within 2^-14 of a
+// half-integer: it is within 1.5 * 2^-16 of the quotient for
+// |x / scale| <= 128, so elsewhere rint(x * inv) is already the code.  It
+// runs per element on a wave-wide vote (for N(0,1) bf16 groups about one
+// element position in ten for Q4, whose ties are common, one in twenty for
+// Q8).  Beyond q_max everything clamps to q_max.  With a zero scale inv is 1 and every element is below
+// 2^-18 in magnitude (a nonzero max / q_max that rounds to fp16 zero is below
+// 2^-25), so its code is 0.
 constexpr int kCodecLanes = 4;   // lanes per group of 64, both directions
 
 template <int kBits>
@@ -1821,9 +1849,11 @@ __global__ __launch_bounds__(kThreads) void codec_encode_kernel(CodecArgs a, con
   if (!live) group = 0;
   const bool is_v = group >= gpt;
   const int gi = is_v ? group - gpt : group;
-  const uint16_t* src = (is_v ? v_pool : k_pool) + codec_pool_elem(a, gi, part);
-  const u32x4 x0 = *reinterpret_cast<const u32x4*>(src);        // elements 8 part ..
-  const u32x4 x1 = *reinterpret_cast<const u32x4*>(src + 32);   // elements 32 + 8 part ..
+  bool valid;                                        // the 4 lanes of a group agree on it
+  const uint16_t* src = (is_v ? v_pool : k_pool) + codec_pool_elem(a, gi, part, &valid);
+  u32x4 x0 = *reinterpret_cast<const u32x4*>(src);              // elements 8 part ..
+  u32x4 x1 = *reinterpret_cast<const u32x4*>(src + 32);         // elements 32 + 8 part ..
+  if (!valid) x0 = x1 = u32x4{0u, 0u, 0u, 0u};       // a position off the pool encodes as zeros
   float f[16];
 #pragma unroll
   for (int w = 0; w < 4; ++w) {
@@ -1839,11 +1869,27 @@ __global__ __launch_bounds__(kThreads) void codec_encode_kernel(CodecArgs a, con
   amax = fmaxf(amax, __shfl_xor(amax, 2));
   const _Float16 s16 = static_cast<_Float16>(amax / kQMax);
   const float sf = static_cast<float>(s16);
-  const float inv = 1.f / (sf > 0.f ? sf : 1.f);      // correctly rounded, once per lane
+  const float sd = sf > 0.f ? sf : 1.f;
+  const float inv = 1.f / sd;                         // correctly rounded, once per lane
+  const float half = 0.5f * sd;
   uint32_t c[16];                                     // low bits: the codes
 #pragma unroll
-  for (int i = 0; i < 16; ++i)
-    c[i] = __float_as_uint(__builtin_amdgcn_fmed3f(f[i] * inv, -kQMax, kQMax) + kRound);
+  for (int i = 0; i < 16; ++i) {
+    const float y = __builtin_amdgcn_fmed3f(f[i] * inv, -kQMax, kQMax);
+    const float r = y + kRound;
+    c[i] = __float_as_uint(r);
+    // Element i is corrected in every lane when any lane's product is near a
+    // half-integer (a wave-uniform branch; the correction is exact in every
+    // lane).  The test is exact: both terms are below 2^7.
+    if (__builtin_amdgcn_ballot_w64(fabsf(y - (r - kRound)) > 0.5f - 0x1p-14f)) {
+      const float cf = r - kRound;
+      const float e = __builtin_fmaf(-cf, sd, f[i]);    // x - c * scale, exact
+      const float ae = fabsf(e);
+      const bool step = ae > half || (ae == half && (c[i] & 1u));
+      const float cn = step ? cf + __builtin_copysignf(1.f, e) : cf;
+      c[i] = __float_as_uint(__builtin_amdgcn_fmed3f(cn, -kQMax, kQMax) + kRound);
+    }
+  }
   if (!live) return;
   const int64_t e = static_cast<int64_t>(group) * 64;   // first element of the group in the payload
   if constexpr (kBits == 8) {
@@ -1894,22 +1940,36 @@ __global__ __launch_bounds__(kThreads) void codec_decode_kernel(CodecArgs a, uin
   const int gi = is_v ? group - gpt : group;
   const int64_t e = static_cast<int64_t>(group) * 64;   // first element of the group in the payload
   const float sf = static_cast<float>(__builtin_bit_cast(_Float16, scales[group]));
-  uint16_t* dst = (is_v ? v_pool : k_pool) + codec_pool_elem(a, gi, part);
+  // The payload loads do not depend on the table entry, so they are issued
+  // together with it; only the stores wait for the validity test.
+  constexpr int kIt = 8 / kL;
+  uint32_t w[kIt][kBits == 8 ? 2 : 1];
 #pragma unroll
-  for (int h = 0; h < 8 / kL; ++h) {
+  for (int h = 0; h < kIt; ++h) {
     const int chunk = part + kL * h;
+    if constexpr (kBits == 8) {
+      const uint2 x = *reinterpret_cast<const uint2*>(codes + e + 8 * chunk);
+      w[h][0] = x.x;
+      w[h][1] = x.y;
+    } else {
+      w[h][0] = *reinterpret_cast<const uint32_t*>(codes + e / 2 + 4 * chunk);
+    }
+  }
+  bool valid;
+  uint16_t* dst = (is_v ? v_pool : k_pool) + codec_pool_elem(a, gi, part, &valid);
+  if (!valid) return;                                // a position off the pool is not written
+#pragma unroll
+  for (int h = 0; h < kIt; ++h) {
     int c[8];
     if constexpr (kBits == 8) {
-      const uint2 w = *reinterpret_cast<const uint2*>(codes + e + 8 * chunk);
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        c[i] = static_cast<int8_t>(w.x >> (8 * i));
-        c[4 + i] = static_cast<int8_t>(w.y >> (8 * i));
+        c[i] = static_cast<int8_t>(w[h][0] >> (8 * i));
+        c[4 + i] = static_cast<int8_t>(w[h][1] >> (8 * i));
       }
     } else {
-      const uint32_t w = *reinterpret_cast<const uint32_t*>(codes + e / 2 + 4 * chunk);
 #pragma unroll
-      for (int i = 0; i < 8; ++i) c[i] = static_cast<int>(static_cast<int32_t>(w << (28 - 4 * i)) >> 28);
+      for (int i = 0; i < 8; ++i) c[i] = static_cast<int>(static_cast<int32_t>(w[h][0] << (28 - 4 * i)) >> 28);
     }
     f32x4 lo, hi;
 #pragma unroll

@@ -1,6 +1,7 @@
 """GPU parity of the group-wise low-bit KV codec (ReKV, section 2.2) against
-the oracle: payload bytes and restored pool bytes are bit-exact (both sides
-take the same fp32 / fp16 steps), and attention over restored pages is within
+the oracle: payload bytes and restored pool bytes are bit-exact (codes are the
+correctly rounded fp32 quotient x / scale rounded to nearest, ties to even, on
+both sides), and attention over restored pages is within
 the bf16 bars of the oracle over the dequantized values.  Destination pools
 start NaN-filled, so a slot the restore should not touch stays NaN."""
 
@@ -94,6 +95,72 @@ def test_restore_bit_exact_and_attention(bits, L, D, ps, hkv):
                synth.bf16_bits_to_f32(_bf16_bits(dv)).astype(np.float64), r.scale)
     err = np.abs(out - e)
     assert np.isfinite(out).all() and err.max() <= BF16_MAX and err.mean() <= BF16_MEAN
+
+
+@pytest.mark.parametrize("bits", [4, 8])
+def test_encode_exact_ties_bit_exact(bits):
+    """Groups whose elements are exact half-integer multiples of their scale:
+    max 1.53125 gives the Q4 scale 7/32 exactly, and (2k + 1) * 7/64 is
+    (k + 1/2) * scale, so the division lands on exact ties that go to even.
+    Powers of two move the groups across binades without losing exactness.
+    A per-group reciprocal would round some of these the other way; the
+    kernel must match the division."""
+    L, D, ps, hkv = 40, 128, 16, 8
+    print(f"codec encode exact ties bits={bits}", flush=True)
+    rng = np.random.default_rng(500 + bits)
+    s, seq, k, v = _stored_sequence(L, D, ps, hkv, seed=11 + bits)
+    ties = np.array([(2 * j + 1) * 7 / 64 for j in range(7)])
+    for t in (k, v):
+        for p in range(L):
+            for h in range(hkv):
+                g = np.concatenate([[1.53125], rng.choice(ties, 63) * rng.choice([-1.0, 1.0], 63)])
+                t[p, h, :64] = synth.f32_to_bf16_bits((g * 2.0 ** rng.integers(-6, 7)).astype(np.float32))
+    s.store(seq, 0, k, v, synth.BF16)
+    n = pkv.codec_payload_bytes(L, hkv, D, bits)
+    payload = torch.full((n,), 0xA5, dtype=torch.uint8, device=DEV)
+    pkv.codec_encode(s.desc, s.k_pool, s.v_pool, i32(s.alloc.block_table(seq)), L, bits, payload)
+    torch.cuda.synchronize()
+    kf, vf = synth.to_f64(k, synth.BF16), synth.to_f64(v, synth.BF16)
+    expect = oracle_encode(kf, vf, bits)
+    assert np.array_equal(payload.cpu().numpy(), expect)
+    if bits == 4:    # the input does separate the two readings
+        x = kf[:, :, :64].astype(np.float32)
+        sc = (np.abs(x).max(-1, keepdims=True) / np.float32(7)).astype(np.float16).astype(np.float32)
+        by_recip = np.clip(np.rint((x * (np.float32(1) / sc)).astype(np.float32)), -7, 7)
+        by_div = np.clip(np.rint((x / sc).astype(np.float32)), -7, 7)
+        assert (by_recip != by_div).sum() > 100
+
+
+def test_table_entries_off_the_pool():
+    """A block-table entry that is not a page of the pool (-1, num_pages)
+    encodes its positions as zeros and is skipped by the restore: no other
+    page is read in its place or written."""
+    L, D, ps, hkv, bits = 48, 128, 16, 8, 8
+    print("codec table entries off the pool", flush=True)
+    s, seq, k, v = _stored_sequence(L, D, ps, hkv, seed=21)
+    bt = s.alloc.block_table(seq).copy()
+    bt[1] = -1                                       # positions 16..31
+    payload = torch.empty((pkv.codec_payload_bytes(L, hkv, D, bits),), dtype=torch.uint8, device=DEV)
+    pkv.codec_encode(s.desc, s.k_pool, s.v_pool, i32(bt), L, bits, payload)
+    torch.cuda.synchronize()
+    kf, vf = synth.to_f64(k, synth.BF16), synth.to_f64(v, synth.BF16)
+    kf[16:32] = 0
+    vf[16:32] = 0
+    assert np.array_equal(payload.cpu().numpy(), oracle_encode(kf, vf, bits))
+    # restore with entries -1 and num_pages: those positions stay NaN, the others are restored
+    r = Session.open(_Pools(D, ps, hkv, 12, seed=5))
+    rseq = r.alloc.seq_new()
+    r.alloc.reserve(rseq, L)
+    rbt = r.alloc.block_table(rseq).copy()
+    rbt[0], rbt[2] = -1, r.desc.num_pages
+    pkv.codec_decode(r.desc, r.k_pool, r.v_pool, i32(rbt), L, bits, payload)
+    torch.cuda.synchronize()
+    dk, _ = oracle_decode(payload.cpu().numpy(), (L, hkv, D), bits)
+    kp = r.k_pool.view(torch.int16).cpu().numpy().view(np.uint16)
+    page = int(rbt[1])
+    assert np.array_equal(kp[page].transpose(1, 0, 2), _bf16_bits(dk[16:32]))
+    others = [p for p in range(r.desc.num_pages) if p != page]
+    assert np.isnan(host_f64(r.k_pool)[others]).all() and np.isnan(host_f64(r.v_pool)[others]).all()
 
 
 def test_empty_prefix_is_a_no_op():
