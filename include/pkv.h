@@ -170,7 +170,13 @@ int pkv_retention_take(pkv_alloc* a, int32_t seq, int32_t* available);
 /* Sum of the retained sequences' page counts. */
 int pkv_retention_pages(const pkv_alloc* a, int64_t* pages);
 
+/* Queries of the allocator's state.  These four are helpers with no source
+ * passage of their own: they read back what the calls above maintain (for
+ * tests, sizing and callers' bookkeeping) and change nothing.  Errors:
+ * INVALID_ARG (null pointer, unknown sequence or page). */
+/* Positions stored in `seq`. */
 int pkv_seq_len(const pkv_alloc* a, int32_t seq, int32_t* len);
+/* Pages on the free stack. */
 int pkv_num_free(const pkv_alloc* a, int32_t* n);
 /* Reference count of one page (0 = free). */
 int pkv_page_refcount(const pkv_alloc* a, int32_t page, int32_t* count);
@@ -315,20 +321,26 @@ size_t pkv_codec_payload_bytes(int32_t n_positions, int32_t num_kv_heads, int32_
 
 /* Encode positions 0..n_positions-1 of one sequence, read in place through
  * its device block table (>= ceil(n_positions / page_size) entries), into
- * `payload` (device, 16-byte aligned, pkv_codec_payload_bytes).  Errors:
- * INVALID_ARG, UNSUPPORTED (dtype other than PKV_BF16, bits), DEVICE. */
+ * `payload` (device, 16-byte aligned, pkv_codec_payload_bytes).  A position
+ * whose table entry is not a page of the pool (< 0 or >= num_pages) encodes
+ * as zeros.  Errors: INVALID_ARG, UNSUPPORTED (dtype other than PKV_BF16,
+ * bits), DEVICE. */
 int pkv_codec_encode(const pkv_pool_desc* desc, const void* k_pool, const void* v_pool, const int32_t* block_table,
                      int32_t n_positions, int32_t bits, void* payload, void* stream);
 
 /* Restore a payload written by pkv_codec_encode into positions
  * 0..n_positions-1 of a sequence whose block table names the destination
- * pages (bf16(scale * code) per element; other slots untouched). */
+ * pages (bf16(scale * code) per element; other slots untouched).  Positions
+ * whose table entry is not a page of the pool are skipped, never written
+ * elsewhere.  Errors: INVALID_ARG, UNSUPPORTED, DEVICE. */
 int pkv_codec_decode(const pkv_pool_desc* desc, void* k_pool, void* v_pool, const int32_t* block_table,
                      int32_t n_positions, int32_t bits, const void* payload, void* stream);
 
 /* Bytes of device workspace pkv_decode / pkv_prefill_append need for these
  * sizes (0 when a launch needs none).  Pass the same scalars to the call.
- * Returns 0 for unsupported descriptors as well; the call then reports it. */
+ * Returns 0 for unsupported descriptors as well; the call then reports it.
+ * A helper with no source passage: it sizes the caller-owned scratch
+ * (split partial states, schedule offsets) that the library never allocates. */
 size_t pkv_workspace_bytes(const pkv_pool_desc* desc, int32_t n_seqs, int32_t num_q_heads,
                            int32_t max_q_per_seq, int32_t max_seq_len);
 
@@ -370,6 +382,11 @@ int pkv_decode(const pkv_pool_desc* desc, const void* k_pool, const void* v_pool
  * positions' K/V must already be stored (pkv_store_kv).
  *   q, out:       device [total_q][num_q_heads][head_dim]; rows >= total_q are
  *                 never touched
+ *   total_q:      host row count of q and out.  Not in the statement of the
+ *                 problem: cu_q lives in device memory, which the host does
+ *                 not read before launching, so this host bound is what
+ *                 keeps every kernel's rows inside q and out whatever cu_q
+ *                 holds (and it sizes the grid)
  *   cu_q:         device int32 [n_seqs + 1], non-decreasing, cu_q[0] = 0
  *   max_q_per_seq: host upper bound of n_b (queries beyond it are not computed)
  *   other arguments as for pkv_decode; workspace >= pkv_workspace_bytes(desc,

@@ -2,15 +2,15 @@
 
 TEST INFRASTRUCTURE ONLY (see ``oracle/__init__.py``).
 
-Source: TileInfer.jl docs, "KV cache", section "INT8 cache".  With the INT8
-cache the pools hold Int8 codes and one Float32 scale per cached vector (one
-KV head at one position).  The quantizer is symmetric: a value x is
-represented as scale * code with scale = max|x| / 127 over the vector.  A
-vector is quantized once, when its position is written, and its scale never
-changes afterwards.  Attention reads the codes as they are: the key's scale
-multiplies that key's scores, and the value's scale multiplies its
-probability before the PV product.  A 128-element vector then takes 132
-bytes (128 codes and a 4-byte scale) instead of 256 in BFloat16.
+Source: TileInfer.jl docs, "KV cache", section "INT8 cache".  In this mode
+each cached vector (the keys or values of one KV head at one position) is
+stored as Int8 codes plus a single Float32 scale, and x is approximated by
+scale * code, symmetrically, with the scale set from the vector's largest
+magnitude divided by 127.  Quantization happens at write time only, so no
+scale is ever revised.  The attention kernels work on the codes directly and
+apply the scales as factors: per key on its scores, per value on its
+probability ahead of the PV product.  Storage per 128-element vector drops
+from 256 bytes (BFloat16) to 132 (codes plus the 4-byte scale).
 
 Readings where the page leaves a choice open (each is listed in the design
 notes):

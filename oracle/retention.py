@@ -2,18 +2,18 @@
 
 TEST INFRASTRUCTURE ONLY (see ``oracle/__init__.py``).
 
-Source: Quail docs, "KV", section "KV retention".  An operator may need a
-document that an earlier operator already processed; keeping that document's
-KV avoids processing it again.  The executor keeps selected KV within a
-memory limit that leaves room for two forward passes.  When the retention
-pool is full, the KV with the lowest priority is removed, where
+Source: Quail docs, "KV", section "KV retention".  Retained KV lets a later
+operator reuse a document's keys and values instead of running the document
+through the model a second time.  What is retained is bounded: the budget is
+the memory left after setting aside enough for two forward passes.  Over
+budget, entries go in increasing order of
 
     priority = probability_of_reuse * recompute_seconds / pages
 
-(the estimated compute saved per page): ``probability_of_reuse`` estimates
-whether a later operator reads the document, ``recompute_seconds`` the time to
-process it again, and ``pages`` is its KV page count.  A later operator that
-needs removed KV computes the document again.
+which is the expected compute saved per page held: ``probability_of_reuse``
+is the chance that a later operator reads the document, ``recompute_seconds``
+the cost of processing it anew, and ``pages`` its page count.  An operator
+that finds its document's KV gone simply recomputes it.
 
 Readings (also listed in the design notes):
 * The unit of retention is a sequence of the page allocator; removing it is

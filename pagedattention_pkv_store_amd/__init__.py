@@ -359,6 +359,36 @@ def _stream(stream):
     return ctypes.c_void_p(s.cuda_stream)
 
 
+# Shape checks run before any pointer is taken: a tensor smaller than the call
+# assumes would make a kernel read or write past its allocation.
+def _need_shape(t, name, shape):
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} must have shape {tuple(shape)}, got {tuple(t.shape)}")
+
+
+def _need_rows(t, name, n, dims=None):
+    if dims is not None and t.dim() != dims:
+        raise ValueError(f"{name} must have {dims} dimension(s), got {t.dim()}")
+    rows = int(t.shape[0]) if t.dim() else 0
+    if rows < n:
+        raise ValueError(f"{name} must have at least {n} rows, got {rows}")
+
+
+def _need_pools(desc: "PoolDesc", k_pool, v_pool):
+    need = desc.pool_bytes()
+    for t, name in ((k_pool, "k_pool"), (v_pool, "v_pool")):
+        have = t.numel() * t.element_size()
+        if have < need:
+            raise ValueError(f"{name} holds {have} bytes; the pool descriptor needs {need}")
+
+
+def _need_heads(desc: "PoolDesc", hq: int, d: int, name: str):
+    if d != desc.head_dim:
+        raise ValueError(f"{name}: last dimension {d} differs from the pool's head_dim {desc.head_dim}")
+    if desc.num_kv_heads <= 0 or hq % desc.num_kv_heads:
+        raise ValueError(f"{name}: {hq} query heads are not a multiple of {desc.num_kv_heads} KV heads")
+
+
 class BoundCall:
     """A device call whose arguments were checked and marshalled once.
 
@@ -384,6 +414,12 @@ def bind_store_kv(desc: PoolDesc, k_pool, v_pool, k_new, v_new, slots, stream=No
     dt = desc.torch_dtype()
     pdt = desc.pool_torch_dtype()
     n = int(slots.numel())
+    _need_pools(desc, k_pool, v_pool)
+    row = desc.num_kv_heads * desc.head_dim
+    for t, name in ((k_new, "k_new"), (v_new, "v_new")):
+        if t.numel() < n * row:
+            raise ValueError(f"{name} must hold at least slots.numel() * num_kv_heads * head_dim = {n * row} "
+                             f"elements, got {t.numel()}")
     c_desc = desc.c()
     args = (ctypes.byref(c_desc), _dev(k_pool, "k_pool", pdt), _dev(v_pool, "v_pool", pdt),
             _dev(k_new, "k_new", dt), _dev(v_new, "v_new", dt), _dev(slots, "slots", torch.int64),
@@ -404,6 +440,7 @@ def copy_pages(desc: PoolDesc, k_pool, v_pool, copies, stream=None) -> None:
     n = int(copies.shape[0]) if copies.dim() == 2 else 0
     if copies.dim() != 2 or copies.shape[1] != 2:
         raise ValueError("copies must be [n][2]")
+    _need_pools(desc, k_pool, v_pool)
     c_desc = desc.c()
     _check(_lib.lib().pkv_copy_pages(ctypes.byref(c_desc), _dev(k_pool, "k_pool", pdt), _dev(v_pool, "v_pool", pdt),
                                      _dev(copies, "copies", torch.int32), n, _stream(stream)))
@@ -432,12 +469,26 @@ def codec_payload_bytes(n_positions: int, num_kv_heads: int, head_dim: int, bits
     return n
 
 
+def _need_codec(desc, k_pool, v_pool, block_table, n_positions, bits, payload):
+    _need_pools(desc, k_pool, v_pool)
+    if n_positions < 0:
+        raise ValueError("n_positions must be >= 0")
+    blocks = -(-n_positions // desc.page_size) if desc.page_size > 0 else 0
+    if block_table.numel() < blocks:
+        raise ValueError(f"block_table must hold ceil(n_positions / page_size) = {blocks} entries, "
+                         f"got {block_table.numel()}")
+    need = codec_payload_bytes(n_positions, desc.num_kv_heads, desc.head_dim, bits) if n_positions else 0
+    if payload.numel() * payload.element_size() < need:
+        raise ValueError(f"payload must hold {need} bytes, got {payload.numel() * payload.element_size()}")
+
+
 def codec_encode(desc: PoolDesc, k_pool, v_pool, block_table, n_positions: int, bits: int, payload,
                  stream=None) -> None:
     """Quantize a sequence's first n_positions K/V (read through its device
     block table) into a device uint8 payload (pkv_codec_encode)."""
     import torch
     pdt = desc.pool_torch_dtype()
+    _need_codec(desc, k_pool, v_pool, block_table, n_positions, bits, payload)
     _check(_lib.lib().pkv_codec_encode(ctypes.byref(desc.c()), _dev(k_pool, "k_pool", pdt),
                                        _dev(v_pool, "v_pool", pdt), _dev(block_table, "block_table", torch.int32),
                                        n_positions, bits, _dev(payload, "payload", torch.uint8), _stream(stream)))
@@ -448,6 +499,7 @@ def codec_decode(desc: PoolDesc, k_pool, v_pool, block_table, n_positions: int, 
     """Restore a payload into a sequence's first n_positions (pkv_codec_decode)."""
     import torch
     pdt = desc.pool_torch_dtype()
+    _need_codec(desc, k_pool, v_pool, block_table, n_positions, bits, payload)
     _check(_lib.lib().pkv_codec_decode(ctypes.byref(desc.c()), _dev(k_pool, "k_pool", pdt),
                                        _dev(v_pool, "v_pool", pdt), _dev(block_table, "block_table", torch.int32),
                                        n_positions, bits, _dev(payload, "payload", torch.uint8), _stream(stream)))
@@ -473,7 +525,14 @@ def bind_decode(desc: PoolDesc, k_pool, v_pool, q, block_tables, seq_lens, max_s
     """pkv_decode with its arguments bound (see decode)."""
     import torch
     dt = desc.torch_dtype()
-    n_seqs, hq, _ = q.shape
+    if q.dim() != 3:
+        raise ValueError(f"q must be [n_seqs][num_q_heads][head_dim], got {tuple(q.shape)}")
+    n_seqs, hq, d = (int(x) for x in q.shape)
+    _need_heads(desc, hq, d, "q")
+    _need_shape(out, "out", q.shape)
+    _need_rows(block_tables, "block_tables", n_seqs, dims=2)
+    _need_rows(seq_lens, "seq_lens", n_seqs, dims=1)
+    _need_pools(desc, k_pool, v_pool)
     pdt = desc.pool_torch_dtype()
     need = workspace_bytes(desc, n_seqs, hq, 1, max_seq_len)
     ws_ptr, ws_bytes = _workspace(workspace, need)
@@ -499,8 +558,17 @@ def bind_prefill_append(desc: PoolDesc, k_pool, v_pool, q, cu_q, block_tables, s
     """pkv_prefill_append with its arguments bound (see prefill_append)."""
     import torch
     dt = desc.torch_dtype()
-    total_q, hq, _ = q.shape
+    if q.dim() != 3:
+        raise ValueError(f"q must be [total_q][num_q_heads][head_dim], got {tuple(q.shape)}")
+    total_q, hq, d = (int(x) for x in q.shape)
+    _need_heads(desc, hq, d, "q")
+    _need_shape(out, "out", q.shape)
+    if cu_q.dim() != 1 or cu_q.numel() < 1:
+        raise ValueError("cu_q must be a 1-D tensor of n_seqs + 1 offsets")
     n_seqs = int(cu_q.numel()) - 1
+    _need_rows(block_tables, "block_tables", n_seqs, dims=2)
+    _need_rows(seq_lens, "seq_lens", n_seqs, dims=1)
+    _need_pools(desc, k_pool, v_pool)
     pdt = desc.pool_torch_dtype()
     need = workspace_bytes(desc, n_seqs, hq, max_q_per_seq, max_seq_len)
     ws_ptr, ws_bytes = _workspace(workspace, need)
