@@ -6,9 +6,9 @@ max-abs and 1e-2 mean-abs for bf16 K/V with fp32 accumulation.  Pools start
 NaN-filled, so any read of a slot that was never written (or of another
 sequence's page) would turn an output into NaN.
 
-Small cases run the oracle on every output; the full-size workloads (the five
-configurations at their stated sizes, in the same launch configuration the
-benchmark times) compare seeded samples of outputs row by row.
+Small cases run the oracle on every output.  The full-size workloads (at
+their stated sizes, in the launch configuration the benchmark times) are in
+test_gpu_full.py.
 """
 
 import math
@@ -461,90 +461,3 @@ def test_prefill_variants(dtype, D, ps, hq, hkv, ctx, news):
                        synth.to_f64(kv[b][1], dtype), s.scale)
             check_close(out[row:row + news[b]], e, dtype, f"prefill variant seq {b}")
         row += news[b]
-
-
-# ---------------------------------------------------------------------------
-# full-size workloads, sampled outputs
-# ---------------------------------------------------------------------------
-def _sample(rng, n, k):
-    return sorted(set(rng.choice(n, size=min(n, k), replace=False).tolist()))
-
-
-def test_full_decode_workload2():
-    print("full workload 2", flush=True)
-    w = synth.decode_batch()
-    s, seqs, out = run_decode(w)
-    oalloc, _ = ref.decode_allocator(w)
-    check_slots_and_tables(s, oalloc, seqs)
-    rng = np.random.default_rng(0)
-    rows = [(b, h) for b in _sample(rng, 64, 24) for h in _sample(rng, 32, 4)]
-    expect = ref.decode_reference(w, s.scale, rows)
-    o = host_f64(out)
-    got = np.stack([o[b, h] for b, h in rows])
-    check_close(got, np.stack([expect[r] for r in rows]), w.dtype, "full decode")
-
-
-def test_full_prefix_workload3():
-    print("full workload 3", flush=True)
-    w = synth.prefix_traces()
-    s, (order, parent, shared), seqs, n_new, out = run_prefix(w)
-    o_order, o_parent, o_shared = ref.prefix_plan(w)
-    assert order.tolist() == o_order and shared.tolist() == o_shared
-    assert [None if p < 0 else int(p) for p in parent] == o_parent
-    assert shared[:3].tolist() == [0, 992, 1392]
-    rng = np.random.default_rng(1)
-    cu = np.concatenate([[0], np.cumsum(n_new)])
-    rows = []
-    for d in _sample(rng, len(seqs), 40):
-        for i in {0, n_new[d] - 1, int(rng.integers(0, n_new[d]))}:
-            rows.append((d, i, int(rng.integers(0, w.num_q_heads))))
-    expect = ref.prefix_reference_rows(w, o_shared, s.scale, rows)
-    o = host_f64(out[torch.tensor([cu[d] + i for d, i, _ in rows], device=DEV)])
-    got = np.stack([o[j, h] for j, (_, _, h) in enumerate(rows)])
-    check_close(got, np.stack([expect[r] for r in rows]), w.dtype, "full prefix")
-
-
-def test_full_rewind_workload4():
-    print("full workload 4", flush=True)
-    w = synth.rewind_docs()
-    s, seqs, outs = run_rewind(w)
-    rng = np.random.default_rng(2)
-    docs = _sample(rng, 1000, 12)
-    expect = ref.rewind_reference(w, s.scale, docs)
-    for p in range(2):
-        o = outs[p].reshape(1000, w.q_len, w.num_q_heads, w.head_dim)
-        got = host_f64(o[torch.tensor(docs, device=DEV)])
-        check_close(got, np.stack([expect[p][d] for d in docs]), w.dtype, f"full rewind {p + 1}")
-
-
-def test_full_spec_workload5():
-    print("full workload 5", flush=True)
-    w = synth.spec_decode()
-    s, seqs, outs = run_spec(w)
-    grp = w.num_q_heads // w.num_kv_heads
-    rng = np.random.default_rng(3)
-    kept = {b: int(w.ctx_len[b]) for b in range(8)}
-    for st in range(w.keep.shape[0]):
-        o = host_f64(outs[st]).reshape(8, w.drafts, w.num_q_heads, w.head_dim)
-        if st in (0, 7, 15):
-            for b in _sample(rng, 8, 3):
-                lo = int(w.ctx_offsets[b])
-                L0 = int(w.ctx_len[b])
-                # logical K/V of the sequence: its context, the drafts kept in
-                # earlier steps, then this step's drafts
-                ks_, vs_ = [w.ctx_k[lo:lo + L0]], [w.ctx_v[lo:lo + L0]]
-                for p in range(st):
-                    ks_.append(w.draft_k[p, b, : int(w.keep[p, b])])
-                    vs_.append(w.draft_v[p, b, : int(w.keep[p, b])])
-                ks_.append(w.draft_k[st, b])
-                vs_.append(w.draft_v[st, b])
-                for i in (0, w.drafts - 1):
-                    h = int(rng.integers(0, w.num_q_heads))
-                    g = h // grp
-                    K = synth.to_f64(np.concatenate([x[:, g] for x in ks_]), w.dtype)
-                    V = synth.to_f64(np.concatenate([x[:, g] for x in vs_]), w.dtype)
-                    pos = kept[b] + i
-                    e = attend_row(synth.to_f64(w.draft_q[st, b, i, h], w.dtype), K, V, pos, s.scale)
-                    check_close(o[b, i, h][None], e[None], w.dtype, f"full spec step {st} seq {b}")
-        for b in range(8):
-            kept[b] += int(w.keep[st, b])
