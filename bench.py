@@ -17,11 +17,13 @@ the 256 MB Infinity Cache).  Sequences keep growing by one token per use.
 
 Printed: one JSON line.  ``value`` = KV bytes the decode steps must read
 (sum of lengths x 2 x 8 heads x 128 x 2 bytes) / wall time of the timed steps
-(host work and copies included).  ``roofline`` = the decode kernels' own
-algorithmic bytes per launch / their average duration from HIP events on the
-launch stream (every 4th timed step carries the event pair, 50 of the
-default 200), against the 8 TB/s HBM peak.  ``cpu_baseline`` = the fp64 CPU
-oracle on a bounded sample of the same sequences.
+(host work and copies included).  ``roofline`` = the decode call's
+algorithmic bytes per launch / its median duration over at least 30 calls
+timed one by one with HIP events on the launch stream after the step loop
+(the mean is reported beside it, and so is the sampled in-step timing),
+against the 8 TB/s HBM peak.  ``cpu_baseline`` = the fp64 CPU oracle on a
+bounded sample of the same sequences; the prefill, rewind and rollback legs
+carry their own.
 """
 
 from __future__ import annotations
@@ -77,10 +79,14 @@ def parse():
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--instances", type=int, default=4)
+    ap.add_argument("--call-reps", type=int, default=60,
+                    help="decode calls timed one by one after the step loop (at least 30)")
     ap.add_argument("--cpu-seconds", type=float, default=15.0,
                     help="bound on the CPU oracle's sample (0 disables the cpu_baseline leg)")
+    ap.add_argument("--cpu-seconds-other", type=float, default=8.0,
+                    help="oracle seconds for each of the prefix, rewind and rollback CPU baselines (0: none)")
     ap.add_argument("--seed", type=int, default=0)
-    ap.add_argument("--prefill-reps", type=int, default=10,
+    ap.add_argument("--prefill-reps", type=int, default=30,
                     help="timed repetitions of the prefix-shared prefill leg (0 disables it)")
     ap.add_argument("--int8", type=int, default=1,
                     help="also time the decode batch on INT8 pages (1) or not (0)")
@@ -284,7 +290,7 @@ def rewind_leg(args, torch, pkv, dev: str) -> dict:
     scale = 1.0 / float(np.sqrt(D))
     store = pkv.bind_store_kv(desc, k_pool, v_pool, k_new, v_new, d_slots)
     append = pkv.bind_prefill_append(desc, k_pool, v_pool, q, cu, d_bt, d_lens, q_len, max_len, scale, out, ws)
-    reps = 12
+    reps = 30
     evs = [tuple(torch.cuda.Event(enable_timing=True) for _ in range(3)) for _ in range(reps)]
     for i in range(reps + 2):
         ev = evs[i - 2] if i >= 2 else None
@@ -329,11 +335,12 @@ def spec_leg(args, torch, pkv, synth, dev: str) -> dict:
     bf16.  A step reserves 5 drafts per sequence, stores their K/V (40
     tokens) and runs a 5-query causal append (the split decode kernel and its
     merge); then each sequence keeps a random 0..5 drafts (host truncate,
-    untimed).  16 steps."""
+    untimed).  The 16-step pattern of kept drafts runs twice: 32 timed steps."""
     B, drafts, steps, ps, hq, hkv, D = 8, 5, 16, 64, 64, 8, 128
+    timed_steps = 2 * steps
     ctx = synth.generator(5, "lengths", args.seed).integers(32_768, 131_072, size=B, endpoint=True).astype(np.int64)
     keep = np.random.default_rng(5100 + args.seed).integers(0, drafts + 1, size=(steps, B))
-    num_pages = int(2 * sum(-(-int(x + steps * drafts) // ps) for x in ctx))
+    num_pages = int(2 * sum(-(-int(x + timed_steps * drafts) // ps) for x in ctx))
     desc = pkv.PoolDesc(pkv.PKV_BF16, num_pages, ps, hkv, D)
     gen = torch.Generator(device=dev)
     gen.manual_seed(5000 + args.seed)
@@ -343,7 +350,7 @@ def spec_leg(args, torch, pkv, synth, dev: str) -> dict:
     alloc = pkv.Allocator(num_pages, ps, order)
     seqs = np.array([alloc.seq_new() for _ in range(B)], np.int32)
     alloc.prepare_step(seqs, ctx.astype(np.int32), 0)
-    max_len = int(ctx.max()) + steps * drafts
+    max_len = int(ctx.max()) + timed_steps * drafts
     stride = -(-max_len // ps)
     n_new = np.full(B, drafts, np.int32)
     cu = torch.from_numpy(np.arange(0, (B + 1) * drafts, drafts, dtype=np.int32)).to(dev)
@@ -354,7 +361,7 @@ def spec_leg(args, torch, pkv, synth, dev: str) -> dict:
     ws = torch.empty(max(16, pkv.workspace_bytes(desc, B, hq, drafts, max_len)), dtype=torch.uint8, device=dev)
     scale = 1.0 / float(np.sqrt(D))
     store_ms, attn_ms, kv = [], [], []
-    for st in range(steps + 2):                 # two untimed warm-up steps, then 16
+    for st in range(timed_steps + 2):           # two untimed warm-up steps, then 32
         slots, bt, lens = alloc.prepare_step(seqs, n_new, stride)
         d_slots, d_bt, d_lens = (torch.from_numpy(x.copy()).to(dev) for x in (slots, bt, lens))
         ev = tuple(torch.cuda.Event(enable_timing=True) for _ in range(3))
@@ -381,7 +388,7 @@ def spec_leg(args, torch, pkv, synth, dev: str) -> dict:
                     f"{num_pages:,}-page shuffled pool, 64 q / 8 KV heads, head_dim 128, bf16; step = store_kv of 5 "
                     "drafts per sequence + one 5-query causal prefill_append (split decode kernel + merge), then "
                     "keep 0..5 drafts",
-        "value": round(float(np.mean(kv)) / step_s / 1e9, 1), "unit": "GB/s", "steps": steps,
+        "value": round(float(np.mean(kv)) / step_s / 1e9, 1), "unit": "GB/s", "steps": timed_steps,
         "ms_per_step": round(step_s * 1e3, 3), "mean_context": round(float(np.mean(kv)) / 4096 / B, 1),
         "store_kv_avg_us": round(float(np.mean(store_ms)) * 1e3, 1),
         "roofline": _append_roofline(int(np.mean(kv)), qo, attn_s, "spec_rollback",
@@ -538,11 +545,7 @@ def cpu_baseline(w, scale: float, budget_s: float):
     """Time the fp64 oracle on whole sequences of the batch until the budget ends."""
     import synth
     from oracle.attention import attend
-    try:
-        from threadpoolctl import threadpool_info
-        threads = max([p.get("num_threads", 1) for p in threadpool_info()] + [1])
-    except Exception:
-        threads = 1
+    threads = _blas_threads()
     per_pos = kv_bytes_per_position(w.num_kv_heads, w.head_dim, 2)
     done_bytes = 0
     done = 0
@@ -567,6 +570,119 @@ def cpu_baseline(w, scale: float, budget_s: float):
                   f"({done_bytes / 1e6:.1f} MB of K/V, {elapsed:.1f} s incl. bf16->fp64 widening), "
                   f"host cores available {len(os.sched_getaffinity(0))}",
     }
+
+
+def host_info() -> dict:
+    """The host the CPU baselines ran on: CPU model (as lscpu reports it, from
+    /proc/cpuinfo), cores available to this process, BLAS threads."""
+    model = ""
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    return {"cpu_model": model, "cores_available": len(os.sched_getaffinity(0)), "blas_threads": _blas_threads(),
+            "OMP_NUM_THREADS": os.environ.get("OMP_NUM_THREADS"),
+            "OPENBLAS_NUM_THREADS": os.environ.get("OPENBLAS_NUM_THREADS")}
+
+
+def _blas_threads() -> int:
+    try:
+        from threadpoolctl import threadpool_info
+        return int(max([p.get("num_threads", 1) for p in threadpool_info()] + [1]))
+    except Exception:
+        return 1
+
+
+def cpu_baseline_prefix(args, budget_s: float) -> dict:
+    """The fp64 oracle on the prefix-shared prefill workload: documents of the
+    256-row workload (its lengths and its plan from the oracle planner) in a
+    seeded order, each one attend() of its unshared suffix over its whole
+    context, until the budget is spent.  Values are N(0,1) fp64 of one trace,
+    drawn once outside the timed region (the oracle's time does not depend on
+    them).  Reported as processed tokens/s and fp64 flop/s."""
+    import synth
+    from oracle.attention import attend
+    from oracle.planner import plan_prefix
+    w = synth.prefix_traces(seed=args.seed, values=False)
+    n = len(w.row_len)
+    _, _, shared = plan_prefix([w.row_tokens(r).tolist() for r in range(n)], w.page_size)
+    hq, hkv, D = w.num_q_heads, w.num_kv_heads, w.head_dim
+    rng = np.random.default_rng(7000 + args.seed)
+    t_len = int(w.row_len.max())
+    q = rng.standard_normal((t_len, hq, D))
+    k = rng.standard_normal((t_len, hkv, D))
+    v = rng.standard_normal((t_len, hkv, D))
+    scale = 1.0 / float(np.sqrt(D))
+    tokens = pairs = done = 0
+    t0 = time.perf_counter()
+    for d in rng.permutation(n).tolist():
+        if time.perf_counter() - t0 >= budget_s:
+            break
+        L, sh = int(w.row_len[d]), int(shared[d])
+        attend(q[sh:L], k[:L], v[:L], scale)
+        tokens += L - sh
+        pairs += (L * (L + 1) - sh * (sh + 1)) // 2
+        done += 1
+    el = time.perf_counter() - t0
+    return {"value": round(tokens / el, 1), "unit": "tokens/s", "cores": _blas_threads(), "kind": "oracle",
+            "fp64_gflops": round(4.0 * D * hq * pairs / el / 1e9, 2),
+            "sample": f"fp64 NumPy oracle on {done} of the 256 prefix-shared rows ({tokens} suffix tokens over "
+                      f"their contexts, {pairs} unmasked pairs per head, {el:.1f} s)"}
+
+
+def cpu_baseline_rewind(args, budget_s: float) -> dict:
+    """The fp64 oracle on the KV rewind workload: one 50-query causal append
+    over a document's 350 positions per call (32 / 8 heads of 128), repeated
+    on fresh seeded N(0,1) documents until the budget is spent; tokens/s."""
+    from oracle.attention import attend
+    rng = np.random.default_rng(7100 + args.seed)
+    q_len, ctx, hq, hkv, D = 50, 350, 32, 8, 128
+    scale = 1.0 / float(np.sqrt(D))
+    done, busy = 0, 0.0
+    while busy < budget_s:
+        q = rng.standard_normal((q_len, hq, D))
+        k = rng.standard_normal((ctx, hkv, D))
+        v = rng.standard_normal((ctx, hkv, D))
+        t0 = time.perf_counter()
+        attend(q, k, v, scale)
+        busy += time.perf_counter() - t0
+        done += 1
+    return {"value": round(done * q_len / busy, 1), "unit": "tokens/s", "cores": _blas_threads(), "kind": "oracle",
+            "sample": f"fp64 NumPy oracle, {done} documents of the rewind workload (50 new queries over 350 "
+                      f"positions each, {busy:.1f} s of oracle time)"}
+
+
+def cpu_baseline_spec(args, budget_s: float) -> dict:
+    """The fp64 oracle on the speculative-rollback workload: one 5-draft
+    causal append per call over a context of the workload's lengths
+    (U{32K..128K}, 64 / 8 heads of 128), until the budget is spent; GB/s of
+    bf16 KV the call covers (the unit the GPU leg reports).  One seeded N(0,1)
+    fp64 K/V of the longest context is drawn once and read by prefix."""
+    import synth
+    from oracle.attention import attend
+    ctx = synth.generator(5, "lengths", args.seed).integers(32_768, 131_072, size=8, endpoint=True)
+    rng = np.random.default_rng(7200 + args.seed)
+    drafts, hq, hkv, D = 5, 64, 8, 128
+    Lmax = int(ctx.max()) + drafts
+    k = rng.standard_normal((Lmax, hkv, D))
+    v = rng.standard_normal((Lmax, hkv, D))
+    q = rng.standard_normal((drafts, hq, D))
+    scale = 1.0 / float(np.sqrt(D))
+    done, kv, busy = 0, 0, 0.0
+    while busy < budget_s:
+        L = int(ctx[done % len(ctx)]) + drafts
+        t0 = time.perf_counter()
+        attend(q, k[:L], v[:L], scale)
+        busy += time.perf_counter() - t0
+        kv += L * kv_bytes_per_position(hkv, D, 2)
+        done += 1
+    return {"value": round(kv / busy / 1e9, 4), "unit": "GB/s", "cores": _blas_threads(), "kind": "oracle",
+            "sample": f"fp64 NumPy oracle, {done} sequence-steps of the speculative-rollback workload (5 drafts "
+                      f"over {kv / 4096 / done:.0f} positions on average, {busy:.1f} s of oracle time)"}
 
 
 def decode_leg(args, torch, pkv, synth, w, dev: str, kv_int8: bool) -> dict:
@@ -718,6 +834,7 @@ def decode_leg(args, torch, pkv, synth, w, dev: str, kv_int8: bool) -> dict:
     for slot in range(EV_RING):
         read_slot(slot)
 
+
     # The last step's decode once more, its tables copied in stream order into
     # a fresh buffer: the timed steps must have read exactly what they uploaded.
     last = sets[(args.warmup + args.steps - 1) % NSETS]
@@ -728,19 +845,42 @@ def decode_leg(args, torch, pkv, synth, w, dev: str, kv_int8: bool) -> dict:
     pkv.decode(desc, k_pool, v_pool, q, f_bt, f_lens, max_len, scale, out_check, ws)
     torch.cuda.synchronize()
     assert torch.equal(out, out_check), "the timed steps' decode differs from a stream-ordered rerun"
+
+    # The decode call alone, timed call by call: CALL_REPS launches back to
+    # back, each between its own event pair, over the upload sets of completed
+    # steps.  Consecutive sets hold different instances, so consecutive calls
+    # read disjoint pages; the pending set (the next step's tables, whose new
+    # position is not stored yet) is skipped.
+    total = args.warmup + args.steps
+    pending = total % NSETS
+    ready = sorted({k % NSETS for k in range(max(0, total - NSETS), total)} - {pending})
+    call_reps = max(30, args.call_reps)
+    call_ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+               for _ in range(call_reps)]
+    call_bytes = []
+    torch.cuda.synchronize()
+    for i, (a, b) in enumerate(call_ev):
+        st = sets[ready[i % len(ready)]]
+        a.record(stream)
+        st["decode"]()
+        b.record(stream)
+        call_bytes.append(int(st["np"][2].astype(np.int64).sum()) * per_pos)
+    torch.cuda.synchronize()
+    call_ms = np.array([a.elapsed_time(b) for a, b in call_ev])
     dec_ms = np.array(dec_ms)
     assert torch.isfinite(out.float()).all(), "non-finite decode output"
     total_kv = float(sum(kv_bytes))
     qo_bytes = 2 * B * hq * D * 2                      # q read + out written per launch
     assert len(dec_ms) == len(kv_bytes_timed_calls) > 0, "no timed decode call"
-    dec_avg_s = float(dec_ms.mean()) / 1e3
     res = {
-        "per_pos": per_pos, "total_kv": total_kv, "wall": wall, "dec_ms": dec_ms,
-        "alg_per_launch": float(np.mean(kv_bytes_timed_calls)) + qo_bytes, "dec_avg_s": dec_avg_s,
-        "timed_calls": len(dec_ms),
+        "per_pos": per_pos, "total_kv": total_kv, "wall": wall,
+        "in_step_avg_us": float(dec_ms.mean()) * 1e3, "in_step_calls": len(dec_ms),
+        "call_ms": call_ms, "alg_per_launch": float(np.mean(call_bytes)) + qo_bytes,
+        "dec_avg_s": float(call_ms.mean()) / 1e3, "dec_median_s": float(np.median(call_ms)) / 1e3,
+        "timed_calls": len(call_ms),
         "B": B, "hq": hq, "hkv": hkv, "D": D, "ps": ps, "scale": scale,
     }
-    res["achieved"] = res["alg_per_launch"] / dec_avg_s / 1e9
+    res["achieved"] = res["alg_per_launch"] / res["dec_median_s"] / 1e9
     torch.cuda.synchronize()
     del k_pool, v_pool, ws, sets, prep
     torch.cuda.synchronize()
@@ -796,9 +936,12 @@ def main():
             "frac": round(d["achieved"] / HBM_PEAK_GBS, 4),
             "traffic": measured_traffic("decode"),
             "kernel": "pkv_decode (paged_decode_kernel + merge_segments_kernel)",
+            "achieved_from": "median call",
             "kernel_avg_us": round(d["dec_avg_s"] * 1e6, 2),
-            "kernel_median_us": round(float(np.median(d["dec_ms"])) * 1e3, 2),
+            "kernel_median_us": round(d["dec_median_s"] * 1e6, 2),
             "timed_launches": d["timed_calls"],
+            "in_step_avg_us": round(d["in_step_avg_us"], 2),
+            "in_step_timed_launches": d["in_step_calls"],
             "algorithmic_bytes_per_launch": int(d["alg_per_launch"]),
         },
     }
@@ -820,11 +963,12 @@ def main():
                 "frac": round(d8["achieved"] / HBM_PEAK_GBS, 4),
                 "traffic": measured_traffic("decode_int8"),
                 "kernel": "pkv_decode on PKV_I8 pools (paged_decode_kernel + merge_segments_kernel)",
+                "achieved_from": "median call",
                 "kernel_avg_us": round(d8["dec_avg_s"] * 1e6, 2),
-                "kernel_median_us": round(float(np.median(d8["dec_ms"])) * 1e3, 2),
+                "kernel_median_us": round(d8["dec_median_s"] * 1e6, 2),
                 "timed_launches": d8["timed_calls"],
                 "algorithmic_bytes_per_launch": int(d8["alg_per_launch"]),
-                "speedup_vs_bf16_kernel": round(d["dec_avg_s"] / d8["dec_avg_s"], 3),
+                "speedup_vs_bf16_kernel": round(d["dec_median_s"] / d8["dec_median_s"], 3),
             },
         }
     if args.copy_pairs > 0:
@@ -863,6 +1007,12 @@ def main():
         del src, dst
     if args.cpu_seconds > 0:
         rec["cpu_baseline"] = cpu_baseline(w, d["scale"], args.cpu_seconds)
+        rec["cpu_baseline"]["host"] = host_info()
+    if args.cpu_seconds_other > 0:
+        for key, fn in (("prefill_append", cpu_baseline_prefix), ("rewind_append", cpu_baseline_rewind),
+                        ("spec_rollback", cpu_baseline_spec)):
+            if key in rec:
+                rec[key]["cpu_baseline"] = fn(args, args.cpu_seconds_other)
     print(json.dumps(rec), flush=True)
 
 
