@@ -372,6 +372,26 @@ int pkv_decode(const pkv_pool_desc* desc, const void* k_pool, const void* v_pool
                int32_t bt_stride, const int32_t* seq_lens, int32_t max_seq_len, float scale,
                void* out, void* workspace, size_t ws_bytes, void* stream);
 
+/* pkv_decode for callers that cannot allocate device memory (code under HIP
+ * graph capture, tight serving loops, harnesses that forbid hipMalloc): the
+ * same kernels and the same result as pkv_decode, with the workspace taken
+ * from a static device array of PKV_NOALLOC_SCRATCH_BYTES (32 MiB) that each
+ * device holds from the library's load until the process ends.  Nothing is
+ * allocated or freed: the array's device address is looked up once per
+ * device (hipGetSymbolAddress) on the first call made with that device
+ * current, and the call's stream must belong to the current device.
+ * Arguments as for pkv_decode, without the workspace.  A batch whose
+ * workspace (pkv_workspace_bytes(desc, n_seqs, num_q_heads, 1, max_seq_len))
+ * exceeds the array is refused with BUFFER_TOO_SMALL before anything is
+ * enqueued.  Every call on one device shares that device's array and nothing
+ * in it needs clearing between calls; calls that can overlap on one device
+ * (different streams without ordering between them) race on it.  Errors as
+ * for pkv_decode. */
+#define PKV_NOALLOC_SCRATCH_BYTES ((size_t)32 << 20)
+int pkv_decode_noalloc(const pkv_pool_desc* desc, const void* k_pool, const void* v_pool, const void* q,
+                       int32_t n_seqs, int32_t num_q_heads, const int32_t* block_tables, int32_t bt_stride,
+                       const int32_t* seq_lens, int32_t max_seq_len, float scale, void* out, void* stream);
+
 /* Paged prefill / append: sequence b has n_b = cu_q[b+1] - cu_q[b] new queries
  * (packed rows cu_q[b] .. cu_q[b+1]-1 of q and out) at positions
  * seq_lens[b] - n_b .. seq_lens[b] - 1; new query i attends causally to

@@ -21,7 +21,7 @@ from ._lib import PKV_BF16, PKV_F32, PKV_I8  # noqa: F401
 
 __all__ = [
     "PkvError", "OutOfPagesError", "SharedPageError", "UnsupportedError",
-    "PoolDesc", "Allocator", "plan_prefix", "store_kv", "copy_pages", "decode", "prefill_append",
+    "PoolDesc", "Allocator", "plan_prefix", "store_kv", "copy_pages", "decode", "decode_noalloc", "prefill_append",
     "codec_payload_bytes", "codec_encode", "codec_decode",
     "workspace_bytes", "validate_tables", "PKV_F32", "PKV_BF16", "PKV_I8",
     "BoundCall", "bind_store_kv", "bind_decode", "bind_prefill_append",
@@ -550,6 +550,29 @@ def decode(desc: PoolDesc, k_pool, v_pool, q, block_tables, seq_lens, max_seq_le
     """Paged decode: q [B][Hq][D] -> out [B][Hq][D] (one new query per sequence)."""
     bind_decode(desc, k_pool, v_pool, q, block_tables, seq_lens, max_seq_len, scale, out,
                 workspace, stream)()
+
+
+def decode_noalloc(desc: PoolDesc, k_pool, v_pool, q, block_tables, seq_lens, max_seq_len: int,
+                   scale: float, out, stream=None) -> None:
+    """pkv_decode_noalloc: decode with the library's static scratch instead of
+    a workspace (allocates nothing); refused when the batch needs more than
+    PKV_NOALLOC_SCRATCH_BYTES of scratch."""
+    import torch
+    dt = desc.torch_dtype()
+    if q.dim() != 3:
+        raise ValueError(f"q must be [n_seqs][num_q_heads][head_dim], got {tuple(q.shape)}")
+    n_seqs, hq, d = (int(x) for x in q.shape)
+    _need_heads(desc, hq, d, "q")
+    _need_shape(out, "out", q.shape)
+    _need_rows(block_tables, "block_tables", n_seqs, dims=2)
+    _need_rows(seq_lens, "seq_lens", n_seqs, dims=1)
+    _need_pools(desc, k_pool, v_pool)
+    pdt = desc.pool_torch_dtype()
+    c_desc = desc.c()
+    _check(_lib.lib().pkv_decode_noalloc(
+        ctypes.byref(c_desc), _dev(k_pool, "k_pool", pdt), _dev(v_pool, "v_pool", pdt), _dev(q, "q", dt), n_seqs, hq,
+        _dev(block_tables, "block_tables", torch.int32), int(block_tables.shape[1]),
+        _dev(seq_lens, "seq_lens", torch.int32), max_seq_len, float(scale), _dev(out, "out", dt), _stream(stream)))
 
 
 def bind_prefill_append(desc: PoolDesc, k_pool, v_pool, q, cu_q, block_tables, seq_lens,

@@ -24,6 +24,8 @@ PKV_F32 = 0
 PKV_BF16 = 1
 PKV_I8 = 2
 
+PKV_NOALLOC_SCRATCH_BYTES = 32 << 20
+
 i32p = POINTER(c_int32)
 i64p = POINTER(ctypes.c_int64)
 
@@ -71,6 +73,8 @@ _SIGNATURES = {
     "pkv_decode": (c_int, [POINTER(PoolDescC), c_void_p, c_void_p, c_void_p, c_int32, c_int32,
                            c_void_p, c_int32, c_void_p, c_int32, c_float, c_void_p, c_void_p,
                            c_size_t, c_void_p]),
+    "pkv_decode_noalloc": (c_int, [POINTER(PoolDescC), c_void_p, c_void_p, c_void_p, c_int32, c_int32,
+                                   c_void_p, c_int32, c_void_p, c_int32, c_float, c_void_p, c_void_p]),
     "pkv_prefill_append": (c_int, [POINTER(PoolDescC), c_void_p, c_void_p, c_void_p, c_int32,
                                    c_void_p, c_int32, c_int32, c_void_p, c_int32, c_void_p,
                                    c_int32, c_int32, c_float, c_void_p, c_void_p, c_size_t,

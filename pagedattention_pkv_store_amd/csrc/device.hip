@@ -38,6 +38,7 @@
 #include <algorithm>
 #include <cmath>
 #include <cstdint>
+#include <mutex>
 #include <string>
 #include <type_traits>
 
@@ -2364,6 +2365,44 @@ int codec_setup(const char* fn, const pkv_pool_desc* desc, const void* k_pool, c
 
 }  // namespace
 
+// ---------------------------------------------------------------------------
+// Scratch of pkv_decode_noalloc: the decode kernels' workspace (the
+// per-sequence block prefix and the split partial states) in a static device
+// array, for callers that cannot allocate.  Each device holds its own copy
+// from module load until the process ends.  Host code never passes the
+// array's name to a kernel (on the host it is only a stand-in for the
+// symbol): the device address comes from hipGetSymbolAddress, taken once per
+// device with that device current, and is kept per device.
+// ---------------------------------------------------------------------------
+static __device__ __align__(256) unsigned char scratch[PKV_NOALLOC_SCRATCH_BYTES];
+
+namespace {
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+// The device address of `scratch` on the current device.
+int scratch_address(const char* fn, void** out) {
+  int dev = -1;
+  hipError_t err = hipGetDevice(&dev);
+  if (err != hipSuccess) return fail(PKV_ERR_DEVICE, std::string(fn) + ": hipGetDevice: " + hipGetErrorString(err));
+  if (dev < 0 || dev >= kMaxDevices)
+    return fail(PKV_ERR_UNSUPPORTED, std::string(fn) + ": device index " + std::to_string(dev) + " out of range");
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* ptr = nullptr;
+    err = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    if (err != hipSuccess || !ptr)
+      return fail(PKV_ERR_DEVICE, std::string(fn) + ": hipGetSymbolAddress(scratch): " + hipGetErrorString(err));
+    g_scratch_ptr[dev] = ptr;
+  }
+  *out = g_scratch_ptr[dev];
+  return PKV_OK;
+}
+
+}  // namespace
+
 extern "C" {
 
 int pkv_store_kv(const pkv_pool_desc* desc, void* k_pool, void* v_pool, const void* k_new,
@@ -2542,6 +2581,28 @@ int pkv_decode(const pkv_pool_desc* desc, const void* k_pool, const void* v_pool
   return run_attention("pkv_decode", desc, k_pool, v_pool, q, n_seqs, nullptr, n_seqs,
                        num_q_heads, block_tables, bt_stride, seq_lens, 1, max_seq_len, scale,
                        out, workspace, ws_bytes, stream);
+}
+
+int pkv_decode_noalloc(const pkv_pool_desc* desc, const void* k_pool, const void* v_pool, const void* q,
+                       int32_t n_seqs, int32_t num_q_heads, const int32_t* block_tables, int32_t bt_stride,
+                       const int32_t* seq_lens, int32_t max_seq_len, float scale, void* out, void* stream) {
+  const char* fn = "pkv_decode_noalloc";
+  Plan p;
+  int rc = make_plan(desc, n_seqs, num_q_heads, 1, max_seq_len, &p, fn);
+  if (rc != PKV_OK) return rc;
+  if (p.ws_bytes > PKV_NOALLOC_SCRATCH_BYTES)
+    return fail(PKV_ERR_BUFFER_TOO_SMALL, std::string(fn) + ": this batch needs " + std::to_string(p.ws_bytes) +
+                                              " bytes of scratch, above the static " +
+                                              std::to_string(PKV_NOALLOC_SCRATCH_BYTES) +
+                                              "; call pkv_decode with a workspace");
+  void* ws = nullptr;
+  if (p.ws_bytes > 0 && n_seqs > 0) {
+    rc = scratch_address(fn, &ws);
+    if (rc != PKV_OK) return rc;
+  }
+  return run_attention(fn, desc, k_pool, v_pool, q, n_seqs, nullptr, n_seqs, num_q_heads, block_tables,
+                       bt_stride, seq_lens, 1, max_seq_len, scale, out, ws, ws ? PKV_NOALLOC_SCRATCH_BYTES : 0,
+                       stream);
 }
 
 int pkv_prefill_append(const pkv_pool_desc* desc, const void* k_pool, const void* v_pool,
