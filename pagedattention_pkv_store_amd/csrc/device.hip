@@ -1148,6 +1148,21 @@ constexpr int kPfShortCtx = PKV_PREFILL_SHORT_CTX;
 #endif
 constexpr int kPfKeys = PKV_PREFILL_KEYS;   // positions per staged tile (computed 64 at a time)
 constexpr int kPfMaxRows = 16 * kPfRb * kPfWaves;   // rows of the larger workgroup shape
+// Contexts up to kPfStreamCtx positions take the persistent stream kernel
+// (paged_prefill_stream_kernel): kPfStreamWaves waves, kPfStreamKeys-position
+// tiles.
+#ifndef PKV_PREFILL_STREAM_CTX
+#define PKV_PREFILL_STREAM_CTX 2048
+#endif
+#ifndef PKV_PREFILL_STREAM_WAVES
+#define PKV_PREFILL_STREAM_WAVES 8
+#endif
+#ifndef PKV_PREFILL_STREAM_KEYS
+#define PKV_PREFILL_STREAM_KEYS 64
+#endif
+constexpr int kPfStreamCtx = PKV_PREFILL_STREAM_CTX;
+constexpr int kPfStreamWaves = PKV_PREFILL_STREAM_WAVES;
+constexpr int kPfStreamKeys = PKV_PREFILL_STREAM_KEYS;
 
 template <int D>
 constexpr int pf_k_row_bytes() { return D * 2 + 16; }
@@ -1164,9 +1179,13 @@ template <int D, bool kI8>
 constexpr int pf_wave_rows() { return kWave / (D * (kI8 ? 1 : 2) / static_cast<int>(sizeof(KvLoad<kI8>))); }
 
 // row_off[k] = sum over blocks < k of (q-tiles of the block) * n_splits,
-// where a block's q-tiles are the most any of its 8 units needs.
+// where a block's q-tiles are the most any of its 8 units needs.  With `rec`
+// (the persistent short-append launch) it also writes one record per work
+// item id = 8 * row + slot: int32 {b, g, q0, n_b, start, row0, kv_end, split},
+// b = -1 for an item with no work.
 __global__ __launch_bounds__(kThreads) void prefill_schedule_kernel(AttnArgs a, int32_t* row_off,
-                                                                    int n_blocks, int tile_rows) {
+                                                                    int n_blocks, int tile_rows,
+                                                                    int32_t* __restrict__ rec) {
   __shared__ int s_scan[kThreads];
   __shared__ int s_carry;
   const int tid = threadIdx.x;
@@ -1199,6 +1218,34 @@ __global__ __launch_bounds__(kThreads) void prefill_schedule_kernel(AttnArgs a, 
       __syncthreads();
     }
     if (blk < n_blocks) row_off[blk + 1] = s_carry + s_scan[tid];
+    if (rec && blk < n_blocks) {
+      const int r0 = s_carry + s_scan[tid] - v;
+      for (int slot = 0; slot < 8; ++slot) {
+        const int u = blk * 8 + slot;
+        const int b = u < units ? u / a.num_kv_heads : -1;
+        int q0 = 0, n_b = 0, start = 0, rows_total = 0;
+        if (b >= 0) {
+          q0 = a.cu_q[b];
+          n_b = a.cu_q[b + 1] - q0;
+          start = a.seq_lens[b] - n_b;
+          rows_total = min(n_b, a.max_q) * a.group;
+        }
+        for (int local = 0; local < v; ++local) {
+          const int qt = tiles - 1 - local / a.n_splits;
+          const int split = local - (local / a.n_splits) * a.n_splits;
+          const int row0 = qt * tile_rows;
+          int kv_end = 0;
+          bool ok = b >= 0 && row0 < rows_total;
+          if (ok) {
+            kv_end = min(start + (min(row0 + tile_rows, rows_total) - 1) / a.group + 1, a.kv_cap);
+            ok = split * a.split_len < kv_end;
+          }
+          int32_t* o = rec + 8 * (static_cast<int64_t>(r0 + local) * 8 + slot);
+          *reinterpret_cast<int4*>(o) = ok ? make_int4(b, u - b * a.num_kv_heads, q0, n_b) : make_int4(-1, 0, 0, 0);
+          *reinterpret_cast<int4*>(o + 4) = make_int4(start, row0, kv_end, split);
+        }
+      }
+    }
     __syncthreads();
     if (tid == kThreads - 1) s_carry += s_scan[tid];
     __syncthreads();
@@ -1534,6 +1581,479 @@ __global__ __launch_bounds__(kPfThreads, kPfRb >= 3 ? 1 : 2) void paged_prefill_
         a.ws_ml[slot * 2 + 1] = l;
       }
     }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Short appends, persistent ("stream"): paged_prefill_stream_kernel runs the
+// same tiles, staging, scores and products as paged_prefill_kernel, but a
+// workgroup takes the work items id = blockIdx.x + k * gridDim.x in turn
+// (gridDim.x a multiple of 8, so every item of a unit slot stays on one XCD)
+// and never drains between them: the K/V loads run one tile ahead and the
+// block-table lookups two tiles ahead across item boundaries, and the next
+// item's queries load during the current item's last tile.  Items come from
+// records the schedule kernel writes (one scalar load per item, two items
+// ahead).  With few tiles per item (a 50-token question over a 300-token
+// document is 6 tiles of 64 positions) the per-item start and drain
+// latency, not the tiles, had bounded the one-item-per-workgroup launch.
+// The next item's queries go straight from memory to an LDS buffer
+// (global_load_lds_dwordx4, issued before the last tile's K/V loads, so the
+// wait that stages that tile also covers them) and into registers at the
+// switch: holding them in registers during the last tile would spill.
+// ---------------------------------------------------------------------------
+// 8-wave workgroups (one per CU) take the next item's queries through an
+// LDS buffer; 4-wave workgroups (two per CU, which hide each other's waits)
+// load them into registers at the switch.
+template <int kThreads_>
+constexpr bool pf_stream_q_lds() { return kThreads_ >= 512; }
+template <int D, int kKeys, int kThreads_>
+constexpr int pf_stream_lds_bytes() {
+  return pf_lds_bytes<D, kKeys, false>() + (pf_stream_q_lds<kThreads_>() ? 16 * kPfRb * (kThreads_ / kWave) * D * 2 : 0);
+}
+
+template <int D, int kPageMode, int kPfThreads, int kPfKeys, bool kI8>
+__global__ __launch_bounds__(kPfThreads, kPfThreads >= 512 ? 1 : 2) void paged_prefill_stream_kernel(
+    AttnArgs a, const int32_t* __restrict__ row_off, int n_blocks, const int32_t* __restrict__ rec) {
+  constexpr int kPfRows = 16 * kPfRb * (kPfThreads / kWave);   // query rows per item
+  constexpr int kKRowB = pf_k_row_bytes<D>();
+  constexpr int kVRowB = pf_v_row_bytes<D>();
+  using Ld = KvLoad<kI8>;
+  constexpr int kLdB = sizeof(Ld);
+  constexpr int kGRowB = D * (kI8 ? 1 : 2);
+  constexpr int kCpr = kGRowB / kLdB;
+  constexpr int kChunks = kPfKeys * kCpr / kPfThreads;
+  constexpr int kRowsPerPass = kPfThreads / kCpr;
+  constexpr int kQk = D / 32;
+  constexpr int kDb = D / 16;
+  constexpr int kKTileB = kPfKeys * kKRowB;
+  constexpr int kBufB = pf_buf_bytes<D, kPfKeys, kI8>();
+  static_assert(kChunks * kRowsPerPass == kPfKeys, "tile split");
+  extern __shared__ __align__(16) char smem[];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & (kWave - 1);
+  const int wave = tid / kWave;
+  const int lrow = lane & 15;
+  const int lgrp = lane >> 4;
+  const int hkv = a.num_kv_heads;
+  const int group = a.group;
+  const int n_sp = a.n_splits;
+  const int G = gridDim.x;
+  const int n_ids = row_off[n_blocks] * 8;   // records written by the schedule kernel
+
+  // ---- work items ----
+  struct Item {
+    int valid, b, g, q0, n_b, start, row0, kv_end, split, k_lo, k_hi, n_tiles, rows_total;
+  };
+  auto make_item = [&](int4 x, int4 y) __attribute__((always_inline)) {
+    Item it;
+    it.valid = x.x >= 0;
+    it.b = max(x.x, 0);
+    it.g = x.y;
+    it.q0 = x.z;
+    it.n_b = x.w;
+    it.start = y.x;
+    it.row0 = y.y;
+    it.kv_end = y.z;
+    it.split = y.w;
+    it.rows_total = min(it.n_b, a.max_q) * group;
+    it.k_lo = it.split * a.split_len;
+    it.k_hi = min(it.k_lo + a.split_len, it.kv_end);
+    it.n_tiles = it.valid ? (it.k_hi - it.k_lo + kPfKeys - 1) / kPfKeys : 0;
+    return it;
+  };
+  // The records of the next ids are loaded one item before they are used;
+  // ids without work are skipped (a wait on a record only then).
+  int next_id = blockIdx.x;
+  int4 pend_x = make_int4(-1, 0, 0, 0), pend_y = make_int4(0, 0, 0, 0);
+  // Records and (page mode 0) block-table entries are wave-uniform: read
+  // through the constant address space they are scalar loads, waited on with
+  // lgkmcnt, and never hold back the vmcnt waits of the K/V tiles.
+  typedef int i32x4 __attribute__((ext_vector_type(4)));
+  typedef const __attribute__((address_space(4))) int32_t* cptr;
+  typedef const __attribute__((address_space(4))) i32x4* cptr4;
+  auto load_rec = [&](int id, int4& x, int4& y) __attribute__((always_inline)) {
+    if (id < n_ids) {
+      cptr4 p4 = (cptr4)((cptr)(rec) + 8 * static_cast<int64_t>(id));
+      const i32x4 vx = p4[0], vy = p4[1];
+      x = make_int4(vx.x, vx.y, vx.z, vx.w);
+      y = make_int4(vy.x, vy.y, vy.z, vy.w);
+    } else {
+      x = make_int4(-1, 0, 0, 0);
+      y = make_int4(0, 0, 0, 0);
+    }
+  };
+  // the next item with work: the pending record, else records further on
+  auto take_item = [&]() __attribute__((always_inline)) {
+    int4 x = pend_x, y = pend_y;
+    while (x.x < 0 && next_id < n_ids) {
+      load_rec(next_id, x, y);
+      next_id += G;
+    }
+    load_rec(next_id, pend_x, pend_y);   // the item after it, used at the next switch
+    next_id += G;
+    return make_item(x, y);
+  };
+  load_rec(next_id, pend_x, pend_y);
+  next_id += G;
+  Item W0 = take_item();
+  if (!W0.valid) return;
+  Item W1 = take_item();
+  Item W2 = take_item();
+
+  // ---- staging (as paged_prefill_kernel; the item is an argument) ----
+  const int ps = a.page_size;
+  const int ps_shift = a.ps_shift;
+  const uint32_t head_bytes = static_cast<uint32_t>(a.head_bytes);
+  const uint32_t scale_off = static_cast<uint32_t>(ps) * D;
+  const char* kbytes = static_cast<const char*>(a.k_pool);
+  const char* vbytes = static_cast<const char*>(a.v_pool);
+  const int srow0 = tid / kCpr;
+  const int spart = tid - srow0 * kCpr;
+  const int wrow0 = __builtin_amdgcn_readfirstlane(srow0);
+
+  int pg_next[kChunks], pg_next2[kChunks];
+  Ld kr[kChunks], vr[kChunks];
+  float ksr[kChunks], vsr[kChunks];
+  auto pos_of = [&](const Item& it, int t, int row) __attribute__((always_inline)) {
+    return min(it.k_lo + t * kPfKeys + row, it.k_hi - 1);
+  };
+  auto blk_of = [&](int pos) __attribute__((always_inline)) {
+    if constexpr (kPageMode <= 1) return pos >> ps_shift;
+    else return pos / ps;
+  };
+  auto fetch_pages = [&](const Item& it, int t) __attribute__((always_inline)) {
+    const int64_t row = static_cast<int64_t>(it.b) * a.bt_stride;
+#pragma unroll
+    for (int c = 0; c < kChunks; ++c) {
+      if constexpr (kPageMode == 0)
+        pg_next2[c] = ((cptr)(a.block_tables))[row + blk_of(pos_of(it, t, wrow0 + c * kRowsPerPass))];
+      else
+        pg_next2[c] = a.block_tables[row + blk_of(pos_of(it, t, srow0 + c * kRowsPerPass))];
+    }
+  };
+  auto load_kv = [&](const Item& it, int t) __attribute__((always_inline)) {
+#pragma unroll
+    for (int c = 0; c < kChunks; ++c) {
+      const int pos = pos_of(it, t, srow0 + c * kRowsPerPass);
+      const uint32_t page = static_cast<uint32_t>(min(max(pg_next[c], 0), a.num_pages - 1));
+      const uint32_t off = kPageMode <= 1 ? (pos & (ps - 1)) : (pos - blk_of(pos) * ps);
+      const uint32_t voff = off * kGRowB + spart * kLdB;
+      const uint64_t base = static_cast<uint64_t>(page * hkv + it.g) * head_bytes;
+      if constexpr (kI8) {
+        ksr[c] = *reinterpret_cast<const float*>(kbytes + base + scale_off + 4 * off);
+        vsr[c] = *reinterpret_cast<const float*>(vbytes + base + scale_off + 4 * off);
+      }
+      kr[c] = *reinterpret_cast<const Ld*>(kbytes + base + voff);
+      vr[c] = *reinterpret_cast<const Ld*>(vbytes + base + voff);
+    }
+  };
+  auto stage = [&](int buf) __attribute__((always_inline)) {
+    char* kb = smem + buf * kBufB;
+    char* vb = kb + kKTileB;
+#pragma unroll
+    for (int c = 0; c < kChunks; ++c) {
+      const int row = srow0 + c * kRowsPerPass;
+      if constexpr (kI8) {
+        *reinterpret_cast<u32x4*>(kb + row * kKRowB + spart * 16) = i8x8_scaled_to_bf16(kr[c], ksr[c]);
+        *reinterpret_cast<u32x4*>(vb + row * kVRowB + spart * 16) = i8x8_scaled_to_bf16(vr[c], vsr[c]);
+      } else {
+        *reinterpret_cast<u32x4*>(kb + row * kKRowB + spart * 16) = kr[c];
+        *reinterpret_cast<u32x4*>(vb + row * kVRowB + spart * 16) = vr[c];
+      }
+    }
+  };
+  // The tile k steps after tile tc of W0 (k = 1, 2): (item 0..2, tile).  Past
+  // the last item with work it names the last tile of the stream (reloaded,
+  // never computed).
+  auto after = [&](int tc, int k, int& which, int& t) __attribute__((always_inline)) {
+    const int r0 = W0.n_tiles - 1 - tc;
+    if (k <= r0) { which = 0; t = tc + k; return; }
+    int kk = k - r0 - 1;                              // tile index into W1, W2, ...
+    if (W1.valid && kk < W1.n_tiles) { which = 1; t = kk; return; }
+    if (!W1.valid) { which = 0; t = W0.n_tiles - 1; return; }
+    kk -= W1.n_tiles;
+    if (W2.valid && kk < W2.n_tiles) { which = 2; t = kk; return; }
+    if (!W2.valid) { which = 1; t = W1.n_tiles - 1; return; }
+    which = 2;
+    t = W2.n_tiles - 1;
+  };
+  auto item_ref = [&](int which) __attribute__((always_inline)) -> const Item& {
+    return which == 0 ? W0 : which == 1 ? W1 : W2;
+  };
+
+  // ---- query rows of an item (B operand of S^T = K Q^T) ----
+  constexpr int kWr = 16 * kPfRb;
+  bf16x8 qf[kPfRb][kQk];
+  // The next item's query tile, memory -> LDS: chunk q = c * kPfThreads + tid
+  // of the tile (row q / kQcpr, 16-byte part q % kQcpr) lands at byte 16 q of
+  // the buffer (each wave instruction writes 1 KB at its M0).  Rows without a
+  // query read the item's first query row (finite; never written out).
+  constexpr int kQcpr = D * 2 / 16;
+  constexpr int kQChunks = kPfRows * kQcpr / kPfThreads;
+  static_assert(kQChunks * kPfThreads == kPfRows * kQcpr, "query tile split");
+  char* qbuf = smem + 2 * kBufB;
+  auto dma_q = [&](const Item& it) __attribute__((always_inline)) {
+#pragma unroll
+    for (int c = 0; c < kQChunks; ++c) {
+      const int qc = c * kPfThreads + tid;
+      const int row = qc / kQcpr;
+      const int part = qc - row * kQcpr;
+      const int rr = it.row0 + row;
+      const int qi = rr / group;
+      const bool ok = rr < it.rows_total && it.q0 + qi < a.total_q;
+      const uint16_t* src = static_cast<const uint16_t*>(a.q) +
+                            (static_cast<int64_t>(it.q0 + (ok ? qi : 0)) * a.num_q_heads + it.g * group +
+                             (ok ? rr - qi * group : 0)) * D + part * 8;
+      // Inline asm: the compiler neither counts these loads in its vmcnt
+      // waits (so its waits stay sufficient, only stronger) nor makes LDS
+      // reads wait for them; the staging wait of the tile loads issued
+      // right after covers them (loads retire in order).
+      const uint32_t m0 = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(
+          (__attribute__((address_space(3))) char*)(qbuf + (c * kPfThreads + wave * kWave) * 16)));
+      asm volatile("global_load_lds_dwordx4 %0, off" ::"v"(src), "{m0}"(m0) : "memory");
+    }
+  };
+  auto read_q_lds = [&]() __attribute__((always_inline)) {
+#pragma unroll
+    for (int rb = 0; rb < kPfRb; ++rb) {
+      const char* src = qbuf + (kWr * wave + 16 * rb + lrow) * (D * 2) + lgrp * (D / 4) * 2;
+#pragma unroll
+      for (int kk = 0; kk < kQk; ++kk) qf[rb][kk] = *reinterpret_cast<const bf16x8*>(src + kk * 16);
+    }
+    __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0): read before the buffer is refilled
+  };
+  auto load_q = [&](const Item& it, bf16x8 (&dst)[kPfRb][kQk]) __attribute__((always_inline)) {
+    const int wr0 = it.row0 + kWr * wave;
+#pragma unroll
+    for (int rb = 0; rb < kPfRb; ++rb) {
+      const int rr = wr0 + 16 * rb + lrow;
+      const int qi = rr / group;
+      const bool ok = rr < it.rows_total && it.q0 + qi < a.total_q;
+      const uint16_t* src = static_cast<const uint16_t*>(a.q) +
+                            (static_cast<int64_t>(it.q0 + (ok ? qi : 0)) * a.num_q_heads + it.g * group +
+                             (ok ? rr - qi * group : 0)) * D + lgrp * (D / 4);
+#pragma unroll
+      for (int kk = 0; kk < kQk; ++kk) {
+        u32x4 v = *reinterpret_cast<const u32x4*>(src + kk * 8);
+        if (!ok) v = u32x4{0u, 0u, 0u, 0u};
+        dst[rb][kk] = __builtin_bit_cast(bf16x8, v);
+      }
+    }
+  };
+
+  // per-item, per-wave row bookkeeping
+  int qpos[kPfRb];
+  bool w_active;
+  int w_qmin, w_qmax, wr0;
+  auto enter_item = [&](const Item& it) __attribute__((always_inline)) {
+    wr0 = it.row0 + kWr * wave;
+#pragma unroll
+    for (int rb = 0; rb < kPfRb; ++rb) {
+      const int rr = wr0 + 16 * rb + lrow;
+      const int qi = rr / group;
+      const bool ok = rr < it.rows_total && it.q0 + qi < a.total_q;
+      qpos[rb] = ok ? min(it.start + qi, it.kv_end - 1) : -1;
+    }
+    w_active = wr0 < it.rows_total;
+    w_qmin = min(it.start + wr0 / group, it.kv_end - 1);
+    w_qmax = min(it.start + (min(wr0 + kWr - 1, it.rows_total - 1)) / group, it.kv_end - 1);
+  };
+  const float c2 = a.scale_log2;
+  f32x4 o[kDb][kPfRb];
+  f32x4 lsum[kPfRb];
+  float mc[kPfRb];
+  auto reset_state = [&]() __attribute__((always_inline)) {
+#pragma unroll
+    for (int rb = 0; rb < kPfRb; ++rb) {
+      lsum[rb] = f32x4{0.f, 0.f, 0.f, 0.f};
+      mc[rb] = -INFINITY;
+#pragma unroll
+      for (int d = 0; d < kDb; ++d) o[d][rb] = f32x4{0.f, 0.f, 0.f, 0.f};
+    }
+  };
+  const bf16x8 ones = __builtin_bit_cast(bf16x8, u32x4{0x3f803f80u, 0x3f803f80u, 0x3f803f80u, 0x3f803f80u});
+  const int k_lane = lrow * kKRowB + lgrp * (D / 4) * 2;
+  const int v_lane = (4 * lgrp + (lrow >> 2)) * kVRowB + ((lrow & 3) >> 1) * 16 + (lrow & 1) * 8;
+
+  auto compute = [&](const char* kt, const char* vt, int tb, auto mask_tag) __attribute__((always_inline)) {
+    constexpr bool kMask = decltype(mask_tag)::value;
+    f32x4 s[4][kPfRb];
+#pragma unroll
+    for (int kb = 0; kb < 4; ++kb) {
+      bf16x8 kf[kQk];
+#pragma unroll
+      for (int kk = 0; kk < kQk; ++kk)
+        kf[kk] = *reinterpret_cast<const bf16x8*>(kt + k_lane + kb * 16 * kKRowB + kk * 16);
+#pragma unroll
+      for (int rb = 0; rb < kPfRb; ++rb) {
+        f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int kk = 0; kk < kQk; ++kk) acc = mfma_qk(kf[kk], qf[rb][kk], acc);
+        s[kb][rb] = acc;
+      }
+    }
+    float muse[kPfRb];
+    bool up_any = false;
+    float alpha[kPfRb];
+#pragma unroll
+    for (int rb = 0; rb < kPfRb; ++rb) {
+      if constexpr (kMask) {
+#pragma unroll
+        for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+          for (int i = 0; i < 4; ++i)
+            s[kb][rb][i] = (tb + kb * 16 + 4 * lgrp + i <= qpos[rb]) ? s[kb][rb][i] : -INFINITY;
+      }
+      float mx = fmaxf(s[0][rb][0], s[0][rb][1]);
+#pragma unroll
+      for (int e = 2; e < 16; e += 2) mx = fmaxf(fmaxf(mx, s[e >> 2][rb][e & 3]), s[e >> 2][rb][(e & 3) + 1]);
+      mx = max_xor32(max_xor16(mx));
+      const float mxc = mx * c2;
+      const bool up = mxc > mc[rb] + 8.f;
+      const float mnew = up ? mxc : mc[rb];
+      alpha[rb] = up ? fast_exp2(mc[rb] - mnew) : 1.f;
+      mc[rb] = mnew;
+      up_any = up_any || up;
+      muse[rb] = mnew == -INFINITY ? 0.f : mnew;
+    }
+    if (__any(up_any)) {
+#pragma unroll
+      for (int rb = 0; rb < kPfRb; ++rb) {
+        lsum[rb] *= alpha[rb];
+#pragma unroll
+        for (int d = 0; d < kDb; ++d) o[d][rb] *= alpha[rb];
+      }
+    }
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks) {
+      bf16x8 pk[kPfRb];
+#pragma unroll
+      for (int rb = 0; rb < kPfRb; ++rb) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const float e0 = fast_exp2(fmaf(s[2 * ks][rb][i], c2, -muse[rb]));
+          const float e1 = fast_exp2(fmaf(s[2 * ks + 1][rb][i], c2, -muse[rb]));
+          pk[rb][i] = static_cast<__bf16>(e0);
+          pk[rb][4 + i] = static_cast<__bf16>(e1);
+        }
+        lsum[rb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ones, pk[rb], lsum[rb], 0, 0, 0);
+      }
+#pragma unroll
+      for (int d = 0; d < kDb; ++d) {
+        const char* vp = vt + v_lane + 32 * ks * kVRowB + d * 32;
+        const bf16x4 v0 = lds_read_tr(vp);
+        const bf16x4 v1 = lds_read_tr(vp + 16 * kVRowB);
+        const bf16x8 vf = __builtin_shufflevector(v0, v1, 0, 1, 2, 3, 4, 5, 6, 7);
+#pragma unroll
+        for (int rb = 0; rb < kPfRb; ++rb)
+          o[d][rb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf, pk[rb], o[d][rb], 0, 0, 0);
+      }
+    }
+  };
+
+  auto epilogue = [&](const Item& it) __attribute__((always_inline)) {
+    if (!w_active) return;
+    const bool final_write = n_sp == 1;
+#pragma unroll
+    for (int rb = 0; rb < kPfRb; ++rb) {
+      const int rr = wr0 + 16 * rb + lrow;
+      if (qpos[rb] < 0) continue;
+      const int qi = rr / group;
+      const int tok = it.q0 + qi;
+      const int64_t orow = static_cast<int64_t>(tok) * a.num_q_heads + it.g * group + (rr - qi * group);
+      const float l = lsum[rb][0];
+      if (final_write) {
+        const float inv = l > 0.f ? 1.f / l : 0.f;
+        uint16_t* dst = static_cast<uint16_t*>(a.out) + orow * D + 4 * lgrp;
+#pragma unroll
+        for (int d = 0; d < kDb; ++d)
+          *reinterpret_cast<i16x4*>(dst + 16 * d) = pack_bf16x4(o[d][rb] * inv);
+      } else {
+        if (tok >= a.ws_tokens) continue;
+        const int64_t slot = orow * n_sp + it.split;
+        float* dst = a.ws_o + slot * D + 4 * lgrp;
+#pragma unroll
+        for (int d = 0; d < kDb; ++d) *reinterpret_cast<f32x4*>(dst + 16 * d) = o[d][rb];
+        if (lgrp == 0) {
+          a.ws_ml[slot * 2] = mc[rb];
+          a.ws_ml[slot * 2 + 1] = l;
+        }
+      }
+    }
+  };
+
+  // ---- prologue: the first item's queries, pages and first tile ----
+  load_q(W0, qf);
+  enter_item(W0);
+  reset_state();
+  fetch_pages(W0, 0);
+#pragma unroll
+  for (int c = 0; c < kChunks; ++c) pg_next[c] = pg_next2[c];
+  load_kv(W0, 0);
+  {
+    int wh, t;
+    after(0, 1, wh, t);
+    fetch_pages(item_ref(wh), t);
+  }
+  stage(0);
+#pragma unroll
+  for (int c = 0; c < kChunks; ++c) pg_next[c] = pg_next2[c];
+  __syncthreads();
+
+  // ---- the stream of tiles ----
+  int buf = 0;
+  int tc = 0;
+  while (true) {
+    const bool last = tc == W0.n_tiles - 1;
+    if constexpr (pf_stream_q_lds<kPfThreads>())
+      if (last && W1.valid) dma_q(W1);
+    {
+      int wh, t;
+      after(tc, 1, wh, t);
+      load_kv(item_ref(wh), t);
+      after(tc, 2, wh, t);
+      fetch_pages(item_ref(wh), t);
+    }
+#pragma unroll
+    for (int sub = 0; sub < kPfKeys / 64; ++sub) {
+      const int tb = W0.k_lo + tc * kPfKeys + 64 * sub;
+      if (w_active && tb <= w_qmax) {
+        const char* kt = smem + buf * kBufB + sub * 64 * kKRowB;
+        const char* vt = smem + buf * kBufB + kKTileB + sub * 64 * kVRowB;
+        if (tb + 63 <= w_qmin)
+          compute(kt, vt, tb, std::integral_constant<bool, false>());
+        else
+          compute(kt, vt, tb, std::integral_constant<bool, true>());
+      }
+    }
+    stage(buf ^ 1);
+#pragma unroll
+    for (int c = 0; c < kChunks; ++c) pg_next[c] = pg_next2[c];
+    __syncthreads();
+    buf ^= 1;
+    if (!last) {
+      ++tc;
+      continue;
+    }
+    epilogue(W0);
+    if (!W1.valid) break;
+    W0 = W1;
+    W1 = W2;
+    W2 = take_item();
+    if constexpr (pf_stream_q_lds<kPfThreads>()) {
+      read_q_lds();
+      // Every wave's query DMA writes rows that other waves read here.  An
+      // item of one tile issues the next item's DMA in its first iteration,
+      // so all reads must finish first; with more tiles a tile barrier lies
+      // between.
+      if (W0.n_tiles == 1 && W1.valid) __syncthreads();
+    } else {
+      load_q(W0, qf);
+    }
+    enter_item(W0);
+    reset_state();
+    tc = 0;
   }
 }
 
@@ -2057,6 +2577,9 @@ struct Plan {
   bool decode = false;  // decode path (few rows) vs a tile kernel
   bool prefill = false; // bf16 tiles: paged_prefill_kernel, else paged_attention_kernel
   bool pf_short = false; // prefill: the 4-wave, 64-position shape
+  bool pf_stream = false; // prefill: persistent workgroups over work-item records
+  size_t rec_off = 0;     // prefill stream: the records in the workspace
+  int64_t n_ids = 0;      // prefill stream: upper bound of the work-item ids
   int n_blocks = 0;     // prefill: blocks of 8 (sequence, KV head) units
   int rbw = 1;          // decode: 16-row blocks each wave holds
   int epi_rows = 16;    // decode: rows of a block that carry queries
@@ -2115,9 +2638,10 @@ int make_plan(const pkv_pool_desc* d, int n_seqs, int hq, int max_q, int max_seq
     // paged_prefill_kernel: 128-row tiles; KV splits only when the units'
     // tiles alone cannot fill the chip.
     p->prefill = true;
-    p->pf_short = max_seq_len <= kPfShortCtx;
-    const int keys = p->pf_short ? kPfShortKeys : kPfKeys;
-    p->tile_rows = p->pf_short ? 16 * kPfRb * kPfShortWaves : kPfMaxRows;
+    p->pf_stream = max_seq_len <= kPfStreamCtx;
+    p->pf_short = !p->pf_stream && max_seq_len <= kPfShortCtx;
+    const int keys = p->pf_stream ? kPfStreamKeys : p->pf_short ? kPfShortKeys : kPfKeys;
+    p->tile_rows = p->pf_stream ? 16 * kPfRb * kPfStreamWaves : p->pf_short ? 16 * kPfRb * kPfShortWaves : kPfMaxRows;
     if (rows > (int64_t{1} << 28)) return fail(PKV_ERR_UNSUPPORTED, std::string(fn) + ": too many queries per sequence");
     const int64_t q_tiles = (rows + p->tile_rows - 1) / p->tile_rows;
     p->q_tiles = static_cast<int>(q_tiles);
@@ -2133,6 +2657,12 @@ int make_plan(const pkv_pool_desc* d, int n_seqs, int hq, int max_q, int max_seq
     if (sched_rows > (int64_t{1} << 27)) return fail(PKV_ERR_UNSUPPORTED, std::string(fn) + ": too many work items");
     p->items_off = 0;
     p->partial_off = (static_cast<size_t>(p->n_blocks + 1) * sizeof(int32_t) + 255) & ~size_t{255};
+    if (p->pf_stream) {
+      p->n_ids = sched_rows * 8;
+      if (p->n_ids > (int64_t{1} << 24)) return fail(PKV_ERR_UNSUPPORTED, std::string(fn) + ": too many work items");
+      p->rec_off = p->partial_off;
+      p->partial_off = (p->rec_off + static_cast<size_t>(p->n_ids) * 8 * sizeof(int32_t) + 255) & ~size_t{255};
+    }
     p->ws_bytes = p->partial_off;
     if (p->n_splits > 1)
       p->ws_bytes += static_cast<size_t>(n_seqs) * max_q * hq * p->n_splits * (d->head_dim + 2) * sizeof(float);
@@ -2204,7 +2734,7 @@ int launch_prefill_t(const AttnArgs& a, const Plan& p, char* ws, hipStream_t st)
                                                      hipFuncAttributeMaxDynamicSharedMemorySize, kLds);
   if (attr != hipSuccess) return fail(PKV_ERR_DEVICE, std::string("prefill: LDS attribute: ") + hipGetErrorString(attr));
   int32_t* row_off = reinterpret_cast<int32_t*>(ws + p.items_off);
-  prefill_schedule_kernel<<<1, kThreads, 0, st>>>(a, row_off, p.n_blocks, p.tile_rows);
+  prefill_schedule_kernel<<<1, kThreads, 0, st>>>(a, row_off, p.n_blocks, p.tile_rows, nullptr);
   const int64_t grid = prefill_grid(p, a.n_seqs, a.num_kv_heads, a.group, a.total_q);
   if (grid > INT32_MAX) return fail(PKV_ERR_UNSUPPORTED, "prefill: grid too large");
   if (grid > 0) kern<<<static_cast<int>(grid), dim3(kWaves * kWave), kLds, st>>>(a, row_off, p.n_blocks);
@@ -2215,8 +2745,42 @@ int launch_prefill_t(const AttnArgs& a, const Plan& p, char* ws, hipStream_t st)
   return PKV_OK;
 }
 
+// Compute units of the current device (the stream launch fills each once).
+int device_cus() {
+  int dev = 0, cus = 0;
+  if (hipGetDevice(&dev) != hipSuccess ||
+      hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0)
+    cus = 256;
+  return cus;
+}
+
+template <int D, int kPageMode, int kWaves, int kKeys, bool kI8>
+int launch_prefill_stream_t(const AttnArgs& a, const Plan& p, char* ws, hipStream_t st) {
+  constexpr int kLds = pf_stream_lds_bytes<D, kKeys, kWaves * kWave>();
+  static_assert(kLds <= 160 * 1024, "stream kernel LDS");
+  auto* kern = &paged_prefill_stream_kernel<D, kPageMode, kWaves * kWave, kKeys, kI8>;
+  static const hipError_t attr = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
+                                                     hipFuncAttributeMaxDynamicSharedMemorySize, kLds);
+  if (attr != hipSuccess) return fail(PKV_ERR_DEVICE, std::string("prefill: LDS attribute: ") + hipGetErrorString(attr));
+  int32_t* row_off = reinterpret_cast<int32_t*>(ws + p.items_off);
+  int32_t* rec = reinterpret_cast<int32_t*>(ws + p.rec_off);
+  prefill_schedule_kernel<<<1, kThreads, 0, st>>>(a, row_off, p.n_blocks, p.tile_rows, rec);
+  // one workgroup per CU (two for 4-wave workgroups), a multiple of 8
+  const int64_t per_cu = kWaves >= 8 ? 1 : 2;
+  int64_t grid = std::min<int64_t>(device_cus() * per_cu, p.n_ids);
+  grid = (grid + 7) / 8 * 8;
+  if (grid > 0)
+    kern<<<static_cast<int>(grid), dim3(kWaves * kWave), kLds, st>>>(a, row_off, p.n_blocks, rec);
+  if (p.n_splits > 1) {
+    dim3 mg(a.num_q_heads, p.max_q, a.n_seqs);
+    merge_chunks_kernel<uint16_t, D><<<mg, dim3(kWave), 0, st>>>(a);
+  }
+  return PKV_OK;
+}
+
 template <int D, int kPageMode, bool kI8>
 int launch_prefill_shape(const AttnArgs& a, const Plan& p, char* ws, hipStream_t st) {
+  if (p.pf_stream) return launch_prefill_stream_t<D, kPageMode, kPfStreamWaves, kPfStreamKeys, kI8>(a, p, ws, st);
   return p.pf_short ? launch_prefill_t<D, kPageMode, kPfShortWaves, kPfShortKeys, kI8>(a, p, ws, st)
                     : launch_prefill_t<D, kPageMode, kPfWaves, kPfKeys, kI8>(a, p, ws, st);
 }
