@@ -21,10 +21,14 @@
 //    a range boundary split, by log-sum-exp.
 //  * paged_prefill_kernel (bf16 and INT8 pages, longer appends): a
 //    workgroup owns 32 query rows per wave of one (sequence, KV head) unit
-//    (8 waves and 128-position K/V tiles, or 4 waves and 64-position tiles
-//    when no context exceeds 2048 positions), stages K/V tiles in two LDS
-//    buffers through the block table, and runs both products on
-//    v_mfma_f32_16x16x32_bf16 with V^T read by ds_read_b64_tr_b16.
+//    (8 waves, 128-position K/V tiles), stages K/V tiles in two LDS buffers
+//    through the block table, and runs both products on
+//    v_mfma_f32_16x16x32_bf16 with V^T read by ds_read_b64_tr_b16.  INT8
+//    codes are staged as exact bf16 integers: the key scale multiplies the
+//    scores and the value scale the probabilities.
+//  * paged_prefill_stream_kernel (the same, when no context exceeds 2048
+//    positions): persistent 8-wave workgroups with 64-position tiles that
+//    run through their work items without draining between them.
 //  * paged_attention_kernel: the fp32 prefill (4 waves, 64-position tiles,
 //    v_mfma_f32_16x16x4_f32), kept for the fp32 parity cases.
 //  * copy_pages_kernel, codec_encode_kernel / codec_decode_kernel,
@@ -189,24 +193,6 @@ __device__ __forceinline__ u32x4 i8x8_to_bf16(uint2 x) {
     const uint32_t v = w ? x.y : x.x;
     const f32x4 f = {static_cast<float>(static_cast<int8_t>(v)), static_cast<float>(static_cast<int8_t>(v >> 8)),
                      static_cast<float>(static_cast<int8_t>(v >> 16)), static_cast<float>(static_cast<int8_t>(v >> 24))};
-    const auto p = __builtin_bit_cast(uint2, pack_bf16x4(f));
-    o[2 * w] = p.x;
-    o[2 * w + 1] = p.y;
-  }
-  return o;
-}
-
-// Eight int8 codes times their vector's scale -> eight bf16 (each product
-// rounded once, to nearest even).
-__device__ __forceinline__ u32x4 i8x8_scaled_to_bf16(uint2 x, float scale) {
-  u32x4 o;
-#pragma unroll
-  for (int w = 0; w < 2; ++w) {
-    const uint32_t v = w ? x.y : x.x;
-    const f32x4 f = {static_cast<float>(static_cast<int8_t>(v)) * scale,
-                     static_cast<float>(static_cast<int8_t>(v >> 8)) * scale,
-                     static_cast<float>(static_cast<int8_t>(v >> 16)) * scale,
-                     static_cast<float>(static_cast<int8_t>(v >> 24)) * scale};
     const auto p = __builtin_bit_cast(uint2, pack_bf16x4(f));
     o[2 * w] = p.x;
     o[2 * w + 1] = p.y;
@@ -1168,10 +1154,11 @@ template <int D>
 constexpr int pf_k_row_bytes() { return D * 2 + 16; }
 template <int D>
 constexpr int pf_v_row_bytes() { return D * 2 + 32; }
-// LDS of one staged K + V buffer (INT8 pages are staged dequantized, in the
-// same layout), two buffers per workgroup.
+// LDS of one staged K + V buffer, two buffers per workgroup.  INT8 codes are
+// staged as bf16 in the same layout, followed by the tile's key scales and
+// value scales (fp32, kKeys of each).
 template <int D, int kKeys, bool kI8>
-constexpr int pf_buf_bytes() { return kKeys * (pf_k_row_bytes<D>() + pf_v_row_bytes<D>()); }
+constexpr int pf_buf_bytes() { return kKeys * (pf_k_row_bytes<D>() + pf_v_row_bytes<D>()) + (kI8 ? 8 * kKeys : 0); }
 template <int D, int kKeys, bool kI8>
 constexpr int pf_lds_bytes() { return 2 * pf_buf_bytes<D, kKeys, kI8>(); }
 // Rows one wave stages per pass (a pass = one 16-byte chunk per thread).
@@ -1265,9 +1252,11 @@ __device__ __forceinline__ bf16x4 lds_read_tr(const char* p) {
 
 // kPageMode 0: page_size a power of two >= the rows a wave stages per pass
 // (those rows then share one page: scalar lookup); 1: other powers of two;
-// 2: any page size.  kI8: INT8 pages, staged dequantized as bf16(code x
-// scale) in the bf16 tile layout, so the scores and probabilities take the
-// bf16 path unchanged.
+// 2: any page size.  kI8: INT8 pages (TileInfer.jl docs, "KV cache", "INT8
+// cache"): the codes are staged as bf16 (exact, |code| <= 127), each score
+// is multiplied by its key's scale before the softmax, and each probability
+// by its value's scale before it enters O^T; the row sums take the unscaled
+// probabilities.
 template <int D, int kPageMode, int kPfThreads, int kPfKeys, bool kI8>
 __global__ __launch_bounds__(kPfThreads, kPfRb >= 3 ? 1 : 2) void paged_prefill_kernel(AttnArgs a,
                                                                    const int32_t* __restrict__ row_off,
@@ -1384,10 +1373,14 @@ __global__ __launch_bounds__(kPfThreads, kPfRb >= 3 ? 1 : 2) void paged_prefill_
     for (int c = 0; c < kChunks; ++c) {
       const int row = srow0 + c * kRowsPerPass;
       if constexpr (kI8) {
-        // keys and values are staged dequantized, bf16(code x scale): the
-        // scores and probabilities then take the bf16 path unchanged
-        *reinterpret_cast<u32x4*>(kb + row * kKRowB + spart * 16) = i8x8_scaled_to_bf16(kr[c], ksr[c]);
-        *reinterpret_cast<u32x4*>(vb + row * kVRowB + spart * 16) = i8x8_scaled_to_bf16(vr[c], vsr[c]);
+        // codes as exact bf16; part 0 of each row writes the row's scales
+        *reinterpret_cast<u32x4*>(kb + row * kKRowB + spart * 16) = i8x8_to_bf16(kr[c]);
+        *reinterpret_cast<u32x4*>(vb + row * kVRowB + spart * 16) = i8x8_to_bf16(vr[c]);
+        if (spart == 0) {
+          float* sc = reinterpret_cast<float*>(vb + kPfKeys * kVRowB);
+          sc[row] = ksr[c];
+          sc[kPfKeys + row] = vsr[c];
+        }
       } else {
         *reinterpret_cast<u32x4*>(kb + row * kKRowB + spart * 16) = kr[c];
         *reinterpret_cast<u32x4*>(vb + row * kVRowB + spart * 16) = vr[c];
@@ -1439,9 +1432,19 @@ __global__ __launch_bounds__(kPfThreads, kPfRb >= 3 ? 1 : 2) void paged_prefill_
   // lane parts of the LDS operand addresses
   const int k_lane = lrow * kKRowB + lgrp * (D / 4) * 2;
   const int v_lane = (4 * lgrp + (lrow >> 2)) * kVRowB + ((lrow & 3) >> 1) * 16 + (lrow & 1) * 8;
+  // INT8: each score times its key's scale (lane keys kb * 16 + 4 lgrp + i)
+  auto scale_scores = [&](f32x4 (&s)[4][kPfRb], const float* sk) __attribute__((always_inline)) {
+#pragma unroll
+    for (int kb = 0; kb < 4; ++kb) {
+      const f32x4 ksc = *reinterpret_cast<const f32x4*>(sk + kb * 16 + 4 * lgrp);
+#pragma unroll
+      for (int rb = 0; rb < kPfRb; ++rb) s[kb][rb] *= ksc;
+    }
+  };
 
-  // kt, vt: the sub-tile's staged K and V rows.
-  auto compute = [&](const char* kt, const char* vt, int tb, auto mask_tag)
+  // kt, vt: the sub-tile's staged K and V rows; sk (INT8): its key scales,
+  // value scales at sk + kPfKeys.
+  auto compute = [&](const char* kt, const char* vt, const float* sk, int tb, auto mask_tag)
       __attribute__((always_inline)) {
     constexpr bool kMask = decltype(mask_tag)::value;
     f32x4 s[4][kPfRb];
@@ -1461,6 +1464,7 @@ __global__ __launch_bounds__(kPfThreads, kPfRb >= 3 ? 1 : 2) void paged_prefill_
       }
     }
     if constexpr (PKV_PREFILL_SETPRIO) __builtin_amdgcn_s_setprio(0);
+    if constexpr (kI8) scale_scores(s, sk);
     // row maxima, then one (rarely taken) rescale branch for both row blocks
     float muse[kPfRb];
     bool up_any = false;
@@ -1497,7 +1501,13 @@ __global__ __launch_bounds__(kPfThreads, kPfRb >= 3 ? 1 : 2) void paged_prefill_
     }
 #pragma unroll
     for (int ks = 0; ks < 2; ++ks) {
-      bf16x8 pk[kPfRb];   // probabilities: row sums and PV
+      bf16x8 pk[kPfRb];   // probabilities: row sums (and PV for bf16 pages)
+      bf16x8 pv[kPfRb];   // INT8: probabilities times the value scales, for PV
+      f32x4 vs0, vs1;     // INT8: value scales of this lane's keys
+      if constexpr (kI8) {
+        vs0 = *reinterpret_cast<const f32x4*>(sk + kPfKeys + 32 * ks + 4 * lgrp);
+        vs1 = *reinterpret_cast<const f32x4*>(sk + kPfKeys + 32 * ks + 16 + 4 * lgrp);
+      }
 #pragma unroll
       for (int rb = 0; rb < kPfRb; ++rb) {
 #pragma unroll
@@ -1506,6 +1516,10 @@ __global__ __launch_bounds__(kPfThreads, kPfRb >= 3 ? 1 : 2) void paged_prefill_
           const float e1 = fast_exp2(fmaf(s[2 * ks + 1][rb][i], c2, -muse[rb]));
           pk[rb][i] = static_cast<__bf16>(e0);
           pk[rb][4 + i] = static_cast<__bf16>(e1);
+          if constexpr (kI8) {
+            pv[rb][i] = static_cast<__bf16>(e0 * vs0[i]);
+            pv[rb][4 + i] = static_cast<__bf16>(e1 * vs1[i]);
+          }
         }
         lsum[rb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ones, pk[rb], lsum[rb], 0, 0, 0);
       }
@@ -1517,7 +1531,7 @@ __global__ __launch_bounds__(kPfThreads, kPfRb >= 3 ? 1 : 2) void paged_prefill_
         const bf16x8 vf = __builtin_shufflevector(v0, v1, 0, 1, 2, 3, 4, 5, 6, 7);
 #pragma unroll
         for (int rb = 0; rb < kPfRb; ++rb)
-          o[d][rb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf, pk[rb], o[d][rb], 0, 0, 0);
+          o[d][rb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf, kI8 ? pv[rb] : pk[rb], o[d][rb], 0, 0, 0);
       }
     }
   };
@@ -1541,10 +1555,11 @@ __global__ __launch_bounds__(kPfThreads, kPfRb >= 3 ? 1 : 2) void paged_prefill_
       if (w_active && tb <= w_qmax) {
         const char* kt = smem + (t & 1) * kBufB + sub * 64 * kKRowB;
         const char* vt = smem + (t & 1) * kBufB + kKTileB + sub * 64 * kVRowB;
+        const float* sk = reinterpret_cast<const float*>(smem + (t & 1) * kBufB + kKTileB + kPfKeys * kVRowB) + sub * 64;
         if (tb + 63 <= w_qmin)
-          compute(kt, vt, tb, std::integral_constant<bool, false>());
+          compute(kt, vt, sk, tb, std::integral_constant<bool, false>());
         else
-          compute(kt, vt, tb, std::integral_constant<bool, true>());
+          compute(kt, vt, sk, tb, std::integral_constant<bool, true>());
       }
     }
     stage((t + 1) & 1);
@@ -1606,9 +1621,9 @@ __global__ __launch_bounds__(kPfThreads, kPfRb >= 3 ? 1 : 2) void paged_prefill_
 // load them into registers at the switch.
 template <int kThreads_>
 constexpr bool pf_stream_q_lds() { return kThreads_ >= 512; }
-template <int D, int kKeys, int kThreads_>
+template <int D, int kKeys, int kThreads_, bool kI8>
 constexpr int pf_stream_lds_bytes() {
-  return pf_lds_bytes<D, kKeys, false>() + (pf_stream_q_lds<kThreads_>() ? 16 * kPfRb * (kThreads_ / kWave) * D * 2 : 0);
+  return pf_lds_bytes<D, kKeys, kI8>() + (pf_stream_q_lds<kThreads_>() ? 16 * kPfRb * (kThreads_ / kWave) * D * 2 : 0);
 }
 
 template <int D, int kPageMode, int kPfThreads, int kPfKeys, bool kI8>
@@ -1755,8 +1770,14 @@ __global__ __launch_bounds__(kPfThreads, kPfThreads >= 512 ? 1 : 2) void paged_p
     for (int c = 0; c < kChunks; ++c) {
       const int row = srow0 + c * kRowsPerPass;
       if constexpr (kI8) {
-        *reinterpret_cast<u32x4*>(kb + row * kKRowB + spart * 16) = i8x8_scaled_to_bf16(kr[c], ksr[c]);
-        *reinterpret_cast<u32x4*>(vb + row * kVRowB + spart * 16) = i8x8_scaled_to_bf16(vr[c], vsr[c]);
+        // codes as exact bf16; part 0 of each row writes the row's scales
+        *reinterpret_cast<u32x4*>(kb + row * kKRowB + spart * 16) = i8x8_to_bf16(kr[c]);
+        *reinterpret_cast<u32x4*>(vb + row * kVRowB + spart * 16) = i8x8_to_bf16(vr[c]);
+        if (spart == 0) {
+          float* sc = reinterpret_cast<float*>(vb + kPfKeys * kVRowB);
+          sc[row] = ksr[c];
+          sc[kPfKeys + row] = vsr[c];
+        }
       } else {
         *reinterpret_cast<u32x4*>(kb + row * kKRowB + spart * 16) = kr[c];
         *reinterpret_cast<u32x4*>(vb + row * kVRowB + spart * 16) = vr[c];
@@ -1875,8 +1896,18 @@ __global__ __launch_bounds__(kPfThreads, kPfThreads >= 512 ? 1 : 2) void paged_p
   const bf16x8 ones = __builtin_bit_cast(bf16x8, u32x4{0x3f803f80u, 0x3f803f80u, 0x3f803f80u, 0x3f803f80u});
   const int k_lane = lrow * kKRowB + lgrp * (D / 4) * 2;
   const int v_lane = (4 * lgrp + (lrow >> 2)) * kVRowB + ((lrow & 3) >> 1) * 16 + (lrow & 1) * 8;
+  // INT8: each score times its key's scale (lane keys kb * 16 + 4 lgrp + i)
+  auto scale_scores = [&](f32x4 (&s)[4][kPfRb], const float* sk) __attribute__((always_inline)) {
+#pragma unroll
+    for (int kb = 0; kb < 4; ++kb) {
+      const f32x4 ksc = *reinterpret_cast<const f32x4*>(sk + kb * 16 + 4 * lgrp);
+#pragma unroll
+      for (int rb = 0; rb < kPfRb; ++rb) s[kb][rb] *= ksc;
+    }
+  };
 
-  auto compute = [&](const char* kt, const char* vt, int tb, auto mask_tag) __attribute__((always_inline)) {
+  auto compute = [&](const char* kt, const char* vt, const float* sk, int tb, auto mask_tag)
+      __attribute__((always_inline)) {
     constexpr bool kMask = decltype(mask_tag)::value;
     f32x4 s[4][kPfRb];
 #pragma unroll
@@ -1893,6 +1924,7 @@ __global__ __launch_bounds__(kPfThreads, kPfThreads >= 512 ? 1 : 2) void paged_p
         s[kb][rb] = acc;
       }
     }
+    if constexpr (kI8) scale_scores(s, sk);
     float muse[kPfRb];
     bool up_any = false;
     float alpha[kPfRb];
@@ -1927,7 +1959,13 @@ __global__ __launch_bounds__(kPfThreads, kPfThreads >= 512 ? 1 : 2) void paged_p
     }
 #pragma unroll
     for (int ks = 0; ks < 2; ++ks) {
-      bf16x8 pk[kPfRb];
+      bf16x8 pk[kPfRb];   // probabilities: row sums (and PV for bf16 pages)
+      bf16x8 pv[kPfRb];   // INT8: probabilities times the value scales, for PV
+      f32x4 vs0, vs1;     // INT8: value scales of this lane's keys
+      if constexpr (kI8) {
+        vs0 = *reinterpret_cast<const f32x4*>(sk + kPfKeys + 32 * ks + 4 * lgrp);
+        vs1 = *reinterpret_cast<const f32x4*>(sk + kPfKeys + 32 * ks + 16 + 4 * lgrp);
+      }
 #pragma unroll
       for (int rb = 0; rb < kPfRb; ++rb) {
 #pragma unroll
@@ -1936,6 +1974,10 @@ __global__ __launch_bounds__(kPfThreads, kPfThreads >= 512 ? 1 : 2) void paged_p
           const float e1 = fast_exp2(fmaf(s[2 * ks + 1][rb][i], c2, -muse[rb]));
           pk[rb][i] = static_cast<__bf16>(e0);
           pk[rb][4 + i] = static_cast<__bf16>(e1);
+          if constexpr (kI8) {
+            pv[rb][i] = static_cast<__bf16>(e0 * vs0[i]);
+            pv[rb][4 + i] = static_cast<__bf16>(e1 * vs1[i]);
+          }
         }
         lsum[rb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ones, pk[rb], lsum[rb], 0, 0, 0);
       }
@@ -1947,7 +1989,7 @@ __global__ __launch_bounds__(kPfThreads, kPfThreads >= 512 ? 1 : 2) void paged_p
         const bf16x8 vf = __builtin_shufflevector(v0, v1, 0, 1, 2, 3, 4, 5, 6, 7);
 #pragma unroll
         for (int rb = 0; rb < kPfRb; ++rb)
-          o[d][rb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf, pk[rb], o[d][rb], 0, 0, 0);
+          o[d][rb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf, kI8 ? pv[rb] : pk[rb], o[d][rb], 0, 0, 0);
       }
     }
   };
@@ -2021,10 +2063,11 @@ __global__ __launch_bounds__(kPfThreads, kPfThreads >= 512 ? 1 : 2) void paged_p
       if (w_active && tb <= w_qmax) {
         const char* kt = smem + buf * kBufB + sub * 64 * kKRowB;
         const char* vt = smem + buf * kBufB + kKTileB + sub * 64 * kVRowB;
+        const float* sk = reinterpret_cast<const float*>(smem + buf * kBufB + kKTileB + kPfKeys * kVRowB) + sub * 64;
         if (tb + 63 <= w_qmin)
-          compute(kt, vt, tb, std::integral_constant<bool, false>());
+          compute(kt, vt, sk, tb, std::integral_constant<bool, false>());
         else
-          compute(kt, vt, tb, std::integral_constant<bool, true>());
+          compute(kt, vt, sk, tb, std::integral_constant<bool, true>());
       }
     }
     stage(buf ^ 1);
@@ -2756,7 +2799,7 @@ int device_cus() {
 
 template <int D, int kPageMode, int kWaves, int kKeys, bool kI8>
 int launch_prefill_stream_t(const AttnArgs& a, const Plan& p, char* ws, hipStream_t st) {
-  constexpr int kLds = pf_stream_lds_bytes<D, kKeys, kWaves * kWave>();
+  constexpr int kLds = pf_stream_lds_bytes<D, kKeys, kWaves * kWave, kI8>();
   static_assert(kLds <= 160 * 1024, "stream kernel LDS");
   auto* kern = &paged_prefill_stream_kernel<D, kPageMode, kWaves * kWave, kKeys, kI8>;
   static const hipError_t attr = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),

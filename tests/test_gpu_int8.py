@@ -22,7 +22,8 @@ import synth
 from conftest import ensure_library
 from gpu_path import (DEV, Session, dev_tensor, host_f64, i64, run_decode, run_prefix, run_rewind,
                       run_spec)
-from oracle.quant import quantize, quantize_then_attend, store_rows_int8
+from oracle.attention import attend
+from oracle.quant import dequantize, quantize, quantize_then_attend, store_rows_int8
 
 pytestmark = pytest.mark.gpu
 
@@ -170,6 +171,59 @@ def test_prefill_int8_variants(D, ps, hq, hkv, ctx, news):
             check_close(out[row:row + news[b]], e, f"prefill int8 seq {b}")
         row += news[b]
 
+
+
+# Error budget of the append kernel, per output element (row r, dim d), against
+# the exact result O over the dequantized values:
+#  * the probabilities enter O^T rounded to bf16 (p times the value's scale for
+#    INT8 pages) and the row sum rounded to bf16: at most 2^-9 relative each,
+#    so at most 2^-8 max_j |v_jd| over the positions j the row attends to;
+#  * fp32 scores, exponentials and sums: well under 2^-10 max_j |v_jd| at
+#    these lengths (head_dim 128, a few thousand positions);
+#  * the output's own rounding to bf16: 2^-9 |O_rd|.
+# INT8 codes are exact bf16 integers and the scales are applied in fp32, so
+# the quantization adds no term beyond the dequantized values themselves.
+BUDGET_V, BUDGET_O = 2.0 ** -8 + 2.0 ** -10, 2.0 ** -9
+
+
+@pytest.mark.parametrize("kv_int8", [False, True])
+@pytest.mark.parametrize("ctx,news", [
+    ([2600, 0, 900], [120, 200, 64]),       # a context above 2048: the tiled kernel
+    ([1500, 0, 300], [200, 250, 40]),       # every context within 2048: the stream kernel
+])
+def test_prefill_error_budget(kv_int8, ctx, news):
+    """Every output element is within the error budget above, for bf16 and
+    INT8 pages."""
+    print(f"prefill error budget int8={kv_int8} ctx={ctx} new={news}", flush=True)
+    D, ps, hq, hkv = 128, 16, 32, 8
+    rng = np.random.default_rng(77 + len(ctx) + int(kv_int8))
+    lens = [c + n for c, n in zip(ctx, news)]
+    pages = sum(-(-L // ps) for L in lens) + 3
+    s = Session.open(_Pools(D, ps, hkv, pages, seed=5), kv_int8=kv_int8)
+    seqs = [s.alloc.seq_new() for _ in lens]
+    kv = [synth.normal_values(rng, (2, L, hkv, D), synth.BF16) for L in lens]
+    for b, seq in enumerate(seqs):
+        s.alloc.reserve(seq, lens[b])
+        s.store(seq, 0, kv[b][0], kv[b][1], synth.BF16)
+    qs = [synth.normal_values(rng, (n, hq, D), synth.BF16) for n in news]
+    out = host_f64(s.append(seqs, news, dev_tensor(np.concatenate(qs), synth.BF16)))
+    row, worst = 0, 0.0
+    for b in range(len(lens)):
+        n = news[b]
+        if n:
+            k64, v64 = synth.to_f64(kv[b][0], synth.BF16), synth.to_f64(kv[b][1], synth.BF16)
+            if kv_int8:
+                k64, v64 = dequantize(*quantize(k64)), dequantize(*quantize(v64))
+            e = attend(synth.to_f64(qs[b], synth.BF16), k64, v64, s.scale)         # [n][hq][D]
+            vmax = np.maximum.accumulate(np.abs(v64), axis=0)[lens[b] - n:]        # [n][hkv][D]
+            vmax = np.repeat(vmax, hq // hkv, axis=1)                              # per query head
+            bound = BUDGET_V * vmax + BUDGET_O * np.abs(e)
+            err = np.abs(out[row:row + n] - e)
+            assert np.isfinite(out[row:row + n]).all()
+            assert (err <= bound).all(), f"seq {b}: worst err/bound {(err / bound).max():.3f}"
+            worst = max(worst, float((err / bound).max()))
+        row += n
+    print(f"worst error / budget {worst:.3f}", flush=True)
 
 def test_prefix_shared_prefill_int8_reduced():
     w = synth.prefix_traces(n_rows=20, n_traces=5, first_rows=(100, 140, 190), len_lo=100,
