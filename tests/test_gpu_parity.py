@@ -428,6 +428,19 @@ class _Pools:
         self.free_order = np.random.default_rng(seed).permutation(num_pages).astype(np.int32)
 
 
+@pytest.mark.parametrize("D,ps,hq,hkv,ctx,news", [
+    (128, 16, 32, 8, [2100, 0, 3000], [200, 2300, 1]),     # every wave row count, one sequence all-new
+    (128, 64, 8, 8, [5000, 2040], [17, 63]),               # group 1: rows 17 and 63 of one tile
+    (128, 256, 16, 2, [9000], [65]),                       # a long split context, group 8
+    (128, 32, 32, 4, [2500, 2600, 0], [64, 129, 2100]),
+])
+def test_prefill_long_context_variants(D, ps, hq, hkv, ctx, news):
+    """Appends over contexts above 2048 positions (the tiled prefill kernels,
+    not the persistent one): ragged row counts per wave and tile, one or
+    several KV splits, GQA groups 1..8, page sizes 16..256."""
+    test_prefill_variants(synth.BF16, D, ps, hq, hkv, ctx, news)
+
+
 @pytest.mark.parametrize("dtype,D,ps,hq,hkv,ctx,news", [
     (synth.BF16, 128, 16, 32, 8, [300, 0, 1000], [200, 64, 150]),
     (synth.BF16, 64, 3, 8, 8, [100, 37], [49, 130]),
