@@ -1169,11 +1169,15 @@ constexpr int pf_wave_rows() { return kWave / (D * (kI8 ? 1 : 2) / static_cast<i
 // where a block's q-tiles are the most any of its 8 units needs.  With `rec`
 // (the persistent short-append launch) it also writes one record per work
 // item id = 8 * row + slot: int32 {b, g, q0, n_b, start, row0, kv_end, split},
-// b = -1 for an item with no work.
-__global__ __launch_bounds__(kThreads) void prefill_schedule_kernel(AttnArgs a, int32_t* row_off,
-                                                                    int n_blocks, int tile_rows,
-                                                                    int32_t* __restrict__ rec) {
-  __shared__ int s_scan[kThreads];
+// b = -1 for an item with no work.  One workgroup of kSchedThreads threads,
+// one block per thread per pass: a block's 8 units read their sequence
+// bounds with independent loads before any record is stored, so a pass
+// waits on memory once.
+constexpr int kSchedThreads = 1024;
+__global__ __launch_bounds__(kSchedThreads) void prefill_schedule_kernel(AttnArgs a, int32_t* row_off,
+                                                                         int n_blocks, int tile_rows,
+                                                                         int32_t* __restrict__ rec) {
+  __shared__ int s_scan[kSchedThreads];
   __shared__ int s_carry;
   const int tid = threadIdx.x;
   if (tid == 0) {
@@ -1182,23 +1186,28 @@ __global__ __launch_bounds__(kThreads) void prefill_schedule_kernel(AttnArgs a, 
   }
   __syncthreads();
   const int units = a.n_seqs * a.num_kv_heads;
-  for (int base = 0; base < n_blocks; base += kThreads) {
+  for (int base = 0; base < n_blocks; base += kSchedThreads) {
     const int blk = base + tid;
+    int sb[8], sq0[8], snb[8], sstart[8];
     int tiles = 0;
-    if (blk < n_blocks) {
-      int prev = -1;
-      for (int u = blk * 8; u < min(units, blk * 8 + 8); ++u) {
-        const int b = u / a.num_kv_heads;
-        if (b == prev) continue;
-        prev = b;
-        const int n_b = min(a.cu_q[b + 1] - a.cu_q[b], a.max_q);
-        tiles = max(tiles, (n_b * a.group + tile_rows - 1) / tile_rows);
-      }
+#pragma unroll
+    for (int slot = 0; slot < 8; ++slot) {
+      const int u = blk * 8 + slot;
+      const bool ok = blk < n_blocks && u < units;
+      const int b = ok ? u / a.num_kv_heads : 0;
+      const int q0 = a.cu_q[b];
+      const int q1 = a.cu_q[b + 1];
+      const int len = a.seq_lens[b];
+      sb[slot] = ok ? b : -1;
+      sq0[slot] = q0;
+      snb[slot] = q1 - q0;
+      sstart[slot] = len - (q1 - q0);
+      if (ok) tiles = max(tiles, (min(q1 - q0, a.max_q) * a.group + tile_rows - 1) / tile_rows);
     }
     const int v = tiles * a.n_splits;
     s_scan[tid] = v;
     __syncthreads();
-    for (int off = 1; off < kThreads; off <<= 1) {
+    for (int off = 1; off < kSchedThreads; off <<= 1) {
       const int w = tid >= off ? s_scan[tid - off] : 0;
       __syncthreads();
       s_scan[tid] += w;
@@ -1207,16 +1216,12 @@ __global__ __launch_bounds__(kThreads) void prefill_schedule_kernel(AttnArgs a, 
     if (blk < n_blocks) row_off[blk + 1] = s_carry + s_scan[tid];
     if (rec && blk < n_blocks) {
       const int r0 = s_carry + s_scan[tid] - v;
+#pragma unroll
       for (int slot = 0; slot < 8; ++slot) {
+        const int b = sb[slot];
+        const int n_b = snb[slot];
+        const int rows_total = b >= 0 ? min(n_b, a.max_q) * a.group : 0;
         const int u = blk * 8 + slot;
-        const int b = u < units ? u / a.num_kv_heads : -1;
-        int q0 = 0, n_b = 0, start = 0, rows_total = 0;
-        if (b >= 0) {
-          q0 = a.cu_q[b];
-          n_b = a.cu_q[b + 1] - q0;
-          start = a.seq_lens[b] - n_b;
-          rows_total = min(n_b, a.max_q) * a.group;
-        }
         for (int local = 0; local < v; ++local) {
           const int qt = tiles - 1 - local / a.n_splits;
           const int split = local - (local / a.n_splits) * a.n_splits;
@@ -1224,17 +1229,18 @@ __global__ __launch_bounds__(kThreads) void prefill_schedule_kernel(AttnArgs a, 
           int kv_end = 0;
           bool ok = b >= 0 && row0 < rows_total;
           if (ok) {
-            kv_end = min(start + (min(row0 + tile_rows, rows_total) - 1) / a.group + 1, a.kv_cap);
+            kv_end = min(sstart[slot] + (min(row0 + tile_rows, rows_total) - 1) / a.group + 1, a.kv_cap);
             ok = split * a.split_len < kv_end;
           }
           int32_t* o = rec + 8 * (static_cast<int64_t>(r0 + local) * 8 + slot);
-          *reinterpret_cast<int4*>(o) = ok ? make_int4(b, u - b * a.num_kv_heads, q0, n_b) : make_int4(-1, 0, 0, 0);
-          *reinterpret_cast<int4*>(o + 4) = make_int4(start, row0, kv_end, split);
+          *reinterpret_cast<int4*>(o) =
+              ok ? make_int4(b, u - b * a.num_kv_heads, sq0[slot], n_b) : make_int4(-1, 0, 0, 0);
+          *reinterpret_cast<int4*>(o + 4) = make_int4(sstart[slot], row0, kv_end, split);
         }
       }
     }
     __syncthreads();
-    if (tid == kThreads - 1) s_carry += s_scan[tid];
+    if (tid == kSchedThreads - 1) s_carry += s_scan[tid];
     __syncthreads();
   }
 }
@@ -2777,7 +2783,7 @@ int launch_prefill_t(const AttnArgs& a, const Plan& p, char* ws, hipStream_t st)
                                                      hipFuncAttributeMaxDynamicSharedMemorySize, kLds);
   if (attr != hipSuccess) return fail(PKV_ERR_DEVICE, std::string("prefill: LDS attribute: ") + hipGetErrorString(attr));
   int32_t* row_off = reinterpret_cast<int32_t*>(ws + p.items_off);
-  prefill_schedule_kernel<<<1, kThreads, 0, st>>>(a, row_off, p.n_blocks, p.tile_rows, nullptr);
+  prefill_schedule_kernel<<<1, kSchedThreads, 0, st>>>(a, row_off, p.n_blocks, p.tile_rows, nullptr);
   const int64_t grid = prefill_grid(p, a.n_seqs, a.num_kv_heads, a.group, a.total_q);
   if (grid > INT32_MAX) return fail(PKV_ERR_UNSUPPORTED, "prefill: grid too large");
   if (grid > 0) kern<<<static_cast<int>(grid), dim3(kWaves * kWave), kLds, st>>>(a, row_off, p.n_blocks);
@@ -2807,7 +2813,7 @@ int launch_prefill_stream_t(const AttnArgs& a, const Plan& p, char* ws, hipStrea
   if (attr != hipSuccess) return fail(PKV_ERR_DEVICE, std::string("prefill: LDS attribute: ") + hipGetErrorString(attr));
   int32_t* row_off = reinterpret_cast<int32_t*>(ws + p.items_off);
   int32_t* rec = reinterpret_cast<int32_t*>(ws + p.rec_off);
-  prefill_schedule_kernel<<<1, kThreads, 0, st>>>(a, row_off, p.n_blocks, p.tile_rows, rec);
+  prefill_schedule_kernel<<<1, kSchedThreads, 0, st>>>(a, row_off, p.n_blocks, p.tile_rows, rec);
   // one workgroup per CU (two for 4-wave workgroups), a multiple of 8
   const int64_t per_cu = kWaves >= 8 ? 1 : 2;
   int64_t grid = std::min<int64_t>(device_cus() * per_cu, p.n_ids);
