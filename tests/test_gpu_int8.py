@@ -176,14 +176,15 @@ def test_prefill_int8_variants(D, ps, hq, hkv, ctx, news):
 # Error budget of the append kernel, per output element (row r, dim d), against
 # the exact result O over the dequantized values:
 #  * the probabilities enter O^T rounded to bf16 (p times the value's scale for
-#    INT8 pages) and the row sum rounded to bf16: at most 2^-9 relative each,
-#    so at most 2^-8 max_j |v_jd| over the positions j the row attends to;
+#    INT8 pages) and the row sum rounded to bf16: at most 2^-8 relative each
+#    (bf16 keeps 8 significant bits), so at most 2^-7 max_j |v_jd| over the
+#    positions j the row attends to;
 #  * fp32 scores, exponentials and sums: well under 2^-10 max_j |v_jd| at
 #    these lengths (head_dim 128, a few thousand positions);
-#  * the output's own rounding to bf16: 2^-9 |O_rd|.
+#  * the output's own rounding to bf16: 2^-8 |O_rd|.
 # INT8 codes are exact bf16 integers and the scales are applied in fp32, so
 # the quantization adds no term beyond the dequantized values themselves.
-BUDGET_V, BUDGET_O = 2.0 ** -8 + 2.0 ** -10, 2.0 ** -9
+BUDGET_V, BUDGET_O = 2.0 ** -7 + 2.0 ** -10, 2.0 ** -8
 
 
 @pytest.mark.parametrize("kv_int8", [False, True])
