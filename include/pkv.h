@@ -411,9 +411,9 @@ int pkv_decode_noalloc(const pkv_pool_desc* desc, const void* k_pool, const void
  *   max_q_per_seq: host upper bound of n_b (queries beyond it are not computed)
  *   other arguments as for pkv_decode; workspace >= pkv_workspace_bytes(desc,
  *   n_seqs, num_q_heads, max_q_per_seq, max_seq_len).  On PKV_I8 pools the
- *   MFMA kernel for more than 48 query rows per (sequence, KV head) attends
- *   over bf16(code x scale) keys and values (the same product as the
- *   page's folded scales, with the rounding on the staged vector).
+ *   scales are folded as for pkv_decode ("INT8 cache"): codes enter the
+ *   products as exact bf16 integers, the key scale multiplies the scores and
+ *   the value scale the probabilities; no dequantized key or value is formed.
  * Errors: INVALID_ARG, UNSUPPORTED, BUFFER_TOO_SMALL, DEVICE. */
 int pkv_prefill_append(const pkv_pool_desc* desc, const void* k_pool, const void* v_pool,
                        const void* q, int32_t total_q, const int32_t* cu_q, int32_t n_seqs,
