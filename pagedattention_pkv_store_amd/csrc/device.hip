@@ -1074,10 +1074,10 @@ __global__ __launch_bounds__(kWave, RBW == 1 ? (kI8 ? PKV_DECODE_WAVES_PER_SIMD_
 // ---------------------------------------------------------------------------
 // Paged prefill/append in bf16 for more than 48 query rows per sequence and
 // KV head.
-//  * A workgroup of W waves owns 32 W query rows of one (sequence, KV head)
-//    unit: 8 waves (256 rows) with 128-position tiles, one workgroup per CU;
-//    or, when no context exceeds kPfShortCtx positions, 4 waves (128 rows)
-//    with 64-position tiles, two workgroups per CU.  Rows are (query,
+//  * A workgroup of 8 waves owns 256 query rows of one (sequence, KV head)
+//    unit, with 128-position tiles, one workgroup per CU (when no context
+//    exceeds kPfStreamCtx positions the persistent kernel further below takes
+//    the launch instead).  Rows are (query,
 //    head-in-group) pairs, so every K/V byte it stages serves the whole GQA
 //    group.  Wave w owns rows 32w..32w+31 as two 16-row MFMA blocks and keeps
 //    its own softmax state: no cross-wave combine.
@@ -1118,22 +1118,12 @@ __global__ __launch_bounds__(kWave, RBW == 1 ? (kI8 ? PKV_DECODE_WAVES_PER_SIMD_
 #define PKV_PREFILL_SETPRIO 0
 #endif
 constexpr int kPfRb = PKV_PREFILL_ROW_BLOCKS;   // 16-row MFMA blocks per wave
-// Two workgroup shapes: long contexts take PKV_PREFILL_WAVES waves and
-// PKV_PREFILL_KEYS-position tiles (one workgroup per CU); contexts up to
-// kPfShortCtx take 4 waves and 64-position tiles, two workgroups per CU, so
-// one workgroup's first loads overlap another's compute.
 constexpr int kPfWaves = PKV_PREFILL_WAVES;
-constexpr int kPfShortWaves = 4;
-constexpr int kPfShortKeys = 64;
-#ifndef PKV_PREFILL_SHORT_CTX
-#define PKV_PREFILL_SHORT_CTX 2048
-#endif
-constexpr int kPfShortCtx = PKV_PREFILL_SHORT_CTX;
 #ifndef PKV_PREFILL_KEYS
 #define PKV_PREFILL_KEYS 128
 #endif
 constexpr int kPfKeys = PKV_PREFILL_KEYS;   // positions per staged tile (computed 64 at a time)
-constexpr int kPfMaxRows = 16 * kPfRb * kPfWaves;   // rows of the larger workgroup shape
+constexpr int kPfMaxRows = 16 * kPfRb * kPfWaves;   // rows per workgroup of the tiled kernel
 // Contexts up to kPfStreamCtx positions take the persistent stream kernel
 // (paged_prefill_stream_kernel): kPfStreamWaves waves, kPfStreamKeys-position
 // tiles.
@@ -2625,7 +2615,6 @@ struct Plan {
   int max_q = 0;
   bool decode = false;  // decode path (few rows) vs a tile kernel
   bool prefill = false; // bf16 tiles: paged_prefill_kernel, else paged_attention_kernel
-  bool pf_short = false; // prefill: the 4-wave, 64-position shape
   bool pf_stream = false; // prefill: persistent workgroups over work-item records
   size_t rec_off = 0;     // prefill stream: the records in the workspace
   int64_t n_ids = 0;      // prefill stream: upper bound of the work-item ids
@@ -2684,13 +2673,13 @@ int make_plan(const pkv_pool_desc* d, int n_seqs, int hq, int max_q, int max_seq
     return PKV_OK;
   }
   if (d->dtype == PKV_BF16 || d->dtype == PKV_I8) {
-    // paged_prefill_kernel: 128-row tiles; KV splits only when the units'
-    // tiles alone cannot fill the chip.
+    // paged_prefill_kernel (256-row tiles) or the persistent kernel (contexts
+    // up to kPfStreamCtx); KV splits only when the units' tiles alone cannot
+    // fill the chip.
     p->prefill = true;
     p->pf_stream = max_seq_len <= kPfStreamCtx;
-    p->pf_short = !p->pf_stream && max_seq_len <= kPfShortCtx;
-    const int keys = p->pf_stream ? kPfStreamKeys : p->pf_short ? kPfShortKeys : kPfKeys;
-    p->tile_rows = p->pf_stream ? 16 * kPfRb * kPfStreamWaves : p->pf_short ? 16 * kPfRb * kPfShortWaves : kPfMaxRows;
+    const int keys = p->pf_stream ? kPfStreamKeys : kPfKeys;
+    p->tile_rows = p->pf_stream ? 16 * kPfRb * kPfStreamWaves : kPfMaxRows;
     if (rows > (int64_t{1} << 28)) return fail(PKV_ERR_UNSUPPORTED, std::string(fn) + ": too many queries per sequence");
     const int64_t q_tiles = (rows + p->tile_rows - 1) / p->tile_rows;
     p->q_tiles = static_cast<int>(q_tiles);
@@ -2830,8 +2819,7 @@ int launch_prefill_stream_t(const AttnArgs& a, const Plan& p, char* ws, hipStrea
 template <int D, int kPageMode, bool kI8>
 int launch_prefill_shape(const AttnArgs& a, const Plan& p, char* ws, hipStream_t st) {
   if (p.pf_stream) return launch_prefill_stream_t<D, kPageMode, kPfStreamWaves, kPfStreamKeys, kI8>(a, p, ws, st);
-  return p.pf_short ? launch_prefill_t<D, kPageMode, kPfShortWaves, kPfShortKeys, kI8>(a, p, ws, st)
-                    : launch_prefill_t<D, kPageMode, kPfWaves, kPfKeys, kI8>(a, p, ws, st);
+  return launch_prefill_t<D, kPageMode, kPfWaves, kPfKeys, kI8>(a, p, ws, st);
 }
 
 template <int D, bool kI8>

@@ -150,7 +150,8 @@ class _Pools:
 def test_prefill_int8_variants(D, ps, hq, hkv, ctx, news):
     """Append of several queries per sequence over cached INT8 positions: page
     sizes below, at and above the rows a wave stages per pass, one or several
-    KV splits, both workgroup shapes."""
+    KV splits, contexts within and above 2048 positions (both prefill
+    kernels)."""
     print(f"prefill int8 D={D} ps={ps} hq={hq} hkv={hkv} ctx={ctx} new={news}", flush=True)
     rng = np.random.default_rng(D * 11 + ps)
     lens = [c + n for c, n in zip(ctx, news)]
