@@ -1114,9 +1114,6 @@ __global__ __launch_bounds__(kWave, RBW == 1 ? (kI8 ? PKV_DECODE_WAVES_PER_SIMD_
 #ifndef PKV_PREFILL_WAVES
 #define PKV_PREFILL_WAVES 8
 #endif
-#ifndef PKV_PREFILL_SETPRIO
-#define PKV_PREFILL_SETPRIO 0
-#endif
 constexpr int kPfRb = PKV_PREFILL_ROW_BLOCKS;   // 16-row MFMA blocks per wave
 constexpr int kPfWaves = PKV_PREFILL_WAVES;
 #ifndef PKV_PREFILL_KEYS
@@ -1444,7 +1441,6 @@ __global__ __launch_bounds__(kPfThreads, kPfRb >= 3 ? 1 : 2) void paged_prefill_
       __attribute__((always_inline)) {
     constexpr bool kMask = decltype(mask_tag)::value;
     f32x4 s[4][kPfRb];
-    if constexpr (PKV_PREFILL_SETPRIO) __builtin_amdgcn_s_setprio(1);
 #pragma unroll
     for (int kb = 0; kb < 4; ++kb) {
       bf16x8 kf[kQk];
@@ -1459,7 +1455,6 @@ __global__ __launch_bounds__(kPfThreads, kPfRb >= 3 ? 1 : 2) void paged_prefill_
         s[kb][rb] = acc;
       }
     }
-    if constexpr (PKV_PREFILL_SETPRIO) __builtin_amdgcn_s_setprio(0);
     if constexpr (kI8) scale_scores(s, sk);
     // row maxima, then one (rarely taken) rescale branch for both row blocks
     float muse[kPfRb];
