@@ -607,6 +607,23 @@ typedef __attribute__((address_space(3))) dec_bf16x4 lds_dec_bf16x4;
 #define PKV_DECODE_WAVES_PER_SIMD_I8 2
 #endif
 
+// LDS rows of the decode kernel's staged block.  bf16 (and INT8, staged as
+// bf16): K and V rows padded by 32 bytes; the K operand read of MFMA step c
+// takes dims 32 c + 8 g .. + 7 in lane group g, so it covers 64 contiguous
+// bytes of each of 16 rows, and with this padding neither it nor the
+// transposed V read has bank conflicts (gfx950's LDS has 128 banks).  fp32:
+// K rows padded by 16 bytes, V rows by 32; 512-byte rows stay unpadded.
+template <typename T, int D>
+constexpr int dec_k_row_bytes() {
+  return D * static_cast<int>(sizeof(T)) + (D * static_cast<int>(sizeof(T)) >= 512 ? 0 : (sizeof(T) == 2 ? 32 : 16));
+}
+template <typename T, int D>
+constexpr int dec_v_row_bytes() {
+  return D * static_cast<int>(sizeof(T)) + (D * static_cast<int>(sizeof(T)) >= 512 ? 0 : 32);
+}
+template <typename T, int D>
+constexpr int dec_lds_bytes() { return 16 * (dec_k_row_bytes<T, D>() + dec_v_row_bytes<T, D>()); }
+
 // kPageMode 0: page_size a power of two >= 16 (a 16-position block lies in
 // one page); 1: a power of two < 16; 2: any other page size.  kI8: INT8
 // pages (T is then the bf16 type of the queries and outputs).
@@ -630,12 +647,8 @@ __global__ __launch_bounds__(kWave, RBW == 1 ? (kI8 ? PKV_DECODE_WAVES_PER_SIMD_
   constexpr int kQkMfmas = kDl / Elem<T>::kQkPerMfma;
   constexpr int kDimBlocks = D / 16;
   constexpr int kRowsCap = 16 * RBW;
-  // K rows padded by 16 bytes, V rows by 32 (bf16): the K operand reads (16
-  // rows, one 16-byte column each) and the transposed V reads (8 rows of 32
-  // bytes per half-wave) then hit distinct banks.  512-byte fp32 rows stay
-  // unpadded.
-  constexpr int kKRow = kRowBytes + (kRowBytes >= 512 ? 0 : 16);
-  constexpr int kVRow = kRowBytes + (kRowBytes >= 512 ? 0 : 32);
+  constexpr int kKRow = dec_k_row_bytes<T, D>();
+  constexpr int kVRow = dec_v_row_bytes<T, D>();
   static_assert(kLoads * kWave * kLdB == 16 * kGRowBytes, "block split");
 
   extern __shared__ __align__(16) char smem[];
@@ -751,8 +764,9 @@ __global__ __launch_bounds__(kWave, RBW == 1 ? (kI8 ? PKV_DECODE_WAVES_PER_SIMD_
 
 
   // Query rows (B operand of S^T = K Q^T): row r = (query r / group, head
-  // g * group + r % group); this lane holds row rb * 16 + lrow, dims
-  // lgrp * kDl .. + kDl.  Branch-free: a row without a query reads the
+  // g * group + r % group); this lane holds row rb * 16 + lrow, for MFMA
+  // step c dims 32 c + 8 lgrp .. + 7 (bf16; fp32: dims lgrp * kDl .. + kDl,
+  // the same assignment as K).  Branch-free: a row without a query reads the
   // batch's first query (finite values; its result is never written), and
   // the loaded values are not touched until the unit is computed, so the
   // loads stay in flight behind the K/V loads.
@@ -767,9 +781,10 @@ __global__ __launch_bounds__(kWave, RBW == 1 ? (kI8 ? PKV_DECODE_WAVES_PER_SIMD_
       const int tok_c = ok ? tok : 0;
       const int hh = ok ? g * group + (r - qi * group) : 0;
       const T* src = static_cast<const T*>(args.q) + (static_cast<int64_t>(tok_c) * args.num_q_heads + hh) * D +
-                     lgrp * kDl;
+                     (kEs == 2 ? lgrp * 8 : lgrp * kDl);
 #pragma unroll
-      for (int c = 0; c < kFragChunks; ++c) qv[rb].load16(c, reinterpret_cast<const u32x4*>(src)[c]);
+      for (int c = 0; c < kFragChunks; ++c)
+        qv[rb].load16(c, *reinterpret_cast<const u32x4*>(src + (kEs == 2 ? c * 32 : c * 4)));
     }
   };
 
@@ -884,11 +899,11 @@ __global__ __launch_bounds__(kWave, RBW == 1 ? (kI8 ? PKV_DECODE_WAVES_PER_SIMD_
   // the probabilities entering O^T (not the row sums).
   auto compute_block = [&](int pos0, int kv_end, const QkFrag<T, kDl> (&qv)[RBW], const int (&qpos)[RBW],
                            f32x4 ks, f32x4 vs) __attribute__((always_inline)) {
-    // K fragment: position lrow, dims lgrp * kDl .. + kDl
+    // K fragment: position lrow, the dims this lane's query fragment holds
     QkFrag<T, kDl> kf;
 #pragma unroll
     for (int c = 0; c < kFragChunks; ++c)
-      kf.load16(c, *reinterpret_cast<const u32x4*>(kst + lrow * kKRow + (lgrp * kFragChunks + c) * 16));
+      kf.load16(c, *reinterpret_cast<const u32x4*>(kst + lrow * kKRow + (kEs == 2 ? c * 4 + lgrp : lgrp * kFragChunks + c) * 16));
     f32x4 s[RBW];
 #pragma unroll
     for (int rb = 0; rb < RBW; ++rb) {
@@ -2740,8 +2755,7 @@ void launch_attention_t(const AttnArgs& a, const Plan& p, int n_seqs, int hkv, h
 template <typename T, int D, int RBW, bool kI8>
 void launch_decode_t(const AttnArgs& a, const Plan& p, int n_seqs, char* ws, hipStream_t st) {
   int32_t* seq_blk = reinterpret_cast<int32_t*>(ws + p.items_off);
-  constexpr int kRowB = D * static_cast<int>(sizeof(T));
-  constexpr int kLds = 16 * (2 * kRowB + (kRowB >= 512 ? 0 : 48));
+  constexpr int kLds = dec_lds_bytes<T, D>();
   if (a.ps_shift >= 4)
     paged_decode_kernel<T, D, RBW, 0, kI8><<<p.grid, dim3(kWave), kLds, st>>>(a, seq_blk, a.seq_lens, a.cu_q, a.block_tables);
   else if (a.ps_shift >= 0)
