@@ -1262,6 +1262,119 @@ __device__ __forceinline__ bf16x4 lds_read_tr(const char* p) {
   return __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(p));
 }
 
+// One 64-key sub-tile of the attention core both prefill kernels share, for
+// the wave's kPfRb 16-row blocks: S^T = K Q^T, the online softmax (the
+// reference max of a row is raised only when a tile's max exceeds it by more
+// than 8, log2 units; one rarely taken rescale branch for all row blocks) and
+// O^T += V^T P^T, with the row sums from the same bf16 P.  kt, vt: the
+// sub-tile's staged K and V rows; sk (INT8): its key scales, value scales at
+// sk + kKeys; tb: the position of its first key; k_lane, v_lane: this lane's
+// parts of the LDS operand addresses.
+template <int D, int kKeys, bool kI8, bool kMask>
+__device__ __forceinline__ void pf_sub_tile(const char* kt, const char* vt, const float* sk, int tb, int lgrp,
+                                            int k_lane, int v_lane, float c2, const bf16x8& ones,
+                                            const bf16x8 (&qf)[kPfRb][D / 32], const int (&qpos)[kPfRb],
+                                            f32x4 (&o)[D / 16][kPfRb], f32x4 (&lsum)[kPfRb],
+                                            float (&mc)[kPfRb]) {
+  constexpr int kKRowB = pf_k_row_bytes<D>();
+  constexpr int kVRowB = pf_v_row_bytes<D>();
+  constexpr int kQk = D / 32;
+  constexpr int kDb = D / 16;
+  f32x4 s[4][kPfRb];
+#pragma unroll
+  for (int kb = 0; kb < 4; ++kb) {
+    bf16x8 kf[kQk];
+#pragma unroll
+    for (int kk = 0; kk < kQk; ++kk)
+      kf[kk] = *reinterpret_cast<const bf16x8*>(kt + k_lane + kb * 16 * kKRowB + kk * 64);
+#pragma unroll
+    for (int rb = 0; rb < kPfRb; ++rb) {
+      f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int kk = 0; kk < kQk; ++kk) acc = mfma_qk(kf[kk], qf[rb][kk], acc);
+      s[kb][rb] = acc;
+    }
+  }
+  if constexpr (kI8) {
+    // each score times its key's scale (lane keys kb * 16 + 4 lgrp + i)
+#pragma unroll
+    for (int kb = 0; kb < 4; ++kb) {
+      const f32x4 ksc = *reinterpret_cast<const f32x4*>(sk + kb * 16 + 4 * lgrp);
+#pragma unroll
+      for (int rb = 0; rb < kPfRb; ++rb) s[kb][rb] *= ksc;
+    }
+  }
+  // row maxima, then one (rarely taken) rescale branch for both row blocks
+  float muse[kPfRb];
+  bool up_any = false;
+  float alpha[kPfRb];
+#pragma unroll
+  for (int rb = 0; rb < kPfRb; ++rb) {
+    if constexpr (kMask) {
+#pragma unroll
+      for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          s[kb][rb][i] = (tb + kb * 16 + 4 * lgrp + i <= qpos[rb]) ? s[kb][rb][i] : -INFINITY;
+    }
+    // a linear chain folds into three-input maxima (v_max3_f32)
+    float mx = fmaxf(s[0][rb][0], s[0][rb][1]);
+#pragma unroll
+    for (int e = 2; e < 16; e += 2) mx = fmaxf(fmaxf(mx, s[e >> 2][rb][e & 3]), s[e >> 2][rb][(e & 3) + 1]);
+    mx = max_xor32(max_xor16(mx));
+    const float mxc = mx * c2;
+    const bool up = mxc > mc[rb] + 8.f;
+    const float mnew = up ? mxc : mc[rb];
+    alpha[rb] = up ? fast_exp2(mc[rb] - mnew) : 1.f;
+    mc[rb] = mnew;
+    up_any = up_any || up;
+    muse[rb] = mnew == -INFINITY ? 0.f : mnew;
+  }
+  if (__any(up_any)) {
+#pragma unroll
+    for (int rb = 0; rb < kPfRb; ++rb) {
+      lsum[rb] *= alpha[rb];
+#pragma unroll
+      for (int d = 0; d < kDb; ++d) o[d][rb] *= alpha[rb];
+    }
+  }
+#pragma unroll
+  for (int ks = 0; ks < 2; ++ks) {
+    bf16x8 pk[kPfRb];   // probabilities: row sums (and PV for bf16 pages)
+    bf16x8 pv[kPfRb];   // INT8: probabilities times the value scales, for PV
+    f32x4 vs0, vs1;     // INT8: value scales of this lane's keys
+    if constexpr (kI8) {
+      vs0 = *reinterpret_cast<const f32x4*>(sk + kKeys + 32 * ks + 4 * lgrp);
+      vs1 = *reinterpret_cast<const f32x4*>(sk + kKeys + 32 * ks + 16 + 4 * lgrp);
+    }
+#pragma unroll
+    for (int rb = 0; rb < kPfRb; ++rb) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const float e0 = fast_exp2(fmaf(s[2 * ks][rb][i], c2, -muse[rb]));
+        const float e1 = fast_exp2(fmaf(s[2 * ks + 1][rb][i], c2, -muse[rb]));
+        pk[rb][i] = static_cast<__bf16>(e0);
+        pk[rb][4 + i] = static_cast<__bf16>(e1);
+        if constexpr (kI8) {
+          pv[rb][i] = static_cast<__bf16>(e0 * vs0[i]);
+          pv[rb][4 + i] = static_cast<__bf16>(e1 * vs1[i]);
+        }
+      }
+      lsum[rb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ones, pk[rb], lsum[rb], 0, 0, 0);
+    }
+#pragma unroll
+    for (int d = 0; d < kDb; ++d) {
+      const char* vp = vt + v_lane + 32 * ks * kVRowB + d * 32;
+      const bf16x4 v0 = lds_read_tr(vp);
+      const bf16x4 v1 = lds_read_tr(vp + 16 * kVRowB);
+      const bf16x8 vf = __builtin_shufflevector(v0, v1, 0, 1, 2, 3, 4, 5, 6, 7);
+#pragma unroll
+      for (int rb = 0; rb < kPfRb; ++rb)
+        o[d][rb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf, kI8 ? pv[rb] : pk[rb], o[d][rb], 0, 0, 0);
+    }
+  }
+}
+
 // kPageMode 0: page_size a power of two >= the rows a wave stages per pass
 // (those rows then share one page: scalar lookup); 1: other powers of two;
 // 2: any page size.  kI8: INT8 pages (TileInfer.jl docs, "KV cache", "INT8
@@ -1444,106 +1557,11 @@ __global__ __launch_bounds__(kPfThreads, kPfRb >= 3 ? 1 : 2) void paged_prefill_
   // lane parts of the LDS operand addresses
   const int k_lane = lrow * kKRowB + lgrp * 16;
   const int v_lane = (4 * lgrp + (lrow >> 2)) * kVRowB + ((lrow & 3) >> 1) * 16 + (lrow & 1) * 8;
-  // INT8: each score times its key's scale (lane keys kb * 16 + 4 lgrp + i)
-  auto scale_scores = [&](f32x4 (&s)[4][kPfRb], const float* sk) __attribute__((always_inline)) {
-#pragma unroll
-    for (int kb = 0; kb < 4; ++kb) {
-      const f32x4 ksc = *reinterpret_cast<const f32x4*>(sk + kb * 16 + 4 * lgrp);
-#pragma unroll
-      for (int rb = 0; rb < kPfRb; ++rb) s[kb][rb] *= ksc;
-    }
-  };
-
-  // kt, vt: the sub-tile's staged K and V rows; sk (INT8): its key scales,
-  // value scales at sk + kPfKeys.
+  // kt, vt: the sub-tile's staged K and V rows; sk (INT8): its key scales.
   auto compute = [&](const char* kt, const char* vt, const float* sk, int tb, auto mask_tag)
       __attribute__((always_inline)) {
-    constexpr bool kMask = decltype(mask_tag)::value;
-    f32x4 s[4][kPfRb];
-#pragma unroll
-    for (int kb = 0; kb < 4; ++kb) {
-      bf16x8 kf[kQk];
-#pragma unroll
-      for (int kk = 0; kk < kQk; ++kk)
-        kf[kk] = *reinterpret_cast<const bf16x8*>(kt + k_lane + kb * 16 * kKRowB + kk * 64);
-#pragma unroll
-      for (int rb = 0; rb < kPfRb; ++rb) {
-        f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int kk = 0; kk < kQk; ++kk) acc = mfma_qk(kf[kk], qf[rb][kk], acc);
-        s[kb][rb] = acc;
-      }
-    }
-    if constexpr (kI8) scale_scores(s, sk);
-    // row maxima, then one (rarely taken) rescale branch for both row blocks
-    float muse[kPfRb];
-    bool up_any = false;
-    float alpha[kPfRb];
-#pragma unroll
-    for (int rb = 0; rb < kPfRb; ++rb) {
-      if constexpr (kMask) {
-#pragma unroll
-        for (int kb = 0; kb < 4; ++kb)
-#pragma unroll
-          for (int i = 0; i < 4; ++i)
-            s[kb][rb][i] = (tb + kb * 16 + 4 * lgrp + i <= qpos[rb]) ? s[kb][rb][i] : -INFINITY;
-      }
-      // a linear chain folds into three-input maxima (v_max3_f32)
-      float mx = fmaxf(s[0][rb][0], s[0][rb][1]);
-#pragma unroll
-      for (int e = 2; e < 16; e += 2) mx = fmaxf(fmaxf(mx, s[e >> 2][rb][e & 3]), s[e >> 2][rb][(e & 3) + 1]);
-      mx = max_xor32(max_xor16(mx));
-      const float mxc = mx * c2;
-      const bool up = mxc > mc[rb] + 8.f;
-      const float mnew = up ? mxc : mc[rb];
-      alpha[rb] = up ? fast_exp2(mc[rb] - mnew) : 1.f;
-      mc[rb] = mnew;
-      up_any = up_any || up;
-      muse[rb] = mnew == -INFINITY ? 0.f : mnew;
-    }
-    if (__any(up_any)) {
-#pragma unroll
-      for (int rb = 0; rb < kPfRb; ++rb) {
-        lsum[rb] *= alpha[rb];
-#pragma unroll
-        for (int d = 0; d < kDb; ++d) o[d][rb] *= alpha[rb];
-      }
-    }
-#pragma unroll
-    for (int ks = 0; ks < 2; ++ks) {
-      bf16x8 pk[kPfRb];   // probabilities: row sums (and PV for bf16 pages)
-      bf16x8 pv[kPfRb];   // INT8: probabilities times the value scales, for PV
-      f32x4 vs0, vs1;     // INT8: value scales of this lane's keys
-      if constexpr (kI8) {
-        vs0 = *reinterpret_cast<const f32x4*>(sk + kPfKeys + 32 * ks + 4 * lgrp);
-        vs1 = *reinterpret_cast<const f32x4*>(sk + kPfKeys + 32 * ks + 16 + 4 * lgrp);
-      }
-#pragma unroll
-      for (int rb = 0; rb < kPfRb; ++rb) {
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const float e0 = fast_exp2(fmaf(s[2 * ks][rb][i], c2, -muse[rb]));
-          const float e1 = fast_exp2(fmaf(s[2 * ks + 1][rb][i], c2, -muse[rb]));
-          pk[rb][i] = static_cast<__bf16>(e0);
-          pk[rb][4 + i] = static_cast<__bf16>(e1);
-          if constexpr (kI8) {
-            pv[rb][i] = static_cast<__bf16>(e0 * vs0[i]);
-            pv[rb][4 + i] = static_cast<__bf16>(e1 * vs1[i]);
-          }
-        }
-        lsum[rb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ones, pk[rb], lsum[rb], 0, 0, 0);
-      }
-#pragma unroll
-      for (int d = 0; d < kDb; ++d) {
-        const char* vp = vt + v_lane + 32 * ks * kVRowB + d * 32;
-        const bf16x4 v0 = lds_read_tr(vp);
-        const bf16x4 v1 = lds_read_tr(vp + 16 * kVRowB);
-        const bf16x8 vf = __builtin_shufflevector(v0, v1, 0, 1, 2, 3, 4, 5, 6, 7);
-#pragma unroll
-        for (int rb = 0; rb < kPfRb; ++rb)
-          o[d][rb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf, kI8 ? pv[rb] : pk[rb], o[d][rb], 0, 0, 0);
-      }
-    }
+    pf_sub_tile<D, kPfKeys, kI8, decltype(mask_tag)::value>(kt, vt, sk, tb, lgrp, k_lane, v_lane, c2, ones, qf,
+                                                            qpos, o, lsum, mc);
   };
 
   // ---- main loop over the split's tiles ----
@@ -1906,102 +1924,11 @@ __global__ __launch_bounds__(kPfThreads, kPfThreads >= 512 ? 1 : 2) void paged_p
   const bf16x8 ones = __builtin_bit_cast(bf16x8, u32x4{0x3f803f80u, 0x3f803f80u, 0x3f803f80u, 0x3f803f80u});
   const int k_lane = lrow * kKRowB + lgrp * 16;
   const int v_lane = (4 * lgrp + (lrow >> 2)) * kVRowB + ((lrow & 3) >> 1) * 16 + (lrow & 1) * 8;
-  // INT8: each score times its key's scale (lane keys kb * 16 + 4 lgrp + i)
-  auto scale_scores = [&](f32x4 (&s)[4][kPfRb], const float* sk) __attribute__((always_inline)) {
-#pragma unroll
-    for (int kb = 0; kb < 4; ++kb) {
-      const f32x4 ksc = *reinterpret_cast<const f32x4*>(sk + kb * 16 + 4 * lgrp);
-#pragma unroll
-      for (int rb = 0; rb < kPfRb; ++rb) s[kb][rb] *= ksc;
-    }
-  };
-
+  // kt, vt: the sub-tile's staged K and V rows; sk (INT8): its key scales.
   auto compute = [&](const char* kt, const char* vt, const float* sk, int tb, auto mask_tag)
       __attribute__((always_inline)) {
-    constexpr bool kMask = decltype(mask_tag)::value;
-    f32x4 s[4][kPfRb];
-#pragma unroll
-    for (int kb = 0; kb < 4; ++kb) {
-      bf16x8 kf[kQk];
-#pragma unroll
-      for (int kk = 0; kk < kQk; ++kk)
-        kf[kk] = *reinterpret_cast<const bf16x8*>(kt + k_lane + kb * 16 * kKRowB + kk * 64);
-#pragma unroll
-      for (int rb = 0; rb < kPfRb; ++rb) {
-        f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int kk = 0; kk < kQk; ++kk) acc = mfma_qk(kf[kk], qf[rb][kk], acc);
-        s[kb][rb] = acc;
-      }
-    }
-    if constexpr (kI8) scale_scores(s, sk);
-    float muse[kPfRb];
-    bool up_any = false;
-    float alpha[kPfRb];
-#pragma unroll
-    for (int rb = 0; rb < kPfRb; ++rb) {
-      if constexpr (kMask) {
-#pragma unroll
-        for (int kb = 0; kb < 4; ++kb)
-#pragma unroll
-          for (int i = 0; i < 4; ++i)
-            s[kb][rb][i] = (tb + kb * 16 + 4 * lgrp + i <= qpos[rb]) ? s[kb][rb][i] : -INFINITY;
-      }
-      float mx = fmaxf(s[0][rb][0], s[0][rb][1]);
-#pragma unroll
-      for (int e = 2; e < 16; e += 2) mx = fmaxf(fmaxf(mx, s[e >> 2][rb][e & 3]), s[e >> 2][rb][(e & 3) + 1]);
-      mx = max_xor32(max_xor16(mx));
-      const float mxc = mx * c2;
-      const bool up = mxc > mc[rb] + 8.f;
-      const float mnew = up ? mxc : mc[rb];
-      alpha[rb] = up ? fast_exp2(mc[rb] - mnew) : 1.f;
-      mc[rb] = mnew;
-      up_any = up_any || up;
-      muse[rb] = mnew == -INFINITY ? 0.f : mnew;
-    }
-    if (__any(up_any)) {
-#pragma unroll
-      for (int rb = 0; rb < kPfRb; ++rb) {
-        lsum[rb] *= alpha[rb];
-#pragma unroll
-        for (int d = 0; d < kDb; ++d) o[d][rb] *= alpha[rb];
-      }
-    }
-#pragma unroll
-    for (int ks = 0; ks < 2; ++ks) {
-      bf16x8 pk[kPfRb];   // probabilities: row sums (and PV for bf16 pages)
-      bf16x8 pv[kPfRb];   // INT8: probabilities times the value scales, for PV
-      f32x4 vs0, vs1;     // INT8: value scales of this lane's keys
-      if constexpr (kI8) {
-        vs0 = *reinterpret_cast<const f32x4*>(sk + kPfKeys + 32 * ks + 4 * lgrp);
-        vs1 = *reinterpret_cast<const f32x4*>(sk + kPfKeys + 32 * ks + 16 + 4 * lgrp);
-      }
-#pragma unroll
-      for (int rb = 0; rb < kPfRb; ++rb) {
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const float e0 = fast_exp2(fmaf(s[2 * ks][rb][i], c2, -muse[rb]));
-          const float e1 = fast_exp2(fmaf(s[2 * ks + 1][rb][i], c2, -muse[rb]));
-          pk[rb][i] = static_cast<__bf16>(e0);
-          pk[rb][4 + i] = static_cast<__bf16>(e1);
-          if constexpr (kI8) {
-            pv[rb][i] = static_cast<__bf16>(e0 * vs0[i]);
-            pv[rb][4 + i] = static_cast<__bf16>(e1 * vs1[i]);
-          }
-        }
-        lsum[rb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ones, pk[rb], lsum[rb], 0, 0, 0);
-      }
-#pragma unroll
-      for (int d = 0; d < kDb; ++d) {
-        const char* vp = vt + v_lane + 32 * ks * kVRowB + d * 32;
-        const bf16x4 v0 = lds_read_tr(vp);
-        const bf16x4 v1 = lds_read_tr(vp + 16 * kVRowB);
-        const bf16x8 vf = __builtin_shufflevector(v0, v1, 0, 1, 2, 3, 4, 5, 6, 7);
-#pragma unroll
-        for (int rb = 0; rb < kPfRb; ++rb)
-          o[d][rb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf, kI8 ? pv[rb] : pk[rb], o[d][rb], 0, 0, 0);
-      }
-    }
+    pf_sub_tile<D, kPfKeys, kI8, decltype(mask_tag)::value>(kt, vt, sk, tb, lgrp, k_lane, v_lane, c2, ones, qf,
+                                                            qpos, o, lsum, mc);
   };
 
   auto epilogue = [&](const Item& it) __attribute__((always_inline)) {
