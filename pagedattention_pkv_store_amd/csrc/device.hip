@@ -531,8 +531,9 @@ __global__ __launch_bounds__(kThreads) void paged_attention_kernel(AttnArgs args
 // its range with two blocks in flight, across unit boundaries:
 //  * a block's K and V rows are loaded with fully coalesced 16-byte loads
 //    (each instruction reads 1 KB of whole rows) into registers, two blocks
-//    ahead, then written to the wave's LDS slices (K rows padded by 16 bytes,
-//    V rows by 32, so the operand reads below are free of bank conflicts);
+//    ahead, then written to the wave's LDS slices (rows padded as
+//    dec_k_row_bytes / dec_v_row_bytes state, so the operand reads below are
+//    free of bank conflicts);
 //  * S^T = K Q^T runs on MFMA with the unit's queries held in registers
 //    (loaded when the wave enters the unit); a lane then holds one query row
 //    and 4 positions, so the online softmax takes in-lane work and two
