@@ -16,9 +16,11 @@
 //    (sequence, KV head) units into equal contiguous ranges ("stream-K").
 //    A wave keeps two blocks in flight in registers, stages them in LDS and
 //    runs S^T = K Q^T and O^T += V^T P^T on bf16 MFMA, with each lane
-//    holding one query row, so the online softmax is in-lane work plus two
-//    shuffles.  merge_segments_kernel folds the partial states of units that
-//    a range boundary split, by log-sum-exp.
+//    holding one query row.  A row's reference max is raised only when a
+//    score exceeds it by more than 8 (log2 units), which each lane decides
+//    from its own scores, so the shuffles of a row reduction run only then.
+//    merge_segments_kernel folds the partial states of units that a range
+//    boundary split, by log-sum-exp.
 //  * paged_prefill_kernel (bf16 and INT8 pages, longer appends): a
 //    workgroup owns 32 query rows per wave of one (sequence, KV head) unit
 //    (8 waves, 128-position K/V tiles), stages K/V tiles in two LDS buffers
@@ -536,9 +538,12 @@ __global__ __launch_bounds__(kThreads) void paged_attention_kernel(AttnArgs args
 //    free of bank conflicts);
 //  * S^T = K Q^T runs on MFMA with the unit's queries held in registers
 //    (loaded when the wave enters the unit); a lane then holds one query row
-//    and 4 positions, so the online softmax takes in-lane work and two
-//    wavefront shuffles; O^T += V^T P^T takes V^T straight out of LDS with
-//    ds_read_b64_tr_b16 (bf16);
+//    and 4 positions.  The reference max of a row is raised only when a
+//    score exceeds it by more than 8 (log2 units), so probabilities stay
+//    <= 256; each lane checks its own 4 scores, and the two-shuffle row
+//    reduction and the rescale run only when some lane finds one.
+//    O^T += V^T P^T takes V^T straight out of LDS with ds_read_b64_tr_b16
+//    (bf16);
 //  * loads are never skipped: past the range's end the last block is read
 //    again, past a unit's end rows are masked, so no branch forces a full
 //    wait on outstanding loads.
@@ -883,12 +888,13 @@ __global__ __launch_bounds__(kWave, RBW == 1 ? (kI8 ? PKV_DECODE_WAVES_PER_SIMD_
   };
 
   // ---- online softmax state of the current segment (log2 domain) ----
-  float m_run[RBW], l_part[RBW];
+  float m_run[RBW], m_use[RBW], l_part[RBW];   // m_use: m_run, or 0 while it is -inf
   f32x4 o_acc[RBW][kDimBlocks];
   auto reset_state = [&]() __attribute__((always_inline)) {
 #pragma unroll
     for (int rb = 0; rb < RBW; ++rb) {
       m_run[rb] = -INFINITY;
+      m_use[rb] = 0.f;
       l_part[rb] = 0.f;
 #pragma unroll
       for (int d = 0; d < kDimBlocks; ++d) o_acc[rb][d] = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -915,6 +921,12 @@ __global__ __launch_bounds__(kWave, RBW == 1 ? (kI8 ? PKV_DECODE_WAVES_PER_SIMD_
     f32x4 sc;                          // score scale of each of the lane's positions
 #pragma unroll
     for (int i = 0; i < 4; ++i) sc[i] = kI8 ? ks[i] * args.scale_log2 : args.scale_log2;
+    // The reference max of a row is raised only when a score exceeds it by
+    // more than 8 (log2 units), so probabilities stay <= 256.  A row needs
+    // that exactly when one of its lanes' 4 scores does: the cross-lane
+    // reduction and the rescale sit in one rarely taken branch.
+    float lmx[RBW];
+    bool up_lane = false;
 #pragma unroll
     for (int rb = 0; rb < RBW; ++rb) {
       float mx = -INFINITY;
@@ -925,22 +937,32 @@ __global__ __launch_bounds__(kWave, RBW == 1 ? (kI8 ? PKV_DECODE_WAVES_PER_SIMD_
         s[rb][i] = (pos < kv_end && pos <= qpos[rb]) ? x : -INFINITY;
         mx = fmaxf(mx, s[rb][i]);
       }
-      mx = max_xor32(max_xor16(mx));
-      const float m_new = fmaxf(m_run[rb], mx);
-      const float m_use = m_new == -INFINITY ? 0.f : m_new;
-      const float alpha = fast_exp2(m_run[rb] - m_use);
-      m_run[rb] = m_new;
-      float psum = 0.f;
+      lmx[rb] = mx;
+      up_lane = up_lane || mx > m_run[rb] + 8.f;
+    }
+    if (__any(up_lane)) {
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        s[rb][i] = fast_exp2(s[rb][i] - m_use);
-        psum += s[rb][i];
-      }
-      l_part[rb] = l_part[rb] * alpha + psum;
-      if (__any(alpha != 1.f)) {       // the running max moved for some row
+      for (int rb = 0; rb < RBW; ++rb) {
+        const float mx = max_xor32(max_xor16(lmx[rb]));
+        const bool up = mx > m_run[rb] + 8.f;
+        const float m_new = up ? mx : m_run[rb];
+        const float alpha = up ? fast_exp2(m_run[rb] - m_new) : 1.f;
+        m_run[rb] = m_new;
+        m_use[rb] = m_new == -INFINITY ? 0.f : m_new;
+        l_part[rb] *= alpha;
 #pragma unroll
         for (int d = 0; d < kDimBlocks; ++d) o_acc[rb][d] *= alpha;
       }
+    }
+#pragma unroll
+    for (int rb = 0; rb < RBW; ++rb) {
+      float psum = 0.f;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        s[rb][i] = fast_exp2(s[rb][i] - m_use[rb]);
+        psum += s[rb][i];
+      }
+      l_part[rb] += psum;
     }
     // O^T += V^T P^T
     if constexpr (sizeof(T) == 2) {
@@ -1109,10 +1131,12 @@ __global__ __launch_bounds__(kWave, RBW == 1 ? (kI8 ? PKV_DECODE_WAVES_PER_SIMD_
 //    still.  When a power-of-two page holds all rows a wave stages in one
 //    pass, the page lookup is scalar and each lane adds a 32-bit offset.
 //  * S^T = K Q^T on v_mfma_f32_16x16x32_bf16 with Q held in registers.  A
-//    lane then holds one query row and 4 positions of each 16-key block: the
-//    row max is in-lane work plus two shuffles.  The reference max of a row
-//    is raised only when a tile's max exceeds it by more than 8 (log2
-//    units), so most tiles skip the rescale and probabilities stay <= 256.
+//    lane then holds one query row and 4 positions of each 16-key block.
+//    The reference max of a row is raised only when a tile's max exceeds it
+//    by more than 8 (log2 units), so probabilities stay <= 256.  That holds
+//    for the row exactly when it holds for one of its lanes' 16 scores, so
+//    the two-shuffle row reduction and the rescale sit in one branch that
+//    most tiles skip.
 //  * O^T += V^T P^T on the same MFMA.  P^T is already in B-operand layout
 //    once the MFMA's k index is permuted the same way on both operands
 //    (k-slots 8g..8g+3 <-> keys 4g..4g+3 of the first 16-key block, 8g+4..
@@ -1270,13 +1294,15 @@ __device__ __forceinline__ bf16x4 lds_read_tr(const char* p) {
 // O^T += V^T P^T, with the row sums from the same bf16 P.  kt, vt: the
 // sub-tile's staged K and V rows; sk (INT8): its key scales, value scales at
 // sk + kKeys; tb: the position of its first key; k_lane, v_lane: this lane's
-// parts of the LDS operand addresses.
+// parts of the LDS operand addresses; mc, mu: each row's reference max (log2
+// units) and the same with -inf replaced by 0, the value the exponents
+// subtract.
 template <int D, int kKeys, bool kI8, bool kMask>
 __device__ __forceinline__ void pf_sub_tile(const char* kt, const char* vt, const float* sk, int tb, int lgrp,
                                             int k_lane, int v_lane, float c2, const bf16x8& ones,
                                             const bf16x8 (&qf)[kPfRb][D / 32], const int (&qpos)[kPfRb],
                                             f32x4 (&o)[D / 16][kPfRb], f32x4 (&lsum)[kPfRb],
-                                            float (&mc)[kPfRb]) {
+                                            float (&mc)[kPfRb], float (&mu)[kPfRb]) {
   constexpr int kKRowB = pf_k_row_bytes<D>();
   constexpr int kVRowB = pf_v_row_bytes<D>();
   constexpr int kQk = D / 32;
@@ -1305,10 +1331,12 @@ __device__ __forceinline__ void pf_sub_tile(const char* kt, const char* vt, cons
       for (int rb = 0; rb < kPfRb; ++rb) s[kb][rb] *= ksc;
     }
   }
-  // row maxima, then one (rarely taken) rescale branch for both row blocks
-  float muse[kPfRb];
-  bool up_any = false;
-  float alpha[kPfRb];
+  // Lane-local maxima decide.  A row's maximum exceeds its reference by more
+  // than 8 exactly when one of its lanes' local maxima does (rounding the
+  // product with c2 > 0 is monotone), so the cross-lane reduction, the new
+  // reference and the rescale all sit in one rarely taken branch.
+  float lmx[kPfRb];
+  bool up_lane = false;
 #pragma unroll
   for (int rb = 0; rb < kPfRb; ++rb) {
     if constexpr (kMask) {
@@ -1322,21 +1350,21 @@ __device__ __forceinline__ void pf_sub_tile(const char* kt, const char* vt, cons
     float mx = fmaxf(s[0][rb][0], s[0][rb][1]);
 #pragma unroll
     for (int e = 2; e < 16; e += 2) mx = fmaxf(fmaxf(mx, s[e >> 2][rb][e & 3]), s[e >> 2][rb][(e & 3) + 1]);
-    mx = max_xor32(max_xor16(mx));
-    const float mxc = mx * c2;
-    const bool up = mxc > mc[rb] + 8.f;
-    const float mnew = up ? mxc : mc[rb];
-    alpha[rb] = up ? fast_exp2(mc[rb] - mnew) : 1.f;
-    mc[rb] = mnew;
-    up_any = up_any || up;
-    muse[rb] = mnew == -INFINITY ? 0.f : mnew;
+    lmx[rb] = mx;
+    up_lane = up_lane || mx * c2 > mc[rb] + 8.f;
   }
-  if (__any(up_any)) {
+  if (__any(up_lane)) {
 #pragma unroll
     for (int rb = 0; rb < kPfRb; ++rb) {
-      lsum[rb] *= alpha[rb];
+      const float mxc = max_xor32(max_xor16(lmx[rb])) * c2;
+      const bool up = mxc > mc[rb] + 8.f;
+      const float mnew = up ? mxc : mc[rb];
+      const float alpha = up ? fast_exp2(mc[rb] - mnew) : 1.f;
+      mc[rb] = mnew;
+      mu[rb] = mnew == -INFINITY ? 0.f : mnew;
+      lsum[rb] *= alpha;
 #pragma unroll
-      for (int d = 0; d < kDb; ++d) o[d][rb] *= alpha[rb];
+      for (int d = 0; d < kDb; ++d) o[d][rb] *= alpha;
     }
   }
 #pragma unroll
@@ -1352,8 +1380,8 @@ __device__ __forceinline__ void pf_sub_tile(const char* kt, const char* vt, cons
     for (int rb = 0; rb < kPfRb; ++rb) {
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        const float e0 = fast_exp2(fmaf(s[2 * ks][rb][i], c2, -muse[rb]));
-        const float e1 = fast_exp2(fmaf(s[2 * ks + 1][rb][i], c2, -muse[rb]));
+        const float e0 = fast_exp2(fmaf(s[2 * ks][rb][i], c2, -mu[rb]));
+        const float e1 = fast_exp2(fmaf(s[2 * ks + 1][rb][i], c2, -mu[rb]));
         pk[rb][i] = static_cast<__bf16>(e0);
         pk[rb][4 + i] = static_cast<__bf16>(e1);
         if constexpr (kI8) {
@@ -1546,10 +1574,12 @@ __global__ __launch_bounds__(kPfThreads, kPfRb >= 3 ? 1 : 2) void paged_prefill_
   f32x4 o[kDb][kPfRb];
   f32x4 lsum[kPfRb];
   float mc[kPfRb];                        // reference max per row, log2 units
+  float mu[kPfRb];                        // the same, 0 while it is -inf
 #pragma unroll
   for (int rb = 0; rb < kPfRb; ++rb) {
     lsum[rb] = f32x4{0.f, 0.f, 0.f, 0.f};
     mc[rb] = -INFINITY;
+    mu[rb] = 0.f;
 #pragma unroll
     for (int d = 0; d < kDb; ++d) o[d][rb] = f32x4{0.f, 0.f, 0.f, 0.f};
   }
@@ -1562,7 +1592,7 @@ __global__ __launch_bounds__(kPfThreads, kPfRb >= 3 ? 1 : 2) void paged_prefill_
   auto compute = [&](const char* kt, const char* vt, const float* sk, int tb, auto mask_tag)
       __attribute__((always_inline)) {
     pf_sub_tile<D, kPfKeys, kI8, decltype(mask_tag)::value>(kt, vt, sk, tb, lgrp, k_lane, v_lane, c2, ones, qf,
-                                                            qpos, o, lsum, mc);
+                                                            qpos, o, lsum, mc, mu);
   };
 
   // ---- main loop over the split's tiles ----
@@ -1913,11 +1943,13 @@ __global__ __launch_bounds__(kPfThreads, kPfThreads >= 512 ? 1 : 2) void paged_p
   f32x4 o[kDb][kPfRb];
   f32x4 lsum[kPfRb];
   float mc[kPfRb];
+  float mu[kPfRb];
   auto reset_state = [&]() __attribute__((always_inline)) {
 #pragma unroll
     for (int rb = 0; rb < kPfRb; ++rb) {
       lsum[rb] = f32x4{0.f, 0.f, 0.f, 0.f};
       mc[rb] = -INFINITY;
+      mu[rb] = 0.f;
 #pragma unroll
       for (int d = 0; d < kDb; ++d) o[d][rb] = f32x4{0.f, 0.f, 0.f, 0.f};
     }
@@ -1929,7 +1961,7 @@ __global__ __launch_bounds__(kPfThreads, kPfThreads >= 512 ? 1 : 2) void paged_p
   auto compute = [&](const char* kt, const char* vt, const float* sk, int tb, auto mask_tag)
       __attribute__((always_inline)) {
     pf_sub_tile<D, kPfKeys, kI8, decltype(mask_tag)::value>(kt, vt, sk, tb, lgrp, k_lane, v_lane, c2, ones, qf,
-                                                            qpos, o, lsum, mc);
+                                                            qpos, o, lsum, mc, mu);
   };
 
   auto epilogue = [&](const Item& it) __attribute__((always_inline)) {
