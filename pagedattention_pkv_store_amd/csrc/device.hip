@@ -1302,7 +1302,7 @@ __device__ __forceinline__ void pf_sub_tile(const char* kt, const char* vt, cons
                                             int k_lane, int v_lane, float c2, const bf16x8& ones,
                                             const bf16x8 (&qf)[kPfRb][D / 32], const int (&qpos)[kPfRb],
                                             f32x4 (&o)[D / 16][kPfRb], f32x4 (&lsum)[kPfRb],
-                                            float (&mc)[kPfRb], float (&mu)[kPfRb]) {
+                                            float (&mc)[kPfRb], float (&mu)[kPfRb], float (&mt)[kPfRb]) {
   constexpr int kKRowB = pf_k_row_bytes<D>();
   constexpr int kVRowB = pf_v_row_bytes<D>();
   constexpr int kQk = D / 32;
@@ -1347,21 +1347,22 @@ __device__ __forceinline__ void pf_sub_tile(const char* kt, const char* vt, cons
           s[kb][rb][i] = (tb + kb * 16 + 4 * lgrp + i <= qpos[rb]) ? s[kb][rb][i] : -INFINITY;
     }
     // a linear chain folds into three-input maxima (v_max3_f32)
-    float mx = fmaxf(s[0][rb][0], s[0][rb][1]);
+    float mx = -INFINITY;
 #pragma unroll
-    for (int e = 2; e < 16; e += 2) mx = fmaxf(fmaxf(mx, s[e >> 2][rb][e & 3]), s[e >> 2][rb][(e & 3) + 1]);
+    for (int e = 0; e < 16; e += 2) mx = fmaxf(fmaxf(mx, s[e >> 2][rb][e & 3]), s[e >> 2][rb][(e & 3) + 1]);
     lmx[rb] = mx;
-    up_lane = up_lane || mx * c2 > mc[rb] + 8.f;
+    up_lane = up_lane || mx * c2 > mt[rb];
   }
   if (__any(up_lane)) {
 #pragma unroll
     for (int rb = 0; rb < kPfRb; ++rb) {
       const float mxc = max_xor32(max_xor16(lmx[rb])) * c2;
-      const bool up = mxc > mc[rb] + 8.f;
+      const bool up = mxc > mt[rb];
       const float mnew = up ? mxc : mc[rb];
       const float alpha = up ? fast_exp2(mc[rb] - mnew) : 1.f;
       mc[rb] = mnew;
       mu[rb] = mnew == -INFINITY ? 0.f : mnew;
+      mt[rb] = mnew + 8.f;
       lsum[rb] *= alpha;
 #pragma unroll
       for (int d = 0; d < kDb; ++d) o[d][rb] *= alpha;
@@ -1575,11 +1576,13 @@ __global__ __launch_bounds__(kPfThreads, kPfRb >= 3 ? 1 : 2) void paged_prefill_
   f32x4 lsum[kPfRb];
   float mc[kPfRb];                        // reference max per row, log2 units
   float mu[kPfRb];                        // the same, 0 while it is -inf
+  float mt[kPfRb];                        // the same plus 8: the rescale threshold
 #pragma unroll
   for (int rb = 0; rb < kPfRb; ++rb) {
     lsum[rb] = f32x4{0.f, 0.f, 0.f, 0.f};
     mc[rb] = -INFINITY;
     mu[rb] = 0.f;
+    mt[rb] = -INFINITY;
 #pragma unroll
     for (int d = 0; d < kDb; ++d) o[d][rb] = f32x4{0.f, 0.f, 0.f, 0.f};
   }
@@ -1592,7 +1595,7 @@ __global__ __launch_bounds__(kPfThreads, kPfRb >= 3 ? 1 : 2) void paged_prefill_
   auto compute = [&](const char* kt, const char* vt, const float* sk, int tb, auto mask_tag)
       __attribute__((always_inline)) {
     pf_sub_tile<D, kPfKeys, kI8, decltype(mask_tag)::value>(kt, vt, sk, tb, lgrp, k_lane, v_lane, c2, ones, qf,
-                                                            qpos, o, lsum, mc, mu);
+                                                            qpos, o, lsum, mc, mu, mt);
   };
 
   // ---- main loop over the split's tiles ----
@@ -1944,12 +1947,14 @@ __global__ __launch_bounds__(kPfThreads, kPfThreads >= 512 ? 1 : 2) void paged_p
   f32x4 lsum[kPfRb];
   float mc[kPfRb];
   float mu[kPfRb];
+  float mt[kPfRb];
   auto reset_state = [&]() __attribute__((always_inline)) {
 #pragma unroll
     for (int rb = 0; rb < kPfRb; ++rb) {
       lsum[rb] = f32x4{0.f, 0.f, 0.f, 0.f};
       mc[rb] = -INFINITY;
       mu[rb] = 0.f;
+      mt[rb] = -INFINITY;
 #pragma unroll
       for (int d = 0; d < kDb; ++d) o[d][rb] = f32x4{0.f, 0.f, 0.f, 0.f};
     }
@@ -1961,7 +1966,7 @@ __global__ __launch_bounds__(kPfThreads, kPfThreads >= 512 ? 1 : 2) void paged_p
   auto compute = [&](const char* kt, const char* vt, const float* sk, int tb, auto mask_tag)
       __attribute__((always_inline)) {
     pf_sub_tile<D, kPfKeys, kI8, decltype(mask_tag)::value>(kt, vt, sk, tb, lgrp, k_lane, v_lane, c2, ones, qf,
-                                                            qpos, o, lsum, mc, mu);
+                                                            qpos, o, lsum, mc, mu, mt);
   };
 
   auto epilogue = [&](const Item& it) __attribute__((always_inline)) {
