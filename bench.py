@@ -981,8 +981,9 @@ def main():
         rec["prefill_append"] = prefill_leg(args, torch, pkv, synth, dev)
         if args.int8:
             p8 = prefill_leg(args, torch, pkv, synth, dev, kv_int8=True)
-            p8["workload"] = ("the same prefix-shared prefill on INT8 pages (keys and values staged dequantized, "
-                              "as bf16(code x scale)); bf16 queries and outputs")
+            p8["workload"] = ("the same prefix-shared prefill on INT8 pages (codes staged as exact bf16, key "
+                              "scales applied to the scores, value scales to the probabilities); bf16 queries "
+                              "and outputs")
             p8["roofline"]["kernel"] = "pkv_prefill_append on PKV_I8 pools (prefill_schedule_kernel + paged_prefill_kernel)"
             rec["int8_prefill_append"] = p8
     if args.rewind:
