@@ -203,10 +203,12 @@ __device__ __forceinline__ u32x4 i8x8_to_bf16(uint2 x) {
   return o;
 }
 
-// Streaming load of one K/V load unit, marked non-temporal: the line is not
-// kept for reuse.  For pool reads that touch each byte once this lifts HBM
-// throughput by about a tenth over plain loads (decode: 120.8 -> 107.1 us for
-// the 64-sequence batch, bit-identical outputs).
+// Non-temporal load (16 or 8 bytes): the line is not kept for reuse.  For
+// reads that touch each byte once (the decode's K/V, page copies, the read
+// probe) this lifts HBM throughput by a tenth or more over plain loads
+// (decode: 120.8 -> 107.1 us for the 64-sequence batch).  Kernels that
+// re-read lines from L2 (the prefill's q-tiles) or read one line in two
+// halves (the codec) were slower with it and keep plain loads.
 __device__ __forceinline__ u32x4 ld_stream(const u32x4* p) { return __builtin_nontemporal_load(p); }
 __device__ __forceinline__ uint2 ld_stream(const uint2* p) {
   typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
@@ -2318,7 +2320,9 @@ __global__ __launch_bounds__(kThreads) void store_kv_i8_kernel(
 // head) blocks, so a (source, destination) pair copies one contiguous run per
 // pool.  Grid: x = pair (its page ids are scalar loads), y = a tile of
 // kCopyPer * 256 of the pair's 16-byte chunks (K chunks, then V chunks); each
-// thread issues its kCopyPer loads before its stores.
+// thread issues its kCopyPer loads (non-temporal: 4,096 pairs copy in 88
+// instead of 114 us) before its stores (plain: non-temporal stores were
+// slower).
 constexpr int kCopyPer = PKV_COPY_CHUNKS;
 __global__ __launch_bounds__(kThreads) void copy_pages_kernel(char* __restrict__ k_pool, char* __restrict__ v_pool,
                                                               const int32_t* __restrict__ copies, int32_t page_chunks,
@@ -2335,7 +2339,7 @@ __global__ __launch_bounds__(kThreads) void copy_pages_kernel(char* __restrict__
     if (c >= 2 * page_chunks) continue;
     const bool is_v = c >= page_chunks;
     const char* pool = is_v ? v_pool : k_pool;
-    x[j] = *reinterpret_cast<const u32x4*>(pool + (static_cast<int64_t>(src) * page_chunks + (is_v ? c - page_chunks : c)) * 16);
+    x[j] = ld_stream(reinterpret_cast<const u32x4*>(pool + (static_cast<int64_t>(src) * page_chunks + (is_v ? c - page_chunks : c)) * 16));
   }
 #pragma unroll
   for (int j = 0; j < kCopyPer; ++j) {
@@ -2562,9 +2566,10 @@ __global__ __launch_bounds__(kThreads) void codec_decode_kernel(CodecArgs a, uin
   }
 }
 
-// Streaming read of n16 16-byte chunks: a grid-stride loop, eight loads in
-// flight per thread; workgroup i writes the sum modulo 2^32 of the words it
-// read to sums[i].
+// Streaming read of n16 16-byte chunks: a grid-stride loop, eight
+// non-temporal loads in flight per thread (plain loads reach about a tenth
+// less); workgroup i writes the sum modulo 2^32 of the words it read to
+// sums[i].
 __global__ __launch_bounds__(kThreads) void stream_read_kernel(const u32x4* __restrict__ src, int64_t n16,
                                                                 uint32_t* __restrict__ sums) {
   __shared__ uint32_t s_part[kThreads / kWave];
@@ -2574,7 +2579,7 @@ __global__ __launch_bounds__(kThreads) void stream_read_kernel(const u32x4* __re
   for (; i + 7 * stride < n16; i += 8 * stride) {
     u32x4 v[8];
 #pragma unroll
-    for (int k = 0; k < 8; ++k) v[k] = src[i + k * stride];
+    for (int k = 0; k < 8; ++k) v[k] = ld_stream(src + i + k * stride);
 #pragma unroll
     for (int k = 0; k < 8; ++k) acc += v[k][0] + v[k][1] + v[k][2] + v[k][3];
   }
