@@ -217,8 +217,8 @@ def prefill_leg(args, torch, pkv, synth, dev: str, kv_int8: bool = False) -> dic
 
 
 def read_probe_leg(args, torch, pkv, dev: str) -> dict:
-    """Practical HBM read ceiling: pkv_stream_read (a plain grid-stride
-    streaming read with 16-byte loads, eight in flight per thread) over a
+    """Practical HBM read ceiling: pkv_stream_read (a grid-stride streaming
+    read with non-temporal 16-byte loads, eight in flight per thread) over a
     4 GiB buffer, far beyond the 256 MB Infinity Cache, for a few grid sizes;
     the best is reported beside the 8 TB/s nominal peak."""
     nbytes = 4 << 30

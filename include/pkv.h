@@ -436,8 +436,8 @@ int pkv_validate_tables(const pkv_pool_desc* desc, const int32_t* block_tables, 
  * memory-bound kernels above are compared with.
  *
  * Reads `bytes` (a multiple of 16) of device memory at `buf` (16-byte
- * aligned) once, with coalesced 16-byte loads from a grid-stride loop of
- * n_partials workgroups (1..65535).  Workgroup i writes partial_sums[i] =
+ * aligned) once, with coalesced, non-temporal 16-byte loads from a
+ * grid-stride loop of n_partials workgroups (1..65535).  Workgroup i writes partial_sums[i] =
  * the sum modulo 2^32 of the 32-bit words it read, so the sum of all
  * partials is the sum of every word of the buffer modulo 2^32 (which keeps
  * the loads from being elided and lets a test check that every byte was
