@@ -1,8 +1,9 @@
 """pkv_decode_noalloc (decode with the library's static scratch, for callers
 that cannot allocate) against pkv_decode with a caller workspace: the same
-inputs give bit-identical outputs, on two calls in a row of which the second
-is smaller (the scratch keeps the first call's contents).  A batch whose
-workspace exceeds the static array is refused before anything is enqueued."""
+inputs give bit-identical outputs, on calls in a row of which the second is
+smaller than the first (the scratch keeps the first call's contents) and the
+third, on INT8 pages, larger.  A batch whose workspace exceeds the static
+array is refused before anything is enqueued."""
 
 import ctypes
 
@@ -21,11 +22,11 @@ def _loaded():
     ensure_library()
 
 
-def _decode_both(w, seed):
+def _decode_both(w, seed, kv_int8=False):
     """Store a decode batch, then run pkv_decode (workspace) and
     pkv_decode_noalloc on the same inputs; return both outputs."""
     from gpu_path import DEV, Session, dev_tensor, i32
-    s = Session.open(w)
+    s = Session.open(w, kv_int8=kv_int8)
     seqs = [s.alloc.seq_new() for _ in w.lengths]
     items = []
     for b, seq in enumerate(seqs):
@@ -65,6 +66,12 @@ def test_noalloc_decode_equals_decode_on_two_calls():
     assert need2 < need1
     assert torch.isfinite(ref2.float()).all()
     assert torch.equal(got2, ref2), "call 2: pkv_decode_noalloc differs from pkv_decode"
+    # third call: the 64-sequence batch on INT8 pages (2048 waves: the largest workspace of the three)
+    print("noalloc decode, call 3: 64 sequences on INT8 pages", flush=True)
+    ref3, got3, need3 = _decode_both(w1, 5, kv_int8=True)
+    assert need3 > need1
+    assert torch.isfinite(ref3.float()).all()
+    assert torch.equal(got3, ref3), "call 3: pkv_decode_noalloc differs from pkv_decode on INT8 pages"
 
 
 def test_noalloc_decode_refuses_a_batch_beyond_the_scratch():
