@@ -1338,8 +1338,11 @@ __device__ __forceinline__ bf16x4 lds_read_tr(const char* p) {
 // sk + kKeys; tb: the position of its first key; k_lane, v_lane: this lane's
 // parts of the LDS operand addresses; mc, mu: each row's reference max (log2
 // units) and the same with -inf replaced by 0, the value the exponents
-// subtract.
-template <int D, int kKeys, bool kI8, bool kMask>
+// subtract.  kMask 0: no key is past any row's position; 1: causal mask;
+// 2: causal mask, and every key of the upper 32 is past every row's
+// position, so only the lower 32 are computed (the skipped keys would add
+// exact zeros: the result is the same bit for bit).
+template <int D, int kKeys, bool kI8, int kMask>
 __device__ __forceinline__ void pf_sub_tile(const char* kt, const char* vt, const float* sk, int tb, int lgrp,
                                             int k_lane, int v_lane, float c2, const bf16x8& ones,
                                             const bf16x8 (&qf)[kPfRb][D / 32], const int (&qpos)[kPfRb],
@@ -1349,9 +1352,10 @@ __device__ __forceinline__ void pf_sub_tile(const char* kt, const char* vt, cons
   constexpr int kVRowB = pf_v_row_bytes<D>();
   constexpr int kQk = D / 32;
   constexpr int kDb = D / 16;
+  constexpr int kKb = kMask == 2 ? 2 : 4;   // 16-key blocks computed
   f32x4 s[4][kPfRb];
 #pragma unroll
-  for (int kb = 0; kb < 4; ++kb) {
+  for (int kb = 0; kb < kKb; ++kb) {
     bf16x8 kf[kQk];
 #pragma unroll
     for (int kk = 0; kk < kQk; ++kk)
@@ -1367,7 +1371,7 @@ __device__ __forceinline__ void pf_sub_tile(const char* kt, const char* vt, cons
   if constexpr (kI8) {
     // each score times its key's scale (lane keys kb * 16 + 4 lgrp + i)
 #pragma unroll
-    for (int kb = 0; kb < 4; ++kb) {
+    for (int kb = 0; kb < kKb; ++kb) {
       const f32x4 ksc = *reinterpret_cast<const f32x4*>(sk + kb * 16 + 4 * lgrp);
 #pragma unroll
       for (int rb = 0; rb < kPfRb; ++rb) s[kb][rb] *= ksc;
@@ -1381,9 +1385,9 @@ __device__ __forceinline__ void pf_sub_tile(const char* kt, const char* vt, cons
   bool up_lane = false;
 #pragma unroll
   for (int rb = 0; rb < kPfRb; ++rb) {
-    if constexpr (kMask) {
+    if constexpr (kMask != 0) {
 #pragma unroll
-      for (int kb = 0; kb < 4; ++kb)
+      for (int kb = 0; kb < kKb; ++kb)
 #pragma unroll
         for (int i = 0; i < 4; ++i)
           s[kb][rb][i] = (tb + kb * 16 + 4 * lgrp + i <= qpos[rb]) ? s[kb][rb][i] : -INFINITY;
@@ -1391,7 +1395,7 @@ __device__ __forceinline__ void pf_sub_tile(const char* kt, const char* vt, cons
     // a linear chain folds into three-input maxima (v_max3_f32)
     float mx = -INFINITY;
 #pragma unroll
-    for (int e = 0; e < 16; e += 2) mx = fmaxf(fmaxf(mx, s[e >> 2][rb][e & 3]), s[e >> 2][rb][(e & 3) + 1]);
+    for (int e = 0; e < 4 * kKb; e += 2) mx = fmaxf(fmaxf(mx, s[e >> 2][rb][e & 3]), s[e >> 2][rb][(e & 3) + 1]);
     lmx[rb] = mx;
     up_lane = up_lane || mx * c2 > mt[rb];
   }
@@ -1411,7 +1415,7 @@ __device__ __forceinline__ void pf_sub_tile(const char* kt, const char* vt, cons
     }
   }
 #pragma unroll
-  for (int ks = 0; ks < 2; ++ks) {
+  for (int ks = 0; ks < kKb / 2; ++ks) {
     bf16x8 pk[kPfRb];   // probabilities: row sums (and PV for bf16 pages)
     bf16x8 pv[kPfRb];   // INT8: probabilities times the value scales, for PV
     f32x4 vs0, vs1;     // INT8: value scales of this lane's keys
@@ -1661,9 +1665,9 @@ __global__ __launch_bounds__(kPfThreads, kPfRb >= 3 ? 1 : 2) void paged_prefill_
         const char* vt = smem + (t & 1) * kBufB + kKTileB + sub * 64 * kVRowB;
         const float* sk = reinterpret_cast<const float*>(smem + (t & 1) * kBufB + kKTileB + kPfKeys * kVRowB) + sub * 64;
         if (tb + 63 <= w_qmin)
-          compute(kt, vt, sk, tb, std::integral_constant<bool, false>());
+          compute(kt, vt, sk, tb, std::integral_constant<int, 0>());
         else
-          compute(kt, vt, sk, tb, std::integral_constant<bool, true>());
+          compute(kt, vt, sk, tb, std::integral_constant<int, 1>());
       }
     }
     stage((t + 1) & 1);
@@ -2082,9 +2086,11 @@ __global__ __launch_bounds__(kPfThreads, kPfThreads >= 512 ? 1 : 2) void paged_p
         const char* vt = smem + buf * kBufB + kKTileB + sub * 64 * kVRowB;
         const float* sk = reinterpret_cast<const float*>(smem + buf * kBufB + kKTileB + kPfKeys * kVRowB) + sub * 64;
         if (tb + 63 <= w_qmin)
-          compute(kt, vt, sk, tb, std::integral_constant<bool, false>());
+          compute(kt, vt, sk, tb, std::integral_constant<int, 0>());
+        else if (tb + 32 > w_qmax)
+          compute(kt, vt, sk, tb, std::integral_constant<int, 2>());
         else
-          compute(kt, vt, sk, tb, std::integral_constant<bool, true>());
+          compute(kt, vt, sk, tb, std::integral_constant<int, 1>());
       }
     }
     stage(buf ^ 1);
