@@ -1245,14 +1245,18 @@ constexpr int pf_wave_rows() { return kWave / (D * (kI8 ? 1 : 2) / static_cast<i
 // b = -1 for an item with no work.  One workgroup of kSchedThreads threads,
 // one block per thread per pass: a block's 8 units read their sequence
 // bounds with independent loads before any record is stored, so a pass
-// waits on memory once.
+// waits on memory once.  The prefix over a pass's blocks is taken within
+// each wave (lane shuffles) and then over the 16 wave totals: two barriers
+// per pass.
 constexpr int kSchedThreads = 1024;
 __global__ __launch_bounds__(kSchedThreads) void prefill_schedule_kernel(AttnArgs a, int32_t* row_off,
                                                                          int n_blocks, int tile_rows,
                                                                          int32_t* __restrict__ rec) {
-  __shared__ int s_scan[kSchedThreads];
+  __shared__ int s_wsum[kSchedThreads / kWave];
   __shared__ int s_carry;
   const int tid = threadIdx.x;
+  const int lane = tid & (kWave - 1);
+  const int wave = tid / kWave;
   if (tid == 0) {
     s_carry = 0;
     row_off[0] = 0;
@@ -1278,17 +1282,29 @@ __global__ __launch_bounds__(kSchedThreads) void prefill_schedule_kernel(AttnArg
       if (ok) tiles = max(tiles, (min(q1 - q0, a.max_q) * a.group + tile_rows - 1) / tile_rows);
     }
     const int v = tiles * a.n_splits;
-    s_scan[tid] = v;
-    __syncthreads();
-    for (int off = 1; off < kSchedThreads; off <<= 1) {
-      const int w = tid >= off ? s_scan[tid - off] : 0;
-      __syncthreads();
-      s_scan[tid] += w;
-      __syncthreads();
+    // inclusive scan of v: within each wave, then over the waves' totals
+    int incl = v;
+#pragma unroll
+    for (int off = 1; off < kWave; off <<= 1) {
+      const int w = __shfl_up(incl, off);
+      if (lane >= off) incl += w;
     }
-    if (blk < n_blocks) row_off[blk + 1] = s_carry + s_scan[tid];
+    if (lane == kWave - 1) s_wsum[wave] = incl;
+    __syncthreads();
+    if (wave == 0) {
+      int t = lane < kSchedThreads / kWave ? s_wsum[lane] : 0;
+#pragma unroll
+      for (int off = 1; off < kSchedThreads / kWave; off <<= 1) {
+        const int w = __shfl_up(t, off);
+        if (lane >= off) t += w;
+      }
+      if (lane < kSchedThreads / kWave) s_wsum[lane] = t;
+    }
+    __syncthreads();
+    const int scan = (wave > 0 ? s_wsum[wave - 1] : 0) + incl;
+    if (blk < n_blocks) row_off[blk + 1] = s_carry + scan;
     if (rec && blk < n_blocks) {
-      const int r0 = s_carry + s_scan[tid] - v;
+      const int r0 = s_carry + scan - v;
 #pragma unroll
       for (int slot = 0; slot < 8; ++slot) {
         const int b = sb[slot];
@@ -1313,7 +1329,7 @@ __global__ __launch_bounds__(kSchedThreads) void prefill_schedule_kernel(AttnArg
       }
     }
     __syncthreads();
-    if (tid == kSchedThreads - 1) s_carry += s_scan[tid];
+    if (tid == 0) s_carry += s_wsum[kSchedThreads / kWave - 1];
     __syncthreads();
   }
 }
