@@ -1357,15 +1357,19 @@ __device__ __forceinline__ bf16x4 lds_read_tr(const char* p) {
 // subtract.  kMask 0: no key is past any row's position; 1: causal mask;
 // 2: causal mask, and every key of the upper 32 is past every row's
 // position, so only the lower 32 are computed (the skipped keys would add
-// exact zeros: the result is the same bit for bit).
-template <int D, int kKeys, bool kI8, int kMask>
+// exact zeros: the result is the same bit for bit).  kSwz: rows of D * 2
+// bytes whose 16-byte chunks are XOR-permuted by the row's low 4 bits (the
+// ring layout of the persistent kernel); koff, voff then hold the lane's
+// K and V^T read offsets per MFMA step and per 16-dim block.
+template <int D, int kKeys, bool kI8, int kMask, bool kSwz = false>
 __device__ __forceinline__ void pf_sub_tile(const char* kt, const char* vt, const float* sk, int tb, int lgrp,
                                             int k_lane, int v_lane, float c2, const bf16x8& ones,
                                             const bf16x8 (&qf)[kPfRb][D / 32], const int (&qpos)[kPfRb],
                                             f32x4 (&o)[D / 16][kPfRb], f32x4 (&lsum)[kPfRb],
-                                            float (&mc)[kPfRb], float (&mu)[kPfRb], float (&mt)[kPfRb]) {
-  constexpr int kKRowB = pf_k_row_bytes<D>();
-  constexpr int kVRowB = pf_v_row_bytes<D>();
+                                            float (&mc)[kPfRb], float (&mu)[kPfRb], float (&mt)[kPfRb],
+                                            const int* koff = nullptr, const int* voff = nullptr) {
+  constexpr int kKRowB = kSwz ? D * 2 : pf_k_row_bytes<D>();
+  constexpr int kVRowB = kSwz ? D * 2 : pf_v_row_bytes<D>();
   constexpr int kQk = D / 32;
   constexpr int kDb = D / 16;
   constexpr int kKb = kMask == 2 ? 2 : 4;   // 16-key blocks computed
@@ -1375,7 +1379,7 @@ __device__ __forceinline__ void pf_sub_tile(const char* kt, const char* vt, cons
     bf16x8 kf[kQk];
 #pragma unroll
     for (int kk = 0; kk < kQk; ++kk)
-      kf[kk] = *reinterpret_cast<const bf16x8*>(kt + k_lane + kb * 16 * kKRowB + kk * 64);
+      kf[kk] = *reinterpret_cast<const bf16x8*>(kt + kb * 16 * kKRowB + (kSwz ? koff[kk] : k_lane + kk * 64));
 #pragma unroll
     for (int rb = 0; rb < kPfRb; ++rb) {
       f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -1456,7 +1460,7 @@ __device__ __forceinline__ void pf_sub_tile(const char* kt, const char* vt, cons
     }
 #pragma unroll
     for (int d = 0; d < kDb; ++d) {
-      const char* vp = vt + v_lane + 32 * ks * kVRowB + d * 32;
+      const char* vp = vt + 32 * ks * kVRowB + (kSwz ? voff[d] : v_lane + d * 32);
       const bf16x4 v0 = lds_read_tr(vp);
       const bf16x4 v1 = lds_read_tr(vp + 16 * kVRowB);
       const bf16x8 vf = __builtin_shufflevector(v0, v1, 0, 1, 2, 3, 4, 5, 6, 7);
@@ -1739,15 +1743,27 @@ __global__ __launch_bounds__(kPfThreads, kPfRb >= 3 ? 1 : 2) void paged_prefill_
 // (global_load_lds_dwordx4, issued before the last tile's K/V loads, so the
 // wait that stages that tile also covers them) and into registers at the
 // switch: holding them in registers during the last tile would spill.
+// With bf16 pages and D = 128 the K/V tiles skip the registers as well:
+// they go straight into a ring of three LDS buffers two tiles ahead (the
+// query buffer and the ring fill the CU's 160 KB), one wait and one barrier
+// per tile, and no staging pass.
 // ---------------------------------------------------------------------------
 // 8-wave workgroups (one per CU) take the next item's queries through an
 // LDS buffer; 4-wave workgroups (two per CU, which hide each other's waits)
 // load them into registers at the switch.
 template <int kThreads_>
 constexpr bool pf_stream_q_lds() { return kThreads_ >= 512; }
+// bf16 pages, D = 128, 64-position tiles, 8 waves: the K/V tiles go straight
+// from memory into a ring of three LDS buffers (rows unpadded, their 16-byte
+// chunks XOR-permuted by the row's low 4 bits), loaded two tiles ahead.
+template <int D, int kKeys, int kThreads_, bool kI8>
+constexpr bool pf_stream_ring() { return !kI8 && D == 128 && kKeys == 64 && kThreads_ == 512; }
+template <int D, int kKeys>
+constexpr int pf_ring_buf_bytes() { return 2 * kKeys * D * 2; }
 template <int D, int kKeys, int kThreads_, bool kI8>
 constexpr int pf_stream_lds_bytes() {
-  return pf_lds_bytes<D, kKeys, kI8>() + (pf_stream_q_lds<kThreads_>() ? 16 * kPfRb * (kThreads_ / kWave) * D * 2 : 0);
+  return (pf_stream_ring<D, kKeys, kThreads_, kI8>() ? 3 * pf_ring_buf_bytes<D, kKeys>() : pf_lds_bytes<D, kKeys, kI8>()) +
+         (pf_stream_q_lds<kThreads_>() ? 16 * kPfRb * (kThreads_ / kWave) * D * 2 : 0);
 }
 
 template <int D, int kPageMode, int kPfThreads, int kPfKeys, bool kI8>
@@ -1937,7 +1953,9 @@ __global__ __launch_bounds__(kPfThreads, kPfThreads >= 512 ? 1 : 2) void paged_p
   constexpr int kQcpr = D * 2 / 16;
   constexpr int kQChunks = kPfRows * kQcpr / kPfThreads;
   static_assert(kQChunks * kPfThreads == kPfRows * kQcpr, "query tile split");
-  char* qbuf = smem + 2 * kBufB;
+  constexpr bool kRing = pf_stream_ring<D, kPfKeys, kPfThreads, kI8>();
+  constexpr int kRBufB = pf_ring_buf_bytes<D, kPfKeys>();
+  char* qbuf = smem + (kRing ? 3 * kRBufB : 2 * kBufB);
   auto dma_q = [&](const Item& it) __attribute__((always_inline)) {
 #pragma unroll
     for (int c = 0; c < kQChunks; ++c) {
@@ -2061,6 +2079,154 @@ __global__ __launch_bounds__(kPfThreads, kPfThreads >= 512 ? 1 : 2) void paged_p
       }
     }
   };
+
+  if constexpr (kRing) {
+    // ---- ring: tile t in buffer t % 3, loaded at the top of tile t - 2 ----
+    // Chunk p of staged row r holds the row's chunk p ^ (r & 15): lane
+    // (lrow, lgrp) reads K rows kb * 16 + lrow, chunk (4 kk + lgrp) ^ lrow,
+    // and V^T rows 4 lgrp + (lrow >> 2) (+ 16 / 32 multiples), chunk pair
+    // d ^ (row >> 1 & 7); each group of lanes an LDS read serves then covers
+    // distinct banks.
+    constexpr int kRowB = D * 2;
+    int tc_ring = 0;   // tile of W0 being computed
+    int koff[kQk], voff[kDb];
+#pragma unroll
+    for (int kk = 0; kk < kQk; ++kk) koff[kk] = lrow * kRowB + 16 * ((4 * kk + lgrp) ^ lrow);
+    {
+      const int vr = 4 * lgrp + (lrow >> 2);
+      const int h = (lrow & 3) >> 1;
+#pragma unroll
+      for (int d = 0; d < kDb; ++d) voff[d] = vr * kRowB + 16 * ((2 * d + h) ^ vr) + 8 * (lrow & 1);
+    }
+    // A tile by the fields its loads need (item fields picked by value, so
+    // they stay in scalar registers).
+    struct TileRef {
+      int b, g, k_lo, k_hi, t;
+    };
+    auto tile_ref = [&](int k) __attribute__((always_inline)) {
+      int wh, t;
+      after(tc_ring, k, wh, t);
+      TileRef r;
+      r.b = wh == 0 ? W0.b : (wh == 1 ? W1.b : W2.b);
+      r.g = wh == 0 ? W0.g : (wh == 1 ? W1.g : W2.g);
+      r.k_lo = wh == 0 ? W0.k_lo : (wh == 1 ? W1.k_lo : W2.k_lo);
+      r.k_hi = wh == 0 ? W0.k_hi : (wh == 1 ? W1.k_hi : W2.k_hi);
+      r.t = t;
+      return r;
+    };
+    auto rpos = [&](const TileRef& r, int row) __attribute__((always_inline)) {
+      return min(r.k_lo + r.t * kPfKeys + row, r.k_hi - 1);
+    };
+    auto rfetch = [&](const TileRef& r) __attribute__((always_inline)) {
+      const int64_t brow = static_cast<int64_t>(r.b) * a.bt_stride;
+#pragma unroll
+      for (int c = 0; c < kChunks; ++c) {
+        if constexpr (kPageMode == 0)
+          pg_next2[c] = ((cptr)(a.block_tables))[brow + blk_of(rpos(r, wrow0 + c * kRowsPerPass))];
+        else
+          pg_next2[c] = a.block_tables[brow + blk_of(rpos(r, srow0 + c * kRowsPerPass))];
+      }
+    };
+    // One wave instruction fills 1 KB of LDS at its M0 (lane l at 16 l):
+    // rows wrow0 + c * kRowsPerPass .. + 3, each lane one chunk of its row.
+    auto dma_kv = [&](const TileRef& it, int rb) __attribute__((always_inline)) {
+      char* kb = smem + rb * kRBufB;
+      char* vb = kb + kPfKeys * kRowB;
+#pragma unroll
+      for (int c = 0; c < kChunks; ++c) {
+        const int row = srow0 + c * kRowsPerPass;
+        const int pos = rpos(it, row);
+        const uint32_t page = static_cast<uint32_t>(min(max(pg_next[c], 0), a.num_pages - 1));
+        const uint32_t off = kPageMode <= 1 ? (pos & (ps - 1)) : (pos - blk_of(pos) * ps);
+        const uint32_t voff_g = off * kGRowB + 16 * (spart ^ (row & 15));
+        const uint64_t base = static_cast<uint64_t>(page * hkv + it.g) * head_bytes;
+        const char* ksrc = kbytes + base + voff_g;
+        const char* vsrc = vbytes + base + voff_g;
+        const int mrow = wrow0 + c * kRowsPerPass;
+        const uint32_t mk = static_cast<uint32_t>(
+            reinterpret_cast<uintptr_t>((__attribute__((address_space(3))) char*)(kb + mrow * kRowB)));
+        const uint32_t mv = static_cast<uint32_t>(
+            reinterpret_cast<uintptr_t>((__attribute__((address_space(3))) char*)(vb + mrow * kRowB)));
+        asm volatile("global_load_lds_dwordx4 %0, off" ::"v"(ksrc), "{m0}"(mk) : "memory");
+        asm volatile("global_load_lds_dwordx4 %0, off" ::"v"(vsrc), "{m0}"(mv) : "memory");
+      }
+    };
+    // vmcnt(n), other counters untouched
+    constexpr int kTileDma = 2 * kChunks;   // DMA instructions per wave per tile
+    static_assert(kTileDma < 16, "wait count");
+    auto wait_tile = [&]() __attribute__((always_inline)) {
+      __builtin_amdgcn_s_waitcnt(0x0F70 | kTileDma);   // vmcnt(kTileDma): only the next tile's may be in flight
+    };
+    auto rcompute = [&](const char* kt, const char* vt, int tb, auto mask_tag) __attribute__((always_inline)) {
+      pf_sub_tile<D, kPfKeys, kI8, decltype(mask_tag)::value, true>(kt, vt, nullptr, tb, lgrp, 0, 0, c2, ones, qf, qpos,
+                                                                   o, lsum, mc, mu, mt, koff, voff);
+    };
+
+    // prologue: the first item's queries; tiles 0 and 1 in flight
+    load_q(W0, qf);
+    enter_item(W0);
+    reset_state();
+    {
+      const TileRef r0 = tile_ref(0);
+      rfetch(r0);
+#pragma unroll
+      for (int c = 0; c < kChunks; ++c) pg_next[c] = pg_next2[c];
+      dma_kv(r0, 0);
+      const TileRef r1 = tile_ref(1);
+      rfetch(r1);
+#pragma unroll
+      for (int c = 0; c < kChunks; ++c) pg_next[c] = pg_next2[c];
+      dma_kv(r1, 1);
+    }
+    int rbuf = 0;
+    int& tc = tc_ring;
+    while (true) {
+      const bool last = tc == W0.n_tiles - 1;
+      const TileRef r2 = tile_ref(2);
+      rfetch(r2);        // waited on at the barrier
+      wait_tile();
+      __syncthreads();   // tile tc is in LDS for every wave; tile tc - 1 is no longer read
+      // the next item's queries, into the query buffer read at the switch
+      if (W1.valid && tc == max(W0.n_tiles - 2, 0)) dma_q(W1);
+#pragma unroll
+      for (int c = 0; c < kChunks; ++c) pg_next[c] = pg_next2[c];
+      dma_kv(r2, rbuf == 0 ? 2 : rbuf - 1);
+      {
+        const int tb = W0.k_lo + tc * kPfKeys;
+        if (w_active && tb <= w_qmax) {
+          const char* kt = smem + rbuf * kRBufB;
+          const char* vt = kt + kPfKeys * kRowB;
+          if (tb + 63 <= w_qmin)
+            rcompute(kt, vt, tb, std::integral_constant<int, 0>());
+          else if (tb + 32 > w_qmax)
+            rcompute(kt, vt, tb, std::integral_constant<int, 2>());
+          else
+            rcompute(kt, vt, tb, std::integral_constant<int, 1>());
+        }
+      }
+      rbuf = rbuf == 2 ? 0 : rbuf + 1;
+      if (!last) {
+        ++tc;
+        continue;
+      }
+      if (W0.n_tiles == 1 && W1.valid) {
+        // the queries were requested this iteration, before the tile DMAs
+        wait_tile();
+        __syncthreads();
+      }
+      epilogue(W0);
+      if (!W1.valid) break;
+      W0 = W1;
+      W1 = W2;
+      W2 = take_item();
+      read_q_lds();
+      enter_item(W0);
+      reset_state();
+      tc = 0;
+    }
+    __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0): no DMA outlives the wave
+    return;
+  }
 
   // ---- prologue: the first item's queries, pages and first tile ----
   load_q(W0, qf);
