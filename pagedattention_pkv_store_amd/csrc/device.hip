@@ -1753,16 +1753,20 @@ __global__ __launch_bounds__(kPfThreads, kPfRb >= 3 ? 1 : 2) void paged_prefill_
 // load them into registers at the switch.
 template <int kThreads_>
 constexpr bool pf_stream_q_lds() { return kThreads_ >= 512; }
-// bf16 pages, D = 128, 64-position tiles, 8 waves: the K/V tiles go straight
-// from memory into a ring of three LDS buffers (rows unpadded, their 16-byte
-// chunks XOR-permuted by the row's low 4 bits), loaded two tiles ahead.
-template <int D, int kKeys, int kThreads_, bool kI8>
-constexpr bool pf_stream_ring() { return !kI8 && D == 128 && kKeys == 64 && kThreads_ == 512; }
+// bf16 pages, D = 128, 64-position tiles, 8 waves, page mode 0 (scalar page
+// lookups): the K/V tiles go straight from memory into a ring of three LDS
+// buffers (rows unpadded, their 16-byte chunks XOR-permuted by the row's low
+// 4 bits), loaded two tiles ahead.  Per-lane (vector) page lookups would be
+// waited on together with the tile loads in flight, so the other page modes
+// keep the register-staged double buffer.
+template <int D, int kKeys, int kThreads_, bool kI8, int kPageMode>
+constexpr bool pf_stream_ring() { return !kI8 && D == 128 && kKeys == 64 && kThreads_ == 512 && kPageMode == 0; }
 template <int D, int kKeys>
 constexpr int pf_ring_buf_bytes() { return 2 * kKeys * D * 2; }
-template <int D, int kKeys, int kThreads_, bool kI8>
+template <int D, int kKeys, int kThreads_, bool kI8, int kPageMode>
 constexpr int pf_stream_lds_bytes() {
-  return (pf_stream_ring<D, kKeys, kThreads_, kI8>() ? 3 * pf_ring_buf_bytes<D, kKeys>() : pf_lds_bytes<D, kKeys, kI8>()) +
+  return (pf_stream_ring<D, kKeys, kThreads_, kI8, kPageMode>() ? 3 * pf_ring_buf_bytes<D, kKeys>()
+                                                                : pf_lds_bytes<D, kKeys, kI8>()) +
          (pf_stream_q_lds<kThreads_>() ? 16 * kPfRb * (kThreads_ / kWave) * D * 2 : 0);
 }
 
@@ -1953,7 +1957,7 @@ __global__ __launch_bounds__(kPfThreads, kPfThreads >= 512 ? 1 : 2) void paged_p
   constexpr int kQcpr = D * 2 / 16;
   constexpr int kQChunks = kPfRows * kQcpr / kPfThreads;
   static_assert(kQChunks * kPfThreads == kPfRows * kQcpr, "query tile split");
-  constexpr bool kRing = pf_stream_ring<D, kPfKeys, kPfThreads, kI8>();
+  constexpr bool kRing = pf_stream_ring<D, kPfKeys, kPfThreads, kI8, kPageMode>();
   constexpr int kRBufB = pf_ring_buf_bytes<D, kPfKeys>();
   char* qbuf = smem + (kRing ? 3 * kRBufB : 2 * kBufB);
   auto dma_q = [&](const Item& it) __attribute__((always_inline)) {
@@ -3005,7 +3009,7 @@ int device_cus() {
 
 template <int D, int kPageMode, int kWaves, int kKeys, bool kI8>
 int launch_prefill_stream_t(const AttnArgs& a, const Plan& p, char* ws, hipStream_t st) {
-  constexpr int kLds = pf_stream_lds_bytes<D, kKeys, kWaves * kWave, kI8>();
+  constexpr int kLds = pf_stream_lds_bytes<D, kKeys, kWaves * kWave, kI8, kPageMode>();
   static_assert(kLds <= 160 * 1024, "stream kernel LDS");
   auto* kern = &paged_prefill_stream_kernel<D, kPageMode, kWaves * kWave, kKeys, kI8>;
   static const hipError_t attr = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
