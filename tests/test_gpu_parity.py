@@ -428,6 +428,39 @@ class _Pools:
         self.free_order = np.random.default_rng(seed).permutation(num_pages).astype(np.int32)
 
 
+def test_persistent_prefill_item_mix():
+    """Short appends over short contexts in one launch: 120 sequences with
+    0..200 cached positions and 13..140 new queries (bf16, D 128, page size
+    16, 32 q / 8 KV heads), so the persistent kernel walks some 20 work items
+    per workgroup of 1..6 tiles and 1..3 row tiles each.  Its K/V tiles go
+    through a ring of three LDS buffers that runs on across item boundaries,
+    and an item of one tile takes the next item's queries in the same
+    iteration; every output row is checked against the oracle."""
+    rng = np.random.default_rng(2024)
+    n_seqs, hq, hkv, D, ps = 120, 32, 8, 128, 16
+    ctx = rng.integers(0, 201, n_seqs)
+    ctx[:4] = [0, 1, 63, 64]
+    news = rng.integers(13, 141, n_seqs)
+    news[:4] = [13, 50, 64, 140]
+    lens = [int(c + n) for c, n in zip(ctx, news)]
+    pages = sum(-(-L // ps) for L in lens) + 5
+    s = Session.open(_Pools(synth.BF16, D, ps, hkv, pages, seed=77))
+    seqs = [s.alloc.seq_new() for _ in lens]
+    for b, seq in enumerate(seqs):
+        s.alloc.reserve(seq, lens[b])
+    kv = [synth.normal_values(rng, (2, L, hkv, D), synth.BF16) for L in lens]
+    s.store_many([(seq, 0, kv[b][0], kv[b][1]) for b, seq in enumerate(seqs)], synth.BF16)
+    qs = [synth.normal_values(rng, (int(n), hq, D), synth.BF16) for n in news]
+    print(f"persistent item mix: {n_seqs} seqs, {int(news.sum())} queries", flush=True)
+    out = host_f64(s.append(seqs, [int(n) for n in news], dev_tensor(np.concatenate(qs), synth.BF16)))
+    row = 0
+    for b in range(n_seqs):
+        e = attend(synth.to_f64(qs[b], synth.BF16), synth.to_f64(kv[b][0], synth.BF16),
+                   synth.to_f64(kv[b][1], synth.BF16), s.scale)
+        check_close(out[row:row + int(news[b])], e, synth.BF16, f"item mix seq {b} (ctx {ctx[b]}, new {news[b]})")
+        row += int(news[b])
+
+
 @pytest.mark.parametrize("D,ps,hq,hkv,ctx,news", [
     (128, 16, 32, 8, [2100, 0, 3000], [200, 2300, 1]),     # every wave row count, one sequence all-new
     (128, 64, 8, 8, [5000, 2040], [17, 63]),               # group 1: rows 17 and 63 of one tile
