@@ -1247,8 +1247,12 @@ constexpr int pf_wave_rows() { return kWave / (D * (kI8 ? 1 : 2) / static_cast<i
 // bounds with independent loads before any record is stored, so a pass
 // waits on memory once.  The prefix over a pass's blocks is taken within
 // each wave (lane shuffles) and then over the 16 wave totals: two barriers
-// per pass.
+// per pass.  With several workgroups (the persistent launch) each one takes
+// the whole prefix and stores the records of every gridDim.x-th block, so
+// the record stores (16-byte pieces 256 bytes apart across lanes) are
+// issued from that many CUs; workgroup 0 writes row_off.
 constexpr int kSchedThreads = 1024;
+constexpr int kSchedRecGroups = 16;
 __global__ __launch_bounds__(kSchedThreads) void prefill_schedule_kernel(AttnArgs a, int32_t* row_off,
                                                                          int n_blocks, int tile_rows,
                                                                          int32_t* __restrict__ rec) {
@@ -1257,9 +1261,10 @@ __global__ __launch_bounds__(kSchedThreads) void prefill_schedule_kernel(AttnArg
   const int tid = threadIdx.x;
   const int lane = tid & (kWave - 1);
   const int wave = tid / kWave;
+  const bool off_writer = blockIdx.x == 0;
   if (tid == 0) {
     s_carry = 0;
-    row_off[0] = 0;
+    if (off_writer) row_off[0] = 0;
   }
   __syncthreads();
   const int units = a.n_seqs * a.num_kv_heads;
@@ -1302,8 +1307,8 @@ __global__ __launch_bounds__(kSchedThreads) void prefill_schedule_kernel(AttnArg
     }
     __syncthreads();
     const int scan = (wave > 0 ? s_wsum[wave - 1] : 0) + incl;
-    if (blk < n_blocks) row_off[blk + 1] = s_carry + scan;
-    if (rec && blk < n_blocks) {
+    if (off_writer && blk < n_blocks) row_off[blk + 1] = s_carry + scan;
+    if (rec && blk < n_blocks && blk % static_cast<int>(gridDim.x) == static_cast<int>(blockIdx.x)) {
       const int r0 = s_carry + scan - v;
 #pragma unroll
       for (int slot = 0; slot < 8; ++slot) {
@@ -3017,7 +3022,7 @@ int launch_prefill_stream_t(const AttnArgs& a, const Plan& p, char* ws, hipStrea
   if (attr != hipSuccess) return fail(PKV_ERR_DEVICE, std::string("prefill: LDS attribute: ") + hipGetErrorString(attr));
   int32_t* row_off = reinterpret_cast<int32_t*>(ws + p.items_off);
   int32_t* rec = reinterpret_cast<int32_t*>(ws + p.rec_off);
-  prefill_schedule_kernel<<<1, kSchedThreads, 0, st>>>(a, row_off, p.n_blocks, p.tile_rows, rec);
+  prefill_schedule_kernel<<<kSchedRecGroups, kSchedThreads, 0, st>>>(a, row_off, p.n_blocks, p.tile_rows, rec);
   // one workgroup per CU (two for 4-wave workgroups), a multiple of 8
   const int64_t per_cu = kWaves >= 8 ? 1 : 2;
   int64_t grid = std::min<int64_t>(device_cus() * per_cu, p.n_ids);
