@@ -17,8 +17,8 @@
 //    A wave keeps two blocks in flight in registers (non-temporal loads),
 //    takes K straight from its registers as the MFMA operand (bf16 pages),
 //    stages V in LDS and runs S^T = K Q^T and O^T += V^T P^T on bf16 MFMA,
-//    with each lane holding one query row.  A row's reference max is raised only when a
-//    score exceeds it by more than 8 (log2 units), which each lane decides
+//    with each lane holding one query row.  A row's reference max is raised
+//    only when a score exceeds it by more than 8 (log2 units), which each lane decides
 //    from its own scores, so the shuffles of a row reduction run only then.
 //    merge_segments_kernel folds the partial states of units that a range
 //    boundary split, by log-sum-exp.
@@ -31,7 +31,9 @@
 //    scores and the value scale the probabilities.
 //  * paged_prefill_stream_kernel (the same, when no context exceeds 2048
 //    positions): persistent 8-wave workgroups with 64-position tiles that
-//    run through their work items without draining between them.
+//    run through their work items without draining between them; with bf16
+//    pages, D = 128 and scalar page lookups the K/V tiles go straight from
+//    memory into a ring of three LDS buffers, two tiles ahead.
 //  * paged_attention_kernel: the fp32 prefill (4 waves, 64-position tiles,
 //    v_mfma_f32_16x16x4_f32), kept for the fp32 parity cases.
 //  * copy_pages_kernel, codec_encode_kernel / codec_decode_kernel,
@@ -1748,7 +1750,8 @@ __global__ __launch_bounds__(kPfThreads, kPfRb >= 3 ? 1 : 2) void paged_prefill_
 // (global_load_lds_dwordx4, issued before the last tile's K/V loads, so the
 // wait that stages that tile also covers them) and into registers at the
 // switch: holding them in registers during the last tile would spill.
-// With bf16 pages and D = 128 the K/V tiles skip the registers as well:
+// With bf16 pages, D = 128 and scalar page lookups (page sizes that are
+// powers of two of at least 4) the K/V tiles skip the registers as well:
 // they go straight into a ring of three LDS buffers two tiles ahead (the
 // query buffer and the ring fill the CU's 160 KB), one wait and one barrier
 // per tile, and no staging pass.
