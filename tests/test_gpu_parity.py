@@ -428,30 +428,32 @@ class _Pools:
         self.free_order = np.random.default_rng(seed).permutation(num_pages).astype(np.int32)
 
 
-def test_persistent_prefill_item_mix():
-    """Short appends over short contexts in one launch: 120 sequences with
-    0..200 cached positions and 13..140 new queries (bf16, D 128, page size
-    16, 32 q / 8 KV heads), so the persistent kernel walks some 20 work items
-    per workgroup of 1..6 tiles and 1..3 row tiles each.  Its K/V tiles go
-    through a ring of three LDS buffers that runs on across item boundaries,
-    and an item of one tile takes the next item's queries in the same
-    iteration; every output row is checked against the oracle."""
-    rng = np.random.default_rng(2024)
-    n_seqs, hq, hkv, D, ps = 120, 32, 8, 128, 16
+@pytest.mark.parametrize("ps,n_seqs", [(16, 120), (4, 40), (2, 40), (3, 40)])
+def test_persistent_prefill_item_mix(ps, n_seqs):
+    """Short appends over short contexts in one launch: sequences with 0..200
+    cached positions and 13..140 new queries (bf16, D 128, 32 q / 8 KV
+    heads), so the persistent kernel walks many work items per workgroup of
+    1..6 tiles and 1..3 row tiles each.  With page sizes 16 and 4 its K/V
+    tiles go through a ring of three LDS buffers that runs on across item
+    boundaries, and an item of one tile takes the next item's queries in the
+    same iteration; page sizes 2 and 3 take the register-staged tiles with
+    per-lane page lookups.  Every output row is checked against the oracle."""
+    print(f"persistent item mix: page size {ps}, {n_seqs} sequences", flush=True)
+    rng = np.random.default_rng(2024 + ps)
+    hq, hkv, D = 32, 8, 128
     ctx = rng.integers(0, 201, n_seqs)
     ctx[:4] = [0, 1, 63, 64]
     news = rng.integers(13, 141, n_seqs)
     news[:4] = [13, 50, 64, 140]
     lens = [int(c + n) for c, n in zip(ctx, news)]
     pages = sum(-(-L // ps) for L in lens) + 5
-    s = Session.open(_Pools(synth.BF16, D, ps, hkv, pages, seed=77))
+    s = Session.open(_Pools(synth.BF16, D, ps, hkv, pages, seed=77 + ps))
     seqs = [s.alloc.seq_new() for _ in lens]
     for b, seq in enumerate(seqs):
         s.alloc.reserve(seq, lens[b])
     kv = [synth.normal_values(rng, (2, L, hkv, D), synth.BF16) for L in lens]
     s.store_many([(seq, 0, kv[b][0], kv[b][1]) for b, seq in enumerate(seqs)], synth.BF16)
     qs = [synth.normal_values(rng, (int(n), hq, D), synth.BF16) for n in news]
-    print(f"persistent item mix: {n_seqs} seqs, {int(news.sum())} queries", flush=True)
     out = host_f64(s.append(seqs, [int(n) for n in news], dev_tensor(np.concatenate(qs), synth.BF16)))
     row = 0
     for b in range(n_seqs):
