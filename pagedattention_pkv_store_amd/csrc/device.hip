@@ -1396,12 +1396,17 @@ __device__ __forceinline__ void pf_sub_tile(const char* kt, const char* vt, cons
     }
   }
   if constexpr (kI8) {
-    // each score times its key's scale (lane keys kb * 16 + 4 lgrp + i)
+    // INT8: each score becomes its exponent argument at once, score times
+    // (key scale * c2) minus the row's reference, one fused multiply-add
+    // (lane keys kb * 16 + 4 lgrp + i); the maxima below are taken over
+    // these arguments
 #pragma unroll
     for (int kb = 0; kb < kKb; ++kb) {
-      const f32x4 ksc = *reinterpret_cast<const f32x4*>(sk + kb * 16 + 4 * lgrp);
+      const f32x4 kc = *reinterpret_cast<const f32x4*>(sk + kb * 16 + 4 * lgrp) * c2;
 #pragma unroll
-      for (int rb = 0; rb < kPfRb; ++rb) s[kb][rb] *= ksc;
+      for (int rb = 0; rb < kPfRb; ++rb)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) s[kb][rb][i] = __builtin_fmaf(s[kb][rb][i], kc[i], -mu[rb]);
     }
   }
   // Lane-local maxima decide.  A row's maximum exceeds its reference by more
@@ -1424,17 +1429,28 @@ __device__ __forceinline__ void pf_sub_tile(const char* kt, const char* vt, cons
 #pragma unroll
     for (int e = 0; e < 4 * kKb; e += 2) mx = fmaxf(fmaxf(mx, s[e >> 2][rb][e & 3]), s[e >> 2][rb][(e & 3) + 1]);
     lmx[rb] = mx;
-    up_lane = up_lane || mx * c2 > mt[rb];
+    if constexpr (kI8)
+      up_lane = up_lane || mx > mt[rb] - mu[rb];
+    else
+      up_lane = up_lane || mx * c2 > mt[rb];
   }
   if (__any(up_lane)) {
 #pragma unroll
     for (int rb = 0; rb < kPfRb; ++rb) {
-      const float mxc = max_xor32(max_xor16(lmx[rb])) * c2;
+      const float mxr = max_xor32(max_xor16(lmx[rb]));
+      const float mxc = kI8 ? mxr + mu[rb] : mxr * c2;
       const bool up = mxc > mt[rb];
       const float mnew = up ? mxc : mc[rb];
       const float alpha = up ? fast_exp2(mc[rb] - mnew) : 1.f;
+      const float mu_new = mnew == -INFINITY ? 0.f : mnew;
+      if constexpr (kI8) {
+        // the arguments move with the reference
+        const float shift = mu[rb] - mu_new;
+#pragma unroll
+        for (int kb = 0; kb < kKb; ++kb) s[kb][rb] += shift;
+      }
       mc[rb] = mnew;
-      mu[rb] = mnew == -INFINITY ? 0.f : mnew;
+      mu[rb] = mu_new;
       mt[rb] = mnew + 8.f;
       lsum[rb] *= alpha;
 #pragma unroll
@@ -1454,8 +1470,8 @@ __device__ __forceinline__ void pf_sub_tile(const char* kt, const char* vt, cons
     for (int rb = 0; rb < kPfRb; ++rb) {
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        const float e0 = fast_exp2(fmaf(s[2 * ks][rb][i], c2, -mu[rb]));
-        const float e1 = fast_exp2(fmaf(s[2 * ks + 1][rb][i], c2, -mu[rb]));
+        const float e0 = fast_exp2(kI8 ? s[2 * ks][rb][i] : fmaf(s[2 * ks][rb][i], c2, -mu[rb]));
+        const float e1 = fast_exp2(kI8 ? s[2 * ks + 1][rb][i] : fmaf(s[2 * ks + 1][rb][i], c2, -mu[rb]));
         pk[rb][i] = static_cast<__bf16>(e0);
         pk[rb][4 + i] = static_cast<__bf16>(e1);
         if constexpr (kI8) {
