@@ -463,6 +463,36 @@ def test_persistent_prefill_item_mix(ps, n_seqs):
         row += int(news[b])
 
 
+def test_persistent_prefill_schedule_passes():
+    """1,100 sequences of 8 KV heads: 1,100 blocks of 8 units, so the
+    schedule kernel takes two passes of 1,024 blocks (the row offsets carry
+    from one pass to the next in each of its workgroups, which store the
+    records of every 16th block), and the persistent kernel runs over the
+    records of both passes; every output row is checked against the
+    oracle."""
+    rng = np.random.default_rng(1100)
+    n_seqs, hq, hkv, D, ps = 1100, 32, 8, 128, 16
+    ctx = rng.integers(0, 61, n_seqs)
+    news = rng.integers(13, 21, n_seqs)
+    lens = [int(c + n) for c, n in zip(ctx, news)]
+    pages = sum(-(-L // ps) for L in lens) + 5
+    s = Session.open(_Pools(synth.BF16, D, ps, hkv, pages, seed=1100))
+    seqs = [s.alloc.seq_new() for _ in lens]
+    for b, seq in enumerate(seqs):
+        s.alloc.reserve(seq, lens[b])
+    kv = [synth.normal_values(rng, (2, L, hkv, D), synth.BF16) for L in lens]
+    s.store_many([(seq, 0, kv[b][0], kv[b][1]) for b, seq in enumerate(seqs)], synth.BF16)
+    qs = [synth.normal_values(rng, (int(n), hq, D), synth.BF16) for n in news]
+    print(f"schedule passes: {n_seqs} sequences, {int(news.sum())} queries", flush=True)
+    out = host_f64(s.append(seqs, [int(n) for n in news], dev_tensor(np.concatenate(qs), synth.BF16)))
+    row = 0
+    for b in range(n_seqs):
+        e = attend(synth.to_f64(qs[b], synth.BF16), synth.to_f64(kv[b][0], synth.BF16),
+                   synth.to_f64(kv[b][1], synth.BF16), s.scale)
+        check_close(out[row:row + int(news[b])], e, synth.BF16, f"schedule passes seq {b}")
+        row += int(news[b])
+
+
 @pytest.mark.parametrize("D,ps,hq,hkv,ctx,news", [
     (128, 16, 32, 8, [2100, 0, 3000], [200, 2300, 1]),     # every wave row count, one sequence all-new
     (128, 64, 8, 8, [5000, 2040], [17, 63]),               # group 1: rows 17 and 63 of one tile
